@@ -1,0 +1,200 @@
+/*
+ * mx.h - C ABI of libmx, OCP microscaling (MX) block quantization and
+ * block-scaled GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * Sources the operations follow (cited by page and passage):
+ *   [UE8M0] "EU8M0 FP8 ... domestic compute chips" article (ag-981.com, news 240):
+ *           MX definition paragraph (k = 32, shared E8M0 scale X, Q_i * X ~ V_i),
+ *           glossary entries FP8 / MX / EU8M0 / MXFP8, section 4 of the first part
+ *           (amax-derived exponent, rounding that avoids overflow, saturation),
+ *           second part section 1 (OCP round-down vs. round-up of log2(amax/destmax))
+ *           and section 2 (transposes force re-quantization; dual row/column copies).
+ *   [FP8PY] AstrAI astrai/extension/ops/fp8.py page (commit 432dfec): per-tensor
+ *           quantize / quantize_dual with fused amax, transposed (K-contiguous)
+ *           output, ring-state delayed scaling folded in-kernel by the last block.
+ *   [FAF]   "Format-aware fusion" FP4 article (theaicronicle.com): MXFP4 with a
+ *           fixed-sign 32-point Hadamard transform on the weight-gradient GEMM.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronizes; each call validates its arguments
+ *     on the host, enqueues its kernels on `stream` and returns.
+ *   - Matrices are dense row-major with no padding: element (r, c) of a
+ *     [rows][cols] tensor is at index r * cols + c.
+ *   - Element codes are one byte each for E4M3 / E5M2.  E2M1 (FP4) codes are
+ *     packed two per byte along the contiguous axis, element 2j in the low nibble.
+ *   - Scales are E8M0 bytes: code c in [0, 254] means 2^(c - 127); 255 is NaN.
+ *   - Pointers to tensors read or written with vector accesses (x, q, q_row,
+ *     q_colT, qT, out, a, b) must be 16-byte aligned; scales and scalars have
+ *     no alignment requirement.
+ *   - Errors in the arguments return a status other than MX_OK before anything
+ *     is enqueued.  MX_ERR_LAUNCH reports a failed kernel launch
+ *     (hipGetLastError after the launch).  Device faults surface, as usual in
+ *     HIP, at the caller's next synchronization.
+ *   - Calls are reentrant; calls on different streams may overlap, except that
+ *     two in-flight calls must not share an output or a ring buffer.
+ */
+#ifndef MX_BLOCK_SCALED_QUANTIZE_MX_H
+#define MX_BLOCK_SCALED_QUANTIZE_MX_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element formats ([UE8M0] glossary 'FP8 (E4M3/E5M2)' and 'MXFP8'; values 0 and 1
+ * as the format table of [FP8PY]).  E4M3 is OCP E4M3 (no Inf, NaN = S.1111.111,
+ * max 448); E5M2 is OCP E5M2 (IEEE specials, max 57344); E2M1 has no specials
+ * (max 6). */
+typedef enum { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M1 = 2 } mx_elem_t;
+
+/* Storage type of a floating-point tensor argument. */
+typedef enum { MX_F32 = 0, MX_BF16 = 1, MX_F16 = 2 } mx_dtype_t;
+
+/* Shared-exponent rule for a block with amax > 0 ([UE8M0] second part, section 1):
+ *   MX_SCALE_FLOOR: e = floor(log2 amax) - emax_elem  (OCP v1.0 round-down;
+ *                   elements above the format maximum saturate);
+ *   MX_SCALE_CEIL:  e = smallest integer with amax <= max_elem * 2^e
+ *                   (round-up of log2(amax / destmax); never saturates).
+ * e is clamped to [-127, 127].  A block whose values are all zero gets code 0. */
+typedef enum { MX_SCALE_FLOOR = 0, MX_SCALE_CEIL = 1 } mx_scale_rule_t;
+
+/* Block orientation of an MX quantization ([UE8M0] second part, section 2):
+ *   MX_ROWWISE:   blocks are 32 consecutive elements of a row; codes [rows][cols]
+ *                 (E2M1: [rows][cols/2]), scales [rows][cols/32].
+ *   MX_COLWISE_T: blocks are 32 consecutive rows of a column, stored transposed
+ *                 (the K-contiguous operand layout of an NT GEMM): codes
+ *                 [cols][rows] (E2M1: [cols][rows/2]), scales [cols][rows/32]. */
+typedef enum { MX_ROWWISE = 0, MX_COLWISE_T = 1 } mx_orient_t;
+
+/* Output layout of the per-tensor FP8 quantizer ([FP8PY] quantize(transposed),
+ * quantize_dual): q [rows][cols], qT [cols][rows], or both from one read. */
+typedef enum { FP8_ROW = 0, FP8_TRANSPOSED = 1, FP8_DUAL = 2 } fp8_layout_t;
+
+typedef enum {
+  MX_OK = 0,
+  MX_ERR_NULL = 1,         /* a required pointer is NULL                         */
+  MX_ERR_SHAPE = 2,        /* negative size or a size the layout cannot cut up   */
+  MX_ERR_ALIGN = 3,        /* a vector-accessed pointer is not 16-byte aligned   */
+  MX_ERR_UNSUPPORTED = 4,  /* format / rule / layout / block-size combination    */
+  MX_ERR_LAUNCH = 5,       /* the HIP runtime rejected a kernel launch           */
+  MX_ERR_ARG = 6           /* an out-of-range scalar argument                    */
+} mx_status_t;
+
+/* MX block quantization ([UE8M0] MX definition paragraph and section 4).
+ *
+ * For every block of 32 values V_i (orientation `orient`): amax = max |V_i|,
+ * e = rule(amax) clamped to [-127, 127], scale code = e + 127, and
+ * Q_i = RNE + saturating cast of V_i / 2^e to `fmt`.  A block holding NaN or
+ * +-Inf gets scale code 255 and every Q_i set to the format's NaN with the
+ * input's sign (E2M1, having no NaN: +-6).  -0 keeps its sign.
+ *
+ * hadamard != 0 first replaces each block by H32 * diag(s) * V, where s_j = -1
+ * when bit j of `hadamard_sign_mask` is set and H32 is the unnormalised
+ * Sylvester Hadamard matrix, evaluated as the in-place fast transform with
+ * butterfly spans 1, 2, 4, 8, 16, every addition one FP32 operation ([FAF],
+ * MXFP4 recipe).  A GEMM of two operands transformed with the same mask along
+ * its reduction axis recovers the plain product with alpha = 1/32.
+ *
+ *   x        [rows][cols] input of type `in` (F32, BF16 or F16).
+ *   block    must be 32 (MX defines k = 32 for every element type).
+ *   q, scales  outputs, layouts as described at mx_orient_t.
+ *   amax_out optional (NULL to skip) in/out max-accumulator: on completion it
+ *            holds max(*amax_out, max |x|) over the whole input, NaN entries
+ *            ignored.  It must hold a non-negative FP32 value on entry: 0 gives
+ *            this tensor's amax, an earlier result gives a running amax (e.g.
+ *            over micro-batches).  An empty input leaves it unchanged.
+ * Shapes: MX_ROWWISE needs cols % 32 == 0; MX_COLWISE_T needs rows % 32 == 0
+ * and cols % 8 == 0.  rows == 0 or cols == 0 is valid (nothing is enqueued). */
+mx_status_t mx_quantize(const void* x, mx_dtype_t in, int64_t rows, int64_t cols, int block,
+                        mx_elem_t fmt, mx_scale_rule_t rule, mx_orient_t orient,
+                        int hadamard, uint32_t hadamard_sign_mask,
+                        uint8_t* q, uint8_t* scales, float* amax_out, hipStream_t stream);
+
+/* Dual-orientation MX quantization from a single read of x ([UE8M0] second part,
+ * section 2: training keeps a row-wise and a column-wise quantized copy, and a
+ * transposed MX copy must be re-quantized, not re-laid-out).  Produces exactly
+ * what mx_quantize gives for MX_ROWWISE (q_row, s_row) and for MX_COLWISE_T
+ * (q_colT, s_colT), plus the optional per-tensor amax (a max-accumulator, as
+ * for mx_quantize).
+ * Shapes: rows % 32 == 0 and cols % 32 == 0. */
+mx_status_t mx_quantize_dual(const void* x, mx_dtype_t in, int64_t rows, int64_t cols, int block,
+                             mx_elem_t fmt, mx_scale_rule_t rule,
+                             uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,
+                             float* amax_out, hipStream_t stream);
+
+/* Per-tensor FP8 quantization with delayed scaling ([FP8PY] quantize /
+ * quantize_dual with ring_state, and its commit message).
+ *
+ * ring: caller-owned FP32 device buffer of hist_len + 4 words,
+ *   [hist[0..hist_len-1] | s | m | amax | ticket]
+ * where s is the dequantization scale (x ~ q * s), m = 1/s is the multiplier the
+ * cast uses, and the amax and ticket words are scratch that must read 0 before
+ * the first call (initialise the buffer to hist = 0, s = m = 1, amax = ticket = 0);
+ * every call leaves them 0 again.
+ *
+ * Each call: y = fl32(x * m) with the m the ring holds at launch, q = RNE +
+ * saturating cast of y to `fmt` (Inf saturates, NaN gives NaN), written as
+ * `layout` says; a = max |x| (NaN ignored).  The last workgroup to finish (an
+ * atomic ticket) then sets hist[hist_idx] = a, h = max(hist), and when
+ * 0 < h < Inf publishes s = fl32(fl32(h / fp8_max) / margin), m = fl32(1 / s)
+ * (correctly rounded FP32 divisions); otherwise s and m stay.  The next call on
+ * the same ring sees the new m.  Calls sharing a ring must be ordered (same
+ * stream or explicit events).
+ *
+ *   fmt      MX_E4M3 or MX_E5M2.
+ *   q, qT    outputs: q [rows][cols] for FP8_ROW, qT [cols][rows] for
+ *            FP8_TRANSPOSED, both for FP8_DUAL (the unused one may be NULL).
+ *   hist_len 1..4096; 0 <= hist_idx < hist_len; fp8_max and margin finite > 0.
+ *   amax_out optional: receives a.
+ * Shapes: FP8_ROW needs cols % 8 == 0; FP8_TRANSPOSED and FP8_DUAL need
+ * rows % 32 == 0 and cols % 8 == 0.  An empty input still folds (a = 0). */
+mx_status_t fp8_quantize_delayed(const void* x, mx_dtype_t in, int64_t rows, int64_t cols,
+                                 mx_elem_t fmt, fp8_layout_t layout, uint8_t* q, uint8_t* qT,
+                                 float* ring, int hist_len, int hist_idx, float fp8_max,
+                                 float margin, float* amax_out, hipStream_t stream);
+
+/* MX dequantization ([UE8M0] first part, section 2: decoding an E8M0 scale is an
+ * exponent shift): out = Q_i * 2^(c - 127), computed exactly and rounded once to
+ * `out_dtype` (F32 or BF16; overflow gives +-Inf, scale 255 or a NaN code gives
+ * NaN).  `rows`, `cols` describe the dequantized tensor [rows][cols]:
+ *   MX_ROWWISE:   q [rows][cols] (E2M1 [rows][cols/2]), scales [rows][cols/32];
+ *   MX_COLWISE_T: q [cols][rows] (E2M1 [cols][rows/2]), scales [cols][rows/32],
+ *                 and out is still [rows][cols] (the transpose is undone).
+ * Shapes: the blocked axis must be a multiple of 32. */
+mx_status_t mx_dequantize(const uint8_t* q, const uint8_t* scales, int64_t rows, int64_t cols,
+                          int block, mx_elem_t fmt, mx_orient_t orient, void* out,
+                          mx_dtype_t out_dtype, hipStream_t stream);
+
+/* Block-scaled GEMM ([UE8M0] MX definition paragraph: the matrix unit consumes the
+ * codes and scales of both operands and accumulates in FP32):
+ *   C[m][n] = alpha * sum_k (Qa[m][k] 2^(sa[m][k/32]-127)) (Qb[n][k] 2^(sb[n][k/32]-127))
+ * with FP32 accumulation, then one rounding to `c_dtype` (BF16 or F32).
+ *   a  [M][K] codes (E2M1: [M][K/2]), sa [M][K/32];
+ *   b  [N][K] codes (E2M1: [N][K/2]), sb [N][K/32]  -- B^T, K-contiguous ("NT");
+ *   c  [M][ldc] output rows, ldc >= N; c needs only the alignment of its element
+ *      type (it may be a column slice of a wider matrix).
+ * fmt_a / fmt_b: both FP8 (E4M3 / E5M2, any mix) or both E2M1.
+ * Shapes: K % 32 == 0 (K == 0 writes zeros); any M, N >= 0.
+ * Accumulation: the matrix unit sums the FP8 products of each MFMA step with a
+ * fixed-point alignment of limited width, not with IEEE FP32 rounding after
+ * every product; the FP32 result is within a few 2^-12 of the largest product
+ * of each 64-long K-step of the exact sum. */
+mx_status_t mx_gemm(const uint8_t* a, const uint8_t* sa, mx_elem_t fmt_a,
+                    const uint8_t* b, const uint8_t* sb, mx_elem_t fmt_b,
+                    int64_t M, int64_t N, int64_t K, float alpha,
+                    void* c, mx_dtype_t c_dtype, int64_t ldc, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* mx_status_str(mx_status_t status);
+
+/* Library ABI version (major * 100 + minor). */
+int mx_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MX_BLOCK_SCALED_QUANTIZE_MX_H */

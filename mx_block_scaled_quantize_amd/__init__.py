@@ -1,0 +1,205 @@
+"""Python binding of libmx: OCP MX block quantization and block-scaled GEMM on
+AMD Instinct MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libmx.so`` (built from ``csrc/`` by ``_build.py``); PyTorch only
+provides device memory and the current HIP stream.  There is no CPU fallback:
+importing this module without the built library, or passing host tensors,
+raises.
+
+The functions carry the names of the C entry points declared in
+``include/mx.h`` and return freshly allocated output tensors:
+
+    mx_quantize(x, fmt, rule, orient, hadamard_mask=None, amax=False)
+    mx_quantize_dual(x, fmt, rule, amax=False)
+    fp8_quantize_delayed(x, ring, hist_idx, fmt, layout, fp8_max, margin, amax=False)
+    mx_dequantize(q, scales, rows, cols, fmt, orient, out_dtype)
+    mx_gemm(a, sa, b, sb, fmt_a, fmt_b, alpha, out_dtype)
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmx.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -c 'import __graft_entry__ as g; g.build()' or python mx_block_scaled_quantize_amd/_build.py)")
+
+# torch is imported first so that its HIP runtime is the one libmx binds to
+lib = ctypes.CDLL(LIB_PATH)
+
+# ---------------------------------------------------------------- enums (include/mx.h)
+FMT = {"e4m3": 0, "e5m2": 1, "e2m1": 2}
+DTYPE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+RULE = {"floor": 0, "ceil": 1}
+ORIENT = {"row": 0, "col": 1}
+LAYOUT = {"row": 0, "transposed": 1, "dual": 2}
+STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN", 4: "MX_ERR_UNSUPPORTED",
+          5: "MX_ERR_LAUNCH", 6: "MX_ERR_ARG"}
+DEFAULT_FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+
+_p, _i64, _i32, _u32, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32, ctypes.c_float
+lib.mx_quantize.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _u32, _p, _p, _p, _p]
+lib.mx_quantize_dual.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p]
+lib.fp8_quantize_delayed.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _p, _p, _p, _i32, _i32, _f32, _f32, _p, _p]
+lib.mx_dequantize.argtypes = [_p, _p, _i64, _i64, _i32, _i32, _i32, _p, _i32, _p]
+lib.mx_gemm.argtypes = [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64, _f32, _p, _i32, _i64, _p]
+for _f in (lib.mx_quantize, lib.mx_quantize_dual, lib.fp8_quantize_delayed, lib.mx_dequantize, lib.mx_gemm):
+    _f.restype = ctypes.c_int
+lib.mx_status_str.argtypes = [ctypes.c_int]
+lib.mx_status_str.restype = ctypes.c_char_p
+lib.mx_abi_version.restype = ctypes.c_int
+
+ENTRY_POINTS = ("mx_quantize", "mx_quantize_dual", "fp8_quantize_delayed", "mx_dequantize", "mx_gemm",
+                "mx_status_str", "mx_abi_version")
+
+
+class MXError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(lib.mx_status_str(status).decode())
+
+
+class MXValueError(MXError, ValueError):
+    pass
+
+
+def check(status: int):
+    """Map a status code to an exception (argument errors -> ValueError)."""
+    if status == 0:
+        return
+    if status in (2, 4, 6):
+        raise MXValueError(status)
+    raise MXError(status)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libmx works on device tensors only")
+    return t.data_ptr()
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _lookup(table, key, what):
+    try:
+        return table[key]
+    except KeyError:
+        raise ValueError(f"unsupported {what} {key!r} (expected one of {sorted(table, key=str)})") from None
+
+
+def _amax_buf(amax, device):
+    """amax=True -> a fresh zero accumulator; a float32 device tensor -> itself."""
+    if isinstance(amax, torch.Tensor):
+        if amax.dtype != torch.float32 or amax.numel() < 1:
+            raise ValueError("amax accumulator must be a float32 tensor")
+        return amax
+    return torch.zeros(1, dtype=torch.float32, device=device) if amax else None
+
+
+def _check_2d(x):
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("expected a contiguous 2-D tensor")
+
+
+def code_cols(n: int, fmt: str) -> int:
+    """Bytes per row of n element codes (FP4 packs two per byte)."""
+    return n // 2 if fmt == "e2m1" else n
+
+
+def mx_quantize(x, fmt="e4m3", rule="ceil", orient="row", hadamard_mask=None, amax=False):
+    """MX quantization of a 2-D tensor.  Returns (q, scales) or (q, scales, amax).
+
+    amax=True returns max |x| (NaN ignored) in a fresh 1-element tensor; pass a
+    tensor instead to max-accumulate into it (running amax).
+
+    orient='row': q [R][C] (FP4 [R][C/2]), scales [R][C/32].
+    orient='col': q [C][R] (FP4 [C][R/2]), scales [C][R/32] (transposed storage).
+    """
+    _check_2d(x)
+    R, C = x.shape
+    f = _lookup(FMT, fmt, "format")
+    o = _lookup(ORIENT, orient, "orientation")
+    qr, qc = (R, C) if orient == "row" else (C, R)
+    q = torch.empty((qr, code_cols(qc, fmt)), dtype=torch.uint8, device=x.device)
+    s = torch.empty((qr, qc // 32), dtype=torch.uint8, device=x.device)
+    a = _amax_buf(amax, x.device)
+    check(lib.mx_quantize(_ptr(x), _lookup(DTYPE, x.dtype, "dtype"), R, C, 32, f, _lookup(RULE, rule, "rule"), o,
+                          0 if hadamard_mask is None else 1, 0 if hadamard_mask is None else int(hadamard_mask),
+                          _ptr(q), _ptr(s), _ptr(a), _stream(x)))
+    return (q, s) if a is None else (q, s, a)
+
+
+def mx_quantize_dual(x, fmt="e4m3", rule="ceil", amax=False):
+    """Row-wise and column-wise (transposed) MX copies from one read of x.
+    Returns (q_row, s_row, q_colT, s_colT[, amax])."""
+    _check_2d(x)
+    R, C = x.shape
+    f = _lookup(FMT, fmt, "format")
+    qr = torch.empty((R, code_cols(C, fmt)), dtype=torch.uint8, device=x.device)
+    sr = torch.empty((R, C // 32), dtype=torch.uint8, device=x.device)
+    qc = torch.empty((C, code_cols(R, fmt)), dtype=torch.uint8, device=x.device)
+    sc = torch.empty((C, R // 32), dtype=torch.uint8, device=x.device)
+    a = _amax_buf(amax, x.device)
+    check(lib.mx_quantize_dual(_ptr(x), _lookup(DTYPE, x.dtype, "dtype"), R, C, 32, f, _lookup(RULE, rule, "rule"),
+                               _ptr(qr), _ptr(sr), _ptr(qc), _ptr(sc), _ptr(a), _stream(x)))
+    return (qr, sr, qc, sc) if a is None else (qr, sr, qc, sc, a)
+
+
+def new_ring(hist_len: int, device="cuda") -> torch.Tensor:
+    """A fresh delayed-scaling ring: [hist (zeros) | s = 1 | m = 1 | amax = 0 | ticket = 0]."""
+    r = torch.zeros(hist_len + 4, dtype=torch.float32, device=device)
+    r[hist_len] = 1.0
+    r[hist_len + 1] = 1.0
+    return r
+
+
+def fp8_quantize_delayed(x, ring, hist_idx, fmt="e4m3", layout="transposed", fp8_max=None, margin=1.0, amax=False):
+    """Per-tensor FP8 cast with the ring's multiplier, then the on-device ring
+    fold.  Returns (q or None, qT or None[, amax])."""
+    _check_2d(x)
+    R, C = x.shape
+    if ring.dtype != torch.float32 or ring.dim() != 1 or not ring.is_contiguous():
+        raise ValueError("ring must be a contiguous 1-D float32 tensor")
+    lay = _lookup(LAYOUT, layout, "layout")
+    f = _lookup(FMT, fmt, "format")
+    if fp8_max is None:
+        fp8_max = _lookup(DEFAULT_FP8_MAX, fmt, "FP8 format")
+    q = torch.empty((R, C), dtype=torch.uint8, device=x.device) if layout != "transposed" else None
+    qT = torch.empty((C, R), dtype=torch.uint8, device=x.device) if layout != "row" else None
+    a = torch.empty(1, dtype=torch.float32, device=x.device) if amax else None
+    check(lib.fp8_quantize_delayed(_ptr(x), _lookup(DTYPE, x.dtype, "dtype"), R, C, f, lay, _ptr(q), _ptr(qT),
+                                   _ptr(ring), ring.numel() - 4, int(hist_idx), float(fp8_max), float(margin),
+                                   _ptr(a), _stream(x)))
+    return (q, qT, a) if amax else (q, qT)
+
+
+def mx_dequantize(q, scales, rows, cols, fmt="e4m3", orient="row", out_dtype=torch.float32):
+    """Dequantize MX codes back to a [rows][cols] tensor of out_dtype (float32 or bfloat16)."""
+    out = torch.empty((rows, cols), dtype=out_dtype, device=q.device)
+    check(lib.mx_dequantize(_ptr(q), _ptr(scales), rows, cols, 32, _lookup(FMT, fmt, "format"),
+                            _lookup(ORIENT, orient, "orientation"), _ptr(out), _lookup(DTYPE, out_dtype, "dtype"),
+                            _stream(q)))
+    return out
+
+
+def mx_gemm(a, sa, b, sb, fmt_a="e4m3", fmt_b="e4m3", alpha=1.0, out_dtype=torch.bfloat16, out=None):
+    """C = alpha * deq(A) deq(B)^T with A [M][K], B [N][K] codes (K-contiguous)."""
+    M = a.shape[0]
+    N = b.shape[0]
+    K = a.shape[1] * (2 if fmt_a == "e2m1" else 1)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    check(lib.mx_gemm(_ptr(a), _ptr(sa), _lookup(FMT, fmt_a, "format"), _ptr(b), _ptr(sb),
+                      _lookup(FMT, fmt_b, "format"), M, N, K, float(alpha), _ptr(out),
+                      _lookup(DTYPE, out.dtype, "dtype"), out.stride(0), _stream(a)))
+    return out

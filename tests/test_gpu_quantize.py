@@ -1,0 +1,325 @@
+"""GPU parity of the MX quantizers, the dequantizer and the per-tensor delayed
+quantizer against the CPU oracle: bit-exact codes, scales, amax and ring state
+on the same seeded inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import delayed as odl
+from oracle import formats as F
+from oracle import mx as omx
+from tests.gpu_util import (assert_bytes_equal, assert_float_equal, f32_of_input, host, upload_bf16_bits,
+                            upload_f16_from_f32, upload_f32, upload_u8)
+
+pytestmark = pytest.mark.gpu
+
+mxa = pytest.importorskip("mx_block_scaled_quantize_amd")
+
+FMTS = ["e4m3", "e5m2", "e2m1"]
+RULES = ["floor", "ceil"]
+
+
+def make_input(x32: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "f32":
+        return upload_f32(x32)
+    if dtype == "bf16":
+        return upload_bf16_bits(workloads.to_bf16_bits(x32.astype(np.float64)))
+    return upload_f16_from_f32(x32)
+
+
+def small_inputs():
+    return {
+        "cfg1": workloads.cfg1(96, 256),
+        "wide": workloads.random_tensor((64, 320), 21, "wide"),
+        "rows": workloads.random_tensor((160, 96), 22, "rows"),
+    }
+
+
+# ---------------------------------------------------------------- row-wise
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rule", RULES)
+def test_rowwise_parity(dtype, fmt, rule):
+    for name, x32 in small_inputs().items():
+        x = make_input(x32, dtype)
+        xs = f32_of_input(x)
+        q, s, a = mxa.mx_quantize(x, fmt, rule, "row", amax=True)
+        wq, ws = omx.quantize_rowwise(xs, fmt, rule)
+        assert_bytes_equal(host(s), ws, f"{name} scales")
+        assert_bytes_equal(host(q), wq, f"{name} codes")
+        assert host(a)[0] == omx.tensor_amax(xs)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rule", RULES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rowwise_every_bf16_pattern(fmt, rule, dtype):
+    """Every finite BF16 value, in blocks whose maxima sweep the exponent range,
+    plus hand-picked special blocks (zeros, FP32 subnormals, extremes, NaN, Inf)."""
+    blocks = workloads.all_bf16_blocks()
+    if dtype == "f32":
+        blocks = np.concatenate([blocks, workloads.special_blocks()])
+    x32 = blocks.reshape(-1, 256) if blocks.shape[0] % 8 == 0 else blocks.reshape(-1, 32)
+    x = make_input(x32, dtype)
+    xs = f32_of_input(x)
+    q, s = mxa.mx_quantize(x, fmt, rule, "row")
+    wq, ws = omx.quantize_rowwise(xs, fmt, rule)
+    assert_bytes_equal(host(s), ws, "scales")
+    assert_bytes_equal(host(q), wq, "codes")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_rowwise_hadamard(fmt):
+    mask = 0xA5C3_0F96
+    x32 = workloads.random_tensor((64, 256), 23, "rows")
+    for dtype in ("f32", "bf16"):
+        x = make_input(x32, dtype)
+        xs = f32_of_input(x)
+        q, s = mxa.mx_quantize(x, fmt, "ceil", "row", hadamard_mask=mask)
+        wq, ws = omx.quantize_rowwise(xs, fmt, "ceil", hadamard_mask=mask)
+        assert_bytes_equal(host(s), ws, "scales")
+        assert_bytes_equal(host(q), wq, "codes")
+
+
+# ---------------------------------------------------------------- column-wise / dual
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rule", RULES)
+def test_colwise_parity_ragged(dtype, fmt, rule):
+    # 160 rows (one full and one partial 128-row tile), 200 columns (not a multiple of 32)
+    x32 = workloads.random_tensor((160, 200), 24, "wide")
+    x = make_input(x32, dtype)
+    xs = f32_of_input(x)
+    q, s, a = mxa.mx_quantize(x, fmt, rule, "col", amax=True)
+    wq, ws = omx.quantize_colwise_t(xs, fmt, rule)
+    assert_bytes_equal(host(s), ws, "scales")
+    assert_bytes_equal(host(q), wq, "codes")
+    assert host(a)[0] == omx.tensor_amax(xs)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_colwise_hadamard(fmt):
+    mask = 0x1357_9BDF
+    x32 = workloads.random_tensor((256, 136), 25, "normal")
+    x = make_input(x32, "bf16")
+    xs = f32_of_input(x)
+    q, s = mxa.mx_quantize(x, fmt, "ceil", "col", hadamard_mask=mask)
+    wq, ws = omx.quantize_colwise_t(xs, fmt, "ceil", hadamard_mask=mask)
+    assert_bytes_equal(host(s), ws, "scales")
+    assert_bytes_equal(host(q), wq, "codes")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rule", RULES)
+def test_dual_parity_ragged(dtype, fmt, rule):
+    for shape, seed in (((96, 160), 26), ((288, 416), 27)):
+        x32 = workloads.random_tensor(shape, seed, "rows")
+        x = make_input(x32, dtype)
+        xs = f32_of_input(x)
+        qr, sr, qc, sc, a = mxa.mx_quantize_dual(x, fmt, rule, amax=True)
+        wqr, wsr, wqc, wsc = omx.quantize_dual(xs, fmt, rule)
+        assert_bytes_equal(host(sr), wsr, "row scales")
+        assert_bytes_equal(host(qr), wqr, "row codes")
+        assert_bytes_equal(host(sc), wsc, "col scales")
+        assert_bytes_equal(host(qc), wqc, "col codes")
+        assert host(a)[0] == omx.tensor_amax(xs)
+
+
+def test_dual_matches_single_orientation_calls():
+    """Page-3 style orientation check: the one-read dual output equals the
+    row-wise call and the column-wise call byte for byte."""
+    x = upload_bf16_bits(workloads.cfg2(256, 384))
+    for fmt in FMTS:
+        qr, sr, qc, sc = mxa.mx_quantize_dual(x, fmt, "ceil")
+        q1, s1 = mxa.mx_quantize(x, fmt, "ceil", "row")
+        q2, s2 = mxa.mx_quantize(x, fmt, "ceil", "col")
+        assert torch.equal(qr, q1) and torch.equal(sr, s1)
+        assert torch.equal(qc, q2) and torch.equal(sc, s2)
+
+
+def test_special_blocks_dual():
+    blocks = workloads.special_blocks()          # [18][32]
+    x32 = np.zeros((64, 64), np.float32)
+    x32[:18, :32] = blocks                      # as row blocks
+    x32[32:64, 32:50] = blocks.T                # as column blocks
+    x32[40, :] = np.nan
+    x32[:, 60] = -np.inf
+    x = make_input(x32, "f32")
+    for fmt in FMTS:
+        for rule in RULES:
+            qr, sr, qc, sc, a = mxa.mx_quantize_dual(x, fmt, rule, amax=True)
+            wqr, wsr, wqc, wsc = omx.quantize_dual(x32, fmt, rule)
+            assert_bytes_equal(host(sr), wsr, "row scales")
+            assert_bytes_equal(host(qr), wqr, "row codes")
+            assert_bytes_equal(host(sc), wsc, "col scales")
+            assert_bytes_equal(host(qc), wqc, "col codes")
+            assert host(a)[0] == omx.tensor_amax(x32)
+
+
+def test_empty_inputs():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q, s, a = mxa.mx_quantize(x, "e4m3", "ceil", "row", amax=True)
+    assert q.numel() == 0 and host(a)[0] == 0.0
+    qr, sr, qc, sc, a = mxa.mx_quantize_dual(x, "e4m3", "ceil", amax=True)
+    assert host(a)[0] == 0.0
+    ring = mxa.new_ring(16)
+    out = mxa.fp8_quantize_delayed(x, ring, 3, "e4m3", "transposed", amax=True)
+    assert host(out[2])[0] == 0.0
+    r = host(ring)
+    assert r[16] == 1.0 and r[17] == 1.0 and r[18] == 0.0 and r[19] == 0.0
+
+
+def test_bad_shape_raises_value_error():
+    x = torch.zeros((64, 48), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        mxa.mx_quantize_dual(x)
+
+
+# ---------------------------------------------------------------- dequantize
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("orient", ["row", "col"])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_dequantize_parity(fmt, orient, out_dtype):
+    g = np.random.default_rng(31)
+    rows, cols = 96, 136 if orient == "col" else 160
+    nb = 1 << F.FORMATS[fmt].bits
+    stored_r, stored_c = (rows, cols) if orient == "row" else (cols, rows)
+    codes = g.integers(0, nb, size=(stored_r, stored_c)).astype(np.uint8)
+    scales = g.integers(0, 256, size=(stored_r, stored_c // 32)).astype(np.uint8)
+    scales[0, 0], scales[1, 0], scales[2, 0] = 0, 254, 255
+    packed = omx.pack_fp4(codes) if fmt == "e2m1" else codes
+    out = mxa.mx_dequantize(upload_u8(packed), upload_u8(scales), rows, cols, fmt, orient, out_dtype)
+    kind = "f32" if out_dtype == torch.float32 else "bf16"
+    want = omx.dequantize(packed, scales, fmt, out=kind)
+    if orient == "col":
+        want = np.ascontiguousarray(want.T)
+    got = host(out)
+    if kind == "f32":
+        assert_float_equal(got, want, "dequantized")
+    else:
+        gn = (got & 0x7FFF) > 0x7F80
+        wn = (want & 0x7FFF) > 0x7F80
+        assert np.array_equal(gn, wn)
+        assert_bytes_equal(np.where(gn, 0, got), np.where(wn, 0, want), "dequantized bf16")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_dequantize_roundtrip_cfg1(fmt):
+    x = upload_f32(workloads.cfg1())
+    q, s = mxa.mx_quantize(x, fmt, "floor", "row")
+    d = mxa.mx_dequantize(q, s, 256, 1024, fmt, "row")
+    wq, ws = omx.quantize_rowwise(workloads.cfg1(), fmt, "floor")
+    assert_bytes_equal(host(q), wq, "codes")
+    assert_float_equal(host(d), omx.dequantize(wq, ws, fmt), "roundtrip")
+
+
+# ---------------------------------------------------------------- per-tensor delayed scaling
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("layout", ["row", "transposed", "dual"])
+def test_delayed_sequence_small(fmt, layout):
+    """32 successive steps on one ring (length 16): codes, amax and the whole
+    ring state equal the host fold after every step."""
+    stream = "act" if fmt == "e4m3" else "grad"
+    fp8_max = workloads.CFG3_FP8_MAX[stream]
+    ring = mxa.new_ring(16)
+    oring = odl.Ring(16)
+    for t in range(32):
+        xb = workloads.cfg3_step(stream, t, rows=96, cols=160)
+        x = upload_bf16_bits(xb)
+        xs = workloads.bf16_to_f32(xb)
+        q, qT, a = mxa.fp8_quantize_delayed(x, ring, t % 16, fmt, layout, fp8_max, 1.0, amax=True)
+        wq, wqT, wa = odl.quantize_delayed(xs, fmt, oring, t % 16, fp8_max, 1.0)
+        if q is not None:
+            assert_bytes_equal(host(q), wq, f"step {t} q")
+        if qT is not None:
+            assert_bytes_equal(host(qT), wqT, f"step {t} qT")
+        assert host(a)[0] == wa
+        assert_float_equal(host(ring), oring.as_array(), f"step {t} ring")
+
+
+def test_delayed_resume_from_saved_ring():
+    """The ring is the only state: copying it out at step 16 and resuming from the
+    copy gives the same bytes as the uninterrupted run."""
+    ring = mxa.new_ring(16)
+    outs = []
+    saved = None
+    for t in range(24):
+        if t == 16:
+            saved = ring.clone()
+        x = upload_bf16_bits(workloads.cfg3_step("act", t, rows=64, cols=64))
+        outs.append(mxa.fp8_quantize_delayed(x, ring, t % 16, "e4m3", "transposed")[1])
+    for t in range(16, 24):
+        x = upload_bf16_bits(workloads.cfg3_step("act", t, rows=64, cols=64))
+        qT = mxa.fp8_quantize_delayed(x, saved, t % 16, "e4m3", "transposed")[1]
+        assert torch.equal(qT, outs[t])
+    assert torch.equal(saved, ring)
+
+
+def test_delayed_margin_and_nonfinite():
+    ring = mxa.new_ring(4)
+    oring = odl.Ring(4)
+    x32 = workloads.random_tensor((64, 64), 41, "normal") * 50
+    x32[5, 5] = np.inf
+    x32[6, 6] = np.nan
+    for t, margin in enumerate([2.0, 0.5, 1.0]):
+        y = x32 if t != 1 else np.zeros_like(x32)
+        x = upload_f32(y)
+        q, qT = mxa.fp8_quantize_delayed(x, ring, t, "e5m2", "dual", 57344.0, margin)
+        wq, wqT, _ = odl.quantize_delayed(y, "e5m2", oring, t, 57344.0, margin)
+        assert_bytes_equal(host(q), wq, "q")
+        assert_bytes_equal(host(qT), wqT, "qT")
+        assert_float_equal(host(ring), oring.as_array(), "ring")
+
+
+# ---------------------------------------------------------------- full-size workloads (sampled)
+
+def test_cfg2_dual_full_size_sampled():
+    """BF16 8192 x 4096, E4M3, round-up rule, dual + amax, in the bench's launch
+    configuration; the oracle checks 64 sampled rows and 4 sampled 32-row strips."""
+    xb = workloads.cfg2()
+    x = upload_bf16_bits(xb)
+    qr, sr, qc, sc, a = mxa.mx_quantize_dual(x, "e4m3", "ceil", amax=True)
+    g = np.random.default_rng(5)
+    rows = np.sort(g.choice(8192, size=64, replace=False))
+    xs = workloads.bf16_to_f32(xb[rows])
+    wq, ws = omx.quantize_rowwise(xs, "e4m3", "ceil")
+    assert_bytes_equal(host(qr)[rows], wq, "row codes")
+    assert_bytes_equal(host(sr)[rows], ws, "row scales")
+    qc_h, sc_h = host(qc), host(sc)
+    for strip in g.choice(256, size=4, replace=False):
+        xs = workloads.bf16_to_f32(xb[32 * strip:32 * strip + 32])
+        wq, ws = omx.quantize_colwise_t(xs, "e4m3", "ceil")
+        assert_bytes_equal(qc_h[:, 32 * strip:32 * strip + 32], wq, "col codes")
+        assert_bytes_equal(sc_h[:, strip:strip + 1], ws, "col scales")
+    assert host(a)[0] == omx.tensor_amax(workloads.bf16_to_f32(xb))
+    # zero blocks of the recipe come out as scale code 0
+    assert (host(sr) == 0).sum() >= 16 and (sc_h == 0).sum() >= 16
+
+
+def test_cfg3_delayed_full_size_first_steps():
+    """BF16 8192 x 4096 delayed scaling, both streams, 3 steps each: ring state
+    exact, sampled transposed codes exact."""
+    g = np.random.default_rng(6)
+    for stream, fmt in (("act", "e4m3"), ("grad", "e5m2")):
+        fp8_max = workloads.CFG3_FP8_MAX[stream]
+        ring = mxa.new_ring(16)
+        oring = odl.Ring(16)
+        for t in range(3):
+            xb = workloads.cfg3_step(stream, t)
+            x = upload_bf16_bits(xb)
+            m_before = np.float32(oring.m)
+            _, qT, a = mxa.fp8_quantize_delayed(x, ring, t % 16, fmt, "transposed", fp8_max, 1.0, amax=True)
+            xs_all = workloads.bf16_to_f32(xb)
+            oring.fold(omx.tensor_amax(xs_all), t % 16, fp8_max, 1.0)
+            assert host(a)[0] == omx.tensor_amax(xs_all)
+            assert_float_equal(host(ring), oring.as_array(), f"{stream} step {t} ring")
+            cols = np.sort(g.choice(4096, size=16, replace=False))
+            want = odl.cast_per_tensor(xs_all[:, cols], m_before, fmt).T
+            assert_bytes_equal(host(qT)[cols], want, f"{stream} step {t} qT")
