@@ -1,0 +1,287 @@
+"""Benchmark of the MX quantization hot path on one MI355X.
+
+Prints ONE JSON line.  The headline workload is the dual-orientation MXFP8
+quantization of a BF16 8192 x 4096 activation (hidden size 4096, sequence 8192):
+E4M3 codes along rows and along columns from one read, k = 32 blocks, the
+overflow-safe round-up scale rule and the fused per-tensor amax.  A step is one
+call of ``mx_quantize_dual`` on a fresh input buffer (8 buffer sets of 130 MiB
+rotate, so the 256 MiB last-level cache cannot serve a step from the previous
+one); inputs are resident in HBM before the timed region.
+
+``value`` = algorithmic bytes per step (input read + codes, scales and amax
+written) x steps / wall time of the timed region.  ``roofline.achieved`` = the
+same bytes / the kernel's own average duration (HIP events recorded around each
+launch on the stream the kernel runs on).  The MXFP8 GEMM (8192 x 4096 x 14336)
+and the other workloads are reported under ``gemm`` and ``extra``.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline] [--no-extra]
+       python bench.py --mode dual|gemm|copy ...   (one kernel only, for profiler passes;
+                                                    'copy' is a plain 256 MiB device copy
+                                                    used to calibrate the byte counters)
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0         # dense FP8 / MXFP8 MFMA
+FP4_PEAK_TFLOPS = 10100.0        # dense MXFP4 MFMA
+METRIC = "MX quantize GB/s (% HBM peak); MXFP8 GEMM TFLOP/s (% FP8 MFMA peak)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tile_kernel_dual_bf16_8192x4096_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("quantize.hip", "mx_device.hpp"):
+        with open(os.path.join(ROOT, "mx_block_scaled_quantize_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per dual-quantize launch from the committed rocprofv3 counter
+    summary, or None if absent or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("traffic_bytes_per_launch:"):
+            vals["bytes"] = float(line.split(":")[1])
+        if line.startswith("kernel_source_hash:"):
+            vals["hash"] = line.split(":")[1].strip()
+    if vals.get("hash") != kernel_source_hash() or "bytes" not in vals:
+        return None
+    return vals["bytes"]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--mode", choices=["full", "dual", "gemm", "copy"], default="full")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the quantizers and the GEMM run on a single "
+              "MI355X here (multi-GPU sharding is described, not built); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mx_block_scaled_quantize_amd as mxa
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lib = mxa.lib
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def up_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.mode == "copy":
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        t = time_calls(lambda: dst.copy_(src), args.steps, args.warmup, stream, torch)
+        print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "us": round(t * 1e6, 2),
+                          "GB/s": round(2 * n / t / 1e9, 1)}), flush=True)
+        return
+    if args.mode == "gemm":
+        print(json.dumps({"mode": "gemm", "gemm": bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np,
+                                                             torch, args.steps)}), flush=True)
+        return
+
+    # ------------------------------------------------------------------ headline: dual quantize
+    R, C = 8192, 4096
+    algo_bytes = R * C * 2 + 2 * R * C + 2 * (R * C // 32) + 4      # 136,314,884
+    x0 = up_bf16(workloads.cfg2())
+    nsets = 8
+    sets = []
+    for i in range(nsets):
+        x = x0 if i == 0 else x0.clone()
+        sets.append(dict(x=x,
+                         qr=torch.empty((R, C), dtype=torch.uint8, device=dev),
+                         sr=torch.empty((R, C // 32), dtype=torch.uint8, device=dev),
+                         qc=torch.empty((C, R), dtype=torch.uint8, device=dev),
+                         sc=torch.empty((C, R // 32), dtype=torch.uint8, device=dev),
+                         a=torch.zeros(1, dtype=torch.float32, device=dev)))
+
+    def dual(s):
+        st = lib.mx_quantize_dual(s["x"].data_ptr(), 1, R, C, 32, 0, 1, s["qr"].data_ptr(), s["sr"].data_ptr(),
+                                  s["qc"].data_ptr(), s["sc"].data_ptr(), s["a"].data_ptr(), sp)
+        if st != 0:
+            raise RuntimeError(lib.mx_status_str(st).decode())
+
+    for i in range(args.warmup):
+        dual(sets[i % nsets])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        dual(sets[i % nsets])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_kern_s = sum(kern_ms) / len(kern_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    value = algo_bytes * args.steps / wall / 1e9
+    achieved = algo_bytes / avg_kern_s / 1e9
+    traffic = measured_traffic()
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "MXFP8 E4M3 dual (row + column, one read) quantization of a BF16 8192x4096 "
+                               "activation, k=32, round-up E8M0 scale, fused per-tensor amax",
+                   "rows": R, "cols": C, "in_dtype": "bf16", "element": "e4m3", "scale_rule": "ceil",
+                   "bytes_per_step": algo_bytes, "buffer_sets": nsets},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic)},
+        "kernel_us": {"mean": round(avg_kern_s * 1e6, 2), "min": round(min(kern_ms) * 1e3, 2),
+                      "max": round(max(kern_ms) * 1e3, 2)},
+    }
+
+    # ------------------------------------------------------------------ GEMM + other workloads
+    if args.mode == "dual":
+        print(json.dumps(out), flush=True)
+        return
+    if not args.no_extra:
+        out["gemm"] = bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch)
+        out["extra"] = bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch)
+
+    # ------------------------------------------------------------------ CPU oracle baseline
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(workloads, np)
+
+    print(json.dumps(out), flush=True)
+
+
+def time_calls(fn, n, warm, stream, torch):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return sum(ms) / len(ms) / 1e3
+
+
+def bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=10):
+    """MXFP8 E4M3 GEMM 8192 x 4096 . (14336 x 4096)^T, BF16 out (quantized operands resident)."""
+    M, N, K = 8192, 14336, 4096
+    a_bits, w_bits = workloads.cfg4()
+    qa, sa = mxa.mx_quantize(up_bf16(a_bits), "e4m3", "ceil", "row")
+    qw, sw = mxa.mx_quantize(up_bf16(w_bits), "e4m3", "ceil", "row")
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def call():
+        st = lib.mx_gemm(qa.data_ptr(), sa.data_ptr(), 0, qw.data_ptr(), sw.data_ptr(), 0, M, N, K, 1.0,
+                         c.data_ptr(), 1, N, sp)
+        if st != 0:
+            raise RuntimeError(lib.mx_status_str(st).decode())
+    t = time_calls(call, steps, 2, stream, torch)
+    flops = 2.0 * M * N * K
+    tf = flops / t / 1e12
+    return {"workload": "MXFP8 E4M3 block-scaled GEMM 8192x4096 x (14336x4096)^T, FP32 accumulate, BF16 out",
+            "value": round(tf, 1), "unit": "TFLOP/s", "ms_per_call": round(t * 1e3, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / FP8_PEAK_TFLOPS, 4), "traffic": None}}
+
+
+def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
+    res = {}
+    # row-wise quantize + dequantize, FP32 256 x 1024, round-down rule
+    x = torch.from_numpy(workloads.cfg1()).to(dev)
+    q = torch.empty((256, 1024), dtype=torch.uint8, device=dev)
+    s = torch.empty((256, 32), dtype=torch.uint8, device=dev)
+    d = torch.empty((256, 1024), dtype=torch.float32, device=dev)
+    tq = time_calls(lambda: lib.mx_quantize(x.data_ptr(), 0, 256, 1024, 32, 0, 0, 0, 0, 0, q.data_ptr(),
+                                            s.data_ptr(), None, sp), 50, 5, stream, torch)
+    td = time_calls(lambda: lib.mx_dequantize(q.data_ptr(), s.data_ptr(), 256, 1024, 32, 0, 0, d.data_ptr(), 0, sp),
+                    50, 5, stream, torch)
+    b1 = 256 * 1024 * 4 + 256 * 1024 + 256 * 32
+    res["rowwise_quant_f32_256x1024"] = {"us": round(tq * 1e6, 2), "GB/s": round(b1 / tq / 1e9, 1)}
+    res["dequant_f32_256x1024"] = {"us": round(td * 1e6, 2), "GB/s": round(b1 / td / 1e9, 1)}
+    # per-tensor delayed scaling, BF16 8192 x 4096 -> transposed FP8, ring of 16
+    R, C = 8192, 4096
+    xs = [up_bf16(workloads.cfg3_step("act", t)) for t in range(2)]
+    qT = torch.empty((C, R), dtype=torch.uint8, device=dev)
+    ring = mxa.new_ring(16, dev)
+    cnt = [0]
+
+    def delayed():
+        t = cnt[0]
+        cnt[0] += 1
+        lib.fp8_quantize_delayed(xs[t % 2].data_ptr(), 1, R, C, 0, 1, None, qT.data_ptr(), ring.data_ptr(), 16,
+                                 t % 16, 448.0, 1.0, None, sp)
+    t3 = time_calls(delayed, 32, 4, stream, torch)
+    b3 = R * C * 2 + R * C + 80
+    res["delayed_fp8_transposed_bf16_8192x4096"] = {"us": round(t3 * 1e6, 2), "GB/s": round(b3 / t3 / 1e9, 1),
+                                                    "hbm_frac": round(b3 / t3 / 1e9 / HBM_PEAK_GBS, 4)}
+    del xs, qT
+    # Hadamard + column-wise MXFP4 quantization of both operands, then the MXFP4 GEMM
+    g_bits, x_bits, mask = workloads.cfg5()
+    G, X = up_bf16(g_bits), up_bf16(x_bits)
+    gq = torch.empty((4096, 4096), dtype=torch.uint8, device=dev)
+    gs = torch.empty((4096, 256), dtype=torch.uint8, device=dev)
+    xq = torch.empty_like(gq)
+    xsc = torch.empty_like(gs)
+
+    def quant5():
+        lib.mx_quantize(G.data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, gq.data_ptr(), gs.data_ptr(), None, sp)
+        lib.mx_quantize(X.data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, xq.data_ptr(), xsc.data_ptr(), None, sp)
+    t5q = time_calls(quant5, 20, 3, stream, torch)
+    b5 = 2 * (8192 * 4096 * 2 + 4096 * 4096 + 4096 * 256)
+    dw = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+    t5g = time_calls(lambda: lib.mx_gemm(gq.data_ptr(), gs.data_ptr(), 2, xq.data_ptr(), xsc.data_ptr(), 2, 4096,
+                                         4096, 8192, 1.0 / 32, dw.data_ptr(), 1, 4096, sp), 10, 2, stream, torch)
+    f5 = 2.0 * 4096 * 4096 * 8192
+    res["hadamard_mxfp4_colwise_quant_2x_bf16_8192x4096"] = {"us": round(t5q * 1e6, 2),
+                                                              "GB/s": round(b5 / t5q / 1e9, 1),
+                                                              "hbm_frac": round(b5 / t5q / 1e9 / HBM_PEAK_GBS, 4)}
+    res["mxfp4_gemm_4096x4096x8192"] = {"us": round(t5g * 1e6, 2), "TFLOP/s": round(f5 / t5g / 1e12, 1),
+                                        "mfma_frac": round(f5 / t5g / 1e12 / FP4_PEAK_TFLOPS, 4)}
+    return res
+
+
+def cpu_baseline(workloads, np):
+    """The CPU oracle (numpy, single thread) on a 512-row strip of the same
+    workload: dual quantization + per-tensor amax of BF16 512 x 4096."""
+    from oracle import mx as omx
+    rows, cols = 512, 4096
+    xb = workloads.cfg2()[:rows]
+    xs = workloads.bf16_to_f32(xb)
+    t0 = time.perf_counter()
+    omx.quantize_dual(xs, "e4m3", "ceil")
+    omx.tensor_amax(xs)
+    dt = time.perf_counter() - t0
+    b = rows * cols * 2 + 2 * rows * cols + 2 * (rows * cols // 32) + 4
+    return {"value": round(b / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} rows of the 8192x4096 BF16 input (dual E4M3 quantization + amax), "
+                      f"{dt:.1f} s on the host CPU"}
+
+
+if __name__ == "__main__":
+    main()

@@ -73,6 +73,10 @@ typedef enum { MX_ROWWISE = 0, MX_COLWISE_T = 1 } mx_orient_t;
  * quantize_dual): q [rows][cols], qT [cols][rows], or both from one read. */
 typedef enum { FP8_ROW = 0, FP8_TRANSPOSED = 1, FP8_DUAL = 2 } fp8_layout_t;
 
+/* Size of the delayed-scaling ring state of fp8_quantize_delayed, in FP32 words. */
+#define MX_RING_TICKET_WORDS 1024
+#define MX_RING_WORDS(hist_len) ((hist_len) + 4 + MX_RING_TICKET_WORDS)
+
 typedef enum {
   MX_OK = 0,
   MX_ERR_NULL = 1,         /* a required pointer is NULL                         */
@@ -128,12 +132,17 @@ mx_status_t mx_quantize_dual(const void* x, mx_dtype_t in, int64_t rows, int64_t
 /* Per-tensor FP8 quantization with delayed scaling ([FP8PY] quantize /
  * quantize_dual with ring_state, and its commit message).
  *
- * ring: caller-owned FP32 device buffer of hist_len + 4 words,
- *   [hist[0..hist_len-1] | s | m | amax | ticket]
+ * ring: caller-owned FP32 device buffer of MX_RING_WORDS(hist_len) words,
+ *   [hist[0..hist_len-1] | s | m | amax | ticket | MX_RING_TICKET_WORDS counters]
  * where s is the dequantization scale (x ~ q * s), m = 1/s is the multiplier the
- * cast uses, and the amax and ticket words are scratch that must read 0 before
- * the first call (initialise the buffer to hist = 0, s = m = 1, amax = ticket = 0);
- * every call leaves them 0 again.
+ * cast uses, and the amax, ticket and counter words are scratch that must read 0
+ * before the first call (initialise the buffer to hist = 0, s = m = 1, the rest
+ * 0); every call leaves them 0 again.  The counter words hold 32 groups of
+ * (max, ticket) pairs, one group per 128-byte line, that spread the
+ * per-workgroup ticket over several cache lines, because atomics on one line
+ * serialize; the first hist_len + 4 words are the page's
+ * [hist | scale | legacy | amax | done].  The buffer must be 128-byte aligned
+ * past those first words for the spreading to pay off (any alignment is correct).
  *
  * Each call: y = fl32(x * m) with the m the ring holds at launch, q = RNE +
  * saturating cast of y to `fmt` (Inf saturates, NaN gives NaN), written as

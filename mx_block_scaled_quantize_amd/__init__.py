@@ -42,6 +42,12 @@ LAYOUT = {"row": 0, "transposed": 1, "dual": 2}
 STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN", 4: "MX_ERR_UNSUPPORTED",
           5: "MX_ERR_LAUNCH", 6: "MX_ERR_ARG"}
 DEFAULT_FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+RING_TICKET_WORDS = 1024        # MX_RING_TICKET_WORDS
+
+
+def ring_words(hist_len: int) -> int:
+    """MX_RING_WORDS(hist_len): [hist | s | m | amax | ticket | ticket counters]."""
+    return hist_len + 4 + RING_TICKET_WORDS
 
 _p, _i64, _i32, _u32, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32, ctypes.c_float
 lib.mx_quantize.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _u32, _p, _p, _p, _p]
@@ -156,8 +162,8 @@ def mx_quantize_dual(x, fmt="e4m3", rule="ceil", amax=False):
 
 
 def new_ring(hist_len: int, device="cuda") -> torch.Tensor:
-    """A fresh delayed-scaling ring: [hist (zeros) | s = 1 | m = 1 | amax = 0 | ticket = 0]."""
-    r = torch.zeros(hist_len + 4, dtype=torch.float32, device=device)
+    """A fresh delayed-scaling ring: [hist (zeros) | s = 1 | m = 1 | amax = 0 | ticket = 0 | counters = 0]."""
+    r = torch.zeros(ring_words(hist_len), dtype=torch.float32, device=device)
     r[hist_len] = 1.0
     r[hist_len + 1] = 1.0
     return r
@@ -178,7 +184,8 @@ def fp8_quantize_delayed(x, ring, hist_idx, fmt="e4m3", layout="transposed", fp8
     qT = torch.empty((C, R), dtype=torch.uint8, device=x.device) if layout != "row" else None
     a = torch.empty(1, dtype=torch.float32, device=x.device) if amax else None
     check(lib.fp8_quantize_delayed(_ptr(x), _lookup(DTYPE, x.dtype, "dtype"), R, C, f, lay, _ptr(q), _ptr(qT),
-                                   _ptr(ring), ring.numel() - 4, int(hist_idx), float(fp8_max), float(margin),
+                                   _ptr(ring), ring.numel() - 4 - RING_TICKET_WORDS, int(hist_idx), float(fp8_max),
+                                   float(margin),
                                    _ptr(a), _stream(x)))
     return (q, qT, a) if amax else (q, qT)
 

@@ -29,6 +29,10 @@ constexpr int kGemmThreads = 256;
 
 template <int FA> struct OpBytes { static constexpr int kRow = FA == E2M1 ? kBK / 2 : kBK; };
 
+// Operand-format field of the scaled MFMA: 0 FP8 E4M3, 1 FP8 E5M2, 2 FP6 E2M3,
+// 3 FP6 E3M2, 4 FP4 E2M1.
+template <int F> struct MfmaFmt { static constexpr int kCode = F == E4M3 ? 0 : F == E5M2 ? 1 : 4; };
+
 // One lane's operand for K-step kk (64 K-values) of a row staged in LDS; h = lane / 32.
 //   FP4: the lane holds the 32 codes of K-block 2*kk + h (16 contiguous bytes).
 //   FP8: the lane holds K = 16h .. 16h+15 of the step in bytes 0..15 and
@@ -125,8 +129,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], FA, FB, 0, sa[i], 0,
-                                                                       sb[j]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], MfmaFmt<FA>::kCode,
+                                                                       MfmaFmt<FB>::kCode, 0, sa[i], 0, sb[j]);
     }
     __syncthreads();
   }

@@ -92,21 +92,14 @@ __device__ __forceinline__ uint32_t encode_rne_sat(float v) {
 template <int F, int R>
 __device__ __forceinline__ int shared_exponent(uint32_t abits) {
   using T = Fmt_<F>;
-  if (abits == 0u) return -127;
-  int E;
-  uint32_t frac;
   if (abits >= 0x00800000u) {
-    E = int(abits >> 23) - 127;
-    frac = abits & 0x7FFFFFu;
-  } else {                                        // FP32 subnormal amax
-    const int p = 31 - __clz(abits);
-    E = p - 149;
-    frac = (abits << (23 - p)) & 0x7FFFFFu;
+    // normal amax: the exponent field does it, one compare for the round-up rule
+    const int e = int(abits >> 23) - 127 - T::kEmax + ((R == CEIL && (abits & 0x7FFFFFu) > T::kMaxFrac) ? 1 : 0);
+    return e < -127 ? -127 : e;      // e <= 127 - kEmax + 1 < 127 always
   }
-  int e = E - T::kEmax;
-  if (R == CEIL && frac > T::kMaxFrac) e += 1;
-  e = e < -127 ? -127 : e;
-  return e > 127 ? 127 : e;
+  if (abits == 0u) return -127;
+  // FP32 subnormal amax: e is far below -127 for every format
+  return -127;
 }
 
 // 2^-e as FP32 (exact; e never exceeds 126 for FP32 inputs, 2^-127 is kept as
@@ -200,8 +193,12 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 }
 
 // Agent-scope atomics on the amax / ticket words (multi-XCD coherent).
+// Same-address atomics serialize at the memory side, so the max is only sent
+// when it can change the word: the word only grows, so a value not above what
+// an (atomic) read returns can never be the final maximum.
 __device__ __forceinline__ void atomic_max_u32(uint32_t* p, uint32_t v) {
-  __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (v > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+    __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -260,6 +257,191 @@ __device__ __forceinline__ void hadamard32_quad(float (&v)[8], uint32_t mask, in
       v[i] = upper ? (p - v[i]) : (v[i] + p);
     }
   }
+}
+
+
+// ---------------------------------------------------------------------------
+// gfx950 scaled pair converts (V_CVT_SCALEF32_PK_{FP8,BF8,FP4}_{F32,BF16}).
+// Measured against the CPU oracle on every BF16 value at several scales: for
+// |v / scale| within the format's range the result is exactly RNE(v / scale)
+// (subnormals included), the first operand lands in the low byte (FP4: low
+// nibble) and SEL picks the 16-bit word (FP8) or the byte (FP4) written.  Out of
+// range, FP8 gives NaN / Inf instead of saturating and NaN inputs lose their
+// sign, so callers only use them on finite blocks whose scaled values are in
+// range (round-up rule, or after an explicit clamp) and override the rest.
+// ---------------------------------------------------------------------------
+typedef short v2s_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// Orders one wave's LDS writes before its later LDS reads of other lanes' data:
+// LDS instructions of a wave execute in order, so only the compiler has to be
+// kept from moving memory operations across this point.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+typedef unsigned short v2u16_t __attribute__((ext_vector_type(2)));
+
+template <int F, int SEL>
+__device__ __forceinline__ uint32_t cvt_pair_f32(uint32_t old, float a, float b, float scale) {
+  if constexpr (F == E4M3) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s_t, old), a, b,
+                                                                                 scale, SEL != 0));
+  } else if constexpr (F == E5M2) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(__builtin_bit_cast(v2s_t, old), a, b,
+                                                                                 scale, SEL != 0));
+  } else {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
+  }
+}
+
+// Same on two BF16 values packed in one dword (element 0 in the low half).
+template <int F, int SEL>
+__device__ __forceinline__ uint32_t cvt_pair_bf16(uint32_t old, uint32_t ab, float scale) {
+  const v2bf_t v = __builtin_bit_cast(v2bf_t, ab);
+  if constexpr (F == E4M3) {
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(v2s_t, old), v, scale, SEL != 0));
+  } else if constexpr (F == E5M2) {
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(__builtin_bit_cast(v2s_t, old), v, scale, SEL != 0));
+  } else {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(old, v, scale, SEL);
+  }
+}
+
+// Dwords holding N codes of format F.
+template <int F, int N> struct Words { static constexpr int kN = N * Fmt_<F>::kBits / 32; };
+
+// Pack N codes (low bits of c[j]) into dwords, element 0 lowest.
+template <int F, int N>
+__device__ __forceinline__ void pack_codes(const uint32_t (&c)[N], uint32_t (&w)[Words<F, N>::kN]) {
+  constexpr int kPer = 32 / Fmt_<F>::kBits;
+  constexpr uint32_t kMask = (1u << Fmt_<F>::kBits) - 1u;
+#pragma unroll
+  for (int i = 0; i < Words<F, N>::kN; ++i) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) x |= (c[i * kPer + j] & kMask) << (Fmt_<F>::kBits * j);
+    w[i] = x;
+  }
+}
+
+// N values (pairs in element order) through the pair converter with one scale.
+template <int F, int N>
+__device__ __forceinline__ void cvt_values_f32(const float (&v)[N], float scale, uint32_t (&w)[Words<F, N>::kN]) {
+  if constexpr (Fmt_<F>::kBits == 8) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      uint32_t x = cvt_pair_f32<F, 0>(0u, v[4 * i], v[4 * i + 1], scale);
+      w[i] = cvt_pair_f32<F, 1>(x, v[4 * i + 2], v[4 * i + 3], scale);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+      uint32_t x = cvt_pair_f32<F, 0>(0u, v[8 * i], v[8 * i + 1], scale);
+      x = cvt_pair_f32<F, 1>(x, v[8 * i + 2], v[8 * i + 3], scale);
+      x = cvt_pair_f32<F, 2>(x, v[8 * i + 4], v[8 * i + 5], scale);
+      w[i] = cvt_pair_f32<F, 3>(x, v[8 * i + 6], v[8 * i + 7], scale);
+    }
+  }
+}
+
+// N BF16 values given as N/2 packed pairs.
+template <int F, int N>
+__device__ __forceinline__ void cvt_values_bf16(const uint32_t (&p)[N / 2], float scale,
+                                                uint32_t (&w)[Words<F, N>::kN]) {
+  if constexpr (Fmt_<F>::kBits == 8) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) w[i] = cvt_pair_bf16<F, 1>(cvt_pair_bf16<F, 0>(0u, p[2 * i], scale), p[2 * i + 1], scale);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+      uint32_t x = cvt_pair_bf16<F, 0>(0u, p[4 * i], scale);
+      x = cvt_pair_bf16<F, 1>(x, p[4 * i + 1], scale);
+      x = cvt_pair_bf16<F, 2>(x, p[4 * i + 2], scale);
+      w[i] = cvt_pair_bf16<F, 3>(x, p[4 * i + 3], scale);
+    }
+  }
+}
+
+// Codes of a block whose max |.| bit pattern is NaN / Inf: the format's NaN
+// (E2M1: largest magnitude) with each input's sign.
+template <int F, int N>
+__device__ __forceinline__ void nan_block_words(const float (&v)[N], uint32_t (&w)[Words<F, N>::kN]) {
+  uint32_t c[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) c[j] = Fmt_<F>::kNan | ((__float_as_uint(v[j]) >> 31) << (Fmt_<F>::kBits - 1));
+  pack_codes<F, N>(c, w);
+}
+
+// MX-encode N FP32 values of one block (or a part of it) whose shared exponent
+// e is already known (`nonfinite`: the block holds NaN / Inf).
+template <int F, int R, int N>
+__device__ __forceinline__ void mx_encode_given(const float (&v)[N], bool nonfinite, int e,
+                                                uint32_t (&w)[Words<F, N>::kN]) {
+  if (nonfinite) {
+    nan_block_words<F, N>(v, w);
+  } else if (e > -127) {
+    const float scale = __uint_as_float(uint32_t(127 + e) << 23);
+    if constexpr (R == FLOOR && F != E2M1) {
+      // the round-down rule can put |v| / 2^e above the format maximum: saturate first
+      const float lim = __uint_as_float(Fmt_<F>::kMaxBits + (uint32_t(e) << 23));
+      float c[N];
+#pragma unroll
+      for (int j = 0; j < N; ++j) c[j] = fminf(fmaxf(v[j], -lim), lim);
+      cvt_values_f32<F, N>(c, scale, w);
+    } else {
+      cvt_values_f32<F, N>(v, scale, w);
+    }
+  } else {
+    // e = -127: 2^-127 is not a normal FP32 scale operand; use the integer encoder
+    const float mul = pow2_neg(e);
+    uint32_t c[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) c[j] = encode_rne_sat<F>(v[j] * mul);
+    pack_codes<F, N>(c, w);
+  }
+}
+
+// MX-encode N FP32 values of one block (or this lane's share of it) given the
+// block's max |.| bit pattern; returns the E8M0 scale code.
+template <int F, int R, int N>
+__device__ __forceinline__ uint32_t mx_encode_f32(const float (&v)[N], uint32_t bmax, uint32_t (&w)[Words<F, N>::kN]) {
+  const bool nonfinite = bmax >= 0x7F800000u;
+  const int e = nonfinite ? 0 : shared_exponent<F, R>(bmax);
+  mx_encode_given<F, R, N>(v, nonfinite, e, w);
+  return nonfinite ? 0xFFu : uint32_t(e + 127);
+}
+
+// Per-tensor cast of N FP32 values: y = fl32(v * m), saturating RNE, NaN -> NaN
+// with the input's sign.  `chunk_max` is the max |v| bit pattern of the values.
+template <int F, int N>
+__device__ __forceinline__ void pt_encode_f32(const float (&v)[N], float m, uint32_t chunk_max,
+                                              uint32_t (&w)[Words<F, N>::kN]) {
+  float y[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) y[j] = v[j] * m;
+  if (chunk_max > 0x7F800000u) {               // a NaN among them: integer encoder
+    uint32_t c[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) c[j] = encode_rne_sat<F>(y[j]);
+    pack_codes<F, N>(c, w);
+    return;
+  }
+  const float mx = __uint_as_float(Fmt_<F>::kMaxBits);
+#pragma unroll
+  for (int j = 0; j < N; ++j) y[j] = fminf(fmaxf(y[j], -mx), mx);   // also maps +-Inf to +-max
+  cvt_values_f32<F, N>(y, 1.0f, w);
+}
+
+// max over the two halves of a packed pair of 16-bit magnitudes
+__device__ __forceinline__ uint32_t pk_umax16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(v2u16_t, a),
+                                                                __builtin_bit_cast(v2u16_t, b)));
 }
 
 }  // namespace mxk

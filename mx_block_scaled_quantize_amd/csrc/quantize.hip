@@ -8,20 +8,28 @@
 // (quantize / quantize_dual with fused amax and the in-kernel ring fold).
 //
 // Kernels
-//   rowwise_kernel   row-wise MX blocks.  Row-wise blocks are contiguous in
-//                    memory, so the tensor is treated as a flat array: each
-//                    lane owns 8 consecutive elements (one 16-byte load for
-//                    2-byte inputs), a quad of lanes owns one block, and the
-//                    block amax is a 2-step DPP max inside the quad.
-//   tile_kernel      128 x 128 tiles through LDS: the row-wise half is done
-//                    from registers right after the coalesced loads, the tile
-//                    is staged in LDS in the input type, and each lane then
-//                    walks 32 rows of 2 adjacent columns (conflict-free dword
-//                    reads) for the column-wise half, written transposed as
-//                    16-byte stores.  Used for MX dual, MX column-wise
-//                    (optionally with the in-lane Hadamard transform) and the
-//                    per-tensor FP8 path (row / transposed / dual) whose last
-//                    workgroup folds the amax ring (atomic ticket).
+//   rowwise_kernel  row-wise MX blocks.  Row-wise blocks are contiguous in
+//                   memory, so the tensor is treated as a flat array: each lane
+//                   owns 8 consecutive elements (one 16-byte load for 2-byte
+//                   inputs), a quad of lanes owns one block, and the block amax
+//                   is a 2-step DPP max inside the quad.
+//   pt_row_kernel   per-tensor FP8 cast with row-major output, flat the same way,
+//                   ending with the ring fold.
+//   strip_kernel    one wavefront per 32-row x 128-column strip: coalesced
+//                   16-byte loads (4 rows of 256 bytes per instruction), the
+//                   row-wise half straight from registers, the strip staged in
+//                   LDS in the input type, then each lane walks the 32 rows of
+//                   2 adjacent columns (conflict-free dword reads) for the
+//                   column-wise half, stored transposed with 16-byte stores.
+//                   A single wave needs no cross-wave barrier and keeps ~16
+//                   independent strips in flight per CU.  Workgroup ids are
+//                   mapped so that the 4 strips that share the 128-byte lines of
+//                   the transposed output run on the same XCD (ids are handed
+//                   to the 8 XCDs round-robin).  Used for MX dual, MX
+//                   column-wise (optionally with the in-lane Hadamard transform)
+//                   and the per-tensor transposed / dual outputs.
+//   The per-tensor kernels end with the delayed-scaling fold done by the last
+//   workgroup to finish (atomic ticket).
 
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
@@ -29,153 +37,21 @@
 namespace mxk {
 
 // ---------------------------------------------------------------------------
-// Packing helpers
+// Stores
 // ---------------------------------------------------------------------------
+// 8 codes of a row chunk starting at element `elem` (2 dwords FP8, 1 dword FP4); streaming stores.
 template <int F>
-__device__ __forceinline__ void store_codes8(uint8_t* __restrict__ q, int64_t elem, const uint32_t (&c)[8]) {
+__device__ __forceinline__ void store_row8(uint8_t* __restrict__ q, int64_t elem, const uint32_t (&w)[Words<F, 8>::kN]) {
   if constexpr (Fmt_<F>::kBits == 8) {
-    uint2 w;
-    w.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    w.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-    *reinterpret_cast<uint2*>(q + elem) = w;
+    __builtin_nontemporal_store(u32x2_t{w[0], w[1]}, reinterpret_cast<u32x2_t*>(q + elem));
   } else {
-    uint32_t w = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) w |= (c[j] & 0xFu) << (4 * j);
-    *reinterpret_cast<uint32_t*>(q + elem / 2) = w;
-  }
-}
-
-// 32 codes of one column segment -> 32 bytes (FP8) or 16 bytes (FP4) at dst.
-template <int F>
-__device__ __forceinline__ void store_codes32(uint8_t* __restrict__ dst, const uint32_t (&c)[32]) {
-  if constexpr (Fmt_<F>::kBits == 8) {
-    uint4 w0, w1;
-    w0.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    w0.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-    w0.z = c[8] | (c[9] << 8) | (c[10] << 16) | (c[11] << 24);
-    w0.w = c[12] | (c[13] << 8) | (c[14] << 16) | (c[15] << 24);
-    w1.x = c[16] | (c[17] << 8) | (c[18] << 16) | (c[19] << 24);
-    w1.y = c[20] | (c[21] << 8) | (c[22] << 16) | (c[23] << 24);
-    w1.z = c[24] | (c[25] << 8) | (c[26] << 16) | (c[27] << 24);
-    w1.w = c[28] | (c[29] << 8) | (c[30] << 16) | (c[31] << 24);
-    reinterpret_cast<uint4*>(dst)[0] = w0;
-    reinterpret_cast<uint4*>(dst)[1] = w1;
-  } else {
-    uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < 32; ++j) w[j / 8] |= (c[j] & 0xFu) << (4 * (j % 8));
-    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
-// Quantize N values that form one MX block (or, for the row path, this lane's
-// share of it): given the block-wide max |.| bits, produce codes and the scale.
-template <int F, int R, int N>
-__device__ __forceinline__ uint32_t mx_encode(const float (&v)[N], uint32_t bmax, uint32_t (&c)[N]) {
-  if (bmax >= 0x7F800000u) {                       // NaN or Inf in the block
-#pragma unroll
-    for (int j = 0; j < N; ++j)
-      c[j] = Fmt_<F>::kNan | ((__float_as_uint(v[j]) >> 31) << (Fmt_<F>::kBits - 1));
-    return 0xFFu;
-  }
-  const int e = shared_exponent<F, R>(bmax);
-  const float mul = pow2_neg(e);
-#pragma unroll
-  for (int j = 0; j < N; ++j) c[j] = encode_rne_sat<F>(v[j] * mul);
-  return uint32_t(e + 127);
-}
-
-// ---------------------------------------------------------------------------
-// Row-wise MX quantization (flat)
-// ---------------------------------------------------------------------------
-constexpr int kRowThreads = 256;
-constexpr int kRowUnroll = 4;
-
-template <int IN, int F, int R, bool HAD, bool AMAX>
-__global__ __launch_bounds__(kRowThreads) void rowwise_kernel(const void* __restrict__ x, int64_t nchunks,
-                                                               uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
-                                                               uint32_t* __restrict__ amax_out, uint32_t had_mask) {
-  const int lane_q = threadIdx.x & 3;
-  uint32_t tmax = 0;
-  float v[kRowUnroll][8];
-  int64_t chunk[kRowUnroll];
-#pragma unroll
-  for (int u = 0; u < kRowUnroll; ++u) {
-    chunk[u] = (int64_t(blockIdx.x) * kRowUnroll + u) * kRowThreads + threadIdx.x;
-    if (chunk[u] < nchunks) load8<IN>(x, chunk[u] * 8, v[u]);
-  }
-#pragma unroll
-  for (int u = 0; u < kRowUnroll; ++u) {
-    // nchunks is a multiple of 4 and quads are aligned, so a quad is either
-    // entirely in range or entirely out of range
-    if (chunk[u] >= nchunks) continue;
-    if constexpr (AMAX) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) tmax = umax(tmax, abs_bits_no_nan(v[u][j]));
-    }
-    if constexpr (HAD) hadamard32_quad(v[u], had_mask, lane_q);
-    uint32_t m = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m = umax(m, abs_bits(v[u][j]));
-    m = quad_max(m);
-    uint32_t c[8];
-    const uint32_t sc = mx_encode<F, R, 8>(v[u], m, c);
-    store_codes8<F>(q, chunk[u] * 8, c);
-    if (lane_q == 0) scales[chunk[u] >> 2] = uint8_t(sc);
-  }
-  if constexpr (AMAX) {
-    __shared__ uint32_t red[kRowThreads / 64];
-    tmax = wave_max(tmax);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = tmax;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t m = red[0];
-#pragma unroll
-      for (int w = 1; w < kRowThreads / 64; ++w) m = umax(m, red[w]);
-      atomic_max_u32(amax_out, m);
-    }
+    __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(q + elem / 2));
   }
 }
 
 // ---------------------------------------------------------------------------
-// Tile kernel: MX dual / MX column-wise / per-tensor FP8 (row, transposed, dual)
+// Input chunks: 8 consecutive elements = one 16-byte word (2-byte types) or two (FP32)
 // ---------------------------------------------------------------------------
-constexpr int kTile = 128;          // rows and columns per tile
-constexpr int kTileThreads = 256;
-constexpr int kPasses = kTile * kTile / 8 / kTileThreads;   // 8 chunk loads per lane
-
-enum TileMode : int {
-  MX_DUAL = 0,     // MX row-wise + column-wise (transposed)
-  MX_COL = 1,      // MX column-wise (transposed) only
-  PT_ROW = 2,      // per-tensor FP8, row-major output
-  PT_COL = 3,      // per-tensor FP8, transposed output
-  PT_DUAL = 4,     // per-tensor FP8, both
-};
-
-struct TileArgs {
-  const void* x;
-  int64_t rows, cols;
-  uint8_t* q_row;       // MX_DUAL / PT_ROW / PT_DUAL
-  uint8_t* s_row;       // MX_DUAL
-  uint8_t* q_col;       // transposed codes
-  uint8_t* s_col;       // MX column scales
-  uint32_t* amax_out;   // MX modes: max-accumulator (bit pattern of a non-negative float), may be null
-  float* ring;          // PT modes
-  int hist_len, hist_idx;
-  float fp8_max, margin;
-  float* pt_amax_out;   // PT modes: optional copy of this call's amax
-  uint32_t had_mask;
-  int tiles_c;          // tiles along the column axis
-};
-
-template <int IN> struct LdsWord;   // element storage in LDS
-template <> struct LdsWord<IN_BF16> { using T = uint16_t; };
-template <> struct LdsWord<IN_F16> { using T = uint16_t; };
-template <> struct LdsWord<IN_F32> { using T = float; };
-
-// Raw 8-element chunk as loaded from global memory: one 16-byte word for 2-byte
-// types, two for FP32.
 template <int IN> struct ChunkWords { static constexpr int kN = IN == IN_F32 ? 2 : 1; };
 
 template <int IN>
@@ -183,6 +59,18 @@ __device__ __forceinline__ void load_chunk(const void* __restrict__ base, int64_
   const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(base) + i * (IN == IN_F32 ? 4 : 2));
 #pragma unroll
   for (int k = 0; k < ChunkWords<IN>::kN; ++k) w[k] = p[k];
+}
+
+// Same, with the streaming (non-temporal) hint: the input is read exactly once.
+template <int IN>
+__device__ __forceinline__ void load_chunk_nt(const void* __restrict__ base, int64_t i,
+                                              uint4 (&w)[ChunkWords<IN>::kN]) {
+  const u32x4_t* p = reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(base) + i * (IN == IN_F32 ? 4 : 2));
+#pragma unroll
+  for (int k = 0; k < ChunkWords<IN>::kN; ++k) {
+    const u32x4_t v = __builtin_nontemporal_load(p + k);
+    w[k] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
 }
 
 template <int IN>
@@ -207,166 +95,566 @@ __device__ __forceinline__ void widen_chunk(const uint4 (&c)[ChunkWords<IN>::kN]
   }
 }
 
-// Two adjacent LDS elements (columns 2l, 2l+1 of one row) widened to FP32.
+// Max |x| of a chunk as an FP32 bit pattern (a NaN element makes it > 0x7F800000).
 template <int IN>
-__device__ __forceinline__ void lds_pair(const typename LdsWord<IN>::T* p, float& lo, float& hi) {
-  if constexpr (IN == IN_F32) {
-    const float2 d = *reinterpret_cast<const float2*>(p);
-    lo = d.x;
-    hi = d.y;
+__device__ __forceinline__ uint32_t chunk_absmax(const uint4 (&c)[ChunkWords<IN>::kN], const float (&v)[8]) {
+  if constexpr (IN == IN_BF16) {
+    const uint32_t k = 0x7FFF7FFFu;
+    const uint32_t m = pk_umax16(pk_umax16(c[0].x & k, c[0].y & k), pk_umax16(c[0].z & k, c[0].w & k));
+    return umax(m & 0xFFFFu, m >> 16) << 16;
   } else {
-    const uint32_t d = *reinterpret_cast<const uint32_t*>(p);
-    if constexpr (IN == IN_BF16) {
-      lo = __uint_as_float(d << 16);
-      hi = __uint_as_float(d & 0xFFFF0000u);
-    } else {
-      lo = f16_bits_to_f32(d & 0xFFFFu);
-      hi = f16_bits_to_f32(d >> 16);
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = umax(m, abs_bits(v[j]));
+    return m;
+  }
+}
+
+// Per-tensor amax contribution of a chunk with max-bits m (NaN entries ignored).
+__device__ __forceinline__ uint32_t amax_update(uint32_t tmax, uint32_t m, const float (&v)[8]) {
+  if (m <= 0x7F800000u) return umax(tmax, m);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) tmax = umax(tmax, abs_bits_no_nan(v[j]));
+  return tmax;
+}
+
+// ---------------------------------------------------------------------------
+// Row-wise MX quantization of one 8-element chunk held by a lane of a quad
+// (the quad holds one 32-element block).  Returns the scale code.
+// ---------------------------------------------------------------------------
+template <int IN, int F, int R, bool HAD>
+__device__ __forceinline__ uint32_t row_chunk_mx(const uint4 (&c)[ChunkWords<IN>::kN], float (&v)[8], uint32_t m,
+                                                 uint32_t had_mask, int lane_q, uint32_t (&w)[Words<F, 8>::kN]) {
+  if constexpr (HAD) {
+    hadamard32_quad(v, had_mask, lane_q);
+    m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = umax(m, abs_bits(v[j]));
+  }
+  const uint32_t bmax = quad_max(m);
+  if constexpr (IN == IN_BF16 && R == CEIL && !HAD) {
+    // no element exceeds the format maximum under the round-up rule: convert the
+    // BF16 pairs directly
+    if (bmax < 0x7F800000u) {
+      const int e = shared_exponent<F, R>(bmax);
+      if (e > -127) {
+        const uint32_t p[4] = {c[0].x, c[0].y, c[0].z, c[0].w};
+        cvt_values_bf16<F, 8>(p, __uint_as_float(uint32_t(127 + e) << 23), w);
+        return uint32_t(e + 127);
+      }
+    }
+  }
+  return mx_encode_f32<F, R, 8>(v, bmax, w);
+}
+
+// ---------------------------------------------------------------------------
+// Row-wise MX quantization (flat): row-wise blocks are contiguous in memory
+// ---------------------------------------------------------------------------
+constexpr int kRowThreads = 256;
+constexpr int kRowUnroll = 4;
+
+template <int IN, int F, int R, bool HAD, bool AMAX>
+__global__ __launch_bounds__(kRowThreads) void rowwise_kernel(const void* __restrict__ x, int64_t nchunks,
+                                                               uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
+                                                               uint32_t* __restrict__ amax_out, uint32_t had_mask) {
+  constexpr int kW = ChunkWords<IN>::kN;
+  const int lane_q = threadIdx.x & 3;
+  uint32_t tmax = 0;
+  uint4 raw[kRowUnroll][kW];
+  int64_t chunk[kRowUnroll];
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) {
+    chunk[u] = (int64_t(blockIdx.x) * kRowUnroll + u) * kRowThreads + threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < kW; ++k) raw[u][k] = make_uint4(0, 0, 0, 0);
+    if (chunk[u] < nchunks) load_chunk<IN>(x, chunk[u] * 8, raw[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) {
+    // nchunks is a multiple of 4 and quads are aligned: a quad is entirely in or out of range
+    if (chunk[u] >= nchunks) continue;
+    float v[8];
+    widen_chunk<IN>(raw[u], v);
+    const uint32_t m = chunk_absmax<IN>(raw[u], v);
+    if constexpr (AMAX) tmax = amax_update(tmax, m, v);
+    uint32_t w[Words<F, 8>::kN];
+    const uint32_t sc = row_chunk_mx<IN, F, R, HAD>(raw[u], v, m, had_mask, lane_q, w);
+    store_row8<F>(q, chunk[u] * 8, w);
+    if (lane_q == 0) scales[chunk[u] >> 2] = uint8_t(sc);
+  }
+  if constexpr (AMAX) {
+    __shared__ uint32_t red[kRowThreads / 64];
+    tmax = wave_max(tmax);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = tmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t mm = red[0];
+#pragma unroll
+      for (int w = 1; w < kRowThreads / 64; ++w) mm = umax(mm, red[w]);
+      atomic_max_u32(amax_out, mm);
     }
   }
 }
+
+// ---------------------------------------------------------------------------
+// Delayed-scaling ring fold, run by the last workgroup of a per-tensor kernel
+// ---------------------------------------------------------------------------
+struct RingArgs {
+  float* ring;          // [hist | s | m | amax | ticket]
+  int hist_len, hist_idx;
+  float fp8_max, margin;
+  float* amax_out;      // optional copy of this call's amax
+};
+
+// The fold is reached through a two-level ticket taken by every workgroup
+// (thread 0):
+//   1. as soon as the workgroup knows its max |x|, it posts it to the max word
+//      of its group (workgroup id modulo 32) -- an atomic max, sent only when
+//      an atomic read shows that it can raise the word (the word only grows);
+//   2. after its stores, it increments its group's ticket, an increment that
+//      depends on the value step 1 returned, so it is issued only after that
+//      max has been performed (or found to be covered);
+//   3. the group's last arrival reads the group max (an RMW), clears the group
+//      words, posts the group max to the top amax word and takes a top ticket
+//      (again dependent RMWs);
+//   4. the last top ticket reads the overall max, folds it into the history,
+//      publishes s and m = 1/s and clears the top words.
+// Atomics on one cache line serialize (about 12 ns each on MI355X, more under
+// load) while different lines proceed in parallel, so every group sits on a
+// 128-byte line of its own, and splitting the chain keeps the round trips
+// behind the workgroup's stores instead of after them.
+constexpr unsigned kTicketGroups = 32;
+constexpr unsigned kTicketStride = MX_RING_TICKET_WORDS / kTicketGroups;   // 32 words = 128 bytes
+static_assert(kTicketStride >= 2, "a group needs a max and a ticket word");
+
+struct RingTicket {
+  uint32_t* gmax;
+  uint32_t* gctr;
+  unsigned members;    // workgroups in this group
+};
+
+__device__ __forceinline__ RingTicket ring_ticket(const RingArgs& r, unsigned wg, unsigned num_wg) {
+  uint32_t* scratch = reinterpret_cast<uint32_t*>(r.ring + r.hist_len + 4);
+  const unsigned g = wg % kTicketGroups;
+  return RingTicket{scratch + g * kTicketStride, scratch + g * kTicketStride + 1,
+                    num_wg / kTicketGroups + (g < num_wg % kTicketGroups ? 1u : 0u)};
+}
+
+// step 1: returns the value the ticket increment will depend on
+__device__ __forceinline__ uint32_t ring_post_max(const RingTicket& t, uint32_t wg_max) {
+  const uint32_t seen = __hip_atomic_load(t.gmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (wg_max <= seen) return seen;
+  return __hip_atomic_fetch_max(t.gmax, wg_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// steps 2-4
+__device__ __forceinline__ void ring_finish(const RingArgs& r, const RingTicket& t, uint32_t posted,
+                                            unsigned num_wg) {
+  // posted never holds 0xFFFFFFFF (a NaN-free magnitude): every increment is 1
+  const uint32_t tg = __hip_atomic_fetch_add(t.gctr, posted == 0xFFFFFFFFu ? 2u : 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+  if (tg != t.members - 1) return;
+  const uint32_t gm = __hip_atomic_fetch_or(t.gmax, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(t.gmax, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(t.gctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t* amax_slot = reinterpret_cast<uint32_t*>(r.ring + r.hist_len + 2);
+  uint32_t* ticket = reinterpret_cast<uint32_t*>(r.ring + r.hist_len + 3);
+  const uint32_t tm = __hip_atomic_fetch_max(amax_slot, gm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned ngroups = num_wg < kTicketGroups ? num_wg : kTicketGroups;
+  const uint32_t tt = __hip_atomic_fetch_add(ticket, tm == 0xFFFFFFFFu ? 2u : 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+  if (tt != ngroups - 1) return;
+  const uint32_t ab = __hip_atomic_fetch_or(amax_slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float amax = __uint_as_float(ab);
+  float* hist = r.ring;
+  hist[r.hist_idx] = amax;
+  float h = 0.0f;
+  for (int i = 0; i < r.hist_len; ++i) h = fmaxf(h, hist[i]);
+  if (h > 0.0f && h < __uint_as_float(0x7F800000u)) {
+    const float s = (h / r.fp8_max) / r.margin;   // correctly rounded FP32 divisions
+    r.ring[r.hist_len] = s;
+    r.ring[r.hist_len + 1] = 1.0f / s;
+  }
+  if (r.amax_out) *r.amax_out = amax;
+  __hip_atomic_store(amax_slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The multiplier of a per-tensor call; not-finite values (a degenerate ring)
+// are handled by the integer encoder.
+__device__ __forceinline__ float ring_multiplier(const RingArgs& r, bool& slow) {
+  const float m = r.ring[r.hist_len + 1];
+  slow = !(fabsf(m) < __uint_as_float(0x7F800000u));
+  return m;
+}
+
+// Workgroup max of a per-lane value, result valid in thread 0.
+template <int THREADS>
+__device__ __forceinline__ uint32_t block_max(uint32_t v) {
+  v = wave_max(v);
+  if constexpr (THREADS == 64) {
+    return v;
+  } else {
+    __shared__ uint32_t red[THREADS / 64];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint32_t m = red[0];
+#pragma unroll
+    for (int w = 1; w < THREADS / 64; ++w) m = umax(m, red[w]);
+    return m;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-tensor cast with row-major output (flat), then the fold
+// ---------------------------------------------------------------------------
+// 1024 threads x 4 chunks = 64 KiB of input per workgroup: one ticket per 64 KiB.
+constexpr int kPtRowThreads = 1024;
+
+template <int IN, int F>
+__global__ __launch_bounds__(kPtRowThreads) void pt_row_kernel(const void* __restrict__ x, int64_t nchunks,
+                                                                uint8_t* __restrict__ q, RingArgs r) {
+  constexpr int kW = ChunkWords<IN>::kN;
+  bool slow;
+  const float mult = ring_multiplier(r, slow);
+  uint32_t tmax = 0;
+  const int64_t b = int64_t(blockIdx.x) * kPtRowThreads * kRowUnroll;
+  uint4 raw[kRowUnroll][kW];
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) {
+    const int64_t c = b + u * kPtRowThreads + threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < kW; ++k) raw[u][k] = make_uint4(0, 0, 0, 0);
+    if (c < nchunks) load_chunk_nt<IN>(x, c * 8, raw[u]);
+  }
+  uint32_t w[kRowUnroll][Words<F, 8>::kN];
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) {
+    float v[8];
+    widen_chunk<IN>(raw[u], v);
+    const uint32_t m = chunk_absmax<IN>(raw[u], v);
+    tmax = amax_update(tmax, m, v);
+    pt_encode_f32<F, 8>(v, mult, slow ? 0x7FFFFFFFu : m, w[u]);
+  }
+  const RingTicket tk = ring_ticket(r, blockIdx.x, gridDim.x);
+  const uint32_t bm = block_max<kPtRowThreads>(tmax);
+  uint32_t posted = 0;
+  if (threadIdx.x == 0) posted = ring_post_max(tk, bm);
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) {
+    const int64_t c = b + u * kPtRowThreads + threadIdx.x;
+    if (c < nchunks) store_row8<F>(q, c * 8, w[u]);
+  }
+  if (threadIdx.x == 0) ring_finish(r, tk, posted, gridDim.x);
+}
+
+// ---------------------------------------------------------------------------
+// Strip kernel: MX dual / MX column-wise / per-tensor transposed or dual
+// ---------------------------------------------------------------------------
+constexpr int kStripRows = 32;
+constexpr int kStripCols = 128;
+constexpr int kStripLoads = kStripRows * kStripCols / 8 / 64;   // 8 chunk loads per lane
+
+enum StripMode : int {
+  MX_DUAL = 0,     // MX row-wise + column-wise (transposed)
+  MX_COL = 1,      // MX column-wise (transposed) only
+  PT_COL = 3,      // per-tensor FP8, transposed output
+  PT_DUAL = 4,     // per-tensor FP8, both
+};
+
+struct StripArgs {
+  const void* x;
+  int64_t rows, cols;
+  uint8_t* q_row;       // MX_DUAL / PT_DUAL
+  uint8_t* s_row;       // MX_DUAL
+  uint8_t* q_col;       // transposed codes
+  uint8_t* s_col;       // MX column scales
+  uint32_t* amax_out;   // MX modes: max-accumulator (bit pattern of a non-negative float), may be null
+  RingArgs ring;        // PT modes
+  uint32_t had_mask;
+  int strips_c;         // strips along the column axis
+  int bands;            // 128-row bands (4 strips each)
+  int supertiles;       // bands * strips_c
+};
+
+template <int IN> struct LdsWord;   // element storage in LDS
+template <> struct LdsWord<IN_BF16> { using T = uint16_t; };
+template <> struct LdsWord<IN_F16> { using T = uint16_t; };
+template <> struct LdsWord<IN_F32> { using T = float; };
+
+// Column pass of one lane: columns c, c+1 of a 32-row segment of the LDS strip.
+// Element (i, h) = row i, column c + h.  The LDS strip is re-read per column
+// instead of holding both columns in registers (LDS bandwidth is plentiful,
+// registers are not).
+template <int IN>
+__device__ __forceinline__ float lds_elem(const typename LdsWord<IN>::T* t, int pitch, int i, int h) {
+  if constexpr (IN == IN_F32) {
+    return t[i * pitch + h];
+  } else {
+    const uint32_t d = *reinterpret_cast<const uint32_t*>(t + i * pitch);
+    const uint32_t bits = h ? (d >> 16) : (d & 0xFFFFu);
+    if constexpr (IN == IN_BF16) return __uint_as_float(bits << 16);
+    else return f16_bits_to_f32(bits);
+  }
+}
+
+// Max |x| bit patterns of both columns (NaN > Inf).
+template <int IN>
+__device__ __forceinline__ void col_absmax(const typename LdsWord<IN>::T* t, int pitch, uint32_t (&cmax)[2]) {
+  if constexpr (IN == IN_BF16) {
+    uint32_t mp = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mp = pk_umax16(mp, *reinterpret_cast<const uint32_t*>(t + i * pitch) & 0x7FFF7FFFu);
+    cmax[0] = (mp & 0xFFFFu) << 16;
+    cmax[1] = mp & 0xFFFF0000u;
+  } else {
+    cmax[0] = cmax[1] = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      cmax[0] = umax(cmax[0], abs_bits(lds_elem<IN>(t, pitch, i, 0)));
+      cmax[1] = umax(cmax[1], abs_bits(lds_elem<IN>(t, pitch, i, 1)));
+    }
+  }
+}
+
+// Codes (and MX scale) of column h.
+template <int IN, int F, int R, int MODE, bool HAD>
+__device__ __forceinline__ uint32_t col_encode(const typename LdsWord<IN>::T* __restrict__ t, int pitch, int h,
+                                               uint32_t cmax, float mult, bool pt_slow, uint32_t had_mask,
+                                               uint32_t (&w)[Words<F, 32>::kN]) {
+  constexpr bool kMX = MODE == MX_DUAL || MODE == MX_COL;
+  if constexpr (IN == IN_BF16 && kMX && R == CEIL && !HAD) {
+    // BF16 pairs of consecutive rows of the column straight into the converter
+    if (cmax < 0x7F800000u) {
+      const int e = shared_exponent<F, R>(cmax);
+      if (e > -127) {
+        const float scale = __uint_as_float(uint32_t(127 + e) << 23);
+        const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+        uint32_t p[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t d0 = *reinterpret_cast<const uint32_t*>(t + (2 * i) * pitch);
+          const uint32_t d1 = *reinterpret_cast<const uint32_t*>(t + (2 * i + 1) * pitch);
+          p[i] = __builtin_amdgcn_perm(d1, d0, sel);
+        }
+        cvt_values_bf16<F, 32>(p, scale, w);
+        return uint32_t(e + 127);
+      }
+    }
+  }
+  if constexpr (kMX && HAD) {
+    float cv[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) cv[i] = lds_elem<IN>(t, pitch, i, h);
+    hadamard32_inlane(cv, had_mask);
+    cmax = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) cmax = umax(cmax, abs_bits(cv[i]));
+    return mx_encode_f32<F, R, 32>(cv, cmax, w);
+  } else {
+    // the scale (or the per-tensor multiplier) is known: convert 16 values at a time
+    const bool nonfinite = cmax >= 0x7F800000u;
+    int e = 0;
+    if constexpr (kMX) e = nonfinite ? 0 : shared_exponent<F, R>(cmax);
+    constexpr int kHalfW = Words<F, 16>::kN;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float cv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cv[i] = lds_elem<IN>(t, pitch, 16 * half + i, h);
+      uint32_t wh[kHalfW];
+      if constexpr (kMX) {
+        mx_encode_given<F, R, 16>(cv, nonfinite, e, wh);
+      } else {
+        pt_encode_f32<F, 16>(cv, mult, pt_slow ? 0x7FFFFFFFu : cmax, wh);
+      }
+#pragma unroll
+      for (int k = 0; k < kHalfW; ++k) w[half * kHalfW + k] = wh[k];
+    }
+    if constexpr (kMX) return nonfinite ? 0xFFu : uint32_t(e + 127);
+    return 0;
+  }
+}
+
+// A workgroup of four waves quantizes one 128 x 128 supertile: wave j takes the
+// 32-row strip j.  Each wave loads its strip, does the row-wise half from
+// registers, stages the strip in its own LDS region and converts its column
+// blocks, leaving the transposed codes in that region.  After one workgroup
+// barrier all 256 threads write the supertile's transposed output so that 8
+// consecutive lanes fill each 128-byte line (a lane-per-column store pattern
+// would touch 64 lines per instruction), and the 4 column scales of each
+// column go out as one store.
+constexpr int kStripWaves = 4;
 
 template <int IN, int F, int R, int MODE, bool HAD, bool AMAX>
-__global__ __launch_bounds__(kTileThreads) void tile_kernel(TileArgs a) {
+__global__ __launch_bounds__(64 * kStripWaves) void strip_kernel(StripArgs a) {
   using W = typename LdsWord<IN>::T;
-  constexpr bool kRowOut = MODE == MX_DUAL || MODE == PT_ROW || MODE == PT_DUAL;
-  constexpr bool kColOut = MODE != PT_ROW;
-  constexpr bool kPT = MODE >= PT_ROW;
-  constexpr int kPad = 16 / sizeof(W);      // 16 bytes per LDS row keeps 16-byte alignment
-  constexpr int kPitch = kTile + kPad;
-  __shared__ W tile[kColOut ? kTile * kPitch : 1];
-  __shared__ uint32_t red[kTileThreads / 64];
-
-  const int tid = threadIdx.x;
-  const int tr = blockIdx.x / a.tiles_c, tc = blockIdx.x % a.tiles_c;
-  const int64_t r0 = int64_t(tr) * kTile, c0 = int64_t(tc) * kTile;
-  const int lane_q = tid & 3;
-  float mult = 1.0f;
-  if constexpr (kPT) mult = a.ring[a.hist_len + 1];
-  uint32_t tmax = 0;
-
-  // ---- load the tile: pass p covers row p*16 + tid/16, 8 columns per lane
-  const int lrow = tid >> 4, lcol = (tid & 15) * 8;
-  const bool col_ok = c0 + lcol < a.cols;
+  constexpr bool kRowOut = MODE == MX_DUAL || MODE == PT_DUAL;
+  constexpr bool kPT = MODE == PT_COL || MODE == PT_DUAL;
+  constexpr bool kMXCol = MODE == MX_DUAL || MODE == MX_COL;
   constexpr int kW = ChunkWords<IN>::kN;
-  uint4 raw[kPasses][kW];
-#pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int64_t r = r0 + p * 16 + lrow;
-#pragma unroll
-    for (int k = 0; k < kW; ++k) raw[p][k] = make_uint4(0, 0, 0, 0);
-    if (r < a.rows && col_ok) load_chunk<IN>(a.x, r * a.cols + c0 + lcol, raw[p]);
-  }
-#pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int64_t r = r0 + p * 16 + lrow;
-    const bool ok = r < a.rows && col_ok;
-    if constexpr (kColOut) {
-      // stage the raw input (zeros outside the matrix) for the column pass
-      uint4* lds = reinterpret_cast<uint4*>(&tile[(p * 16 + lrow) * kPitch + lcol]);
-#pragma unroll
-      for (int k = 0; k < kW; ++k) lds[k] = raw[p][k];
-    }
-    if (!ok) continue;
-    if constexpr (AMAX || kPT || kRowOut) {
-      float v[8];
-      widen_chunk<IN>(raw[p], v);
-      if constexpr (AMAX || kPT) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) tmax = umax(tmax, abs_bits_no_nan(v[j]));
-      }
-      if constexpr (kRowOut) {
-        const int64_t e0 = r * a.cols + c0 + lcol;
-        uint32_t c[8];
-        if constexpr (MODE == MX_DUAL) {
-          uint32_t m = 0;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) m = umax(m, abs_bits(v[j]));
-          m = quad_max(m);
-          const uint32_t sc = mx_encode<F, R, 8>(v, m, c);
-          if (lane_q == 0) a.s_row[e0 >> 5] = uint8_t(sc);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) c[j] = encode_rne_sat<F>(v[j] * mult);
-        }
-        store_codes8<F>(a.q_row, e0, c);
-      }
-    }
-  }
+  constexpr int kPitch = kStripCols + 16 / int(sizeof(W));   // 16 bytes of padding keep 16-byte alignment
+  constexpr int kRegion = kStripRows * kPitch * int(sizeof(W));  // bytes of LDS per wave
+  constexpr int kColBytes = kStripRows * Fmt_<F>::kBits / 8;     // codes of one column of a strip: 32 or 16
+  static_assert(kStripCols * kColBytes <= kRegion, "transposed codes must fit the strip region");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_all[kStripWaves][kRegion];
+  __shared__ uint8_t sc_lds[kStripWaves][kStripCols];
+  __shared__ uint32_t red[kStripWaves];
 
-  if constexpr (kColOut) {
-    __syncthreads();
-    // ---- column pass: wave w takes rows 32w..32w+31, lane l columns 2l, 2l+1
-    const int wv = tid >> 6, ln = tid & 63;
-    const int64_t rs = r0 + 32 * wv;
-    const int64_t cc = c0 + 2 * ln;
-    // cols is even, so columns cc and cc+1 are in range together
-    if (rs < a.rows && cc < a.cols) {
-      float cv[2][32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) lds_pair<IN>(&tile[(32 * wv + i) * kPitch + 2 * ln], cv[0][i], cv[1][i]);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int64_t col = cc + h;
-        uint32_t c[32];
-        if constexpr (MODE == MX_DUAL || MODE == MX_COL) {
-          if constexpr (HAD) hadamard32_inlane(cv[h], a.had_mask);
-          uint32_t m = 0;
-#pragma unroll
-          for (int i = 0; i < 32; ++i) m = umax(m, abs_bits(cv[h][i]));
-          const uint32_t sc = mx_encode<F, R, 32>(cv[h], m, c);
-          a.s_col[col * (a.rows >> 5) + (rs >> 5)] = uint8_t(sc);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 32; ++i) c[i] = encode_rne_sat<F>(cv[h][i] * mult);
-        }
-        constexpr int kPerByte = Fmt_<F>::kBits == 8 ? 1 : 2;
-        store_codes32<F>(a.q_col + (col * a.rows + rs) / kPerByte, c);
-      }
-    }
-  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  W* const tile = reinterpret_cast<W*>(lds_all[wave]);
+  const int lane_q = lane & 3;
+  float mult = 1.0f;
+  bool pt_slow = false;
+  if constexpr (kPT) mult = ring_multiplier(a.ring, pt_slow);
+  uint32_t tmax = 0;
+  const int lrow = lane >> 4, lcol = (lane & 15) * 8;
+  const int64_t scale_pitch = a.rows >> 5;        // column scales per column
+  // per-tensor modes: one ticket per workgroup
+  RingTicket tk{};
+  uint32_t posted = 0;
+  if constexpr (kPT) tk = ring_ticket(a.ring, blockIdx.x, gridDim.x);
 
-  // ---- per-tensor amax
-  if constexpr (AMAX || kPT) {
-    tmax = wave_max(tmax);
-    if ((tid & 63) == 0) red[tid >> 6] = tmax;
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t m = red[0];
+  for (int T = blockIdx.x; T < a.supertiles; T += gridDim.x) {
+    const int64_t rb = int64_t(T / a.strips_c) * 128;      // band origin
+    const int64_t r0 = rb + 32 * wave;
+    const int64_t c0 = int64_t(T % a.strips_c) * kStripCols;
+    const bool strip_ok = r0 < a.rows;                      // ragged bottom band
+    const bool col_ok = strip_ok && c0 + lcol < a.cols;
+
+    if (strip_ok) {
+      // ---- load: instruction i covers rows 4i .. 4i+3, 16 lanes (256 bytes) per row
+      const uint8_t* xs = static_cast<const uint8_t*>(a.x) + (r0 * a.cols + c0) * int64_t(sizeof(W));
+      uint4 raw[kStripLoads][kW];
 #pragma unroll
-      for (int w = 1; w < kTileThreads / 64; ++w) m = umax(m, red[w]);
-      if constexpr (!kPT) {
-        atomic_max_u32(a.amax_out, m);
-      } else {
-        // in-kernel delayed-scaling fold by the last workgroup (atomic ticket)
-        uint32_t* amax_slot = reinterpret_cast<uint32_t*>(a.ring + a.hist_len + 2);
-        uint32_t* ticket = reinterpret_cast<uint32_t*>(a.ring + a.hist_len + 3);
-        __hip_atomic_fetch_max(amax_slot, m, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        if (t == gridDim.x - 1) {
-          const uint32_t ab = __hip_atomic_load(amax_slot, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-          const float amax = __uint_as_float(ab);
-          float* hist = a.ring;
-          hist[a.hist_idx] = amax;
-          float h = 0.0f;
-          for (int i = 0; i < a.hist_len; ++i) h = fmaxf(h, hist[i]);
-          if (h > 0.0f && h < __uint_as_float(0x7F800000u)) {
-            const float s = (h / a.fp8_max) / a.margin;   // correctly rounded FP32 divisions
-            a.ring[a.hist_len] = s;
-            a.ring[a.hist_len + 1] = 1.0f / s;
+      for (int i = 0; i < kStripLoads; ++i) {
+#pragma unroll
+        for (int kk = 0; kk < kW; ++kk) raw[i][kk] = make_uint4(0, 0, 0, 0);
+        if (col_ok) load_chunk_nt<IN>(xs, (4 * i + lrow) * a.cols + lcol, raw[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < kStripLoads; ++i) {
+        uint4* l = reinterpret_cast<uint4*>(&tile[(4 * i + lrow) * kPitch + lcol]);
+#pragma unroll
+        for (int kk = 0; kk < kW; ++kk) l[kk] = raw[i][kk];
+        if (!col_ok) continue;
+        if constexpr (AMAX || kPT || kRowOut) {
+          float v[8];
+          widen_chunk<IN>(raw[i], v);
+          const uint32_t m = chunk_absmax<IN>(raw[i], v);
+          if constexpr (AMAX || kPT) tmax = amax_update(tmax, m, v);
+          if constexpr (kRowOut) {
+            const int64_t e0 = (r0 + 4 * i + lrow) * a.cols + c0 + lcol;
+            uint32_t w[Words<F, 8>::kN];
+            if constexpr (MODE == MX_DUAL) {
+              const uint32_t sc = row_chunk_mx<IN, F, R, false>(raw[i], v, m, 0u, lane_q, w);
+              if (lane_q == 0) a.s_row[e0 >> 5] = uint8_t(sc);
+            } else {
+              pt_encode_f32<F, 8>(v, mult, pt_slow ? 0x7FFFFFFFu : m, w);
+            }
+            store_row8<F>(a.q_row, e0, w);
           }
-          if (a.pt_amax_out) *a.pt_amax_out = amax;
-          __hip_atomic_store(amax_slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
+      // LDS accesses of one wave execute in order; keep the compiler from
+      // moving the reads above the writes
+      wave_lds_fence();
+      // ---- column pass: lane l converts columns 2l, 2l+1 (cols is even: both or neither in range)
+      uint32_t w[2][Words<F, 32>::kN];
+      uint32_t sc[2] = {0, 0};
+      const bool cc_ok = c0 + 2 * lane < a.cols;
+      if (cc_ok) {
+        const W* t = &tile[2 * lane];
+        uint32_t cmax[2];
+        col_absmax<IN>(t, kPitch, cmax);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          sc[h] = col_encode<IN, F, R, MODE, HAD>(t, kPitch, h, cmax[h], mult, pt_slow, a.had_mask, w[h]);
+      }
+      wave_lds_fence();   // every lane has read the strip before it is overwritten
+      if (cc_ok) {
+        // transposed codes of this strip: column c at byte c * kColBytes of the region
+        uint4* dst = reinterpret_cast<uint4*>(lds_all[wave] + 2 * lane * kColBytes);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int k = 0; k < kColBytes / 16; ++k)
+            dst[h * (kColBytes / 16) + k] = make_uint4(w[h][4 * k], w[h][4 * k + 1], w[h][4 * k + 2], w[h][4 * k + 3]);
+        }
+        if constexpr (kMXCol) {
+          sc_lds[wave][2 * lane] = uint8_t(sc[0]);
+          sc_lds[wave][2 * lane + 1] = uint8_t(sc[1]);
+        }
+      }
+    }
+    if constexpr (kPT) {
+      const uint32_t wm = wave_max(tmax);
+      if (lane == 0) red[wave] = wm;
+    }
+    __syncthreads();
+    if constexpr (kPT) {
+      // post the workgroup's max now; the dependent ticket is taken after the stores
+      if (threadIdx.x == 0) {
+        uint32_t mm = red[0];
+#pragma unroll
+        for (int k = 1; k < kStripWaves; ++k) mm = umax(mm, red[k]);
+        posted = ring_post_max(tk, mm);
+      }
+    }
+
+    // ---- coalesced transposed stores: output line (column c, 128 rows of the band)
+    {
+      constexpr int kPieces = 128 * Fmt_<F>::kBits / 8 / 16;    // 16-byte pieces per column: 8 (FP8) or 4 (FP4)
+      constexpr int kPerPiece = kPieces / kStripWaves;           // pieces per strip: 2 or 1
+      constexpr int kPerByte = Fmt_<F>::kBits == 8 ? 1 : 2;
+#pragma unroll
+      for (int it = 0; it < kStripCols * kPieces / 256; ++it) {
+        const int item = threadIdx.x + 256 * it;
+        const int c = item / kPieces, pc = item % kPieces;
+        const int sw = pc / kPerPiece;                           // strip (wave region) holding the piece
+        const int64_t col = c0 + c, row = rb + 32 * sw;
+        if (col < a.cols && row < a.rows) {
+          const uint4 v = *reinterpret_cast<const uint4*>(lds_all[sw] + c * kColBytes + (pc % kPerPiece) * 16);
+          *reinterpret_cast<uint4*>(a.q_col + (col * a.rows + rb) / kPerByte + pc * 16) = v;
+        }
+      }
+      if constexpr (kMXCol) {
+        if (threadIdx.x < kStripCols) {
+          const int c = threadIdx.x;
+          const int64_t col = c0 + c;
+          if (col < a.cols) {
+            uint8_t* sp = a.s_col + col * scale_pitch + (rb >> 5);
+            const int nst = a.rows - rb >= 128 ? 4 : int((a.rows - rb) >> 5);
+            if (nst == 4 && (reinterpret_cast<uintptr_t>(sp) & 3u) == 0) {
+              *reinterpret_cast<uint32_t*>(sp) = uint32_t(sc_lds[0][c]) | (uint32_t(sc_lds[1][c]) << 8) |
+                                                 (uint32_t(sc_lds[2][c]) << 16) | (uint32_t(sc_lds[3][c]) << 24);
+            } else {
+              for (int k = 0; k < nst; ++k) sp[k] = sc_lds[k][c];
+            }
+          }
+        }
+      }
+    }
+    if (T + int(gridDim.x) < a.supertiles) __syncthreads();   // LDS is reused by the next supertile
+  }
+
+  if constexpr (kPT) {
+    // an empty input runs no supertile: post nothing, still take the ticket
+    if (threadIdx.x == 0) ring_finish(a.ring, tk, posted, gridDim.x);
+  } else if constexpr (AMAX) {
+    // ---- per-tensor amax: one (conditional) atomic per workgroup
+    const uint32_t m = wave_max(tmax);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t mm = red[0];
+#pragma unroll
+      for (int w = 1; w < kStripWaves; ++w) mm = umax(mm, red[w]);
+      if (mm) atomic_max_u32(a.amax_out, mm);
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// Host-side dispatch
-// ---------------------------------------------------------------------------
 template <typename K, typename... Args>
 static mx_status_t launch(K kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
   hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
@@ -388,20 +676,30 @@ static mx_status_t rowwise_dispatch(const void* x, int64_t n, uint8_t* q, uint8_
 }
 
 template <int IN, int F, int R, int MODE>
-static mx_status_t tile_dispatch(TileArgs& a, bool had, bool amax, hipStream_t st) {
-  const int64_t tr = (a.rows + kTile - 1) / kTile, tcn = (a.cols + kTile - 1) / kTile;
-  a.tiles_c = int(tcn > 0 ? tcn : 1);
-  int64_t nt = tr * tcn;
-  if (nt == 0) nt = 1;   // per-tensor mode still folds an empty input
-  const dim3 grid{unsigned(nt)}, block{unsigned(kTileThreads)};
+static mx_status_t strip_dispatch(StripArgs& a, bool had, bool amax, hipStream_t st) {
+  a.strips_c = int((a.cols + kStripCols - 1) / kStripCols);
+  a.bands = int((a.rows + 127) / 128);
+  a.supertiles = a.strips_c * a.bands;
+  int64_t g = a.supertiles;
+  if (g == 0) g = 1;   // an empty per-tensor input still folds
+  const dim3 grid{unsigned(g)}, block{unsigned(64 * kStripWaves)};
   if constexpr (MODE == MX_COL) {
     if (had) {
-      return amax ? launch(tile_kernel<IN, F, R, MODE, true, true>, grid, block, st, a)
-                  : launch(tile_kernel<IN, F, R, MODE, true, false>, grid, block, st, a);
+      return amax ? launch(strip_kernel<IN, F, R, MODE, true, true>, grid, block, st, a)
+                  : launch(strip_kernel<IN, F, R, MODE, true, false>, grid, block, st, a);
     }
   }
-  return amax ? launch(tile_kernel<IN, F, R, MODE, false, true>, grid, block, st, a)
-              : launch(tile_kernel<IN, F, R, MODE, false, false>, grid, block, st, a);
+  return amax ? launch(strip_kernel<IN, F, R, MODE, false, true>, grid, block, st, a)
+              : launch(strip_kernel<IN, F, R, MODE, false, false>, grid, block, st, a);
+}
+
+template <int IN, int F>
+static mx_status_t pt_row_dispatch(const void* x, int64_t n, uint8_t* q, const RingArgs& r, hipStream_t st) {
+  const int64_t nchunks = n / 8;
+  const int64_t per = int64_t(kPtRowThreads) * kRowUnroll;
+  int64_t g = (nchunks + per - 1) / per;
+  if (g == 0) g = 1;   // an empty input still folds
+  return launch(pt_row_kernel<IN, F>, dim3{unsigned(g)}, dim3{unsigned(kPtRowThreads)}, st, x, nchunks, q, r);
 }
 
 // Expand runtime (in, fmt, rule) into template instances.
@@ -425,23 +723,23 @@ template <int IN, int F, int R> struct RowOp {
   }
 };
 template <int IN, int F, int R> struct ColOp {
-  static mx_status_t run(TileArgs& a, bool had, bool amax, hipStream_t st) {
-    return tile_dispatch<IN, F, R, MX_COL>(a, had, amax, st);
+  static mx_status_t run(StripArgs& a, bool had, bool amax, hipStream_t st) {
+    return strip_dispatch<IN, F, R, MX_COL>(a, had, amax, st);
   }
 };
 template <int IN, int F, int R> struct DualOp {
-  static mx_status_t run(TileArgs& a, bool amax, hipStream_t st) {
-    return tile_dispatch<IN, F, R, MX_DUAL>(a, false, amax, st);
+  static mx_status_t run(StripArgs& a, bool amax, hipStream_t st) {
+    return strip_dispatch<IN, F, R, MX_DUAL>(a, false, amax, st);
   }
 };
 template <int IN, int F, int R> struct PtOp {
-  static mx_status_t run(TileArgs& a, int layout, hipStream_t st) {
+  static mx_status_t run(StripArgs& a, int layout, hipStream_t st) {
     if constexpr (F == E2M1 || R != FLOOR) {
       return MX_ERR_UNSUPPORTED;
     } else {
-      if (layout == FP8_ROW) return tile_dispatch<IN, F, R, PT_ROW>(a, false, false, st);
-      if (layout == FP8_TRANSPOSED) return tile_dispatch<IN, F, R, PT_COL>(a, false, false, st);
-      return tile_dispatch<IN, F, R, PT_DUAL>(a, false, false, st);
+      if (layout == FP8_ROW) return pt_row_dispatch<IN, F>(a.x, a.rows * a.cols, a.q_row, a.ring, st);
+      if (layout == FP8_TRANSPOSED) return strip_dispatch<IN, F, R, PT_COL>(a, false, false, st);
+      return strip_dispatch<IN, F, R, PT_DUAL>(a, false, false, st);
     }
   }
 };
@@ -466,7 +764,7 @@ extern "C" mx_status_t mx_quantize(const void* x, mx_dtype_t in, int64_t rows, i
   if (n == 0) return MX_OK;
   if (orient == MX_ROWWISE)
     return expand<RowOp>(in, fmt, rule, x, n, q, scales, amax, hadamard != 0, hadamard_sign_mask, stream);
-  TileArgs a{};
+  StripArgs a{};
   a.x = x; a.rows = rows; a.cols = cols; a.q_col = q; a.s_col = scales; a.amax_out = amax;
   a.had_mask = hadamard_sign_mask;
   return expand<ColOp>(in, fmt, rule, a, hadamard != 0, amax != nullptr, stream);
@@ -483,7 +781,7 @@ extern "C" mx_status_t mx_quantize_dual(const void* x, mx_dtype_t in, int64_t ro
   // amax_out is a max-accumulator the caller initialises; nothing to do when empty
   uint32_t* amax = reinterpret_cast<uint32_t*>(amax_out);
   if (n == 0) return MX_OK;
-  TileArgs a{};
+  StripArgs a{};
   a.x = x; a.rows = rows; a.cols = cols; a.q_row = q_row; a.s_row = s_row; a.q_col = q_colT; a.s_col = s_colT;
   a.amax_out = amax;
   return expand<DualOp>(in, fmt, rule, a, amax != nullptr, stream);
@@ -505,8 +803,8 @@ extern "C" mx_status_t fp8_quantize_delayed(const void* x, mx_dtype_t in, int64_
   if (n > 0 && (!x || (need_q && !q) || (need_qT && !qT))) return MX_ERR_NULL;
   if (cols % 8 != 0 || (need_qT && rows % 32 != 0)) return MX_ERR_SHAPE;
   if (n > 0 && (misaligned(x) || (need_q && misaligned(q)) || (need_qT && misaligned(qT)))) return MX_ERR_ALIGN;
-  TileArgs a{};
-  a.x = x; a.rows = rows; a.cols = cols; a.q_row = q; a.q_col = qT; a.ring = ring; a.hist_len = hist_len;
-  a.hist_idx = hist_idx; a.fp8_max = fp8_max; a.margin = margin; a.pt_amax_out = amax_out;
+  StripArgs a{};
+  a.x = x; a.rows = rows; a.cols = cols; a.q_row = q; a.q_col = qT;
+  a.ring = RingArgs{ring, hist_len, hist_idx, fp8_max, margin, amax_out};
   return expand<PtOp>(in, fmt, MX_SCALE_FLOOR, a, int(layout), stream);
 }

@@ -40,17 +40,21 @@ class Ring:
         self.s = np.float32(1.0)
         self.m = np.float32(1.0)
 
-    def as_array(self) -> np.ndarray:
-        """The device layout: [hist | s | m | amax(=0) | ticket(=0)]."""
-        return np.concatenate([self.hist, np.array([self.s, self.m, 0.0, 0.0], dtype=np.float32)])
+    def as_array(self, scratch_words: int = 0) -> np.ndarray:
+        """The buffer layout between calls: [hist | s | m | amax(=0) | ticket(=0)],
+        followed by `scratch_words` zero words when the buffer carries extra
+        ticket scratch."""
+        return np.concatenate([self.hist, np.array([self.s, self.m, 0.0, 0.0], dtype=np.float32),
+                               np.zeros(scratch_words, dtype=np.float32)])
 
     @classmethod
-    def from_array(cls, arr):
+    def from_array(cls, arr, scratch_words: int = 0):
         arr = np.asarray(arr, dtype=np.float32)
-        r = cls(arr.size - 4)
-        r.hist = arr[:-4].copy()
-        r.s = np.float32(arr[-4])
-        r.m = np.float32(arr[-3])
+        n = arr.size - 4 - scratch_words
+        r = cls(n)
+        r.hist = arr[:n].copy()
+        r.s = np.float32(arr[n])
+        r.m = np.float32(arr[n + 1])
         return r
 
     def fold(self, amax, hist_idx: int, fp8_max: float, margin: float):
