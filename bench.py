@@ -18,10 +18,12 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline] 
        python bench.py --mode dual|gemm|copy ...   (one kernel only, for profiler passes;
                                                     'copy' is a plain 256 MiB device copy
                                                     used to calibrate the byte counters)
+       python bench.py --summarize OUT.md --stats S.csv --fetch F.csv --write W.csv
+                       --copy-fetch CF.csv --copy-write CW.csv --command "..."
+           (turns rocprofv3 outputs into the committed profile summary)
 """
 
 import argparse
-import ctypes
 import hashlib
 import json
 import os
@@ -35,7 +37,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0         # dense FP8 / MXFP8 MFMA
 FP4_PEAK_TFLOPS = 10100.0        # dense MXFP4 MFMA
 METRIC = "MX quantize GB/s (% HBM peak); MXFP8 GEMM TFLOP/s (% FP8 MFMA peak)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tile_kernel_dual_bf16_8192x4096_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "strip_kernel_dual_mxfp8_bf16_8192x4096.md")
 
 
 def kernel_source_hash() -> str:
@@ -70,7 +72,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--mode", choices=["full", "dual", "gemm", "copy"], default="full")
+    ap.add_argument("--summarize", metavar="OUT_MD")
+    ap.add_argument("--stats")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-fetch")
+    ap.add_argument("--copy-write")
+    ap.add_argument("--command", default="")
+    ap.add_argument("--kernel", default="strip_kernel<1, 0, 1, 0, false, true>")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the quantizers and the GEMM run on a single "
               "MI355X here (multi-GPU sharding is described, not built); use --gpus 1", file=sys.stderr)
@@ -128,16 +141,18 @@ def main():
     for i in range(args.warmup):
         dual(sets[i % nsets])
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # one event pair around the K back-to-back launches on the kernel's stream:
+    # their average is the kernel's average launch duration (no per-launch
+    # event overhead inside the region)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(args.steps):
-        ev[i][0].record(stream)
         dual(sets[i % nsets])
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    avg_kern_s = sum(kern_ms) / len(kern_ms) / 1e3
+    avg_kern_s = e0.elapsed_time(e1) / args.steps / 1e3
     ms_per_step = wall / args.steps * 1e3
     value = algo_bytes * args.steps / wall / 1e9
     achieved = algo_bytes / avg_kern_s / 1e9
@@ -155,8 +170,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic)},
-        "kernel_us": {"mean": round(avg_kern_s * 1e6, 2), "min": round(min(kern_ms) * 1e3, 2),
-                      "max": round(max(kern_ms) * 1e3, 2)},
+        "kernel_us": round(avg_kern_s * 1e6, 2),
     }
 
     # ------------------------------------------------------------------ GEMM + other workloads
@@ -175,17 +189,17 @@ def main():
 
 
 def time_calls(fn, n, warm, stream, torch):
+    """Average duration of fn's launches: one event pair around n back-to-back calls."""
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    for i in range(n):
-        ev[i][0].record(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
         fn()
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in ev]
-    return sum(ms) / len(ms) / 1e3
+    return e0.elapsed_time(e1) / n / 1e3
 
 
 def bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=10):
@@ -266,21 +280,85 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
     return res
 
 
-def cpu_baseline(workloads, np):
-    """The CPU oracle (numpy, single thread) on a 512-row strip of the same
-    workload: dual quantization + per-tensor amax of BF16 512 x 4096."""
+def _pmc_mean(path, kernel_substr, counter):
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize(args):
+    """Write the profile summary of the headline kernel from rocprofv3 CSVs.
+
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by the ratio of the
+    known bytes of a plain 256 MiB device copy to what the same counters read
+    for it; traffic_bytes_per_launch is their scaled sum."""
+    import csv
+    stats = [r for r in csv.DictReader(open(args.stats)) if args.kernel in r["Name"]]
+    avg_ns = float(stats[0]["AverageNs"])
+    calls = int(stats[0]["Calls"])
+    copy_bytes_kib = 256 * 1024
+    cf, _ = _pmc_mean(args.copy_fetch, "copyBuffer", "FETCH_SIZE") if "copyBuffer" in open(args.copy_fetch).read() \
+        else _pmc_mean(args.copy_fetch, "elementwise", "FETCH_SIZE")
+    cw, _ = _pmc_mean(args.copy_write, "copyBuffer", "WRITE_SIZE") if "copyBuffer" in open(args.copy_write).read() \
+        else _pmc_mean(args.copy_write, "elementwise", "WRITE_SIZE")
+    kf, nf = _pmc_mean(args.fetch, args.kernel, "FETCH_SIZE")
+    kw, nw = _pmc_mean(args.write, args.kernel, "WRITE_SIZE")
+    f_scale, w_scale = copy_bytes_kib / cf, copy_bytes_kib / cw
+    fetch_b = kf * f_scale * 1024
+    write_b = kw * w_scale * 1024
+    algo = 8192 * 4096 * 2 + 2 * 8192 * 4096 + 2 * (8192 * 4096 // 32) + 4
+    lines = [
+        f"# {args.kernel} -- MXFP8 E4M3 dual quantization, BF16 8192x4096, round-up scale, amax",
+        "",
+        f"command: {args.command}",
+        "",
+        f"kernel_avg_ns: {avg_ns:.0f}",
+        f"kernel_calls: {calls}",
+        f"algorithmic_bytes_per_launch: {algo}",
+        f"achieved_GBps_at_avg: {algo / avg_ns:.1f}",
+        f"FETCH_SIZE_KiB_per_dispatch_raw: {kf:.1f}  (n={nf})",
+        f"WRITE_SIZE_KiB_per_dispatch_raw: {kw:.1f}  (n={nw})",
+        f"copy_calibration: 256 MiB copy reads FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB "
+        f"-> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}",
+        f"hbm_fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"hbm_write_bytes_per_launch: {write_b:.0f}",
+        f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
+        f"traffic_over_algorithmic: {(fetch_b + write_b) / algo:.4f}",
+        f"kernel_source_hash: {kernel_source_hash()}",
+        "",
+    ]
+    with open(args.summarize, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def cpu_baseline(workloads, np, target_s=10.0):
+    """The CPU oracle (numpy, one thread) on the same workload: dual E4M3
+    quantization + amax of leading row strips of the BF16 8192 x 4096 input,
+    growing the strip until about target_s seconds of host work (or the whole
+    tensor); the rate of the largest strip is reported."""
     from oracle import mx as omx
-    rows, cols = 512, 4096
-    xb = workloads.cfg2()[:rows]
-    xs = workloads.bf16_to_f32(xb)
-    t0 = time.perf_counter()
-    omx.quantize_dual(xs, "e4m3", "ceil")
-    omx.tensor_amax(xs)
-    dt = time.perf_counter() - t0
-    b = rows * cols * 2 + 2 * rows * cols + 2 * (rows * cols // 32) + 4
-    return {"value": round(b / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} rows of the 8192x4096 BF16 input (dual E4M3 quantization + amax), "
-                      f"{dt:.1f} s on the host CPU"}
+    cols = 4096
+    xb_all = workloads.cfg2()
+    rows, spent, rate, dt = 256, 0.0, None, 0.0
+    while True:
+        xs = workloads.bf16_to_f32(xb_all[:rows])
+        t0 = time.perf_counter()
+        omx.quantize_dual(xs, "e4m3", "ceil")
+        omx.tensor_amax(xs)
+        dt = time.perf_counter() - t0
+        spent += dt
+        b = rows * cols * 2 + 2 * rows * cols + 2 * (rows * cols // 32) + 4
+        rate = b / dt / 1e9
+        if rows >= 8192 or spent >= target_s:
+            break
+        rows = min(8192, rows * 2 if spent + 2 * dt < target_s * 1.5 else rows)
+        if spent + 2 * dt >= target_s * 1.5:
+            break
+    return {"value": round(rate, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} of 8192 rows of the BF16 8192x4096 input (dual E4M3 quantization + amax), "
+                      f"{dt:.1f} s for that strip, {spent:.1f} s of oracle work in total on the host CPU"}
 
 
 if __name__ == "__main__":
