@@ -19,6 +19,8 @@
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
 
+#include <utility>
+
 namespace mxk {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -158,9 +160,498 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
       }
 }
 
+// ---------------------------------------------------------------------------
+// gemm256_kernel: the large-shape path (M, N multiples of 256, K of 1024).
+//
+// One workgroup of 4 waves owns a 256 x 256 output tile; each wave owns a
+// 128 x 128 quarter held as 4 x 4 MFMA accumulators (256 FP32 per lane, in
+// AGPRs).  K advances in stages of 64 code bytes per row (two K-blocks of FP8,
+// four of FP4, i.e. one or two 32 x 32 x 64 MFMA steps).  Stages go straight
+// from memory into LDS with gfx950's LDS-DMA loads (no register staging),
+// four deep: a stage's loads are issued three stages before it is consumed.
+//
+// Every buffer the loop reads is its own __shared__ object, written only by
+// LDS-DMA, and the loop is unrolled so that each access names its object
+// statically: the compiler can then tell which in-flight DMA an LDS read may
+// alias and waits for that one alone instead of draining every load.
+//
+// Codes: row r of a stage at r * 64 bytes; its 16-byte chunk c sits at
+// position c ^ swz(r), so the lanes of one ds_read_b128 phase hit distinct
+// banks.  The DMA side applies the permutation by choosing which global chunk
+// each lane fetches.
+//
+// Scales: a scale stage is 16 K-blocks = 4 words per row, fetched by 4-byte
+// LDS-DMA into a word-planar layout ([word][row]) so that the 32 rows read by
+// one instruction hit 32 banks; two scale stages are resident.
+//
+// The MFMA is fed with B as its first operand: the accumulator then holds
+// C^T fragments, i.e. each lane owns 4 consecutive columns of one row of C,
+// which makes the epilogue's stores 8 (BF16) or 16 (FP32) bytes wide.
+// ---------------------------------------------------------------------------
+
+namespace t256 {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTile = 256, kThreads = 256;
+constexpr int kRow = 64;                      // code bytes per tile row per stage
+constexpr int kStages = 4;
+constexpr int kOpBytes = kTile * kRow;        // one operand of one stage: 16 KiB
+constexpr int kLoads = kOpBytes / 1024 / 4;   // 1 KiB DMA instructions per wave per operand per stage
+constexpr int kCodeGroup = 2 * kLoads;        // vector-memory instructions per wave per stage
+constexpr int kKbPerScale = 16;               // K-blocks per scale stage
+constexpr int kMinK = 1024;                   // K granule of this path (two scale stages)
+
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage0[2 * kOpBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage1[2 * kOpBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage2[2 * kOpBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage3[2 * kOpBytes];
+__shared__ __attribute__((aligned(1024))) uint32_t g_scale0[2][4][kTile];   // [A/B][word][row]
+__shared__ __attribute__((aligned(1024))) uint32_t g_scale1[2][4][kTile];
+__shared__ __attribute__((aligned(1024))) uint32_t g_sink[4][64];   // landing area of the L2 prefetches (never read)
+
+template <int I>
+__device__ __forceinline__ uint8_t* stage() {
+  static_assert(I >= 0 && I < kStages, "four stage buffers");
+  if constexpr (I == 0) return g_stage0;
+  else if constexpr (I == 1) return g_stage1;
+  else if constexpr (I == 2) return g_stage2;
+  else return g_stage3;
+}
+
+template <int I>
+__device__ __forceinline__ uint32_t (*scales())[4][kTile] {
+  static_assert(I == 0 || I == 1, "two scale buffers");
+  if constexpr (I == 0) return g_scale0;
+  else return g_scale1;
+}
+
+template <bool FP4>
+struct Geo {
+  static constexpr int kSub = FP4 ? 2 : 1;           // MFMA steps per stage
+  static constexpr int kKb = FP4 ? 4 : 2;            // K-blocks per stage
+  static constexpr int kPerScale = kKbPerScale / kKb;  // stages per scale stage (8 or 4)
+  static constexpr int kUnroll = 2 * kPerScale;      // stages per unrolled loop body
+};
+
+// Chunk permutation of row r (measured on gfx950: 64-byte rows read as row = lane % 32,
+// chunk = lane / 32 (^ a uniform XOR) make ds_read_b128 conflict-free with this choice,
+// i.e. four active LDS cycles per instruction, the 256 B/clock peak).
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+// s_waitcnt vmcnt(vm) expcnt(7) lgkmcnt(0) (gfx9 encoding)
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((VM >> 4) << 14));
+}
+
+// Workgroup barrier that nothing is scheduled across (MFMAs have no memory
+// dependence and would otherwise drift past it).
+__device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+// Cache policy of the operand loads: SC0 (measured ~7% faster than the default here)
+constexpr int kPolicySc0 = 1;
+
+// LDS-DMA: lane i's BYTES bytes at rsrc + voff + soff land at lds_dst + BYTES * i
+// (lds_dst wave-uniform).  soff is uniform and lives in an SGPR.
+template <int BYTES>
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, void* lds_dst) {
+  static_assert(BYTES == 4 || BYTES == 16, "dword or dwordx4");
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, soff, 0,
+                                             kPolicySc0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_dst, 4, voff, soff, 0, 0);
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin; give every XCD a contiguous
+// run of the tile order, and walk tiles in groups of 8 tile-rows so that the
+// tiles running together on one XCD share their A and B panels in its L2.
+__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn, int& a_slice,
+                                         int& b_slice) {
+  const int ntiles = tiles_m * tiles_n;
+  int idx = bid;
+  if ((ntiles & 7) == 0) idx = (bid & 7) * (ntiles >> 3) + (bid >> 3);
+  constexpr int kGroupM = 8;
+  const int group = idx / (kGroupM * tiles_n);
+  const int first = group * kGroupM;
+  const int gm = min(tiles_m - first, kGroupM);
+  const int in = idx - group * kGroupM * tiles_n;
+  tm = first + in % gm;
+  tn = in / gm;
+  // the tiles of one XCD round (32 consecutive positions) are 8 tile-rows x 4 tile-columns:
+  // the 4 sharing an A panel split its rows by tn % 4, the 8 sharing a B panel by tile-row
+  a_slice = tn & 3;
+  b_slice = in % gm;
+}
+
+
+struct Ctx {
+  __amdgpu_buffer_rsrc_t a, b;     // the tile's 256 code rows of A / B
+  __amdgpu_buffer_rsrc_t sa, sb;   // the tile's 256 scale rows of A / B
+  __amdgpu_buffer_rsrc_t a0, b0, sa0, sb0;   // same bases, empty range: loads return 0, touch no memory
+  uint32_t code_off[kLoads];       // lane's byte offset in the tile rows for DMA instruction j
+  uint32_t sc_off;                 // lane's byte offset of its scale row, word `wave`
+  uint32_t sc_step;                // 64 scale rows
+  int rd_a, rd_b;                  // lane's row offset inside a stage object (row-tile 0)
+  int c0, c1;                      // lane's swizzled chunk offsets: chunk h and chunk h + 2
+  int sc_row_a, sc_row_b;          // lane's scale row (row-tile 0)
+  int h8;                          // 8 * (lane / 32): the second K-block of an MFMA step is one byte up
+  __amdgpu_buffer_rsrc_t pf, pf0;  // this wave's L2-prefetch rows (A: wave 0, B: wave 1, none: 2, 3) / empty
+  uint32_t pf_off;                 // lane's prefetch row offset
+};
+
+// Stages t and t + 1 (even t) into buffers SA_ and SB_: for every row block the two
+// instructions fetch the two halves of the same 128-byte lines back to back.  A dead
+// stage (past the end of K) issues the same loads on empty resources (zeros, no
+// memory traffic), which keeps the vmcnt bookkeeping uniform and the loop free of branches.
+template <int SA_, int SB_>
+__device__ __forceinline__ void issue_pair(const Ctx& c, int t, int wave, bool live0, bool live1) {
+  const __amdgpu_buffer_rsrc_t ra0 = live0 ? c.a : c.a0, rb0 = live0 ? c.b : c.b0;
+  const __amdgpu_buffer_rsrc_t ra1 = live1 ? c.a : c.a0, rb1 = live1 ? c.b : c.b0;
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    uint8_t* d0 = stage<SA_>() + (wave * kLoads + j) * 1024;
+    uint8_t* d1 = stage<SB_>() + (wave * kLoads + j) * 1024;
+    dma<16>(ra0, c.code_off[j], uint32_t(t * kRow), d0);
+    dma<16>(ra1, c.code_off[j], uint32_t((t + 1) * kRow), d1);
+    dma<16>(rb0, c.code_off[j], uint32_t(t * kRow), d0 + kOpBytes);
+    dma<16>(rb1, c.code_off[j], uint32_t((t + 1) * kRow), d1 + kOpBytes);
+  }
+}
+
+template <int U>
+__device__ __forceinline__ void issue_scales(const Ctx& c, int u, int wave, bool live) {
+  const __amdgpu_buffer_rsrc_t ra = live ? c.sa : c.sa0, rb = live ? c.sb : c.sb0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    dma<4>(ra, c.sc_off, uint32_t(16 * u) + j * c.sc_step, &scales<U>()[0][wave][64 * j]);
+    dma<4>(rb, c.sc_off, uint32_t(16 * u) + j * c.sc_step, &scales<U>()[1][wave][64 * j]);
+  }
+}
+
+// L2 prefetch of the 128-byte line column holding stages s and s + 1 (s even) for
+// this workgroup's slice of its XCD group's panels: one dword per line into an LDS
+// sink nobody reads.  Data that other workgroups of the group fetch with their
+// DMAs some stages later then hits in L2 instead of waiting on memory.
+constexpr int kPrefetchAhead = 4;   // stages beyond the DMA's own target
+__device__ __forceinline__ void issue_prefetch(const Ctx& c, int s, int wave, bool live) {
+  dma<4>(live ? c.pf : c.pf0, c.pf_off, uint32_t(s * kRow), &g_sink[wave][0]);
+}
+
+// Operands of MFMA step kk of stage t (stage buffer SI, scale buffer U).
+template <bool FP4, int SI, int U, int KK>
+__device__ __forceinline__ void read_step(const Ctx& c, int t, int lane, v8i (&a)[4], v8i (&b)[4], int (&sa)[4],
+                                          int (&sb)[4]) {
+  using G = Geo<FP4>;
+  const uint8_t* base = stage<SI>();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint8_t* pa = base + c.rd_a + i * 32 * kRow;
+    const uint8_t* pb = base + c.rd_b + i * 32 * kRow;
+    if constexpr (FP4) {   // the 32 codes of K-block 2 kk + h: chunk 2 kk + h
+      const int ch = KK == 0 ? c.c0 : c.c1;
+      const uint4 x = *reinterpret_cast<const uint4*>(pa + ch);
+      const uint4 y = *reinterpret_cast<const uint4*>(pb + ch);
+      a[i] = v8i{int(x.x), int(x.y), int(x.z), int(x.w), 0, 0, 0, 0};
+      b[i] = v8i{int(y.x), int(y.y), int(y.z), int(y.w), 0, 0, 0, 0};
+    } else {               // FP8: K = 16 h + [0, 16) and 32 + 16 h + [0, 16): chunks h and h + 2
+      const uint4 x0 = *reinterpret_cast<const uint4*>(pa + c.c0);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(pa + c.c1);
+      const uint4 y0 = *reinterpret_cast<const uint4*>(pb + c.c0);
+      const uint4 y1 = *reinterpret_cast<const uint4*>(pb + c.c1);
+      a[i] = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+      b[i] = v8i{int(y0.x), int(y0.y), int(y0.z), int(y0.w), int(y1.x), int(y1.y), int(y1.z), int(y1.w)};
+    }
+  }
+  // the word holding the lane's K-block (t * kKb) % 16 + 2 kk + h; the byte is
+  // picked by the consumer (scale_byte), after the read has surely landed
+  const int word = ((t * G::kKb) % kKbPerScale + 2 * KK) >> 2;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sa[i] = scales<U>()[0][word][c.sc_row_a + 32 * i];
+    sb[i] = scales<U>()[1][word][c.sc_row_b + 32 * i];
+  }
+}
+
+// Byte of a scale word for MFMA step kk of stage t: K-block (t * kKb + 2 kk + h) % 4.
+template <bool FP4, int KK>
+__device__ __forceinline__ int scale_byte(uint32_t word, int t, int h8) {
+  return (word >> (8 * ((t * Geo<FP4>::kKb + 2 * KK) & 3) + h8)) & 0xFF;
+}
+
+template <int FA, int FB, int KK>
+__device__ __forceinline__ void mfma_all(v16f (&acc)[4][4], const v8i (&a)[4], const v8i (&b)[4], const int (&swa)[4],
+                                         const int (&swb)[4], int t, int h8) {
+  constexpr bool kFp4 = FA == E2M1;
+  int sa[4], sb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sa[i] = scale_byte<kFp4, KK>(swa[i], t, h8);
+    sb[i] = scale_byte<kFp4, KK>(swb[i], t, h8);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], MfmaFmt<FB>::kCode,
+                                                                   MfmaFmt<FA>::kCode, 0, sb[j], 0, sa[i]);
+}
+
+// Scheduling masks of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
+
+// Interleave one MFMA step (16 MFMAs) with the memory instructions issued in
+// the same region -- VM LDS-DMA loads and DS operand reads for the next step --
+// so the LDS reads run in the shadow of the matrix unit instead of after it.
+template <int VM, int DS, int K>
+__device__ __forceinline__ void interleave_slot() {
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+  if constexpr (K < 8 && VM > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (VM + 7) / 8, 0);
+  constexpr int kDs = K < 14 ? DS * (K + 1) / 14 - DS * K / 14 : 0;   // all DS reads within the first 14 MFMAs
+  if constexpr (kDs > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kDs, 0);
+}
+
+template <int VM, int DS, int... K>
+__device__ __forceinline__ void interleave_slots(std::integer_sequence<int, K...>) {
+  (interleave_slot<VM, DS, K>(), ...);
+}
+
+template <int VM, int DS>
+__device__ __forceinline__ void interleave() {
+  static_assert(VM <= 25 && DS <= 24, "one step's worth");
+  interleave_slots<VM, DS>(std::make_integer_sequence<int, 16>{});
+}
+
+struct Regs {
+  v8i a[2][4], b[2][4];
+  int sa[2][4], sb[2][4];
+};
+
+// Stage t = t0 + P (P static inside the unrolled body).  The operands of its
+// first MFMA step are already in register set (P * kSub) & 1.
+// Stage groups are issued in pairs (2m + 4, 2m + 5) after odd stage 2m + 1: the
+// two DMA instructions for the same rows fetch the two 64-byte halves of the
+// same 128-byte lines back to back, so each line is fetched from L2 once.  A pair
+// issued after stage q also brings the next scale stage when q closes a scale stage.
+template <bool FP4>
+constexpr bool pair_has_scales(int q) {   // q: the (odd) stage after which the pair is issued
+  return ((q % Geo<FP4>::kPerScale) + Geo<FP4>::kPerScale) % Geo<FP4>::kPerScale == Geo<FP4>::kPerScale - 1;
+}
+
+// Vector-memory instructions issued after group t + 1 by the time the boundary
+// after stage t waits for it (t = P modulo the unrolled body, which is a
+// multiple of the scale stage, so the pattern is static).
+template <bool FP4, int P>
+constexpr int later_ops() {
+  constexpr int kScaleOps = 8;
+  // issue_pair interleaves its two stages instruction by instruction: the first
+  // stage of a pair is complete only once all but the pair's last instruction are
+  // every pair is followed by its scale stage (if any) and one prefetch instruction
+  if constexpr (P % 2 == 1)   // group t + 1 opens the pair issued after stage t - 2
+    return 1 + (pair_has_scales<FP4>(P - 2) ? kScaleOps : 0) + 1;
+  else                         // group t + 1 closes the pair issued after stage t - 3
+    return (pair_has_scales<FP4>(P - 3) ? kScaleOps : 0) + 1 + 2 * kCodeGroup +
+           (pair_has_scales<FP4>(P - 1) ? kScaleOps : 0) + 1;
+}
+
+template <int FA, int FB, int P>
+__device__ __forceinline__ void stage_steps(const Ctx& c, int t, int T, int nsuper, int lane, int wave, Regs& r,
+                                            v16f (&acc)[4][4]) {
+  constexpr bool kFp4 = FA == E2M1;
+  using G = Geo<kFp4>;
+  constexpr int SI = P % kStages;                          // this stage's buffer
+  constexpr int U = (P / G::kPerScale) & 1;                // this stage's scale buffer
+  constexpr int SIn = (P + 1) % kStages;                   // next stage's buffer
+  constexpr int Un = ((P + 1) / G::kPerScale) & 1;
+#pragma unroll
+  for (int kk = 0; kk < G::kSub; ++kk) {
+    const int cur = (P * G::kSub + kk) & 1, nxt = cur ^ 1;
+    if (kk + 1 < G::kSub) {
+      // next MFMA step is in this stage, already visible
+      read_step<kFp4, SI, U, 1>(c, t, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
+      mfma_all<FA, FB, 0>(acc, r.a[cur], r.b[cur], r.sa[cur], r.sb[cur], t, c.h8);
+      interleave<0, 12>();
+    } else {
+      // own DMA of stage t + 1 landed and own LDS reads done, then everybody's
+      wait_vm_lgkm0<later_ops<kFp4, P>()>();
+      barrier();
+      constexpr bool kIssue = P % 2 == 1;
+      constexpr bool kScales = kIssue && pair_has_scales<kFp4>(P);
+      if constexpr (kIssue) {
+        // stages t - 1 and t are fully read into registers: refill their buffers
+        // with stages t + 3 and t + 4, the two halves of the same lines
+        issue_pair<(P + 3) % kStages, (P + 4) % kStages>(c, t + 3, wave, t + 3 < T, t + 4 < T);
+        if constexpr (kScales) {
+          const int un = (t + 1) / G::kPerScale + 1;
+          issue_scales<((P + 1) / G::kPerScale + 1) & 1>(c, un, wave, un < nsuper);
+        }
+        issue_prefetch(c, t + 3 + kPrefetchAhead, wave, t + 3 + kPrefetchAhead < T);
+      }
+      // after the last stage this reads stale (in-bounds) LDS that no MFMA consumes; an
+      // unconditional read keeps the operand registers free of merge copies
+      read_step<kFp4, SIn, Un, 0>(c, t + 1, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
+      mfma_all<FA, FB, G::kSub - 1>(acc, r.a[cur], r.b[cur], r.sa[cur], r.sb[cur], t, c.h8);
+      interleave<(kIssue ? 2 * kCodeGroup + 1 : 0) + (kScales ? 8 : 0), kFp4 ? 12 : 20>();
+    }
+  }
+}
+
+template <int FA, int FB, int... P>
+__device__ __forceinline__ void unrolled_body(const Ctx& c, int t0, int T, int nsuper, int lane, int wave, Regs& r,
+                                              v16f (&acc)[4][4], std::integer_sequence<int, P...>) {
+  (stage_steps<FA, FB, P>(c, t0 + P, T, nsuper, lane, wave, r, acc), ...);
+}
+
+template <int FA, int FB, bool BF16OUT>
+__global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint8_t* __restrict__ A,
+                                                              const uint8_t* __restrict__ SA,
+                                                              const uint8_t* __restrict__ B,
+                                                              const uint8_t* __restrict__ SB, int K, float alpha,
+                                                              void* __restrict__ C, int64_t ldc, int tiles_m,
+                                                              int tiles_n) {
+  constexpr bool kFp4 = FA == E2M1;
+  using G = Geo<kFp4>;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn, a_slice, b_slice;
+  map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn, a_slice, b_slice);
+  const int kbytes = kFp4 ? K / 2 : K, kblocks = K / 32;
+  const int T = kbytes / kRow, nsuper = kblocks / kKbPerScale;
+
+  Ctx c;
+  c.a = make_rsrc(A + int64_t(tm) * kTile * kbytes, uint32_t(kTile * kbytes));
+  c.b = make_rsrc(B + int64_t(tn) * kTile * kbytes, uint32_t(kTile * kbytes));
+  c.sa = make_rsrc(SA + int64_t(tm) * kTile * kblocks, uint32_t(kTile * kblocks));
+  c.sb = make_rsrc(SB + int64_t(tn) * kTile * kblocks, uint32_t(kTile * kblocks));
+  c.a0 = make_rsrc(A, 0);
+  c.b0 = make_rsrc(B, 0);
+  c.sa0 = make_rsrc(SA, 0);
+  c.sb0 = make_rsrc(SB, 0);
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int row = (wave * kLoads + j) * 16 + (lane >> 2);
+    c.code_off[j] = uint32_t(row) * uint32_t(kbytes) + 16u * uint32_t((lane & 3) ^ swz(row));
+  }
+  c.sc_off = uint32_t(lane) * uint32_t(kblocks) + 4u * uint32_t(wave);
+  c.sc_step = uint32_t(64 * kblocks);
+  const int rr = lane & 31, h = lane >> 5;
+  // rows 32 i + rr of a wave's half share swz(rr): 32 i only changes higher row bits
+  c.rd_a = (wm * 128 + rr) * kRow;
+  c.rd_b = kOpBytes + (wn * 128 + rr) * kRow;
+  c.c0 = 16 * (h ^ swz(rr));
+  c.c1 = c.c0 ^ 32;
+  c.sc_row_a = wm * 128 + rr;
+  c.sc_row_b = wn * 128 + rr;
+  c.h8 = 8 * h;
+  c.pf = wave == 0 ? c.a : wave == 1 ? c.b : c.a0;
+  c.pf0 = c.a0;
+  c.pf_off = uint32_t(wave == 0 ? 64 * a_slice + lane : 32 * b_slice + (lane & 31)) * uint32_t(kbytes);
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  Regs r;
+
+  // prologue: code stages 0..3, scale stages 0 and 1 (T >= 16, nsuper >= 2)
+  // same op pattern as the loop (pair, its scale stage if any, one prefetch) so that
+  // the first boundaries' wait counts hold; the prologue's prefetches are empty
+  issue_scales<0>(c, 0, wave, true);
+  issue_pair<0, 1>(c, 0, wave, true, true);
+  issue_prefetch(c, 0, wave, false);
+  issue_pair<2, 3>(c, 2, wave, true, true);
+  issue_scales<1>(c, 1, wave, true);
+  issue_prefetch(c, 0, wave, false);
+  // scale stage 0 and code stage 0 landed; the pair order interleaves stages 0 and 1
+  // instruction by instruction, so wait for both: what may stay in flight is stages
+  // 2 and 3, scale stage 1 and the two prefetches
+  wait_vm_lgkm0<2 * kCodeGroup + 8 + 2>();
+  barrier();
+  read_step<kFp4, 0, 0, 0>(c, 0, lane, r.a[0], r.b[0], r.sa[0], r.sb[0]);
+
+  for (int t0 = 0; t0 < T; t0 += G::kUnroll)
+    unrolled_body<FA, FB>(c, t0, T, nsuper, lane, wave, r, acc, std::make_integer_sequence<int, G::kUnroll>{});
+
+  // the last groups (empty-range loads) still write LDS: drain them before the
+  // workgroup reuses its LDS or retires and hands it to another one
+  wait_vm_lgkm0<0>();
+
+  // epilogue: accumulator (i, j) holds C^T fragments -- lane (rr, h) owns row
+  // 32 i + rr and columns 32 j + 8 q + 4 h + [0, 4) in registers 4 q + [0, 4)
+  const int64_t row0 = int64_t(tm) * kTile + wm * 128;
+  const int64_t col0 = int64_t(tn) * kTile + wn * 128;
+  if constexpr (BF16OUT) {
+    // BF16: each wave stages its 128 x 128 quarter in a 32 KiB stage buffer (row
+    // pitch 256 B, 16-byte unit u of row r at u ^ (r % 16)), then writes whole
+    // 256-byte row segments: 16 lanes per row, 16 bytes per lane.
+    barrier();   // every wave is done with the stage buffers
+    uint8_t* ep = wave == 0 ? stage<0>() : wave == 1 ? stage<1>() : wave == 2 ? stage<2>() : stage<3>();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = 32 * i + rr, u = 4 * j + q;
+          const bf16x2 lo = __builtin_convertvector(f2{alpha * acc[i][j][4 * q], alpha * acc[i][j][4 * q + 1]}, bf16x2);
+          const bf16x2 hi = __builtin_convertvector(f2{alpha * acc[i][j][4 * q + 2], alpha * acc[i][j][4 * q + 3]}, bf16x2);
+          *reinterpret_cast<uint2*>(ep + row * 256 + 16 * (u ^ (row & 15)) + 8 * h) =
+              make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+        }
+    barrier();
+    const int u = lane & 15;
+#pragma unroll 8
+    for (int it = 0; it < 32; ++it) {
+      const int row = 4 * it + (lane >> 4);
+      const uint4 v = *reinterpret_cast<const uint4*>(ep + row * 256 + 16 * (u ^ (row & 15)));
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(C) + (row0 + row) * ldc + col0 + 8 * u) = v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t off = (row0 + 32 * i + rr) * ldc + col0 + 32 * j + 8 * q + 4 * h;
+          *reinterpret_cast<float4*>(static_cast<float*>(C) + off) =
+              make_float4(alpha * acc[i][j][4 * q], alpha * acc[i][j][4 * q + 1], alpha * acc[i][j][4 * q + 2],
+                          alpha * acc[i][j][4 * q + 3]);
+        }
+  }
+}
+
+}  // namespace t256
+
 template <int FA, int FB, bool BF>
 static mx_status_t gemm_dispatch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, int64_t M,
                                  int64_t N, int64_t K, float alpha, void* c, int64_t ldc, hipStream_t st) {
+  const int esize = BF ? 2 : 4;
+  const bool big = M % t256::kTile == 0 && N % t256::kTile == 0 && K % t256::kMinK == 0 && K > 0 && K <= (int64_t(1) << 22) &&
+                   (M / t256::kTile) * (N / t256::kTile) < (int64_t(1) << 31) && !misaligned(a) && !misaligned(b) &&
+                   !misaligned(sa) && !misaligned(sb) && !misaligned(c) && (ldc * esize) % 16 == 0;
+  if (big) {
+    const int64_t tm = M / t256::kTile, tn = N / t256::kTile;
+    hipLaunchKernelGGL((t256::gemm256_kernel<FA, FB, BF>), dim3(unsigned(tm * tn)), dim3(t256::kThreads), 0, st, a,
+                       sa, b, sb, int(K), alpha, c, ldc, int(tm), int(tn));
+    return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+  }
   const int64_t tm = (M + kBM - 1) / kBM, tn = (N + kBN - 1) / kBN;
   hipLaunchKernelGGL((gemm_kernel<FA, FB, BF>), dim3(unsigned(tm * tn)), dim3(kGemmThreads), 0, st, a, sa, b, sb, M,
                      N, K, alpha, c, ldc, int(tn));

@@ -66,6 +66,61 @@ def test_gemm_small_parity(fa, fb, shape):
     assert og.rel_frobenius(bf16_to_f64(c16), bf16_to_f64(og.f64_to_bf16_bits(ref))) <= BF16_TOL
 
 
+# Shapes on the 256 x 256-tile LDS-DMA path (M, N multiples of 256, K of 1024):
+# one tile at the minimum K; 6 tiles (no XCD regrouping); 8 tiles (regrouped
+# across XCDs, one tile column); a wide tile row at K = 3 * 1024 (odd number of
+# 16-K-block scale stages per unrolled pass).
+TILED_SHAPES = [(256, 256, 1024), (512, 768, 2048), (2048, 256, 1024), (256, 1024, 3072)]
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2"),
+                                   ("e2m1", "e2m1")])
+@pytest.mark.parametrize("shape", TILED_SHAPES)
+def test_gemm_tiled_path_parity(fa, fb, shape):
+    M, N, K = shape
+    qa, sa, qb, sb = quantized_operands(M, N, K, fa, fb, seed=M + 2 * N + 3 * K)
+    args = (upload_u8(qa), upload_u8(sa), upload_u8(qb), upload_u8(sb), fa, fb, -1.25)
+    c32 = host(mxa.mx_gemm(*args, out_dtype=torch.float32))
+    ref = check_fp32(c32, qa, sa, fa, qb, sb, fb, alpha=-1.25)
+    c16 = host(mxa.mx_gemm(*args, out_dtype=torch.bfloat16))
+    assert og.rel_frobenius(bf16_to_f64(c16), bf16_to_f64(og.f64_to_bf16_bits(ref))) <= BF16_TOL
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_gemm_tiled_path_exact_on_integer_valued_operands(fmt):
+    """Integer-valued operands on the tiled path: exact whatever the summation
+    order, so any misplaced code, scale byte or lane shows as an exact mismatch."""
+    g = np.random.default_rng(19)
+    M, N, K = 512, 256, 2048
+    vals = np.array([0, 1, 2, 3, 4, -1, -2, -3, -4], np.float32) if fmt == "e2m1" else \
+        np.arange(-16, 17).astype(np.float32)
+    A = g.choice(vals, size=(M, K)).astype(np.float32) * np.exp2((np.arange(K) // 32) % 5 - 2)[None, :]
+    B = g.choice(vals, size=(N, K)).astype(np.float32)
+    qa, sa = omx.quantize_rowwise(A.astype(np.float32), fmt, "ceil")
+    qb, sb = omx.quantize_rowwise(B, fmt, "ceil")
+    ref = og.gemm_ref(qa, sa, fmt, qb, sb, fmt)
+    c = host(mxa.mx_gemm(upload_u8(qa), upload_u8(sa), upload_u8(qb), upload_u8(sb), fmt, fmt, 1.0,
+                         out_dtype=torch.float32))
+    assert np.array_equal(c.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("ldc,dtype", [(576, torch.float32), (520, torch.bfloat16), (516, torch.bfloat16)])
+def test_gemm_tiled_shape_with_ldc(ldc, dtype):
+    """ldc > N: 16-byte-aligned rows stay on the tiled path, others (516 BF16)
+    take the general kernel; columns past N are never written."""
+    M, N, K = 256, 512, 1024
+    qa, sa, qb, sb = quantized_operands(M, N, K, "e4m3", "e4m3", 23)
+    out = torch.full((M, ldc), 7.0, dtype=dtype, device="cuda")
+    mxa.mx_gemm(upload_u8(qa), upload_u8(sa), upload_u8(qb), upload_u8(sb), "e4m3", "e4m3", 1.0, out=out[:, :N])
+    o = host(out.float())
+    ref = og.gemm_ref(qa, sa, "e4m3", qb, sb, "e4m3")
+    if dtype == torch.float32:
+        check_fp32(o[:, :N], qa, sa, "e4m3", qb, sb, "e4m3")
+    else:
+        assert og.rel_frobenius(o[:, :N].astype(np.float64), bf16_to_f64(og.f64_to_bf16_bits(ref))) <= BF16_TOL
+    assert (o[:, N:] == 7.0).all()
+
+
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
 def test_gemm_exact_on_integer_valued_operands(fmt):
     """Small integers times powers of two: every partial sum is exact in FP32, so
