@@ -345,7 +345,7 @@ __device__ __forceinline__ void issue_scales(const Ctx& c, int u, int wave, bool
 // this workgroup's slice of its XCD group's panels: one dword per line into an LDS
 // sink nobody reads.  Data that other workgroups of the group fetch with their
 // DMAs some stages later then hits in L2 instead of waiting on memory.
-constexpr int kPrefetchAhead = 4;   // stages beyond the DMA's own target
+constexpr int kPrefetchAhead = 6;   // stages beyond the DMA's own target
 __device__ __forceinline__ void issue_prefetch(const Ctx& c, int s, int wave, bool live) {
   dma<4>(live ? c.pf : c.pf0, c.pf_off, uint32_t(s * kRow), &g_sink[wave][0]);
 }
