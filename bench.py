@@ -21,6 +21,8 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline] 
        python bench.py --summarize OUT.md --stats S.csv --fetch F.csv --write W.csv
                        --copy-fetch CF.csv --copy-write CW.csv --command "..."
            (turns rocprofv3 outputs into the committed profile summary)
+       python bench.py --summarize-gemm profiles --stats S.csv [--pmc-gemm P.csv] --command "..."
+           (the same for the MXFP8 and MXFP4 GEMM kernels)
 """
 
 import argparse
@@ -73,6 +75,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--mode", choices=["full", "dual", "gemm", "copy"], default="full")
     ap.add_argument("--summarize", metavar="OUT_MD")
+    ap.add_argument("--summarize-gemm", metavar="OUT_DIR")
+    ap.add_argument("--pmc-gemm")
     ap.add_argument("--stats")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
@@ -81,6 +85,9 @@ def main():
     ap.add_argument("--command", default="")
     ap.add_argument("--kernel", default="strip_kernel<1, 0, 1, 0, false, true>")
     args = ap.parse_args()
+    if args.summarize_gemm:
+        summarize_gemm(args)
+        return
     if args.summarize:
         summarize(args)
         return
@@ -114,7 +121,9 @@ def main():
         return
     if args.mode == "gemm":
         print(json.dumps({"mode": "gemm", "gemm": bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np,
-                                                             torch, args.steps)}), flush=True)
+                                                             torch, args.steps),
+                          "gemm_fp4": bench_gemm_fp4(lib, sp, stream, dev, up_bf16, workloads, torch, args.steps)}),
+              flush=True)
         return
 
     # ------------------------------------------------------------------ headline: dual quantize
@@ -268,16 +277,32 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
         lib.mx_quantize(X.data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, xq.data_ptr(), xsc.data_ptr(), None, sp)
     t5q = time_calls(quant5, 20, 3, stream, torch)
     b5 = 2 * (8192 * 4096 * 2 + 4096 * 4096 + 4096 * 256)
-    dw = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
-    t5g = time_calls(lambda: lib.mx_gemm(gq.data_ptr(), gs.data_ptr(), 2, xq.data_ptr(), xsc.data_ptr(), 2, 4096,
-                                         4096, 8192, 1.0 / 32, dw.data_ptr(), 1, 4096, sp), 10, 2, stream, torch)
-    f5 = 2.0 * 4096 * 4096 * 8192
     res["hadamard_mxfp4_colwise_quant_2x_bf16_8192x4096"] = {"us": round(t5q * 1e6, 2),
                                                               "GB/s": round(b5 / t5q / 1e9, 1),
                                                               "hbm_frac": round(b5 / t5q / 1e9 / HBM_PEAK_GBS, 4)}
-    res["mxfp4_gemm_4096x4096x8192"] = {"us": round(t5g * 1e6, 2), "TFLOP/s": round(f5 / t5g / 1e12, 1),
-                                        "mfma_frac": round(f5 / t5g / 1e12 / FP4_PEAK_TFLOPS, 4)}
+    res["mxfp4_gemm_4096x4096x8192"] = time_gemm_fp4(lib, sp, stream, dev, gq, gs, xq, xsc, torch, 10)
     return res
+
+
+def time_gemm_fp4(lib, sp, stream, dev, gq, gs, xq, xsc, torch, steps):
+    """dW = (1/32) Gq^T Xq, MXFP4 operands [4096][8192 / 2 B] (K = 8192 tokens), BF16 out."""
+    dw = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+    t = time_calls(lambda: lib.mx_gemm(gq.data_ptr(), gs.data_ptr(), 2, xq.data_ptr(), xsc.data_ptr(), 2, 4096,
+                                       4096, 8192, 1.0 / 32, dw.data_ptr(), 1, 4096, sp), steps, 2, stream, torch)
+    f = 2.0 * 4096 * 4096 * 8192
+    return {"us": round(t * 1e6, 2), "TFLOP/s": round(f / t / 1e12, 1), "mfma_frac": round(f / t / 1e12 / FP4_PEAK_TFLOPS, 4)}
+
+
+def bench_gemm_fp4(lib, sp, stream, dev, up_bf16, workloads, torch, steps=10):
+    """The MXFP4 weight-gradient GEMM alone, on the Hadamard + MXFP4 column-wise operands."""
+    g_bits, x_bits, mask = workloads.cfg5()
+    G, X = up_bf16(g_bits), up_bf16(x_bits)
+    gq = torch.empty((4096, 4096), dtype=torch.uint8, device=dev)
+    gs = torch.empty((4096, 256), dtype=torch.uint8, device=dev)
+    xq, xsc = torch.empty_like(gq), torch.empty_like(gs)
+    lib.mx_quantize(G.data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, gq.data_ptr(), gs.data_ptr(), None, sp)
+    lib.mx_quantize(X.data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, xq.data_ptr(), xsc.data_ptr(), None, sp)
+    return time_gemm_fp4(lib, sp, stream, dev, gq, gs, xq, xsc, torch, steps)
 
 
 def _pmc_mean(path, kernel_substr, counter):
@@ -285,6 +310,49 @@ def _pmc_mean(path, kernel_substr, counter):
     vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
             if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
     return sum(vals) / len(vals), len(vals)
+
+
+GEMM_PROFILES = {
+    # kernel name substring -> (file, title, FLOPs per launch, dense peak TFLOP/s)
+    "gemm256_kernel<0, 0, true>": ("gemm256_kernel_mxfp8_8192x14336x4096.md",
+                                   "MXFP8 E4M3 GEMM, A 8192x4096 . (W 14336x4096)^T, BF16 out",
+                                   2.0 * 8192 * 14336 * 4096, FP8_PEAK_TFLOPS),
+    "gemm256_kernel<2, 2, true>": ("gemm256_kernel_mxfp4_4096x4096x8192.md",
+                                   "MXFP4 E2M1 GEMM, dW = (1/32) Gq^T Xq, 4096x4096, K = 8192, BF16 out",
+                                   2.0 * 4096 * 4096 * 8192, FP4_PEAK_TFLOPS),
+}
+
+
+def summarize_gemm(args):
+    """Profile summaries of the GEMM kernels from a rocprofv3 --stats CSV (and,
+    if given, a --pmc CSV with SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE)."""
+    import csv
+    rows = list(csv.DictReader(open(args.stats)))
+    for sub, (fname, title, flops, peak) in GEMM_PROFILES.items():
+        st = [r for r in rows if sub in r["Name"]]
+        if not st:
+            continue
+        r = st[0]
+        avg = float(r["AverageNs"])
+        tf = flops / avg / 1e3
+        lines = [f"# {sub} -- {title}", "", f"command: {args.command}", "",
+                 f"kernel: {r['Name'][:80]}", f"kernel_calls: {r['Calls']}", f"kernel_avg_ns: {avg:.0f}",
+                 f"kernel_min_ns: {float(r['MinNs']):.0f}", f"kernel_max_ns: {float(r['MaxNs']):.0f}",
+                 f"flops_per_launch: {flops:.0f}", f"achieved_TFLOPs_at_avg: {tf:.1f}",
+                 f"fraction_of_dense_peak_{peak:.0f}: {tf / peak:.4f}"]
+        if args.pmc_gemm:
+            busy, n = _pmc_mean(args.pmc_gemm, sub, "SQ_VALU_MFMA_BUSY_CYCLES")
+            grbm, _ = _pmc_mean(args.pmc_gemm, sub, "GRBM_GUI_ACTIVE")
+            # GRBM_GUI_ACTIVE is summed over the 8 XCDs; 1024 SIMDs carry the MFMA busy cycles
+            lines += [f"SQ_VALU_MFMA_BUSY_CYCLES_per_dispatch: {busy:.4g}  (n={n})",
+                      f"GRBM_GUI_ACTIVE_per_dispatch: {grbm:.4g}",
+                      f"mfma_busy_fraction: {busy / (grbm / 8 * 1024):.4f}",
+                      f"gpu_clock_GHz_from_GRBM: {grbm / 8 / avg:.3f}"]
+        lines.append("")
+        out = os.path.join(args.summarize_gemm, fname)
+        with open(out, "w") as f:
+            f.write("\n".join(lines))
+        print("\n".join(lines))
 
 
 def summarize(args):

@@ -675,22 +675,49 @@ static mx_status_t rowwise_dispatch(const void* x, int64_t n, uint8_t* q, uint8_
               : launch(rowwise_kernel<IN, F, R, false, false>, grid, block, st, x, nchunks, q, s, amax, mask);
 }
 
+// Workgroups of `kernel` resident at once on the current device (cached per
+// kernel and device): the strip kernels run as one such wave of persistent
+// workgroups that walk the supertiles (measured ~6-10% faster than one
+// workgroup per supertile, whose launch rounds load and compute in lockstep).
+template <typename K>
+static int64_t resident_workgroups(K kernel, int threads) {
+  static int64_t cached[16] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
+  if (cached[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || cus <= 0 ||
+        per_cu <= 0)
+      return 0;
+    cached[dev] = int64_t(cus) * per_cu;
+  }
+  return cached[dev];
+}
+
+template <typename K>
+static mx_status_t launch_strips(K kernel, const StripArgs& a, hipStream_t st) {
+  const int threads = 64 * kStripWaves;
+  int64_t g = a.supertiles;
+  const int64_t resident = resident_workgroups(kernel, threads);
+  if (resident > 0 && g > resident) g = resident;
+  if (g == 0) g = 1;   // an empty per-tensor input still folds
+  return launch(kernel, dim3{unsigned(g)}, dim3{unsigned(threads)}, st, a);
+}
+
 template <int IN, int F, int R, int MODE>
 static mx_status_t strip_dispatch(StripArgs& a, bool had, bool amax, hipStream_t st) {
   a.strips_c = int((a.cols + kStripCols - 1) / kStripCols);
   a.bands = int((a.rows + 127) / 128);
   a.supertiles = a.strips_c * a.bands;
-  int64_t g = a.supertiles;
-  if (g == 0) g = 1;   // an empty per-tensor input still folds
-  const dim3 grid{unsigned(g)}, block{unsigned(64 * kStripWaves)};
   if constexpr (MODE == MX_COL) {
     if (had) {
-      return amax ? launch(strip_kernel<IN, F, R, MODE, true, true>, grid, block, st, a)
-                  : launch(strip_kernel<IN, F, R, MODE, true, false>, grid, block, st, a);
+      return amax ? launch_strips(strip_kernel<IN, F, R, MODE, true, true>, a, st)
+                  : launch_strips(strip_kernel<IN, F, R, MODE, true, false>, a, st);
     }
   }
-  return amax ? launch(strip_kernel<IN, F, R, MODE, false, true>, grid, block, st, a)
-              : launch(strip_kernel<IN, F, R, MODE, false, false>, grid, block, st, a);
+  return amax ? launch_strips(strip_kernel<IN, F, R, MODE, false, true>, a, st)
+              : launch_strips(strip_kernel<IN, F, R, MODE, false, false>, a, st);
 }
 
 template <int IN, int F>
