@@ -264,6 +264,17 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
     res["delayed_fp8_transposed_bf16_8192x4096"] = {"us": round(t3 * 1e6, 2), "GB/s": round(b3 / t3 / 1e9, 1),
                                                     "hbm_frac": round(b3 / t3 / 1e9 / HBM_PEAK_GBS, 4)}
     del xs, qT
+    # stochastic-rounding MXFP4 row-wise of a BF16 8192 x 4096 gradient, one uint32 word per element
+    gx = up_bf16(workloads.cfg2(R, C))
+    words = torch.from_numpy(workloads.random_words((R, C), 47).view(np.int32)).to(dev)
+    sq = torch.empty((R, C // 2), dtype=torch.uint8, device=dev)
+    ss = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
+    tsr = time_calls(lambda: mxa.check(lib.mx_quantize_sr(gx.data_ptr(), 1, R, C, 32, 2, 1, words.data_ptr(),
+                                                          sq.data_ptr(), ss.data_ptr(), None, sp)), 32, 4, stream, torch)
+    bsr = R * C * 2 + R * C * 4 + R * C // 2 + R * C // 32
+    res["sr_mxfp4_rowwise_bf16_8192x4096"] = {"us": round(tsr * 1e6, 2), "GB/s": round(bsr / tsr / 1e9, 1),
+                                              "hbm_frac": round(bsr / tsr / 1e9 / HBM_PEAK_GBS, 4)}
+    del gx, words, sq, ss
     # Hadamard + column-wise MXFP4 quantization of both operands, then the MXFP4 GEMM
     g_bits, x_bits, mask = workloads.cfg5()
     G, X = up_bf16(g_bits), up_bf16(x_bits)

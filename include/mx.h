@@ -177,6 +177,32 @@ mx_status_t mx_dequantize(const uint8_t* q, const uint8_t* scales, int64_t rows,
                           int block, mx_elem_t fmt, mx_orient_t orient, void* out,
                           mx_dtype_t out_dtype, hipStream_t stream);
 
+/* Row-wise MXFP4 with stochastic rounding ([FAF], the 37.2K tokens/s
+ * configuration: row gradients quantized to MXFP4 with stochastic rounding; the
+ * page names the technique without defining it).  Definition implemented:
+ *   - the block scale X is the ordinary MX scale of `rule` (as mx_quantize);
+ *   - each element V_i has its own random word rand[i]; the magnitude
+ *     y = |V_i| / X is exact; an E2M1 magnitude is kept, y >= 6 saturates to 6,
+ *     and strictly between adjacent magnitudes lo < hi the code is hi iff
+ *     rand[i] < floor(2^32 (y - lo) / (hi - lo)), else lo (up with probability
+ *     (y - lo) / (hi - lo) to within 2^-32);
+ *   - the sign bit is copied (-0 stays -0); a block holding NaN or +-Inf gets
+ *     scale 255 and every code +-6 with the input's sign.
+ *
+ *   x        [rows][cols] input of type `in` (F32, BF16 or F16), 16-byte aligned.
+ *   rand     [rows][cols] uint32 random words (device), 16-byte aligned; the
+ *            caller draws them (any generator); the same words give the same codes.
+ *   fmt      must be MX_E2M1; block must be 32.
+ *   q        [rows][cols/2] packed codes (element 2j in the low nibble), 16-byte aligned.
+ *   scales   [rows][cols/32] E8M0 codes.
+ *   amax_out optional max-accumulator, as for mx_quantize.
+ * Shapes: cols % 32 == 0; rows == 0 or cols == 0 enqueues nothing.  Errors:
+ * MX_ERR_UNSUPPORTED (fmt, in, rule or block), MX_ERR_SHAPE, MX_ERR_NULL,
+ * MX_ERR_ALIGN, returned without a launch; MX_ERR_LAUNCH. */
+mx_status_t mx_quantize_sr(const void* x, mx_dtype_t in, int64_t rows, int64_t cols, int block,
+                           mx_elem_t fmt, mx_scale_rule_t rule, const uint32_t* rand,
+                           uint8_t* q, uint8_t* scales, float* amax_out, hipStream_t stream);
+
 /* Block-scaled GEMM ([UE8M0] MX definition paragraph: the matrix unit consumes the
  * codes and scales of both operands and accumulates in FP32):
  *   C[m][n] = alpha * sum_k (Qa[m][k] 2^(sa[m][k/32]-127)) (Qb[n][k] 2^(sb[n][k/32]-127))

@@ -15,6 +15,7 @@ The functions carry the names of the C entry points declared in
     fp8_quantize_delayed(x, ring, hist_idx, fmt, layout, fp8_max, margin, amax=False)
     mx_dequantize(q, scales, rows, cols, fmt, orient, out_dtype)
     mx_gemm(a, sa, b, sb, fmt_a, fmt_b, alpha, out_dtype)
+    mx_quantize_sr(x, rand, rule, amax=False)
 """
 
 import ctypes
@@ -55,14 +56,16 @@ lib.mx_quantize_dual.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _p, _p,
 lib.fp8_quantize_delayed.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _p, _p, _p, _i32, _i32, _f32, _f32, _p, _p]
 lib.mx_dequantize.argtypes = [_p, _p, _i64, _i64, _i32, _i32, _i32, _p, _i32, _p]
 lib.mx_gemm.argtypes = [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64, _f32, _p, _i32, _i64, _p]
-for _f in (lib.mx_quantize, lib.mx_quantize_dual, lib.fp8_quantize_delayed, lib.mx_dequantize, lib.mx_gemm):
+lib.mx_quantize_sr.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p]
+for _f in (lib.mx_quantize, lib.mx_quantize_dual, lib.fp8_quantize_delayed, lib.mx_dequantize, lib.mx_gemm,
+           lib.mx_quantize_sr):
     _f.restype = ctypes.c_int
 lib.mx_status_str.argtypes = [ctypes.c_int]
 lib.mx_status_str.restype = ctypes.c_char_p
 lib.mx_abi_version.restype = ctypes.c_int
 
 ENTRY_POINTS = ("mx_quantize", "mx_quantize_dual", "fp8_quantize_delayed", "mx_dequantize", "mx_gemm",
-                "mx_status_str", "mx_abi_version")
+                "mx_quantize_sr", "mx_status_str", "mx_abi_version")
 
 
 class MXError(RuntimeError):
@@ -159,6 +162,22 @@ def mx_quantize_dual(x, fmt="e4m3", rule="ceil", amax=False):
     check(lib.mx_quantize_dual(_ptr(x), _lookup(DTYPE, x.dtype, "dtype"), R, C, 32, f, _lookup(RULE, rule, "rule"),
                                _ptr(qr), _ptr(sr), _ptr(qc), _ptr(sc), _ptr(a), _stream(x)))
     return (qr, sr, qc, sc) if a is None else (qr, sr, qc, sc, a)
+
+
+def mx_quantize_sr(x, rand, rule="ceil", amax=False):
+    """Row-wise MXFP4 with stochastic rounding driven by rand (uint32 words, one
+    per element, same shape as x; any integer tensor of 4-byte elements).
+    Returns (q [R][C/2], scales [R][C/32]) or (q, scales, amax)."""
+    _check_2d(x)
+    R, C = x.shape
+    if rand.shape != x.shape or rand.element_size() != 4 or not rand.is_contiguous():
+        raise ValueError("rand must be a contiguous tensor of 32-bit words shaped like x")
+    q = torch.empty((R, C // 2), dtype=torch.uint8, device=x.device)
+    s = torch.empty((R, C // 32), dtype=torch.uint8, device=x.device)
+    a = _amax_buf(amax, x.device)
+    check(lib.mx_quantize_sr(_ptr(x), _lookup(DTYPE, x.dtype, "dtype"), R, C, 32, FMT["e2m1"],
+                             _lookup(RULE, rule, "rule"), _ptr(rand), _ptr(q), _ptr(s), _ptr(a), _stream(x)))
+    return (q, s) if a is None else (q, s, a)
 
 
 def new_ring(hist_len: int, device="cuda") -> torch.Tensor:

@@ -2,7 +2,7 @@
 
 Test infrastructure only (see ``oracle/__init__``).
 
-[FP4 page], the paragraph on the 37.2K tokens/s configuration: row gradients are
+[FAF], the paragraph on the 37.2K tokens/s configuration: row gradients are
 quantized to MXFP4 with stochastic rounding.  The page names the technique
 without defining it.  The reading taken here is the textbook one, driven by
 random bits the caller passes in:

@@ -190,3 +190,8 @@ def random_tensor(shape, seed: int, kind: str = "normal") -> np.ndarray:
     else:
         raise ValueError(kind)
     return x.astype(np.float32)
+
+
+def random_words(shape, seed: int) -> np.ndarray:
+    """uint32 random words (uniform over [0, 2^32)), the stochastic-rounding input."""
+    return rng(2000 + seed).integers(0, 2**32, size=shape, dtype=np.uint64).astype(np.uint32)
