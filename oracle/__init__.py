@@ -18,7 +18,9 @@ The oracle is plain, slow and exact:
   into the next scale.
 * ``hadamard`` - fixed-sign 32-point Walsh-Hadamard preconditioning.
 * ``gemm``     - block-scaled GEMM reference: float64 product of the
-  dequantized operands (the fake-quant emulation the MX studies use).
+  dequantized operands (the fake-quant emulation the MX studies use), and the
+  per-tensor FP8 GEMM (op(a) @ op(b) * scale + bias, batch-broadcast).
+* ``sr``       - stochastic-rounding MXFP4 with caller-supplied random words.
 
 Sources (cited by page and section, see each function):
   [UE8M0]  "EU8M0 FP8 ... domestic compute chips" article (ag-981.com, news 240):
@@ -39,4 +41,4 @@ constants (E4M3 max 448, min 2^-9, E8M0 range, k = 32, 8 scale bits per block)
 are pinned in ``tests/golden/``.
 """
 
-from . import formats, mx, delayed, hadamard, gemm  # noqa: F401
+from . import formats, mx, delayed, hadamard, gemm, sr  # noqa: F401

@@ -38,3 +38,26 @@ def rel_frobenius(c, ref) -> float:
     ref = np.asarray(ref, dtype=np.float64)
     den = np.linalg.norm(ref)
     return float(np.linalg.norm(c - ref) / (den if den > 0 else 1.0))
+
+
+def mm_fp8_ref(a, b, fmt, scale, trans_a=False, trans_b=False, bias=None) -> np.ndarray:
+    """Per-tensor FP8 GEMM reference: float64 op(a) @ op(b) * scale (+ bias).
+
+    [FP8PY] (``mm_fp8``): a and b are FP8 codes of one format, 2-D or 3-D, the
+    batch dimension broadcast as in matmul; op(x) is x transposed in its last two
+    dimensions when the matching flag is set (the flag and an inner-transposed
+    view are the same request); ``scale`` is the combined dequantization scale
+    of both operands; ``bias`` (BF16 bits, length n) is added in the epilogue.
+    The codes decode exactly to float64; the product, the scale and the bias
+    are applied in float64 in that order: (a @ b) * scale + bias."""
+    from .formats import bf16_bits_to_f32, decode
+    A = decode(np.asarray(a), fmt)
+    B = decode(np.asarray(b), fmt)
+    if trans_a:
+        A = np.swapaxes(A, -1, -2)
+    if trans_b:
+        B = np.swapaxes(B, -1, -2)
+    C = np.matmul(A, B) * float(np.float32(scale))
+    if bias is not None:
+        C = C + bf16_bits_to_f32(np.asarray(bias, dtype=np.uint16)).astype(np.float64)
+    return C
