@@ -122,7 +122,8 @@ def main():
     if args.mode == "gemm":
         print(json.dumps({"mode": "gemm", "gemm": bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np,
                                                              torch, args.steps),
-                          "gemm_fp4": bench_gemm_fp4(lib, sp, stream, dev, up_bf16, workloads, torch, args.steps)}),
+                          "gemm_fp4": bench_gemm_fp4(lib, sp, stream, dev, up_bf16, workloads, torch, args.steps),
+                          "mm_fp8": bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, args.steps)}),
               flush=True)
         return
 
@@ -292,6 +293,38 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
                                                               "GB/s": round(b5 / t5q / 1e9, 1),
                                                               "hbm_frac": round(b5 / t5q / 1e9 / HBM_PEAK_GBS, 4)}
     res["mxfp4_gemm_4096x4096x8192"] = time_gemm_fp4(lib, sp, stream, dev, gq, gs, xq, xsc, torch, 10)
+    del G, X, gq, gs, xq, xsc
+    res.update(bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
+    return res
+
+
+def bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=10):
+    """Per-tensor FP8 GEMM (mm_fp8) of the MLP up-projection: x [8192][4096] and
+    w [14336][4096] cast by the delayed-scaling FP8 quantizer (its second step, so
+    the rings hold real scales), scale = s_x s_w on the device, BF16 bias, BF16 out.
+    'nt': w as stored [N][K] (x @ w.t(), K-contiguous); 'nn': its transposed copy
+    [K][N] (N-contiguous, read through the LDS transpose)."""
+    M, N, K = 8192, 14336, 4096
+    a_bits, w_bits = workloads.cfg4()
+    x, w = up_bf16(a_bits), up_bf16(w_bits)
+    rx, rw = mxa.new_ring(16, dev), mxa.new_ring(16, dev)
+    for step in range(2):
+        xq, _ = mxa.fp8_quantize_delayed(x, rx, step, "e4m3", "row")
+        wq, wqT = mxa.fp8_quantize_delayed(w, rw, step, "e4m3", "dual")
+    del x, w
+    scale = (rx[16:17] * rw[16:17]).contiguous()
+    bias = up_bf16(workloads.to_bf16_bits(workloads.rng(4, 2).standard_normal(N) * 0.1))
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    flops = 2.0 * M * N * K
+    res = {}
+    for name, b, tb in (("nt", wq, 1), ("nn", wqT, 0)):
+        def call():
+            mxa.check(lib.mm_fp8(xq.data_ptr(), b.data_ptr(), 0, 1, M, N, K, 0, 0, 0, tb, scale.data_ptr(),
+                                 bias.data_ptr(), c.data_ptr(), sp))
+        t = time_calls(call, steps, 2, stream, torch)
+        tf = flops / t / 1e12
+        res[f"mm_fp8_e4m3_{name}_bias_8192x14336x4096"] = {"us": round(t * 1e6, 2), "TFLOP/s": round(tf, 1),
+                                                            "mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4)}
     return res
 
 

@@ -11,7 +11,8 @@
  *           and section 2 (transposes force re-quantization; dual row/column copies).
  *   [FP8PY] AstrAI astrai/extension/ops/fp8.py page (commit 432dfec): per-tensor
  *           quantize / quantize_dual with fused amax, transposed (K-contiguous)
- *           output, ring-state delayed scaling folded in-kernel by the last block.
+ *           output, ring-state delayed scaling folded in-kernel by the last block,
+ *           and the pre-quantized per-tensor FP8 GEMM mm_fp8.
  *   [FAF]   "Format-aware fusion" FP4 article (theaicronicle.com): MXFP4 with a
  *           fixed-sign 32-point Hadamard transform on the weight-gradient GEMM.
  *
@@ -221,6 +222,33 @@ mx_status_t mx_gemm(const uint8_t* a, const uint8_t* sa, mx_elem_t fmt_a,
                     const uint8_t* b, const uint8_t* sb, mx_elem_t fmt_b,
                     int64_t M, int64_t N, int64_t K, float alpha,
                     void* c, mx_dtype_t c_dtype, int64_t ldc, hipStream_t stream);
+
+/* Per-tensor FP8 GEMM ([FP8PY], mm_fp8: pre-quantized FP8 operands of one format,
+ * 2-D or 3-D with the batch broadcast as in matmul, inner-transposed operands
+ * folded into the layout, the combined dequantization scale, an optional BF16
+ * bias added in the FP32 epilogue, BF16 result):
+ *   C[p] = op(a[p]) op(b[p]) * scale (+ bias),   p = 0 .. batch-1
+ * where op(x) is x transposed when the matching trans flag is set.
+ *   a      trans_a == 0: [batch_a][M][K] codes; trans_a != 0: [batch_a][K][M].
+ *   b      trans_b == 0: [batch_b][K][N] codes; trans_b != 0: [batch_b][N][K].
+ *          batch_a = batch when a_batched != 0, else 1 (the one matrix is used for
+ *          every p); likewise b.  Both 16-byte aligned.
+ *   fmt    MX_E4M3 or MX_E5M2 (both operands).
+ *   scale  device pointer to one float: the combined dequantization scale (for
+ *          the delayed-scaling ring, the product of the two operands' s).  Read by
+ *          the kernel, so it may be produced on the stream without a host sync.
+ *   bias   device BF16 [N] or NULL; 2-byte aligned.
+ *   c      [batch][M][N] BF16, 2-byte aligned.
+ * Each output is fl32(acc * scale + bias) (one FMA; acc * scale without a bias),
+ * rounded once to BF16 (RNE); acc is the FP32 accumulation of the exact FP8
+ * products, with the matrix unit's accumulation described under mx_gemm.
+ * Shapes: K % 16 == 0 (K == 0 writes the bias or zeros); batch <= 65535; any M, N.
+ * Errors: MX_ERR_UNSUPPORTED (fmt), MX_ERR_SHAPE, MX_ERR_NULL (c, scale, or a / b
+ * when K > 0), MX_ERR_ALIGN; MX_ERR_LAUNCH. */
+mx_status_t mm_fp8(const uint8_t* a, const uint8_t* b, mx_elem_t fmt, int64_t batch,
+                   int64_t M, int64_t N, int64_t K, int a_batched, int b_batched,
+                   int trans_a, int trans_b, const float* scale, const uint16_t* bias,
+                   uint16_t* c, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* mx_status_str(mx_status_t status);

@@ -16,6 +16,7 @@ The functions carry the names of the C entry points declared in
     mx_dequantize(q, scales, rows, cols, fmt, orient, out_dtype)
     mx_gemm(a, sa, b, sb, fmt_a, fmt_b, alpha, out_dtype)
     mx_quantize_sr(x, rand, rule, amax=False)
+    mm_fp8(a, b, scale, trans_a, trans_b, bias, fmt)
 """
 
 import ctypes
@@ -57,15 +58,16 @@ lib.fp8_quantize_delayed.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _p, _p, _
 lib.mx_dequantize.argtypes = [_p, _p, _i64, _i64, _i32, _i32, _i32, _p, _i32, _p]
 lib.mx_gemm.argtypes = [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64, _f32, _p, _i32, _i64, _p]
 lib.mx_quantize_sr.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p]
+lib.mm_fp8.argtypes = [_p, _p, _i32, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p]
 for _f in (lib.mx_quantize, lib.mx_quantize_dual, lib.fp8_quantize_delayed, lib.mx_dequantize, lib.mx_gemm,
-           lib.mx_quantize_sr):
+           lib.mx_quantize_sr, lib.mm_fp8):
     _f.restype = ctypes.c_int
 lib.mx_status_str.argtypes = [ctypes.c_int]
 lib.mx_status_str.restype = ctypes.c_char_p
 lib.mx_abi_version.restype = ctypes.c_int
 
 ENTRY_POINTS = ("mx_quantize", "mx_quantize_dual", "fp8_quantize_delayed", "mx_dequantize", "mx_gemm",
-                "mx_quantize_sr", "mx_status_str", "mx_abi_version")
+                "mx_quantize_sr", "mm_fp8", "mx_status_str", "mx_abi_version")
 
 
 class MXError(RuntimeError):
@@ -228,4 +230,68 @@ def mx_gemm(a, sa, b, sb, fmt_a="e4m3", fmt_b="e4m3", alpha=1.0, out_dtype=torch
     check(lib.mx_gemm(_ptr(a), _ptr(sa), _lookup(FMT, fmt_a, "format"), _ptr(b), _ptr(sb),
                       _lookup(FMT, fmt_b, "format"), M, N, K, float(alpha), _ptr(out),
                       _lookup(DTYPE, out.dtype, "dtype"), out.stride(0), _stream(a)))
+    return out
+
+
+_FP8_DTYPES = {torch.float8_e4m3fn: "e4m3", torch.float8_e5m2: "e5m2"}
+
+
+def _fp8_operand(x, name):
+    """(tensor, batch, rows, cols, transposed_view) of a 2-D / 3-D FP8 operand: its
+    last two dimensions must be dense row-major or the transpose of dense row-major."""
+    if x.dim() not in (2, 3):
+        raise ValueError(f"{name} must be 2-D or 3-D")
+    if x.dtype not in _FP8_DTYPES and x.dtype != torch.uint8:
+        raise ValueError(f"{name} must hold FP8 codes (float8_e4m3fn, float8_e5m2 or uint8)")
+    r, c = x.shape[-2], x.shape[-1]
+    sr, sc = x.stride(-2), x.stride(-1)
+    if (sc == 1 and sr == c) or r <= 1 and sc == 1:
+        tview = False
+    elif sr == 1 and sc == r or c <= 1 and sr == 1:
+        tview = True
+    else:
+        raise ValueError(f"{name}: the last two dimensions must be contiguous or a transposed contiguous view")
+    batch = x.shape[0] if x.dim() == 3 else 1
+    if batch > 1 and x.stride(0) != r * c:
+        raise ValueError(f"{name}: batch stride must be rows * cols")
+    return batch, r, c, tview
+
+
+def mm_fp8(a, b, scale, trans_a=False, trans_b=False, bias=None, fmt=None):
+    """Pre-quantized FP8 GEMM: op(a) @ op(b) * scale (+ bias), BF16 out.
+
+    a, b: FP8 codes of one format (torch float8 tensors, or uint8 with ``fmt``),
+    2-D or 3-D (batch broadcast as in matmul); a transposed view of a contiguous
+    tensor is taken as stored, with the transpose folded into the layout.
+    scale: a float32 device tensor with one element (the combined dequantization
+    scale).  bias: BF16 [N] or None."""
+    fa = _FP8_DTYPES.get(a.dtype)
+    fb = _FP8_DTYPES.get(b.dtype)
+    if fa and fb and fa != fb:
+        raise ValueError("a and b must have the same FP8 format")
+    f = fa or fb or fmt or "e4m3"
+    if fmt is not None and fmt != f:
+        raise ValueError("fmt does not match the operand dtype")
+    ba, ra, ca, tva = _fp8_operand(a, "a")
+    bb, rb, cb, tvb = _fp8_operand(b, "b")
+    ka = bool(trans_a) != tva        # stored [K][M]
+    kb = bool(trans_b) != tvb        # stored [N][K]
+    M, K = (ca, ra) if trans_a else (ra, ca)
+    K2, N = (cb, rb) if trans_b else (rb, cb)
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if ba != bb and ba != 1 and bb != 1:
+        raise ValueError(f"batch dimensions {ba} and {bb} do not broadcast")
+    batch = max(ba, bb)
+    if not isinstance(scale, torch.Tensor):
+        raise ValueError("scale must be a float32 device tensor with one element")
+    if scale.dtype != torch.float32 or scale.numel() != 1:
+        raise ValueError("scale must be a float32 device tensor with one element")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.dim() != 1 or bias.numel() != N
+                             or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous BF16 vector of length N")
+    shape = (batch, M, N) if (a.dim() == 3 or b.dim() == 3) else (M, N)
+    out = torch.empty(shape, dtype=torch.bfloat16, device=a.device)
+    check(lib.mm_fp8(_ptr(a), _ptr(b), FMT[f], batch, M, N, K, int(ba > 1), int(bb > 1), int(ka), int(kb),
+                     _ptr(scale), _ptr(bias), _ptr(out), _stream(a)))
     return out

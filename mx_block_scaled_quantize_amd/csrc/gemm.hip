@@ -10,6 +10,12 @@
 // Operand layouts (K-contiguous "NT"): A [M][K] codes, sa [M][K/32];
 // B^T [N][K] codes, sb [N][K/32]; FP4 codes are packed two per byte.
 //
+// The same kernels serve the per-tensor FP8 GEMM of the AstrAI fp8.py page
+// (mm_fp8: C = op(a) op(b) * scale + bias, BF16 out): every block scale is
+// 2^0, the device-resident scale and the BF16 bias are applied in the FP32
+// epilogue, the batch index is the grid's y, and an operand stored with M (or
+// N) contiguous is handled in the kernel (no transposed copy).
+//
 // gemm_kernel: 128 x 128 output tile per workgroup, 4 waves in a 2 x 2 grid
 // with a 64 x 64 sub-tile (2 x 2 MFMA tiles) each, K-steps of 128 staged in LDS
 // (rows padded by 16 bytes so that the 8 lanes of a ds_read_b128 phase hit
@@ -30,6 +36,28 @@ constexpr int kBM = 128, kBN = 128, kBK = 128;
 constexpr int kGemmThreads = 256;
 
 template <int FA> struct OpBytes { static constexpr int kRow = FA == E2M1 ? kBK / 2 : kBK; };
+
+// Arguments of both GEMM kernels.  C[p] = alpha op(A[p]) op(B[p])^T where A is
+// [M][K] and B is [N][K] as the MFMA consumes them.  An operand is stored either
+// K-contiguous ([M][lda] / [N][ldb] bytes) or, per-tensor FP8 only, M- / N-
+// contiguous ([K][lda] / [K][ldb]).  Batch strides are in bytes for A and B (0
+// broadcasts one matrix) and in elements for C.
+struct GemmArgs {
+  const uint8_t* a;
+  const uint8_t* sa;            // MX scales of A [M][K/32] (unused per-tensor)
+  const uint8_t* b;
+  const uint8_t* sb;
+  void* c;
+  const float* alpha_ptr;       // per-tensor: the device-resident combined scale
+  const uint16_t* bias;         // per-tensor: BF16 [N] or null
+  int64_t M, N, K;
+  int64_t lda, ldb, ldc;
+  int64_t batch_a, batch_b, batch_c;
+  float alpha;                  // MX: the host scalar
+  int tiles_m, tiles_n;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
 // Operand-format field of the scaled MFMA: 0 FP8 E4M3, 1 FP8 E5M2, 2 FP6 E2M3,
 // 3 FP6 E3M2, 4 FP4 E2M1.
@@ -53,13 +81,11 @@ __device__ __forceinline__ v8i load_operand(const uint8_t* row, int kk, int h) {
   }
 }
 
-template <int FA, int FB, bool BF16OUT>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA,
-                                                            const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB,
-                                                            int64_t M, int64_t N, int64_t K, float alpha,
-                                                            void* __restrict__ C, int64_t ldc, int tiles_n) {
+template <int FA, int FB, bool BF16OUT, bool PT, bool TA, bool TB>
+__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
   constexpr int kRowA = OpBytes<FA>::kRow, kRowB = OpBytes<FB>::kRow;
   constexpr int kPitchA = kRowA + 16, kPitchB = kRowB + 16;
+  static_assert(!(TA || TB) || (PT && FA != E2M1 && FB != E2M1), "M/N-contiguous operands: per-tensor FP8 only");
   __shared__ __attribute__((aligned(16))) uint8_t sA[kBM * kPitchA];
   __shared__ __attribute__((aligned(16))) uint8_t sB[kBN * kPitchB];
   __shared__ uint8_t sSA[kBM * 4];
@@ -67,8 +93,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = int64_t(blockIdx.x / tiles_n) * kBM;
-  const int64_t n0 = int64_t(blockIdx.x % tiles_n) * kBN;
+  const int64_t m0 = int64_t(blockIdx.x / g.tiles_n) * kBM;
+  const int64_t n0 = int64_t(blockIdx.x % g.tiles_n) * kBN;
+  const int64_t M = g.M, N = g.N, K = g.K;
+  const uint8_t* __restrict__ A = g.a + int64_t(blockIdx.y) * g.batch_a;
+  const uint8_t* __restrict__ B = g.b + int64_t(blockIdx.y) * g.batch_b;
+  const uint8_t* __restrict__ SA = g.sa;
+  const uint8_t* __restrict__ SB = g.sb;
   const int64_t kbytesA = FA == E2M1 ? K / 2 : K, kbytesB = FB == E2M1 ? K / 2 : K;
   const int64_t kblocks = K / 32;
 
@@ -81,34 +112,54 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   for (int64_t k0 = 0; k0 < K; k0 += kBK) {
-    // ---- stage codes: 16-byte chunks, zero past the matrix
+    // ---- stage codes: 16-byte chunks, zero past the matrix (K-contiguous rows are
+    // whole 16-byte chunks: K is a multiple of 16); an M- / N-contiguous operand is
+    // gathered byte by byte, consecutive lanes on consecutive rows of the tile
     constexpr int kChA = kRowA / 16, kChB = kRowB / 16;
-    for (int i = tid; i < kBM * kChA; i += kGemmThreads) {
-      const int r = i / kChA, ch = i % kChA;
-      const int64_t gr = m0 + r;
-      const int64_t kb = (FA == E2M1 ? k0 / 2 : k0) + ch * 16;
-      uint4 d = make_uint4(0, 0, 0, 0);
-      if (gr < M && kb < kbytesA) d = *reinterpret_cast<const uint4*>(A + gr * kbytesA + kb);
-      *reinterpret_cast<uint4*>(&sA[r * kPitchA + ch * 16]) = d;
+    if constexpr (TA) {
+      for (int i = tid; i < kBM * kBK; i += kGemmThreads) {
+        const int r = i % kBM, kk = i / kBM;
+        const int64_t gr = m0 + r, gk = k0 + kk;
+        sA[r * kPitchA + kk] = (gr < M && gk < K) ? A[gk * g.lda + gr] : uint8_t(0);
+      }
+    } else {
+      for (int i = tid; i < kBM * kChA; i += kGemmThreads) {
+        const int r = i / kChA, ch = i % kChA;
+        const int64_t gr = m0 + r;
+        const int64_t kb = (FA == E2M1 ? k0 / 2 : k0) + ch * 16;
+        uint4 d = make_uint4(0, 0, 0, 0);
+        if (gr < M && kb < kbytesA) d = *reinterpret_cast<const uint4*>(A + gr * g.lda + kb);
+        *reinterpret_cast<uint4*>(&sA[r * kPitchA + ch * 16]) = d;
+      }
     }
-    for (int i = tid; i < kBN * kChB; i += kGemmThreads) {
-      const int r = i / kChB, ch = i % kChB;
-      const int64_t gr = n0 + r;
-      const int64_t kb = (FB == E2M1 ? k0 / 2 : k0) + ch * 16;
-      uint4 d = make_uint4(0, 0, 0, 0);
-      if (gr < N && kb < kbytesB) d = *reinterpret_cast<const uint4*>(B + gr * kbytesB + kb);
-      *reinterpret_cast<uint4*>(&sB[r * kPitchB + ch * 16]) = d;
+    if constexpr (TB) {
+      for (int i = tid; i < kBN * kBK; i += kGemmThreads) {
+        const int r = i % kBN, kk = i / kBN;
+        const int64_t gr = n0 + r, gk = k0 + kk;
+        sB[r * kPitchB + kk] = (gr < N && gk < K) ? B[gk * g.ldb + gr] : uint8_t(0);
+      }
+    } else {
+      for (int i = tid; i < kBN * kChB; i += kGemmThreads) {
+        const int r = i / kChB, ch = i % kChB;
+        const int64_t gr = n0 + r;
+        const int64_t kb = (FB == E2M1 ? k0 / 2 : k0) + ch * 16;
+        uint4 d = make_uint4(0, 0, 0, 0);
+        if (gr < N && kb < kbytesB) d = *reinterpret_cast<const uint4*>(B + gr * g.ldb + kb);
+        *reinterpret_cast<uint4*>(&sB[r * kPitchB + ch * 16]) = d;
+      }
     }
     // ---- stage scales: 4 K-blocks per row, 2^0 (code 127) past the matrix
-    for (int i = tid; i < kBM * 4; i += kGemmThreads) {
-      const int r = i >> 2, kb = i & 3;
-      const int64_t gr = m0 + r, gk = k0 / 32 + kb;
-      sSA[i] = (gr < M && gk < kblocks) ? SA[gr * kblocks + gk] : uint8_t(127);
-    }
-    for (int i = tid; i < kBN * 4; i += kGemmThreads) {
-      const int r = i >> 2, kb = i & 3;
-      const int64_t gr = n0 + r, gk = k0 / 32 + kb;
-      sSB[i] = (gr < N && gk < kblocks) ? SB[gr * kblocks + gk] : uint8_t(127);
+    if constexpr (!PT) {
+      for (int i = tid; i < kBM * 4; i += kGemmThreads) {
+        const int r = i >> 2, kb = i & 3;
+        const int64_t gr = m0 + r, gk = k0 / 32 + kb;
+        sSA[i] = (gr < M && gk < kblocks) ? SA[gr * kblocks + gk] : uint8_t(127);
+      }
+      for (int i = tid; i < kBN * 4; i += kGemmThreads) {
+        const int r = i >> 2, kb = i & 3;
+        const int64_t gr = n0 + r, gk = k0 / 32 + kb;
+        sSB[i] = (gr < N && gk < kblocks) ? SB[gr * kblocks + gk] : uint8_t(127);
+      }
     }
     __syncthreads();
 
@@ -124,8 +175,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
         const int rb = wn * 64 + t * 32 + (lane & 31);
         a[t] = load_operand<FA>(&sA[ra * kPitchA], kk, lane >> 5);
         b[t] = load_operand<FB>(&sB[rb * kPitchB], kk, lane >> 5);
-        sa[t] = sSA[ra * 4 + kblk];
-        sb[t] = sSB[rb * 4 + kblk];
+        sa[t] = PT ? 127 : sSA[ra * 4 + kblk];
+        sb[t] = PT ? 127 : sSB[rb * 4 + kblk];
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -138,6 +189,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
   }
 
   // ---- epilogue: D[8*(v/4) + 4*(l/32) + v%4][l%32] of each 32 x 32 tile
+  const float alpha = PT ? *g.alpha_ptr : g.alpha;
+  const int64_t ldc = g.ldc;
+  void* __restrict__ C = static_cast<uint8_t*>(g.c) + int64_t(blockIdx.y) * g.batch_c * (BF16OUT ? 2 : 4);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -147,7 +201,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
         const int64_t row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
         if (row < M && col < N) {
-          const float o = alpha * acc[i][j][v];
+          float o = alpha * acc[i][j][v];
+          if (PT && g.bias) o = __builtin_fmaf(alpha, acc[i][j][v], bf16_to_f32(g.bias[col]));
           if constexpr (BF16OUT) {
             const uint32_t bits = __float_as_uint(o);
             const uint32_t r = (bits & 0x7FFFFFFFu) > 0x7F800000u ? ((bits >> 16) | 0x40u)
@@ -187,6 +242,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
 // The MFMA is fed with B as its first operand: the accumulator then holds
 // C^T fragments, i.e. each lane owns 4 consecutive columns of one row of C,
 // which makes the epilogue's stores 8 (BF16) or 16 (FP32) bytes wide.
+//
+// An M- (or N-) contiguous FP8 operand keeps its storage order in LDS: a stage
+// is 64 K-rows of the tile's 256 columns (256 bytes each), 16-byte chunk c of
+// K-row k at position c ^ 2 (k % 8).  gfx950's ds_read_b64_tr_b8 turns it into
+// MFMA operands: within each group of 16 lanes, output lane i gets byte i % 8
+// of the 8 bytes addressed by lanes 2 b + i / 8 (b = 0..7), so lanes pointing
+// at K-row k0 + j / 2, columns m0 + 8 (j % 2) deliver column m0 + i, K-rows
+// k0 .. k0 + 7 to lane i -- one quarter of an FP8 operand.  With the XOR every
+// 32-lane half of such a read touches 16 distinct 16-byte bank groups.  Per-
+// tensor mode issues no scale loads and feeds every MFMA the scale 2^0.
 // ---------------------------------------------------------------------------
 
 namespace t256 {
@@ -202,6 +267,7 @@ constexpr int kLoads = kOpBytes / 1024 / 4;   // 1 KiB DMA instructions per wave
 constexpr int kCodeGroup = 2 * kLoads;        // vector-memory instructions per wave per stage
 constexpr int kKbPerScale = 16;               // K-blocks per scale stage
 constexpr int kMinK = 1024;                   // K granule of this path (two scale stages)
+constexpr int kMnPitch = kTile;               // M/N-contiguous stage: bytes per K-row
 
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage0[2 * kOpBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage1[2 * kOpBytes];
@@ -298,42 +364,47 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int&
 
 
 struct Ctx {
-  __amdgpu_buffer_rsrc_t a, b;     // the tile's 256 code rows of A / B
+  __amdgpu_buffer_rsrc_t a, b;     // the tile's code rows (K-contiguous) or columns (M/N-contiguous) of A / B
   __amdgpu_buffer_rsrc_t sa, sb;   // the tile's 256 scale rows of A / B
-  __amdgpu_buffer_rsrc_t a0, b0, sa0, sb0;   // same bases, empty range: loads return 0, touch no memory
-  uint32_t code_off[kLoads];       // lane's byte offset in the tile rows for DMA instruction j
+  __amdgpu_buffer_rsrc_t z;        // empty range: loads return 0 and touch no memory (any base will do)
+  uint32_t off_a[kLoads];          // lane's byte offset in the tile for DMA instruction j (A)
+  uint32_t off_b[kLoads];          // same for B
+  uint32_t step_a, step_b;         // bytes between consecutive stages (M/N-contiguous operands)
   uint32_t sc_off;                 // lane's byte offset of its scale row, word `wave`
   uint32_t sc_step;                // 64 scale rows
-  int rd_a, rd_b;                  // lane's row offset inside a stage object (row-tile 0)
+  int rd_a, rd_b;                  // lane's read base inside a stage object (row-tile 0)
   int c0, c1;                      // lane's swizzled chunk offsets: chunk h and chunk h + 2
+  int tp_a, tp_b;                  // M/N-contiguous: lane's swizzled chunk byte offset (row-tile 0)
   int sc_row_a, sc_row_b;          // lane's scale row (row-tile 0)
   int h8;                          // 8 * (lane / 32): the second K-block of an MFMA step is one byte up
-  __amdgpu_buffer_rsrc_t pf, pf0;  // this wave's L2-prefetch rows (A: wave 0, B: wave 1, none: 2, 3) / empty
-  uint32_t pf_off;                 // lane's prefetch row offset
+  __amdgpu_buffer_rsrc_t pf;       // this wave's L2-prefetch lines (A: wave 0, B: wave 1, none: 2, 3)
+  uint32_t pf_off;                 // lane's prefetch line offset
+  uint32_t pf_step;                // bytes between stages of the prefetched operand
 };
 
 // Stages t and t + 1 (even t) into buffers SA_ and SB_: for every row block the two
 // instructions fetch the two halves of the same 128-byte lines back to back.  A dead
 // stage (past the end of K) issues the same loads on empty resources (zeros, no
 // memory traffic), which keeps the vmcnt bookkeeping uniform and the loop free of branches.
-template <int SA_, int SB_>
+template <int SA_, int SB_, bool TA, bool TB>
 __device__ __forceinline__ void issue_pair(const Ctx& c, int t, int wave, bool live0, bool live1) {
-  const __amdgpu_buffer_rsrc_t ra0 = live0 ? c.a : c.a0, rb0 = live0 ? c.b : c.b0;
-  const __amdgpu_buffer_rsrc_t ra1 = live1 ? c.a : c.a0, rb1 = live1 ? c.b : c.b0;
+  const __amdgpu_buffer_rsrc_t ra0 = live0 ? c.a : c.z, rb0 = live0 ? c.b : c.z;
+  const __amdgpu_buffer_rsrc_t ra1 = live1 ? c.a : c.z, rb1 = live1 ? c.b : c.z;
+  const uint32_t step_a = TA ? c.step_a : uint32_t(kRow), step_b = TB ? c.step_b : uint32_t(kRow);
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) {
     uint8_t* d0 = stage<SA_>() + (wave * kLoads + j) * 1024;
     uint8_t* d1 = stage<SB_>() + (wave * kLoads + j) * 1024;
-    dma<16>(ra0, c.code_off[j], uint32_t(t * kRow), d0);
-    dma<16>(ra1, c.code_off[j], uint32_t((t + 1) * kRow), d1);
-    dma<16>(rb0, c.code_off[j], uint32_t(t * kRow), d0 + kOpBytes);
-    dma<16>(rb1, c.code_off[j], uint32_t((t + 1) * kRow), d1 + kOpBytes);
+    dma<16>(ra0, c.off_a[j], uint32_t(t) * step_a, d0);
+    dma<16>(ra1, c.off_a[j], uint32_t(t + 1) * step_a, d1);
+    dma<16>(rb0, c.off_b[j], uint32_t(t) * step_b, d0 + kOpBytes);
+    dma<16>(rb1, c.off_b[j], uint32_t(t + 1) * step_b, d1 + kOpBytes);
   }
 }
 
 template <int U>
 __device__ __forceinline__ void issue_scales(const Ctx& c, int u, int wave, bool live) {
-  const __amdgpu_buffer_rsrc_t ra = live ? c.sa : c.sa0, rb = live ? c.sb : c.sb0;
+  const __amdgpu_buffer_rsrc_t ra = live ? c.sa : c.z, rb = live ? c.sb : c.z;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     dma<4>(ra, c.sc_off, uint32_t(16 * u) + j * c.sc_step, &scales<U>()[0][wave][64 * j]);
@@ -346,42 +417,62 @@ __device__ __forceinline__ void issue_scales(const Ctx& c, int u, int wave, bool
 // sink nobody reads.  Data that other workgroups of the group fetch with their
 // DMAs some stages later then hits in L2 instead of waiting on memory.
 constexpr int kPrefetchAhead = 6;   // stages beyond the DMA's own target
+template <bool TA, bool TB>
 __device__ __forceinline__ void issue_prefetch(const Ctx& c, int s, int wave, bool live) {
-  dma<4>(live ? c.pf : c.pf0, c.pf_off, uint32_t(s * kRow), &g_sink[wave][0]);
+  const uint32_t step = (TA || TB) ? c.pf_step : uint32_t(kRow);
+  dma<4>(live ? c.pf : c.z, c.pf_off, uint32_t(s) * step, &g_sink[wave][0]);
+}
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+
+// FP8 operand from an M/N-contiguous stage: p is the lane's transpose-read address
+// for K-rows 16 h .. 16 h + 7; the other quarters sit 8, 32 and 40 K-rows down.
+__device__ __forceinline__ v8i mn_operand(const uint8_t* p) {
+  uint8_t* q = const_cast<uint8_t*>(p);
+  const v2i x0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(q));
+  const v2i x1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(q + 8 * kMnPitch));
+  const v2i x2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(q + 32 * kMnPitch));
+  const v2i x3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(q + 40 * kMnPitch));
+  return v8i{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+}
+
+// Operand from a K-contiguous stage row p (the lane's row start).
+template <bool FP4, int KK>
+__device__ __forceinline__ v8i km_operand(const Ctx& c, const uint8_t* p) {
+  if constexpr (FP4) {   // the 32 codes of K-block 2 kk + h: chunk 2 kk + h
+    const int ch = KK == 0 ? c.c0 : c.c1;
+    const uint4 x = *reinterpret_cast<const uint4*>(p + ch);
+    return v8i{int(x.x), int(x.y), int(x.z), int(x.w), 0, 0, 0, 0};
+  } else {               // FP8: K = 16 h + [0, 16) and 32 + 16 h + [0, 16): chunks h and h + 2
+    const uint4 x0 = *reinterpret_cast<const uint4*>(p + c.c0);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(p + c.c1);
+    return v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+  }
 }
 
 // Operands of MFMA step kk of stage t (stage buffer SI, scale buffer U).
-template <bool FP4, int SI, int U, int KK>
+template <bool FP4, int SI, int U, int KK, bool PT, bool TA, bool TB>
 __device__ __forceinline__ void read_step(const Ctx& c, int t, int lane, v8i (&a)[4], v8i (&b)[4], int (&sa)[4],
                                           int (&sb)[4]) {
   using G = Geo<FP4>;
   const uint8_t* base = stage<SI>();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint8_t* pa = base + c.rd_a + i * 32 * kRow;
-    const uint8_t* pb = base + c.rd_b + i * 32 * kRow;
-    if constexpr (FP4) {   // the 32 codes of K-block 2 kk + h: chunk 2 kk + h
-      const int ch = KK == 0 ? c.c0 : c.c1;
-      const uint4 x = *reinterpret_cast<const uint4*>(pa + ch);
-      const uint4 y = *reinterpret_cast<const uint4*>(pb + ch);
-      a[i] = v8i{int(x.x), int(x.y), int(x.z), int(x.w), 0, 0, 0, 0};
-      b[i] = v8i{int(y.x), int(y.y), int(y.z), int(y.w), 0, 0, 0, 0};
-    } else {               // FP8: K = 16 h + [0, 16) and 32 + 16 h + [0, 16): chunks h and h + 2
-      const uint4 x0 = *reinterpret_cast<const uint4*>(pa + c.c0);
-      const uint4 x1 = *reinterpret_cast<const uint4*>(pa + c.c1);
-      const uint4 y0 = *reinterpret_cast<const uint4*>(pb + c.c0);
-      const uint4 y1 = *reinterpret_cast<const uint4*>(pb + c.c1);
-      a[i] = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
-      b[i] = v8i{int(y0.x), int(y0.y), int(y0.z), int(y0.w), int(y1.x), int(y1.y), int(y1.z), int(y1.w)};
-    }
+    if constexpr (TA) a[i] = mn_operand(base + c.rd_a + (c.tp_a ^ (32 * i)));
+    else a[i] = km_operand<FP4, KK>(c, base + c.rd_a + i * 32 * kRow);
+    if constexpr (TB) b[i] = mn_operand(base + c.rd_b + (c.tp_b ^ (32 * i)));
+    else b[i] = km_operand<FP4, KK>(c, base + c.rd_b + i * 32 * kRow);
   }
-  // the word holding the lane's K-block (t * kKb) % 16 + 2 kk + h; the byte is
-  // picked by the consumer (scale_byte), after the read has surely landed
-  const int word = ((t * G::kKb) % kKbPerScale + 2 * KK) >> 2;
+  if constexpr (!PT) {
+    // the word holding the lane's K-block (t * kKb) % 16 + 2 kk + h; the byte is
+    // picked by the consumer (scale_byte), after the read has surely landed
+    const int word = ((t * G::kKb) % kKbPerScale + 2 * KK) >> 2;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sa[i] = scales<U>()[0][word][c.sc_row_a + 32 * i];
-    sb[i] = scales<U>()[1][word][c.sc_row_b + 32 * i];
+    for (int i = 0; i < 4; ++i) {
+      sa[i] = scales<U>()[0][word][c.sc_row_a + 32 * i];
+      sb[i] = scales<U>()[1][word][c.sc_row_b + 32 * i];
+    }
   }
 }
 
@@ -391,15 +482,15 @@ __device__ __forceinline__ int scale_byte(uint32_t word, int t, int h8) {
   return (word >> (8 * ((t * Geo<FP4>::kKb + 2 * KK) & 3) + h8)) & 0xFF;
 }
 
-template <int FA, int FB, int KK>
+template <int FA, int FB, int KK, bool PT>
 __device__ __forceinline__ void mfma_all(v16f (&acc)[4][4], const v8i (&a)[4], const v8i (&b)[4], const int (&swa)[4],
                                          const int (&swb)[4], int t, int h8) {
   constexpr bool kFp4 = FA == E2M1;
   int sa[4], sb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    sa[i] = scale_byte<kFp4, KK>(swa[i], t, h8);
-    sb[i] = scale_byte<kFp4, KK>(swb[i], t, h8);
+    sa[i] = PT ? 127 : scale_byte<kFp4, KK>(swa[i], t, h8);   // per-tensor: every block scale is 2^0
+    sb[i] = PT ? 127 : scale_byte<kFp4, KK>(swb[i], t, h8);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -430,7 +521,7 @@ __device__ __forceinline__ void interleave_slots(std::integer_sequence<int, K...
 
 template <int VM, int DS>
 __device__ __forceinline__ void interleave() {
-  static_assert(VM <= 25 && DS <= 24, "one step's worth");
+  static_assert(VM <= 25 && DS <= 32, "one step's worth");
   interleave_slots<VM, DS>(std::make_integer_sequence<int, 16>{});
 }
 
@@ -453,9 +544,9 @@ constexpr bool pair_has_scales(int q) {   // q: the (odd) stage after which the 
 // Vector-memory instructions issued after group t + 1 by the time the boundary
 // after stage t waits for it (t = P modulo the unrolled body, which is a
 // multiple of the scale stage, so the pattern is static).
-template <bool FP4, int P>
+template <bool FP4, int P, bool PT>
 constexpr int later_ops() {
-  constexpr int kScaleOps = 8;
+  constexpr int kScaleOps = PT ? 0 : 8;   // per-tensor mode issues no scale loads
   // issue_pair interleaves its two stages instruction by instruction: the first
   // stage of a pair is complete only once all but the pair's last instruction are
   // every pair is followed by its scale stage (if any) and one prefetch instruction
@@ -466,7 +557,14 @@ constexpr int later_ops() {
            (pair_has_scales<FP4>(P - 1) ? kScaleOps : 0) + 1;
 }
 
-template <int FA, int FB, int P>
+// LDS reads of one operand step: MX FP8 keeps its measured hint; per-tensor counts
+// 8 ds_read_b128 per K-contiguous operand and 16 transpose reads per M/N-contiguous one
+template <bool FP4, bool PT, bool TA, bool TB>
+constexpr int kDsReads() {
+  return PT ? (TA ? 16 : 8) + (TB ? 16 : 8) : FP4 ? 12 : 20;
+}
+
+template <int FA, int FB, int P, bool PT, bool TA, bool TB>
 __device__ __forceinline__ void stage_steps(const Ctx& c, int t, int T, int nsuper, int lane, int wave, Regs& r,
                                             v16f (&acc)[4][4]) {
   constexpr bool kFp4 = FA == E2M1;
@@ -480,85 +578,108 @@ __device__ __forceinline__ void stage_steps(const Ctx& c, int t, int T, int nsup
     const int cur = (P * G::kSub + kk) & 1, nxt = cur ^ 1;
     if (kk + 1 < G::kSub) {
       // next MFMA step is in this stage, already visible
-      read_step<kFp4, SI, U, 1>(c, t, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
-      mfma_all<FA, FB, 0>(acc, r.a[cur], r.b[cur], r.sa[cur], r.sb[cur], t, c.h8);
+      read_step<kFp4, SI, U, 1, PT, TA, TB>(c, t, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
+      mfma_all<FA, FB, 0, PT>(acc, r.a[cur], r.b[cur], r.sa[cur], r.sb[cur], t, c.h8);
       interleave<0, 12>();
     } else {
       // own DMA of stage t + 1 landed and own LDS reads done, then everybody's
-      wait_vm_lgkm0<later_ops<kFp4, P>()>();
+      wait_vm_lgkm0<later_ops<kFp4, P, PT>()>();
       barrier();
       constexpr bool kIssue = P % 2 == 1;
-      constexpr bool kScales = kIssue && pair_has_scales<kFp4>(P);
+      constexpr bool kScales = kIssue && !PT && pair_has_scales<kFp4>(P);
       if constexpr (kIssue) {
         // stages t - 1 and t are fully read into registers: refill their buffers
         // with stages t + 3 and t + 4, the two halves of the same lines
-        issue_pair<(P + 3) % kStages, (P + 4) % kStages>(c, t + 3, wave, t + 3 < T, t + 4 < T);
+        issue_pair<(P + 3) % kStages, (P + 4) % kStages, TA, TB>(c, t + 3, wave, t + 3 < T, t + 4 < T);
         if constexpr (kScales) {
           const int un = (t + 1) / G::kPerScale + 1;
           issue_scales<((P + 1) / G::kPerScale + 1) & 1>(c, un, wave, un < nsuper);
         }
-        issue_prefetch(c, t + 3 + kPrefetchAhead, wave, t + 3 + kPrefetchAhead < T);
+        issue_prefetch<TA, TB>(c, t + 3 + kPrefetchAhead, wave, t + 3 + kPrefetchAhead < T);
       }
       // after the last stage this reads stale (in-bounds) LDS that no MFMA consumes; an
       // unconditional read keeps the operand registers free of merge copies
-      read_step<kFp4, SIn, Un, 0>(c, t + 1, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
-      mfma_all<FA, FB, G::kSub - 1>(acc, r.a[cur], r.b[cur], r.sa[cur], r.sb[cur], t, c.h8);
-      interleave<(kIssue ? 2 * kCodeGroup + 1 : 0) + (kScales ? 8 : 0), kFp4 ? 12 : 20>();
+      read_step<kFp4, SIn, Un, 0, PT, TA, TB>(c, t + 1, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
+      mfma_all<FA, FB, G::kSub - 1, PT>(acc, r.a[cur], r.b[cur], r.sa[cur], r.sb[cur], t, c.h8);
+      interleave<(kIssue ? 2 * kCodeGroup + 1 : 0) + (kScales ? 8 : 0), kDsReads<kFp4, PT, TA, TB>()>();
     }
   }
 }
 
-template <int FA, int FB, int... P>
+template <int FA, int FB, bool PT, bool TA, bool TB, int... P>
 __device__ __forceinline__ void unrolled_body(const Ctx& c, int t0, int T, int nsuper, int lane, int wave, Regs& r,
                                               v16f (&acc)[4][4], std::integer_sequence<int, P...>) {
-  (stage_steps<FA, FB, P>(c, t0 + P, T, nsuper, lane, wave, r, acc), ...);
+  (stage_steps<FA, FB, P, PT, TA, TB>(c, t0 + P, T, nsuper, lane, wave, r, acc), ...);
 }
 
-template <int FA, int FB, bool BF16OUT>
-__global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint8_t* __restrict__ A,
-                                                              const uint8_t* __restrict__ SA,
-                                                              const uint8_t* __restrict__ B,
-                                                              const uint8_t* __restrict__ SB, int K, float alpha,
-                                                              void* __restrict__ C, int64_t ldc, int tiles_m,
-                                                              int tiles_n) {
+template <int FA, int FB, bool BF16OUT, bool PT, bool TA, bool TB>
+__global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) {
   constexpr bool kFp4 = FA == E2M1;
+  static_assert(!(TA || TB) || (PT && !kFp4 && BF16OUT), "M/N-contiguous operands: per-tensor FP8, BF16 out");
   using G = Geo<kFp4>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn, a_slice, b_slice;
-  map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn, a_slice, b_slice);
+  map_tile(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn, a_slice, b_slice);
+  const int K = int(g.K);
   const int kbytes = kFp4 ? K / 2 : K, kblocks = K / 32;
   const int T = kbytes / kRow, nsuper = kblocks / kKbPerScale;
+  // row pitch of the stored operands: K bytes when K-contiguous
+  const int lda = TA ? int(g.lda) : kbytes, ldb = TB ? int(g.ldb) : kbytes;
+  const uint8_t* A = g.a + int64_t(blockIdx.y) * g.batch_a;
+  const uint8_t* B = g.b + int64_t(blockIdx.y) * g.batch_b;
 
   Ctx c;
-  c.a = make_rsrc(A + int64_t(tm) * kTile * kbytes, uint32_t(kTile * kbytes));
-  c.b = make_rsrc(B + int64_t(tn) * kTile * kbytes, uint32_t(kTile * kbytes));
-  c.sa = make_rsrc(SA + int64_t(tm) * kTile * kblocks, uint32_t(kTile * kblocks));
-  c.sb = make_rsrc(SB + int64_t(tn) * kTile * kblocks, uint32_t(kTile * kblocks));
-  c.a0 = make_rsrc(A, 0);
-  c.b0 = make_rsrc(B, 0);
-  c.sa0 = make_rsrc(SA, 0);
-  c.sb0 = make_rsrc(SB, 0);
+  if constexpr (TA)   // columns tm * 256 .. + 255 of every K-row
+    c.a = make_rsrc(A + int64_t(tm) * kTile, uint32_t(int64_t(K - 1) * lda + kTile));
+  else
+    c.a = make_rsrc(A + int64_t(tm) * kTile * kbytes, uint32_t(kTile * kbytes));
+  if constexpr (TB)
+    c.b = make_rsrc(B + int64_t(tn) * kTile, uint32_t(int64_t(K - 1) * ldb + kTile));
+  else
+    c.b = make_rsrc(B + int64_t(tn) * kTile * kbytes, uint32_t(kTile * kbytes));
+  c.z = make_rsrc(A, 0);
+  if constexpr (!PT) {
+    c.sa = make_rsrc(g.sa + int64_t(tm) * kTile * kblocks, uint32_t(kTile * kblocks));
+    c.sb = make_rsrc(g.sb + int64_t(tn) * kTile * kblocks, uint32_t(kTile * kblocks));
+  }
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) {
+    // K-contiguous: instruction j of a wave covers 16 rows x 64 bytes; M/N-contiguous: 4 K-rows x 256 bytes
     const int row = (wave * kLoads + j) * 16 + (lane >> 2);
-    c.code_off[j] = uint32_t(row) * uint32_t(kbytes) + 16u * uint32_t((lane & 3) ^ swz(row));
+    const uint32_t km = uint32_t(row) * uint32_t(kbytes) + 16u * uint32_t((lane & 3) ^ swz(row));
+    const int kr = (wave * kLoads + j) * 4 + (lane >> 4);
+    const uint32_t mn_chunk = 16u * uint32_t((lane & 15) ^ (2 * (kr & 7)));
+    c.off_a[j] = TA ? uint32_t(kr) * uint32_t(lda) + mn_chunk : km;
+    c.off_b[j] = TB ? uint32_t(kr) * uint32_t(ldb) + mn_chunk : km;
   }
+  c.step_a = uint32_t(kRow) * uint32_t(TA ? lda : 1);
+  c.step_b = uint32_t(kRow) * uint32_t(TB ? ldb : 1);
   c.sc_off = uint32_t(lane) * uint32_t(kblocks) + 4u * uint32_t(wave);
   c.sc_step = uint32_t(64 * kblocks);
   const int rr = lane & 31, h = lane >> 5;
-  // rows 32 i + rr of a wave's half share swz(rr): 32 i only changes higher row bits
-  c.rd_a = (wm * 128 + rr) * kRow;
-  c.rd_b = kOpBytes + (wn * 128 + rr) * kRow;
+  // K-contiguous: rows 32 i + rr of a wave's half share swz(rr): 32 i only changes higher row bits
+  // M/N-contiguous: transpose-read lane j = lane % 16 of group lane / 16 points at K-row
+  // 16 h + j / 2 (+ 8, 32, 40), byte 8 (j % 2) of the group's 16-column chunk
+  const int tr_base = (16 * h + ((lane & 15) >> 1)) * kMnPitch + 8 * (lane & 1);
+  c.rd_a = TA ? tr_base : (wm * 128 + rr) * kRow;
+  c.rd_b = kOpBytes + (TB ? tr_base : (wn * 128 + rr) * kRow);
+  c.tp_a = 16 * ((8 * wm) ^ (lane & 14) ^ ((lane >> 4) & 1));
+  c.tp_b = 16 * ((8 * wn) ^ (lane & 14) ^ ((lane >> 4) & 1));
   c.c0 = 16 * (h ^ swz(rr));
   c.c1 = c.c0 ^ 32;
   c.sc_row_a = wm * 128 + rr;
   c.sc_row_b = wn * 128 + rr;
   c.h8 = 8 * h;
-  c.pf = wave == 0 ? c.a : wave == 1 ? c.b : c.a0;
-  c.pf0 = c.a0;
-  c.pf_off = uint32_t(wave == 0 ? 64 * a_slice + lane : 32 * b_slice + (lane & 31)) * uint32_t(kbytes);
+  c.pf = wave == 0 ? c.a : wave == 1 ? c.b : c.z;
+  // wave 0 covers a quarter of the A lines of a stage pair, wave 1 an eighth of the B lines
+  const uint32_t pf_a = TA ? uint32_t(32 * a_slice + (lane >> 1)) * uint32_t(lda) + 128u * uint32_t(lane & 1)
+                           : uint32_t(64 * a_slice + lane) * uint32_t(kbytes);
+  const uint32_t pf_b = TB ? uint32_t(16 * b_slice + ((lane & 31) >> 1)) * uint32_t(ldb) + 128u * uint32_t(lane & 1)
+                           : uint32_t(32 * b_slice + (lane & 31)) * uint32_t(kbytes);
+  c.pf_off = wave == 0 ? pf_a : pf_b;
+  c.pf_step = wave == 0 ? c.step_a : c.step_b;
 
   v16f acc[4][4];
 #pragma unroll
@@ -572,21 +693,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint8_t* __r
   // prologue: code stages 0..3, scale stages 0 and 1 (T >= 16, nsuper >= 2)
   // same op pattern as the loop (pair, its scale stage if any, one prefetch) so that
   // the first boundaries' wait counts hold; the prologue's prefetches are empty
-  issue_scales<0>(c, 0, wave, true);
-  issue_pair<0, 1>(c, 0, wave, true, true);
-  issue_prefetch(c, 0, wave, false);
-  issue_pair<2, 3>(c, 2, wave, true, true);
-  issue_scales<1>(c, 1, wave, true);
-  issue_prefetch(c, 0, wave, false);
+  if constexpr (!PT) issue_scales<0>(c, 0, wave, true);
+  issue_pair<0, 1, TA, TB>(c, 0, wave, true, true);
+  issue_prefetch<TA, TB>(c, 0, wave, false);
+  issue_pair<2, 3, TA, TB>(c, 2, wave, true, true);
+  if constexpr (!PT) issue_scales<1>(c, 1, wave, true);
+  issue_prefetch<TA, TB>(c, 0, wave, false);
   // scale stage 0 and code stage 0 landed; the pair order interleaves stages 0 and 1
   // instruction by instruction, so wait for both: what may stay in flight is stages
   // 2 and 3, scale stage 1 and the two prefetches
-  wait_vm_lgkm0<2 * kCodeGroup + 8 + 2>();
+  wait_vm_lgkm0<2 * kCodeGroup + (PT ? 0 : 8) + 2>();
   barrier();
-  read_step<kFp4, 0, 0, 0>(c, 0, lane, r.a[0], r.b[0], r.sa[0], r.sb[0]);
+  read_step<kFp4, 0, 0, 0, PT, TA, TB>(c, 0, lane, r.a[0], r.b[0], r.sa[0], r.sb[0]);
 
   for (int t0 = 0; t0 < T; t0 += G::kUnroll)
-    unrolled_body<FA, FB>(c, t0, T, nsuper, lane, wave, r, acc, std::make_integer_sequence<int, G::kUnroll>{});
+    unrolled_body<FA, FB, PT, TA, TB>(c, t0, T, nsuper, lane, wave, r, acc,
+                                      std::make_integer_sequence<int, G::kUnroll>{});
 
   // the last groups (empty-range loads) still write LDS: drain them before the
   // workgroup reuses its LDS or retires and hands it to another one
@@ -594,9 +716,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint8_t* __r
 
   // epilogue: accumulator (i, j) holds C^T fragments -- lane (rr, h) owns row
   // 32 i + rr and columns 32 j + 8 q + 4 h + [0, 4) in registers 4 q + [0, 4)
+  const float alpha = PT ? *g.alpha_ptr : g.alpha;
+  const int64_t ldc = g.ldc;
   const int64_t row0 = int64_t(tm) * kTile + wm * 128;
   const int64_t col0 = int64_t(tn) * kTile + wn * 128;
   if constexpr (BF16OUT) {
+    uint16_t* C = static_cast<uint16_t*>(g.c) + int64_t(blockIdx.y) * g.batch_c;
+    // per-tensor bias of the lane's 64 columns, added to alpha * acc with one rounding
+    float bias[4][4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint2 bw = make_uint2(0, 0);
+        if (PT && g.bias) bw = *reinterpret_cast<const uint2*>(g.bias + col0 + 32 * j + 8 * q + 4 * h);
+        bias[j][q][0] = __uint_as_float(bw.x << 16);
+        bias[j][q][1] = __uint_as_float(bw.x & 0xFFFF0000u);
+        bias[j][q][2] = __uint_as_float(bw.y << 16);
+        bias[j][q][3] = __uint_as_float(bw.y & 0xFFFF0000u);
+      }
+    const bool has_bias = PT && g.bias;
     // BF16: each wave stages its 128 x 128 quarter in a 32 KiB stage buffer (row
     // pitch 256 B, 16-byte unit u of row r at u ^ (r % 16)), then writes whole
     // 256-byte row segments: 16 lanes per row, 16 bytes per lane.
@@ -609,8 +748,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint8_t* __r
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = 32 * i + rr, u = 4 * j + q;
-          const bf16x2 lo = __builtin_convertvector(f2{alpha * acc[i][j][4 * q], alpha * acc[i][j][4 * q + 1]}, bf16x2);
-          const bf16x2 hi = __builtin_convertvector(f2{alpha * acc[i][j][4 * q + 2], alpha * acc[i][j][4 * q + 3]}, bf16x2);
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[e] = has_bias ? __builtin_fmaf(alpha, acc[i][j][4 * q + e], bias[j][q][e]) : alpha * acc[i][j][4 * q + e];
+          const bf16x2 lo = __builtin_convertvector(f2{o[0], o[1]}, bf16x2);
+          const bf16x2 hi = __builtin_convertvector(f2{o[2], o[3]}, bf16x2);
           *reinterpret_cast<uint2*>(ep + row * 256 + 16 * (u ^ (row & 15)) + 8 * h) =
               make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
         }
@@ -620,9 +763,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint8_t* __r
     for (int it = 0; it < 32; ++it) {
       const int row = 4 * it + (lane >> 4);
       const uint4 v = *reinterpret_cast<const uint4*>(ep + row * 256 + 16 * (u ^ (row & 15)));
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(C) + (row0 + row) * ldc + col0 + 8 * u) = v;
+      *reinterpret_cast<uint4*>(C + (row0 + row) * ldc + col0 + 8 * u) = v;
     }
   } else {
+    float* C = static_cast<float*>(g.c) + int64_t(blockIdx.y) * g.batch_c;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -630,7 +774,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint8_t* __r
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t off = (row0 + 32 * i + rr) * ldc + col0 + 32 * j + 8 * q + 4 * h;
-          *reinterpret_cast<float4*>(static_cast<float*>(C) + off) =
+          *reinterpret_cast<float4*>(C + off) =
               make_float4(alpha * acc[i][j][4 * q], alpha * acc[i][j][4 * q + 1], alpha * acc[i][j][4 * q + 2],
                           alpha * acc[i][j][4 * q + 3]);
         }
@@ -643,19 +787,64 @@ template <int FA, int FB, bool BF>
 static mx_status_t gemm_dispatch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, int64_t M,
                                  int64_t N, int64_t K, float alpha, void* c, int64_t ldc, hipStream_t st) {
   const int esize = BF ? 2 : 4;
+  GemmArgs g{};
+  g.a = a;
+  g.sa = sa;
+  g.b = b;
+  g.sb = sb;
+  g.c = c;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = FA == E2M1 ? K / 2 : K;
+  g.ldb = FB == E2M1 ? K / 2 : K;
+  g.ldc = ldc;
+  g.alpha = alpha;
   const bool big = M % t256::kTile == 0 && N % t256::kTile == 0 && K % t256::kMinK == 0 && K > 0 && K <= (int64_t(1) << 22) &&
                    (M / t256::kTile) * (N / t256::kTile) < (int64_t(1) << 31) && !misaligned(a) && !misaligned(b) &&
                    !misaligned(sa) && !misaligned(sb) && !misaligned(c) && (ldc * esize) % 16 == 0;
   if (big) {
-    const int64_t tm = M / t256::kTile, tn = N / t256::kTile;
-    hipLaunchKernelGGL((t256::gemm256_kernel<FA, FB, BF>), dim3(unsigned(tm * tn)), dim3(t256::kThreads), 0, st, a,
-                       sa, b, sb, int(K), alpha, c, ldc, int(tm), int(tn));
+    g.tiles_m = int(M / t256::kTile);
+    g.tiles_n = int(N / t256::kTile);
+    hipLaunchKernelGGL((t256::gemm256_kernel<FA, FB, BF, false, false, false>), dim3(unsigned(g.tiles_m * g.tiles_n)),
+                       dim3(t256::kThreads), 0, st, g);
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
   }
-  const int64_t tm = (M + kBM - 1) / kBM, tn = (N + kBN - 1) / kBN;
-  hipLaunchKernelGGL((gemm_kernel<FA, FB, BF>), dim3(unsigned(tm * tn)), dim3(kGemmThreads), 0, st, a, sa, b, sb, M,
-                     N, K, alpha, c, ldc, int(tn));
+  g.tiles_m = int((M + kBM - 1) / kBM);
+  g.tiles_n = int((N + kBN - 1) / kBN);
+  hipLaunchKernelGGL((gemm_kernel<FA, FB, BF, false, false, false>), dim3(unsigned(g.tiles_m * g.tiles_n)),
+                     dim3(kGemmThreads), 0, st, g);
   return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+// Per-tensor FP8: TA / TB say that the MFMA's A ([M][K]) / B ([N][K]) is stored
+// M- / N-contiguous.
+template <int F, bool TA, bool TB>
+static mx_status_t mm_launch(GemmArgs g, int64_t batch, hipStream_t st) {
+  constexpr int64_t kTile = t256::kTile;
+  const bool big = g.M % kTile == 0 && g.N % kTile == 0 && g.K % t256::kMinK == 0 && g.K > 0 &&
+                   g.K <= (int64_t(1) << 22) && (g.M / kTile) * (g.N / kTile) < (int64_t(1) << 31) &&
+                   g.K * g.lda < (int64_t(1) << 31) && g.K * g.ldb < (int64_t(1) << 31) && !misaligned(g.a) &&
+                   !misaligned(g.b) && !misaligned(g.c) && (g.batch_a % 16) == 0 && (g.batch_b % 16) == 0 &&
+                   (reinterpret_cast<uintptr_t>(g.bias) & 7u) == 0;
+  if (big) {
+    g.tiles_m = int(g.M / kTile);
+    g.tiles_n = int(g.N / kTile);
+    hipLaunchKernelGGL((t256::gemm256_kernel<F, F, true, true, TA, TB>),
+                       dim3(unsigned(g.tiles_m * g.tiles_n), unsigned(batch)), dim3(t256::kThreads), 0, st, g);
+    return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+  }
+  g.tiles_m = int((g.M + kBM - 1) / kBM);
+  g.tiles_n = int((g.N + kBN - 1) / kBN);
+  hipLaunchKernelGGL((gemm_kernel<F, F, true, true, TA, TB>), dim3(unsigned(g.tiles_m * g.tiles_n), unsigned(batch)),
+                     dim3(kGemmThreads), 0, st, g);
+  return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+template <int F>
+static mx_status_t mm_layouts(const GemmArgs& g, bool ta, bool tb, int64_t batch, hipStream_t st) {
+  if (ta) return tb ? mm_launch<F, true, true>(g, batch, st) : mm_launch<F, true, false>(g, batch, st);
+  return tb ? mm_launch<F, false, true>(g, batch, st) : mm_launch<F, false, false>(g, batch, st);
 }
 
 template <bool BF>
@@ -689,4 +878,39 @@ extern "C" mx_status_t mx_gemm(const uint8_t* a, const uint8_t* sa, mx_elem_t fm
   if (K > 0 && (misaligned(a) || misaligned(b))) return MX_ERR_ALIGN;
   return c_dtype == MX_BF16 ? gemm_formats<true>(fmt_a, fmt_b, a, sa, b, sb, M, N, K, alpha, c, ldc, stream)
                             : gemm_formats<false>(fmt_a, fmt_b, a, sa, b, sb, M, N, K, alpha, c, ldc, stream);
+}
+
+extern "C" mx_status_t mm_fp8(const uint8_t* a, const uint8_t* b, mx_elem_t fmt, int64_t batch, int64_t M, int64_t N,
+                              int64_t K, int a_batched, int b_batched, int trans_a, int trans_b, const float* scale,
+                              const uint16_t* bias, uint16_t* c, hipStream_t stream) {
+  if (fmt != MX_E4M3 && fmt != MX_E5M2) return MX_ERR_UNSUPPORTED;
+  if (batch < 0 || M < 0 || N < 0 || K < 0 || K % 16 != 0) return MX_ERR_SHAPE;
+  if (batch > 65535 || M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return MX_ERR_SHAPE;
+  if (batch == 0 || M == 0 || N == 0) return MX_OK;
+  if (!c || !scale || (K > 0 && (!a || !b))) return MX_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(c) & 1u) || (reinterpret_cast<uintptr_t>(bias) & 1u)) return MX_ERR_ALIGN;
+  if (K > 0 && (misaligned(a) || misaligned(b))) return MX_ERR_ALIGN;
+  GemmArgs g{};
+  g.a = a;
+  g.b = b;
+  g.c = c;
+  g.alpha_ptr = scale;
+  g.bias = bias;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = trans_a ? M : K;         // a stored [K][M] when transposed, else [M][K]
+  g.ldb = trans_b ? K : N;         // b stored [N][K] when transposed, else [K][N]
+  g.ldc = N;
+  g.batch_a = a_batched ? M * K : 0;
+  g.batch_b = b_batched ? K * N : 0;
+  g.batch_c = M * N;
+  if (!trans_a && a_batched && !b_batched && batch * M <= (int64_t(1) << 31)) {   // one GEMM with M' = batch M
+    g.M = batch * M;
+    g.batch_a = g.batch_c = 0;
+    batch = 1;
+  }
+  // the MFMA's B is op(b)^T: N-contiguous exactly when b is not transposed
+  return fmt == MX_E4M3 ? mm_layouts<E4M3>(g, trans_a != 0, trans_b == 0, batch, stream)
+                        : mm_layouts<E5M2>(g, trans_a != 0, trans_b == 0, batch, stream);
 }

@@ -145,6 +145,34 @@ def test_mx_gemm_argument_errors():
     assert f(None, None, 0, None, None, 0, 0, 64, 64, 1.0, None, 1, 64, None) == OK
 
 
+def test_mm_fp8_argument_errors():
+    f = lib.mm_fp8
+    # (a, b, fmt, batch, M, N, K, a_batched, b_batched, trans_a, trans_b, scale, bias, c, stream)
+    assert f(FAKE, FAKE, 2, 1, 64, 64, 64, 0, 0, 0, 0, FAKE, None, FAKE, None) == UNSUP   # FP4 is not FP8
+    assert f(FAKE, FAKE, 0, 1, 64, 64, 40, 0, 0, 0, 0, FAKE, None, FAKE, None) == SHAPE   # K % 16
+    assert f(FAKE, FAKE, 0, 70000, 64, 64, 64, 1, 1, 0, 0, FAKE, None, FAKE, None) == SHAPE   # batch limit
+    assert f(FAKE, FAKE, 0, 1, -1, 64, 64, 0, 0, 0, 0, FAKE, None, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, 0, 1, 64, 64, 64, 0, 0, 0, 0, None, None, FAKE, None) == NULL    # scale
+    assert f(None, FAKE, 0, 1, 64, 64, 64, 0, 0, 0, 0, FAKE, None, FAKE, None) == NULL
+    assert f(FAKE, FAKE, 0, 1, 64, 64, 64, 0, 0, 0, 0, FAKE, None, None, None) == NULL
+    assert f(FAKE + 8, FAKE, 0, 1, 64, 64, 64, 0, 0, 0, 0, FAKE, None, FAKE, None) == ALIGN
+    assert f(FAKE, FAKE, 1, 1, 64, 64, 64, 0, 0, 0, 0, FAKE, FAKE + 1, FAKE, None) == ALIGN   # odd bias
+    assert f(FAKE, FAKE, 1, 1, 64, 64, 64, 0, 0, 0, 0, FAKE, None, FAKE + 1, None) == ALIGN   # odd c
+    assert f(None, None, 0, 0, 64, 64, 64, 0, 0, 0, 0, None, None, None, None) == OK      # batch 0
+    assert f(None, None, 0, 1, 0, 64, 64, 0, 0, 0, 0, None, None, None, None) == OK       # M 0
+
+
+def test_mx_quantize_sr_argument_errors():
+    f = lib.mx_quantize_sr
+    # (x, in, rows, cols, block, fmt, rule, rand, q, scales, amax, stream)
+    assert f(FAKE, 1, 64, 64, 32, 0, 1, FAKE, FAKE, FAKE, None, None) == UNSUP     # E4M3: SR is MXFP4 only
+    assert f(FAKE, 1, 64, 48, 32, 2, 1, FAKE, FAKE, FAKE, None, None) == SHAPE
+    assert f(FAKE, 1, 64, 64, 16, 2, 1, FAKE, FAKE, FAKE, None, None) == UNSUP     # block must be 32
+    assert f(FAKE, 1, 64, 64, 32, 2, 1, None, FAKE, FAKE, None, None) == NULL      # no random words
+    assert f(FAKE, 1, 64, 64, 32, 2, 1, FAKE + 4, FAKE, FAKE, None, None) == ALIGN
+    assert f(None, 1, 0, 64, 32, 2, 1, None, None, None, None, None) == OK
+
+
 def test_binding_rejects_host_tensors_and_bad_names():
     import torch
     x = torch.zeros(32, 32)
