@@ -230,10 +230,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
 // statically: the compiler can then tell which in-flight DMA an LDS read may
 // alias and waits for that one alone instead of draining every load.
 //
-// Codes: row r of a stage at r * 64 bytes; its 16-byte chunk c sits at
-// position c ^ swz(r), so the lanes of one ds_read_b128 phase hit distinct
-// banks.  The DMA side applies the permutation by choosing which global chunk
-// each lane fetches.
+// Codes: stages 2m and 2m + 1 share one __shared__ object (a stage pair), so
+// that one DMA instruction fetches 8 whole 128-byte lines (a K-contiguous row of
+// the pair holds stage 2m in its first 64 bytes and stage 2m + 1 in the second).
+// 16-byte chunk c (0..7) of row r sits at position c ^ swz(r), so the lanes of
+// one ds_read_b128 phase hit distinct banks; the DMA side applies the
+// permutation by choosing which global chunk each lane fetches.
 //
 // Scales: a scale stage is 16 K-blocks = 4 words per row, fetched by 4-byte
 // LDS-DMA into a word-planar layout ([word][row]) so that the 32 rows read by
@@ -263,27 +265,26 @@ constexpr int kTile = 256, kThreads = 256;
 constexpr int kRow = 64;                      // code bytes per tile row per stage
 constexpr int kStages = 4;
 constexpr int kOpBytes = kTile * kRow;        // one operand of one stage: 16 KiB
-constexpr int kLoads = kOpBytes / 1024 / 4;   // 1 KiB DMA instructions per wave per operand per stage
-constexpr int kCodeGroup = 2 * kLoads;        // vector-memory instructions per wave per stage
+constexpr int kPairOp = 2 * kOpBytes;         // one operand of a stage pair: 32 KiB
+constexpr int kPairRow = 2 * kRow;            // K-contiguous row of a stage pair: one 128-byte line
+constexpr int kPairLoads = kPairOp / 1024 / 4;   // 1 KiB DMA instructions per wave per operand per pair
+constexpr int kCodeGroup = kPairLoads;        // vector-memory instructions per wave per stage (both operands)
 constexpr int kKbPerScale = 16;               // K-blocks per scale stage
 constexpr int kMinK = 1024;                   // K granule of this path (two scale stages)
 constexpr int kMnPitch = kTile;               // M/N-contiguous stage: bytes per K-row
 
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage0[2 * kOpBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage1[2 * kOpBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage2[2 * kOpBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage3[2 * kOpBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_pair0[2 * kPairOp];   // stages 4n, 4n + 1: [A | B]
+__shared__ __attribute__((aligned(1024))) uint8_t g_pair1[2 * kPairOp];   // stages 4n + 2, 4n + 3
 __shared__ __attribute__((aligned(1024))) uint32_t g_scale0[2][4][kTile];   // [A/B][word][row]
 __shared__ __attribute__((aligned(1024))) uint32_t g_scale1[2][4][kTile];
 __shared__ __attribute__((aligned(1024))) uint32_t g_sink[4][64];   // landing area of the L2 prefetches (never read)
 
+// The object holding stage buffer I (0..3): stage pair I / 2; stage I is its half I % 2.
 template <int I>
 __device__ __forceinline__ uint8_t* stage() {
-  static_assert(I >= 0 && I < kStages, "four stage buffers");
-  if constexpr (I == 0) return g_stage0;
-  else if constexpr (I == 1) return g_stage1;
-  else if constexpr (I == 2) return g_stage2;
-  else return g_stage3;
+  static_assert(I >= 0 && I < kStages, "four stage buffers in two pairs");
+  if constexpr (I / 2 == 0) return g_pair0;
+  else return g_pair1;
 }
 
 template <int I>
@@ -301,10 +302,10 @@ struct Geo {
   static constexpr int kUnroll = 2 * kPerScale;      // stages per unrolled loop body
 };
 
-// Chunk permutation of row r (measured on gfx950: 64-byte rows read as row = lane % 32,
+// Chunk permutation of a 128-byte row r (measured on gfx950: rows read as row = lane % 32,
 // chunk = lane / 32 (^ a uniform XOR) make ds_read_b128 conflict-free with this choice,
 // i.e. four active LDS cycles per instruction, the 256 B/clock peak).
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 // s_waitcnt vmcnt(vm) expcnt(7) lgkmcnt(0) (gfx9 encoding)
 template <int VM>
@@ -367,8 +368,10 @@ struct Ctx {
   __amdgpu_buffer_rsrc_t a, b;     // the tile's code rows (K-contiguous) or columns (M/N-contiguous) of A / B
   __amdgpu_buffer_rsrc_t sa, sb;   // the tile's 256 scale rows of A / B
   __amdgpu_buffer_rsrc_t z;        // empty range: loads return 0 and touch no memory (any base will do)
-  uint32_t off_a[kLoads];          // lane's byte offset in the tile for DMA instruction j (A)
-  uint32_t off_b[kLoads];          // same for B
+  uint32_t off_a[4];               // lane's byte offset in the tile: K-contiguous, for DMA instructions of
+                                   // parity j % 2 ([0], [1]); M/N-contiguous, for instruction jj of a stage
+  uint32_t off_b[4];               // same for B
+  uint32_t js_a, js_b;             // K-contiguous: bytes between the rows of DMA instructions j and j + 1
   uint32_t step_a, step_b;         // bytes between consecutive stages (M/N-contiguous operands)
   uint32_t sc_off;                 // lane's byte offset of its scale row, word `wave`
   uint32_t sc_step;                // 64 scale rows
@@ -382,23 +385,32 @@ struct Ctx {
   uint32_t pf_step;                // bytes between stages of the prefetched operand
 };
 
-// Stages t and t + 1 (even t) into buffers SA_ and SB_: for every row block the two
-// instructions fetch the two halves of the same 128-byte lines back to back.  A dead
-// stage (past the end of K) issues the same loads on empty resources (zeros, no
-// memory traffic), which keeps the vmcnt bookkeeping uniform and the loop free of branches.
+// Stage pair (t, t + 1) (t even) into stage buffers SA_, SB_ (= SA_ + 1): for each
+// operand 8 instructions per wave, each 1 KiB.  K-contiguous: 8 rows x one 128-byte
+// line holding both stages.  M/N-contiguous: 4 K-rows x 256 bytes, instructions
+// 0..3 for stage t, 4..7 for stage t + 1.  A dead stage (past the end of K) issues
+// the same loads on the empty resource (zeros, no memory traffic), which keeps the
+// vmcnt bookkeeping uniform and the loop free of branches.
 template <int SA_, int SB_, bool TA, bool TB>
 __device__ __forceinline__ void issue_pair(const Ctx& c, int t, int wave, bool live0, bool live1) {
-  const __amdgpu_buffer_rsrc_t ra0 = live0 ? c.a : c.z, rb0 = live0 ? c.b : c.z;
-  const __amdgpu_buffer_rsrc_t ra1 = live1 ? c.a : c.z, rb1 = live1 ? c.b : c.z;
-  const uint32_t step_a = TA ? c.step_a : uint32_t(kRow), step_b = TB ? c.step_b : uint32_t(kRow);
+  static_assert(SA_ % 2 == 0 && SB_ == SA_ + 1, "a pair starts at an even stage");
+  uint8_t* dst = stage<SA_>();
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) {
-    uint8_t* d0 = stage<SA_>() + (wave * kLoads + j) * 1024;
-    uint8_t* d1 = stage<SB_>() + (wave * kLoads + j) * 1024;
-    dma<16>(ra0, c.off_a[j], uint32_t(t) * step_a, d0);
-    dma<16>(ra1, c.off_a[j], uint32_t(t + 1) * step_a, d1);
-    dma<16>(rb0, c.off_b[j], uint32_t(t) * step_b, d0 + kOpBytes);
-    dma<16>(rb1, c.off_b[j], uint32_t(t + 1) * step_b, d1 + kOpBytes);
+  for (int j = 0; j < kPairLoads; ++j) {
+    const int e = j / 4, jj = j % 4;   // M/N-contiguous: stage t + e, instruction jj of that stage
+    const bool live = e == 0 ? live0 : live1;
+    if constexpr (TA)
+      dma<16>(live ? c.a : c.z, c.off_a[jj], uint32_t(t + e) * c.step_a,
+              dst + e * kOpBytes + (wave * 4 + jj) * 1024);
+    else
+      dma<16>(live0 ? c.a : c.z, c.off_a[j & 1], uint32_t(t) * kRow + uint32_t(j) * c.js_a,
+              dst + (wave * kPairLoads + j) * 1024);
+    if constexpr (TB)
+      dma<16>(live ? c.b : c.z, c.off_b[jj], uint32_t(t + e) * c.step_b,
+              dst + kPairOp + e * kOpBytes + (wave * 4 + jj) * 1024);
+    else
+      dma<16>(live0 ? c.b : c.z, c.off_b[j & 1], uint32_t(t) * kRow + uint32_t(j) * c.js_b,
+              dst + kPairOp + (wave * kPairLoads + j) * 1024);
   }
 }
 
@@ -437,16 +449,17 @@ __device__ __forceinline__ v8i mn_operand(const uint8_t* p) {
   return v8i{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
 }
 
-// Operand from a K-contiguous stage row p (the lane's row start).
-template <bool FP4, int KK>
+// Operand from a K-contiguous stage-pair row p (the lane's row start); HALF is the
+// stage's half of the row (chunks 4 HALF .. 4 HALF + 3, before the permutation).
+template <bool FP4, int KK, int HALF>
 __device__ __forceinline__ v8i km_operand(const Ctx& c, const uint8_t* p) {
   if constexpr (FP4) {   // the 32 codes of K-block 2 kk + h: chunk 2 kk + h
-    const int ch = KK == 0 ? c.c0 : c.c1;
+    const int ch = (KK == 0 ? c.c0 : c.c1) ^ (64 * HALF);
     const uint4 x = *reinterpret_cast<const uint4*>(p + ch);
     return v8i{int(x.x), int(x.y), int(x.z), int(x.w), 0, 0, 0, 0};
   } else {               // FP8: K = 16 h + [0, 16) and 32 + 16 h + [0, 16): chunks h and h + 2
-    const uint4 x0 = *reinterpret_cast<const uint4*>(p + c.c0);
-    const uint4 x1 = *reinterpret_cast<const uint4*>(p + c.c1);
+    const uint4 x0 = *reinterpret_cast<const uint4*>(p + (c.c0 ^ (64 * HALF)));
+    const uint4 x1 = *reinterpret_cast<const uint4*>(p + (c.c1 ^ (64 * HALF)));
     return v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
   }
 }
@@ -456,13 +469,14 @@ template <bool FP4, int SI, int U, int KK, bool PT, bool TA, bool TB>
 __device__ __forceinline__ void read_step(const Ctx& c, int t, int lane, v8i (&a)[4], v8i (&b)[4], int (&sa)[4],
                                           int (&sb)[4]) {
   using G = Geo<FP4>;
+  constexpr int kHalf = SI % 2;   // stage SI is this half of its pair
   const uint8_t* base = stage<SI>();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if constexpr (TA) a[i] = mn_operand(base + c.rd_a + (c.tp_a ^ (32 * i)));
-    else a[i] = km_operand<FP4, KK>(c, base + c.rd_a + i * 32 * kRow);
-    if constexpr (TB) b[i] = mn_operand(base + c.rd_b + (c.tp_b ^ (32 * i)));
-    else b[i] = km_operand<FP4, KK>(c, base + c.rd_b + i * 32 * kRow);
+    if constexpr (TA) a[i] = mn_operand(base + kHalf * kOpBytes + c.rd_a + (c.tp_a ^ (32 * i)));
+    else a[i] = km_operand<FP4, KK, kHalf>(c, base + c.rd_a + i * 32 * kPairRow);
+    if constexpr (TB) b[i] = mn_operand(base + kHalf * kOpBytes + c.rd_b + (c.tp_b ^ (32 * i)));
+    else b[i] = km_operand<FP4, KK, kHalf>(c, base + c.rd_b + i * 32 * kPairRow);
   }
   if constexpr (!PT) {
     // the word holding the lane's K-block (t * kKb) % 16 + 2 kk + h; the byte is
@@ -547,11 +561,11 @@ constexpr bool pair_has_scales(int q) {   // q: the (odd) stage after which the 
 template <bool FP4, int P, bool PT>
 constexpr int later_ops() {
   constexpr int kScaleOps = PT ? 0 : 8;   // per-tensor mode issues no scale loads
-  // issue_pair interleaves its two stages instruction by instruction: the first
-  // stage of a pair is complete only once all but the pair's last instruction are
-  // every pair is followed by its scale stage (if any) and one prefetch instruction
+  // both stages of a pair arrive with every one of its instructions, so the first
+  // stage of a pair is complete only once the whole pair is; every pair is followed
+  // by its scale stage (if any) and one prefetch instruction
   if constexpr (P % 2 == 1)   // group t + 1 opens the pair issued after stage t - 2
-    return 1 + (pair_has_scales<FP4>(P - 2) ? kScaleOps : 0) + 1;
+    return (pair_has_scales<FP4>(P - 2) ? kScaleOps : 0) + 1;
   else                         // group t + 1 closes the pair issued after stage t - 3
     return (pair_has_scales<FP4>(P - 3) ? kScaleOps : 0) + 1 + 2 * kCodeGroup +
            (pair_has_scales<FP4>(P - 1) ? kScaleOps : 0) + 1;
@@ -645,26 +659,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
     c.sb = make_rsrc(g.sb + int64_t(tn) * kTile * kblocks, uint32_t(kTile * kblocks));
   }
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) {
-    // K-contiguous: instruction j of a wave covers 16 rows x 64 bytes; M/N-contiguous: 4 K-rows x 256 bytes
-    const int row = (wave * kLoads + j) * 16 + (lane >> 2);
-    const uint32_t km = uint32_t(row) * uint32_t(kbytes) + 16u * uint32_t((lane & 3) ^ swz(row));
-    const int kr = (wave * kLoads + j) * 4 + (lane >> 4);
+  for (int j = 0; j < 4; ++j) {
+    // K-contiguous: instruction j of a wave covers rows 64 wave + 8 j + [0, 8), one 128-byte
+    // line each; swz of those rows depends on j only through j % 2 (the 8 j term moves it by 4 j)
+    const int row = 64 * wave + 8 * (j & 1) + (lane >> 3);
+    const uint32_t km = uint32_t(64 * wave + (lane >> 3)) * uint32_t(kbytes) + 16u * uint32_t((lane & 7) ^ swz(row));
+    // M/N-contiguous: instruction jj of a stage covers K-rows 16 wave + 4 jj + [0, 4), 256 bytes each
+    const int kr = 16 * wave + 4 * j + (lane >> 4);
     const uint32_t mn_chunk = 16u * uint32_t((lane & 15) ^ (2 * (kr & 7)));
     c.off_a[j] = TA ? uint32_t(kr) * uint32_t(lda) + mn_chunk : km;
     c.off_b[j] = TB ? uint32_t(kr) * uint32_t(ldb) + mn_chunk : km;
   }
+  c.js_a = uint32_t(8 * kbytes);
+  c.js_b = uint32_t(8 * kbytes);
   c.step_a = uint32_t(kRow) * uint32_t(TA ? lda : 1);
   c.step_b = uint32_t(kRow) * uint32_t(TB ? ldb : 1);
   c.sc_off = uint32_t(lane) * uint32_t(kblocks) + 4u * uint32_t(wave);
   c.sc_step = uint32_t(64 * kblocks);
   const int rr = lane & 31, h = lane >> 5;
-  // K-contiguous: rows 32 i + rr of a wave's half share swz(rr): 32 i only changes higher row bits
+  // K-contiguous: rows 32 i + rr of a wave's half share swz(rr): 32 i only changes higher row bits;
+  // chunk h (stage half 0) at h ^ swz, chunk h + 2 at that ^ 2
   // M/N-contiguous: transpose-read lane j = lane % 16 of group lane / 16 points at K-row
   // 16 h + j / 2 (+ 8, 32, 40), byte 8 (j % 2) of the group's 16-column chunk
   const int tr_base = (16 * h + ((lane & 15) >> 1)) * kMnPitch + 8 * (lane & 1);
-  c.rd_a = TA ? tr_base : (wm * 128 + rr) * kRow;
-  c.rd_b = kOpBytes + (TB ? tr_base : (wn * 128 + rr) * kRow);
+  c.rd_a = TA ? tr_base : (wm * 128 + rr) * kPairRow;
+  c.rd_b = kPairOp + (TB ? tr_base : (wn * 128 + rr) * kPairRow);
   c.tp_a = 16 * ((8 * wm) ^ (lane & 14) ^ ((lane >> 4) & 1));
   c.tp_b = 16 * ((8 * wn) ^ (lane & 14) ^ ((lane >> 4) & 1));
   c.c0 = 16 * (h ^ swz(rr));
@@ -740,7 +759,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
     // pitch 256 B, 16-byte unit u of row r at u ^ (r % 16)), then writes whole
     // 256-byte row segments: 16 lanes per row, 16 bytes per lane.
     barrier();   // every wave is done with the stage buffers
-    uint8_t* ep = wave == 0 ? stage<0>() : wave == 1 ? stage<1>() : wave == 2 ? stage<2>() : stage<3>();
+    uint8_t* ep = (wave < 2 ? stage<0>() : stage<2>()) + (wave & 1) * kPairOp;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
