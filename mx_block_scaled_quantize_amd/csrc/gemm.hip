@@ -237,9 +237,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
 // one ds_read_b128 phase hit distinct banks; the DMA side applies the
 // permutation by choosing which global chunk each lane fetches.
 //
-// Scales: a scale stage is 16 K-blocks = 4 words per row, fetched by 4-byte
-// LDS-DMA into a word-planar layout ([word][row]) so that the 32 rows read by
-// one instruction hit 32 banks; two scale stages are resident.
+// Scales: a scale stage is 16 K-blocks = one 16-byte group per row, fetched by
+// 16-byte LDS-DMA (64 rows per instruction) into [row][16 bytes]; two scale
+// stages are resident.  (4-byte loads of one word per row cost the address
+// unit as many cache-line lookups as all the code loads together.)
 //
 // The MFMA is fed with B as its first operand: the accumulator then holds
 // C^T fragments, i.e. each lane owns 4 consecutive columns of one row of C,
@@ -275,8 +276,8 @@ constexpr int kMnPitch = kTile;               // M/N-contiguous stage: bytes per
 
 __shared__ __attribute__((aligned(1024))) uint8_t g_pair0[2 * kPairOp];   // stages 4n, 4n + 1: [A | B]
 __shared__ __attribute__((aligned(1024))) uint8_t g_pair1[2 * kPairOp];   // stages 4n + 2, 4n + 3
-__shared__ __attribute__((aligned(1024))) uint32_t g_scale0[2][4][kTile];   // [A/B][word][row]
-__shared__ __attribute__((aligned(1024))) uint32_t g_scale1[2][4][kTile];
+__shared__ __attribute__((aligned(1024))) uint32_t g_scale0[2][kTile][4];   // [A/B][row][word]
+__shared__ __attribute__((aligned(1024))) uint32_t g_scale1[2][kTile][4];
 __shared__ __attribute__((aligned(1024))) uint32_t g_sink[4][64];   // landing area of the L2 prefetches (never read)
 
 // The object holding stage buffer I (0..3): stage pair I / 2; stage I is its half I % 2.
@@ -288,7 +289,7 @@ __device__ __forceinline__ uint8_t* stage() {
 }
 
 template <int I>
-__device__ __forceinline__ uint32_t (*scales())[4][kTile] {
+__device__ __forceinline__ uint32_t (*scales())[kTile][4] {
   static_assert(I == 0 || I == 1, "two scale buffers");
   if constexpr (I == 0) return g_scale0;
   else return g_scale1;
@@ -373,8 +374,7 @@ struct Ctx {
   uint32_t off_b[4];               // same for B
   uint32_t js_a, js_b;             // K-contiguous: bytes between the rows of DMA instructions j and j + 1
   uint32_t step_a, step_b;         // bytes between consecutive stages (M/N-contiguous operands)
-  uint32_t sc_off;                 // lane's byte offset of its scale row, word `wave`
-  uint32_t sc_step;                // 64 scale rows
+  uint32_t sc_off;                 // lane's byte offset of its scale row (row 64 wave + lane)
   int rd_a, rd_b;                  // lane's read base inside a stage object (row-tile 0)
   int c0, c1;                      // lane's swizzled chunk offsets: chunk h and chunk h + 2
   int tp_a, tp_b;                  // M/N-contiguous: lane's swizzled chunk byte offset (row-tile 0)
@@ -414,14 +414,12 @@ __device__ __forceinline__ void issue_pair(const Ctx& c, int t, int wave, bool l
   }
 }
 
+// Scale stage u (K-blocks 16 u .. 16 u + 15) of rows 64 wave .. 64 wave + 63: two instructions per wave.
+constexpr int kScaleOps = 2;
 template <int U>
 __device__ __forceinline__ void issue_scales(const Ctx& c, int u, int wave, bool live) {
-  const __amdgpu_buffer_rsrc_t ra = live ? c.sa : c.z, rb = live ? c.sb : c.z;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    dma<4>(ra, c.sc_off, uint32_t(16 * u) + j * c.sc_step, &scales<U>()[0][wave][64 * j]);
-    dma<4>(rb, c.sc_off, uint32_t(16 * u) + j * c.sc_step, &scales<U>()[1][wave][64 * j]);
-  }
+  dma<16>(live ? c.sa : c.z, c.sc_off, uint32_t(16 * u), &scales<U>()[0][64 * wave][0]);
+  dma<16>(live ? c.sb : c.z, c.sc_off, uint32_t(16 * u), &scales<U>()[1][64 * wave][0]);
 }
 
 // L2 prefetch of the 128-byte line column holding stages s and s + 1 (s even) for
@@ -484,8 +482,8 @@ __device__ __forceinline__ void read_step(const Ctx& c, int t, int lane, v8i (&a
     const int word = ((t * G::kKb) % kKbPerScale + 2 * KK) >> 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sa[i] = scales<U>()[0][word][c.sc_row_a + 32 * i];
-      sb[i] = scales<U>()[1][word][c.sc_row_b + 32 * i];
+      sa[i] = scales<U>()[0][c.sc_row_a + 32 * i][word];
+      sb[i] = scales<U>()[1][c.sc_row_b + 32 * i][word];
     }
   }
 }
@@ -560,15 +558,15 @@ constexpr bool pair_has_scales(int q) {   // q: the (odd) stage after which the 
 // multiple of the scale stage, so the pattern is static).
 template <bool FP4, int P, bool PT>
 constexpr int later_ops() {
-  constexpr int kScaleOps = PT ? 0 : 8;   // per-tensor mode issues no scale loads
+  constexpr int kSO = PT ? 0 : kScaleOps;   // per-tensor mode issues no scale loads
   // both stages of a pair arrive with every one of its instructions, so the first
   // stage of a pair is complete only once the whole pair is; every pair is followed
   // by its scale stage (if any) and one prefetch instruction
   if constexpr (P % 2 == 1)   // group t + 1 opens the pair issued after stage t - 2
-    return (pair_has_scales<FP4>(P - 2) ? kScaleOps : 0) + 1;
+    return (pair_has_scales<FP4>(P - 2) ? kSO : 0) + 1;
   else                         // group t + 1 closes the pair issued after stage t - 3
-    return (pair_has_scales<FP4>(P - 3) ? kScaleOps : 0) + 1 + 2 * kCodeGroup +
-           (pair_has_scales<FP4>(P - 1) ? kScaleOps : 0) + 1;
+    return (pair_has_scales<FP4>(P - 3) ? kSO : 0) + 1 + 2 * kCodeGroup +
+           (pair_has_scales<FP4>(P - 1) ? kSO : 0) + 1;
 }
 
 // LDS reads of one operand step: MX FP8 keeps its measured hint; per-tensor counts
@@ -615,7 +613,7 @@ __device__ __forceinline__ void stage_steps(const Ctx& c, int t, int T, int nsup
       // unconditional read keeps the operand registers free of merge copies
       read_step<kFp4, SIn, Un, 0, PT, TA, TB>(c, t + 1, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
       mfma_all<FA, FB, G::kSub - 1, PT>(acc, r.a[cur], r.b[cur], r.sa[cur], r.sb[cur], t, c.h8);
-      interleave<(kIssue ? 2 * kCodeGroup + 1 : 0) + (kScales ? 8 : 0), kDsReads<kFp4, PT, TA, TB>()>();
+      interleave<(kIssue ? 2 * kCodeGroup + 1 : 0) + (kScales ? kScaleOps : 0), kDsReads<kFp4, PT, TA, TB>()>();
     }
   }
 }
@@ -674,8 +672,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   c.js_b = uint32_t(8 * kbytes);
   c.step_a = uint32_t(kRow) * uint32_t(TA ? lda : 1);
   c.step_b = uint32_t(kRow) * uint32_t(TB ? ldb : 1);
-  c.sc_off = uint32_t(lane) * uint32_t(kblocks) + 4u * uint32_t(wave);
-  c.sc_step = uint32_t(64 * kblocks);
+  c.sc_off = uint32_t(64 * wave + lane) * uint32_t(kblocks);
   const int rr = lane & 31, h = lane >> 5;
   // K-contiguous: rows 32 i + rr of a wave's half share swz(rr): 32 i only changes higher row bits;
   // chunk h (stage half 0) at h ^ swz, chunk h + 2 at that ^ 2
@@ -721,7 +718,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   // scale stage 0 and code stage 0 landed; the pair order interleaves stages 0 and 1
   // instruction by instruction, so wait for both: what may stay in flight is stages
   // 2 and 3, scale stage 1 and the two prefetches
-  wait_vm_lgkm0<2 * kCodeGroup + (PT ? 0 : 8) + 2>();
+  wait_vm_lgkm0<2 * kCodeGroup + (PT ? 0 : kScaleOps) + 2>();
   barrier();
   read_step<kFp4, 0, 0, 0, PT, TA, TB>(c, 0, lane, r.a[0], r.b[0], r.sa[0], r.sb[0]);
 
