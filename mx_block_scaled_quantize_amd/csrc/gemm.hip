@@ -555,7 +555,7 @@ constexpr bool pair_has_scales(int q) {   // q: the (odd) stage after which the 
 
 // Vector-memory instructions issued after group t + 1 by the time the boundary
 // after stage t waits for it (t = P modulo the unrolled body, which is a
-// multiple of the scale stage, so the pattern is static).
+// multiple of the scale stage, so the pattern is static).  Only odd P waits.
 template <bool FP4, int P, bool PT>
 constexpr int later_ops() {
   constexpr int kSO = PT ? 0 : kScaleOps;   // per-tensor mode issues no scale loads
@@ -594,12 +594,15 @@ __device__ __forceinline__ void stage_steps(const Ctx& c, int t, int T, int nsup
       mfma_all<FA, FB, 0, PT>(acc, r.a[cur], r.b[cur], r.sa[cur], r.sb[cur], t, c.h8);
       interleave<0, 12>();
     } else {
-      // own DMA of stage t + 1 landed and own LDS reads done, then everybody's
-      wait_vm_lgkm0<later_ops<kFp4, P, PT>()>();
-      barrier();
+      // Only a boundary into a new stage pair (odd P) synchronizes: stage t + 1 of an
+      // even P arrived with stage t, in the same pair, and is visible since the
+      // barrier that opened the pair.
       constexpr bool kIssue = P % 2 == 1;
       constexpr bool kScales = kIssue && !PT && pair_has_scales<kFp4>(P);
       if constexpr (kIssue) {
+        // own DMA of the next pair landed and own LDS reads done, then everybody's
+        wait_vm_lgkm0<later_ops<kFp4, P, PT>()>();
+        barrier();
         // stages t - 1 and t are fully read into registers: refill their buffers
         // with stages t + 3 and t + 4, the two halves of the same lines
         issue_pair<(P + 3) % kStages, (P + 4) % kStages, TA, TB>(c, t + 3, wave, t + 3 < T, t + 4 < T);
