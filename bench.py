@@ -123,7 +123,9 @@ def main():
         print(json.dumps({"mode": "gemm", "gemm": bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np,
                                                              torch, args.steps),
                           "gemm_fp4": bench_gemm_fp4(lib, sp, stream, dev, up_bf16, workloads, torch, args.steps),
-                          "mm_fp8": bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, args.steps)}),
+                          "mm_fp8": bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, args.steps),
+                          "requant": bench_gemm_requant(lib, sp, stream, dev, up_bf16, mxa, workloads, torch,
+                                                        args.steps)}),
               flush=True)
         return
 
@@ -295,7 +297,27 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
     res["mxfp4_gemm_4096x4096x8192"] = time_gemm_fp4(lib, sp, stream, dev, gq, gs, xq, xsc, torch, 10)
     del G, X, gq, gs, xq, xsc
     res.update(bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
+    res.update(bench_gemm_requant(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
     return res
+
+
+def bench_gemm_requant(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=10):
+    """The cfg4 MXFP8 GEMM with its FP32 result re-quantized to MXFP8 E4M3 (round-up
+    scale) in the epilogue: codes [8192][14336] + scales instead of a BF16 matrix."""
+    M, N, K = 8192, 14336, 4096
+    a_bits, w_bits = workloads.cfg4()
+    qa, sa = mxa.mx_quantize(up_bf16(a_bits), "e4m3", "ceil", "row")
+    qw, sw = mxa.mx_quantize(up_bf16(w_bits), "e4m3", "ceil", "row")
+    qc = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    sc = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
+
+    def call():
+        mxa.check(lib.mx_gemm_requant(qa.data_ptr(), sa.data_ptr(), 0, qw.data_ptr(), sw.data_ptr(), 0, M, N, K, 1.0,
+                                      0, 1, qc.data_ptr(), sc.data_ptr(), None, sp))
+    t = time_calls(call, steps, 2, stream, torch)
+    tf = 2.0 * M * N * K / t / 1e12
+    return {"mxfp8_gemm_requant_e4m3_8192x14336x4096": {"us": round(t * 1e6, 2), "TFLOP/s": round(tf, 1),
+                                                        "mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4)}}
 
 
 def bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=10):

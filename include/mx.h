@@ -223,6 +223,26 @@ mx_status_t mx_gemm(const uint8_t* a, const uint8_t* sa, mx_elem_t fmt_a,
                     int64_t M, int64_t N, int64_t K, float alpha,
                     void* c, mx_dtype_t c_dtype, int64_t ldc, hipStream_t stream);
 
+/* Block-scaled GEMM with the result re-quantized to MX in the epilogue ([UE8M0]
+ * MX definition paragraph: the accumulated FP32 output is quantized to MX when the
+ * next operator needs MX; [FAF], format-aware fusion: the quantizing producer is
+ * fused with the GEMM that feeds it).  The FP32 result
+ *   C32[m][n] = fl32(alpha * acc[m][n])     (acc and alpha exactly as mx_gemm with F32 out)
+ * is never written; its row-wise MX quantization (k = 32 along n, `fmt_c`, `rule_c`,
+ * the mx_quantize rules: amax, shared E8M0 scale, RNE + saturation, NaN/Inf blocks)
+ * is, byte for byte what mx_quantize(C32, fmt_c, rule_c, MX_ROWWISE) would give:
+ *   qc        [M][N] codes (E2M1: [M][N/2] packed), 16-byte aligned;
+ *   sc        [M][N/32] E8M0 scales;
+ *   amax_out  optional max-accumulator of |C32| (NaN excluded), as for mx_quantize.
+ * Operands as mx_gemm.  Shapes: K % 32 == 0, N % 32 == 0, any M.
+ * Errors: as mx_gemm, plus MX_ERR_UNSUPPORTED for fmt_c / rule_c and MX_ERR_NULL for
+ * qc / sc. */
+mx_status_t mx_gemm_requant(const uint8_t* a, const uint8_t* sa, mx_elem_t fmt_a,
+                            const uint8_t* b, const uint8_t* sb, mx_elem_t fmt_b,
+                            int64_t M, int64_t N, int64_t K, float alpha,
+                            mx_elem_t fmt_c, mx_scale_rule_t rule_c, uint8_t* qc, uint8_t* sc,
+                            float* amax_out, hipStream_t stream);
+
 /* Per-tensor FP8 GEMM ([FP8PY], mm_fp8: pre-quantized FP8 operands of one format,
  * 2-D or 3-D with the batch broadcast as in matmul, inner-transposed operands
  * folded into the layout, the combined dequantization scale, an optional BF16

@@ -17,6 +17,7 @@ The functions carry the names of the C entry points declared in
     mx_gemm(a, sa, b, sb, fmt_a, fmt_b, alpha, out_dtype)
     mx_quantize_sr(x, rand, rule, amax=False)
     mm_fp8(a, b, scale, trans_a, trans_b, bias, fmt)
+    mx_gemm_requant(a, sa, b, sb, fmt_a, fmt_b, alpha, fmt_c, rule_c, amax=False)
 """
 
 import ctypes
@@ -59,15 +60,16 @@ lib.mx_dequantize.argtypes = [_p, _p, _i64, _i64, _i32, _i32, _i32, _p, _i32, _p
 lib.mx_gemm.argtypes = [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64, _f32, _p, _i32, _i64, _p]
 lib.mx_quantize_sr.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p]
 lib.mm_fp8.argtypes = [_p, _p, _i32, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p]
+lib.mx_gemm_requant.argtypes = [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64, _f32, _i32, _i32, _p, _p, _p, _p]
 for _f in (lib.mx_quantize, lib.mx_quantize_dual, lib.fp8_quantize_delayed, lib.mx_dequantize, lib.mx_gemm,
-           lib.mx_quantize_sr, lib.mm_fp8):
+           lib.mx_quantize_sr, lib.mm_fp8, lib.mx_gemm_requant):
     _f.restype = ctypes.c_int
 lib.mx_status_str.argtypes = [ctypes.c_int]
 lib.mx_status_str.restype = ctypes.c_char_p
 lib.mx_abi_version.restype = ctypes.c_int
 
 ENTRY_POINTS = ("mx_quantize", "mx_quantize_dual", "fp8_quantize_delayed", "mx_dequantize", "mx_gemm",
-                "mx_quantize_sr", "mm_fp8", "mx_status_str", "mx_abi_version")
+                "mx_quantize_sr", "mm_fp8", "mx_gemm_requant", "mx_status_str", "mx_abi_version")
 
 
 class MXError(RuntimeError):
@@ -180,6 +182,22 @@ def mx_quantize_sr(x, rand, rule="ceil", amax=False):
     check(lib.mx_quantize_sr(_ptr(x), _lookup(DTYPE, x.dtype, "dtype"), R, C, 32, FMT["e2m1"],
                              _lookup(RULE, rule, "rule"), _ptr(rand), _ptr(q), _ptr(s), _ptr(a), _stream(x)))
     return (q, s) if a is None else (q, s, a)
+
+
+def mx_gemm_requant(a, sa, b, sb, fmt_a="e4m3", fmt_b="e4m3", alpha=1.0, fmt_c="e4m3", rule_c="ceil", amax=False):
+    """C32 = fl32(alpha * deq(A) deq(B)^T), re-quantized row-wise to MX in the GEMM
+    epilogue.  Returns (q [M][N] (E2M1: [M][N/2]), scales [M][N/32]) or (q, scales, amax)."""
+    M = a.shape[0]
+    N = b.shape[0]
+    K = a.shape[1] * (2 if fmt_a == "e2m1" else 1)
+    fc = _lookup(FMT, fmt_c, "format")
+    q = torch.empty((M, N // 2 if fmt_c == "e2m1" else N), dtype=torch.uint8, device=a.device)
+    s = torch.empty((M, N // 32), dtype=torch.uint8, device=a.device)
+    am = _amax_buf(amax, a.device)
+    check(lib.mx_gemm_requant(_ptr(a), _ptr(sa), _lookup(FMT, fmt_a, "format"), _ptr(b), _ptr(sb),
+                              _lookup(FMT, fmt_b, "format"), M, N, K, float(alpha), fc, _lookup(RULE, rule_c, "rule"),
+                              _ptr(q), _ptr(s), _ptr(am), _stream(a)))
+    return (q, s) if am is None else (q, s, am)
 
 
 def new_ring(hist_len: int, device="cuda") -> torch.Tensor:

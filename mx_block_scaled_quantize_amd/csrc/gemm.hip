@@ -55,6 +55,12 @@ struct GemmArgs {
   int64_t batch_a, batch_b, batch_c;
   float alpha;                  // MX: the host scalar
   int tiles_m, tiles_n;
+  // MX re-quantization of the FP32 result (row-wise, k = 32): codes [M][N] (E2M1
+  // packed [M][N/2]), E8M0 scales [M][N/32], optional max-accumulator
+  uint8_t* qc;
+  uint8_t* sc;
+  uint32_t* amax;
+  int fc, rc;                   // element format and scale rule of the re-quantization
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
@@ -81,7 +87,22 @@ __device__ __forceinline__ v8i load_operand(const uint8_t* row, int kk, int h) {
   }
 }
 
-template <int FA, int FB, bool BF16OUT, bool PT, bool TA, bool TB>
+// Row-wise MX encoding of one 32-value block of the FP32 result, then its stores:
+// 32 (FP8) or 16 (E2M1) code bytes at qrow, the scale byte at *srow.
+template <int FC, int RC>
+__device__ __forceinline__ void requant_block32(const float (&v)[32], uint8_t* __restrict__ qrow,
+                                                uint8_t* __restrict__ srow) {
+  uint32_t bmax = 0;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) bmax = umax(bmax, abs_bits(v[k]));
+  uint32_t w[Words<FC, 32>::kN];
+  *srow = uint8_t(mx_encode_f32<FC, RC, 32>(v, bmax, w));
+#pragma unroll
+  for (int k = 0; k < Words<FC, 32>::kN / 4; ++k)
+    reinterpret_cast<uint4*>(qrow)[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+}
+
+template <int FA, int FB, bool BF16OUT, bool PT, bool TA, bool TB, bool RQ = false>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
   constexpr int kRowA = OpBytes<FA>::kRow, kRowB = OpBytes<FB>::kRow;
   constexpr int kPitchA = kRowA + 16, kPitchB = kRowB + 16;
@@ -190,6 +211,52 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
 
   // ---- epilogue: D[8*(v/4) + 4*(l/32) + v%4][l%32] of each 32 x 32 tile
   const float alpha = PT ? *g.alpha_ptr : g.alpha;
+  if constexpr (RQ) {
+    // MX re-quantization: the FP32 tile passes through LDS in two halves of 64 rows
+    // (the two wave rows), then each thread encodes one 32-column block of a row
+    __shared__ float sC[64][kBN + 1];
+    uint32_t tmax = 0;
+    const int lr = tid >> 2, blk = tid & 3;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      __syncthreads();
+      if (wm == half) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              sC[i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)][wn * 64 + j * 32 + (lane & 31)] = alpha * acc[i][j][v];
+      }
+      __syncthreads();
+      const int64_t row = m0 + 64 * half + lr, col = n0 + 32 * blk;
+      if (row < M && col < N) {
+        float v[32];
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          v[k] = sC[lr][32 * blk + k];
+          tmax = umax(tmax, abs_bits_no_nan(v[k]));
+        }
+        const int64_t nb = N / 32;
+        uint8_t* srow = g.sc + row * nb + col / 32;
+        const int bits = g.fc == E2M1 ? 4 : 8;
+        uint8_t* qrow = g.qc + (row * N + col) * bits / 8;
+        const int sel = g.fc * 2 + g.rc;
+        if (sel == E4M3 * 2 + FLOOR) requant_block32<E4M3, FLOOR>(v, qrow, srow);
+        else if (sel == E4M3 * 2 + CEIL) requant_block32<E4M3, CEIL>(v, qrow, srow);
+        else if (sel == E5M2 * 2 + FLOOR) requant_block32<E5M2, FLOOR>(v, qrow, srow);
+        else if (sel == E5M2 * 2 + CEIL) requant_block32<E5M2, CEIL>(v, qrow, srow);
+        else if (sel == E2M1 * 2 + FLOOR) requant_block32<E2M1, FLOOR>(v, qrow, srow);
+        else requant_block32<E2M1, CEIL>(v, qrow, srow);
+      }
+    }
+    if (g.amax) {
+      const uint32_t m = wave_max(tmax);
+      if (lane == 0 && m) atomic_max_u32(g.amax, m);
+    }
+    return;
+  }
   const int64_t ldc = g.ldc;
   void* __restrict__ C = static_cast<uint8_t*>(g.c) + int64_t(blockIdx.y) * g.batch_c * (BF16OUT ? 2 : 4);
 #pragma unroll
@@ -627,7 +694,60 @@ __device__ __forceinline__ void unrolled_body(const Ctx& c, int t0, int T, int n
   (stage_steps<FA, FB, P, PT, TA, TB>(c, t0 + P, T, nsuper, lane, wave, r, acc), ...);
 }
 
-template <int FA, int FB, bool BF16OUT, bool PT, bool TA, bool TB>
+// MX re-quantization of a wave's 128 x 128 quarter of C (row-wise blocks of 32
+// columns), one 32-row tile at a time: the wave stages the tile's FP32 values in
+// its LDS region ([32][132] floats; lane (rr, h) holds row rr, columns
+// 32 j + 8 q + 4 h + [0, 4)), then each lane encodes two whole blocks (four
+// consecutive lanes cover the four blocks of a row, so the code stores of a row
+// are contiguous).
+constexpr int kRqPitch = 132;   // floats per staged row (16-byte aligned, rows 4 banks apart)
+template <int FC, int RC>
+__device__ __forceinline__ void requant_quarter(const v16f (&acc)[4][4], float alpha, int lane, uint8_t* ep,
+                                                const GemmArgs& g, int64_t row0, int64_t col0, uint32_t& tmax) {
+  constexpr int kBits = Fmt_<FC>::kBits;
+  const int rr = lane & 31, h = lane >> 5;
+  const int64_t nb = g.N / 32, qpitch = g.N * kBits / 8;
+  float* t = reinterpret_cast<float*>(ep);
+  // the register tile is picked statically (accumulators cannot be indexed at run
+  // time); the encoding below is shared by the four tiles
+  auto stage_tile = [&](const v16f (&ai)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(t + rr * kRqPitch + 32 * j + 8 * q + 4 * h) =
+            make_float4(alpha * ai[j][4 * q], alpha * ai[j][4 * q + 1], alpha * ai[j][4 * q + 2],
+                        alpha * ai[j][4 * q + 3]);
+  };
+#pragma unroll 1
+  for (int i = 0; i < 4; ++i) {
+    if (i == 0) stage_tile(acc[0]);
+    else if (i == 1) stage_tile(acc[1]);
+    else if (i == 2) stage_tile(acc[2]);
+    else stage_tile(acc[3]);
+    wave_lds_fence();
+#pragma unroll 1
+    for (int k = 0; k < 2; ++k) {
+      const int b = lane + 64 * k, row = b >> 2, blk = b & 3;
+      float v[32];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float4 x = *reinterpret_cast<const float4*>(t + row * kRqPitch + 32 * blk + 4 * c);
+        v[4 * c] = x.x;
+        v[4 * c + 1] = x.y;
+        v[4 * c + 2] = x.z;
+        v[4 * c + 3] = x.w;
+      }
+#pragma unroll
+      for (int c = 0; c < 32; ++c) tmax = umax(tmax, abs_bits_no_nan(v[c]));
+      const int64_t r = row0 + 32 * i + row;
+      requant_block32<FC, RC>(v, g.qc + r * qpitch + (col0 + 32 * blk) * kBits / 8, g.sc + r * nb + col0 / 32 + blk);
+    }
+    wave_lds_fence();   // the tile is read before the next one overwrites it
+  }
+}
+
+template <int FA, int FB, bool BF16OUT, bool PT, bool TA, bool TB, bool RQ = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) {
   constexpr bool kFp4 = FA == E2M1;
   static_assert(!(TA || TB) || (PT && !kFp4 && BF16OUT), "M/N-contiguous operands: per-tensor FP8, BF16 out");
@@ -739,6 +859,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   const int64_t ldc = g.ldc;
   const int64_t row0 = int64_t(tm) * kTile + wm * 128;
   const int64_t col0 = int64_t(tn) * kTile + wn * 128;
+  if constexpr (RQ) {
+    barrier();   // every wave is done with the stage buffers
+    uint8_t* ep = (wave < 2 ? stage<0>() : stage<2>()) + (wave & 1) * kPairOp;
+    uint32_t tmax = 0;
+    const int sel = g.fc * 2 + g.rc;
+    if (sel == E4M3 * 2 + FLOOR) requant_quarter<E4M3, FLOOR>(acc, alpha, lane, ep, g, row0, col0, tmax);
+    else if (sel == E4M3 * 2 + CEIL) requant_quarter<E4M3, CEIL>(acc, alpha, lane, ep, g, row0, col0, tmax);
+    else if (sel == E5M2 * 2 + FLOOR) requant_quarter<E5M2, FLOOR>(acc, alpha, lane, ep, g, row0, col0, tmax);
+    else if (sel == E5M2 * 2 + CEIL) requant_quarter<E5M2, CEIL>(acc, alpha, lane, ep, g, row0, col0, tmax);
+    else if (sel == E2M1 * 2 + FLOOR) requant_quarter<E2M1, FLOOR>(acc, alpha, lane, ep, g, row0, col0, tmax);
+    else requant_quarter<E2M1, CEIL>(acc, alpha, lane, ep, g, row0, col0, tmax);
+    if (g.amax) {
+      const uint32_t m = wave_max(tmax);
+      if (lane == 0 && m) atomic_max_u32(g.amax, m);
+    }
+    return;
+  }
   if constexpr (BF16OUT) {
     uint16_t* C = static_cast<uint16_t*>(g.c) + int64_t(blockIdx.y) * g.batch_c;
     // per-tensor bias of the lane's 64 columns, added to alpha * acc with one rounding
@@ -866,6 +1003,27 @@ static mx_status_t mm_layouts(const GemmArgs& g, bool ta, bool tb, int64_t batch
   return tb ? mm_launch<F, false, true>(g, batch, st) : mm_launch<F, false, false>(g, batch, st);
 }
 
+template <int FA, int FB>
+static mx_status_t requant_dispatch(GemmArgs g, hipStream_t st) {
+  const int64_t M = g.M, N = g.N, K = g.K;
+  const bool big = M % t256::kTile == 0 && N % t256::kTile == 0 && K % t256::kMinK == 0 && K > 0 &&
+                   K <= (int64_t(1) << 22) && (M / t256::kTile) * (N / t256::kTile) < (int64_t(1) << 31) &&
+                   !misaligned(g.a) && !misaligned(g.b) && !misaligned(g.sa) && !misaligned(g.sb) &&
+                   (reinterpret_cast<uintptr_t>(g.sc) & 3u) == 0;
+  if (big) {
+    g.tiles_m = int(M / t256::kTile);
+    g.tiles_n = int(N / t256::kTile);
+    hipLaunchKernelGGL((t256::gemm256_kernel<FA, FB, true, false, false, false, true>),
+                       dim3(unsigned(g.tiles_m * g.tiles_n)), dim3(t256::kThreads), 0, st, g);
+    return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+  }
+  g.tiles_m = int((M + kBM - 1) / kBM);
+  g.tiles_n = int((N + kBN - 1) / kBN);
+  hipLaunchKernelGGL((gemm_kernel<FA, FB, true, false, false, false, true>), dim3(unsigned(g.tiles_m * g.tiles_n)),
+                     dim3(kGemmThreads), 0, st, g);
+  return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
 template <bool BF>
 static mx_status_t gemm_formats(int fa, int fb, const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                                 const uint8_t* sb, int64_t M, int64_t N, int64_t K, float alpha, void* c, int64_t ldc,
@@ -932,4 +1090,40 @@ extern "C" mx_status_t mm_fp8(const uint8_t* a, const uint8_t* b, mx_elem_t fmt,
   // the MFMA's B is op(b)^T: N-contiguous exactly when b is not transposed
   return fmt == MX_E4M3 ? mm_layouts<E4M3>(g, trans_a != 0, trans_b == 0, batch, stream)
                         : mm_layouts<E5M2>(g, trans_a != 0, trans_b == 0, batch, stream);
+}
+
+extern "C" mx_status_t mx_gemm_requant(const uint8_t* a, const uint8_t* sa, mx_elem_t fmt_a, const uint8_t* b,
+                                       const uint8_t* sb, mx_elem_t fmt_b, int64_t M, int64_t N, int64_t K,
+                                       float alpha, mx_elem_t fmt_c, mx_scale_rule_t rule_c, uint8_t* qc,
+                                       uint8_t* sc, float* amax_out, hipStream_t stream) {
+  const bool f8a = fmt_a == MX_E4M3 || fmt_a == MX_E5M2, f8b = fmt_b == MX_E4M3 || fmt_b == MX_E5M2;
+  if (!((f8a && f8b) || (fmt_a == MX_E2M1 && fmt_b == MX_E2M1))) return MX_ERR_UNSUPPORTED;
+  if (fmt_c != MX_E4M3 && fmt_c != MX_E5M2 && fmt_c != MX_E2M1) return MX_ERR_UNSUPPORTED;
+  if (rule_c != MX_SCALE_FLOOR && rule_c != MX_SCALE_CEIL) return MX_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || N % 32 != 0) return MX_ERR_SHAPE;
+  if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return MX_ERR_SHAPE;
+  if (M == 0 || N == 0) return MX_OK;
+  if (!qc || !sc || (K > 0 && (!a || !sa || !b || !sb))) return MX_ERR_NULL;
+  if (misaligned(qc) || (K > 0 && (misaligned(a) || misaligned(b)))) return MX_ERR_ALIGN;
+  GemmArgs g{};
+  g.a = a;
+  g.sa = sa;
+  g.b = b;
+  g.sb = sb;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = fmt_a == MX_E2M1 ? K / 2 : K;
+  g.ldb = fmt_b == MX_E2M1 ? K / 2 : K;
+  g.alpha = alpha;
+  g.qc = qc;
+  g.sc = sc;
+  g.amax = reinterpret_cast<uint32_t*>(amax_out);
+  g.fc = int(fmt_c);
+  g.rc = int(rule_c);
+  if (fmt_a == MX_E4M3 && fmt_b == MX_E4M3) return requant_dispatch<E4M3, E4M3>(g, stream);
+  if (fmt_a == MX_E4M3 && fmt_b == MX_E5M2) return requant_dispatch<E4M3, E5M2>(g, stream);
+  if (fmt_a == MX_E5M2 && fmt_b == MX_E4M3) return requant_dispatch<E5M2, E4M3>(g, stream);
+  if (fmt_a == MX_E5M2 && fmt_b == MX_E5M2) return requant_dispatch<E5M2, E5M2>(g, stream);
+  return requant_dispatch<E2M1, E2M1>(g, stream);
 }

@@ -162,6 +162,20 @@ def test_mm_fp8_argument_errors():
     assert f(None, None, 0, 1, 0, 64, 64, 0, 0, 0, 0, None, None, None, None) == OK       # M 0
 
 
+def test_mx_gemm_requant_argument_errors():
+    f = lib.mx_gemm_requant
+    # (a, sa, fa, b, sb, fb, M, N, K, alpha, fc, rc, qc, sc, amax, stream)
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 2, 64, 64, 64, 1.0, 0, 1, FAKE, FAKE, None, None) == UNSUP   # FP8 x FP4
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, 3, 1, FAKE, FAKE, None, None) == UNSUP   # output format
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, 0, 2, FAKE, FAKE, None, None) == UNSUP   # rule
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 48, 64, 1.0, 0, 1, FAKE, FAKE, None, None) == SHAPE   # N % 32
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 48, 1.0, 0, 1, FAKE, FAKE, None, None) == SHAPE   # K % 32
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, 0, 1, None, FAKE, None, None) == NULL
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, 0, 1, FAKE, None, None, None) == NULL
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, 0, 1, FAKE + 8, FAKE, None, None) == ALIGN
+    assert f(None, None, 0, None, None, 0, 0, 64, 64, 1.0, 0, 1, None, None, None, None) == OK
+
+
 def test_mx_quantize_sr_argument_errors():
     f = lib.mx_quantize_sr
     # (x, in, rows, cols, block, fmt, rule, rand, q, scales, amax, stream)
