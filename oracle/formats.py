@@ -13,14 +13,19 @@ Definitions followed ([UE8M0] glossary entries "FP8 (E4M3/E5M2)", "EU8M0",
   Largest finite 1.75 * 2^15 = 57344, smallest subnormal 2^-16.
 * E2M1 - 1 sign, 2 exponent (bias 1), 1 mantissa bit, no specials:
   magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+* E2M3 - 1 sign, 2 exponent (bias 1), 3 mantissa bits, no specials (FP6 of the
+  MXFP8/6/4 family named on the page): largest 1.875 * 4 = 7.5, smallest
+  subnormal 2^-3.
+* E3M2 - 1 sign, 3 exponent (bias 3), 2 mantissa bits, no specials: largest
+  1.75 * 16 = 28, smallest subnormal 2^-4.
 * E8M0 - unsigned, 8 exponent bits, no mantissa: code c in [0, 254] is 2^(c-127),
   code 255 is NaN.
 
 Element casts round to nearest, ties to even, and saturate: a finite magnitude
 beyond the largest finite value becomes that value ([UE8M0] section 4, on the
 scale algorithm clamping values above the upper limit).  Infinite inputs
-saturate the same way; NaN inputs give the format's NaN (E2M1 has none, so it
-gives the largest magnitude with the input's sign).
+saturate the same way; NaN inputs give the format's NaN (E2M1, E2M3 and E3M2
+have none, so they give the largest magnitude with the input's sign).
 """
 
 from dataclasses import dataclass
@@ -73,7 +78,11 @@ E5M2 = ElemFormat("e5m2", ebits=5, mbits=2, bias=15, emax=15, max_mant=0b111, ha
 # OCP E2M1 (FP4): no Inf/NaN.
 E2M1 = ElemFormat("e2m1", ebits=2, mbits=1, bias=1, emax=2, max_mant=0b11, has_inf=False, nan_code=0x7)
 
-FORMATS = {"e4m3": E4M3, "e5m2": E5M2, "e2m1": E2M1}
+# OCP E2M3 / E3M2 (FP6): no Inf/NaN.
+E2M3 = ElemFormat("e2m3", ebits=2, mbits=3, bias=1, emax=2, max_mant=0b1111, has_inf=False, nan_code=0x1F)
+E3M2 = ElemFormat("e3m2", ebits=3, mbits=2, bias=3, emax=4, max_mant=0b111, has_inf=False, nan_code=0x1F)
+
+FORMATS = {"e4m3": E4M3, "e5m2": E5M2, "e2m1": E2M1, "e2m3": E2M3, "e3m2": E3M2}
 
 
 def fmt_of(f) -> ElemFormat:

@@ -99,10 +99,51 @@ def unpack_fp4(packed) -> np.ndarray:
     return out
 
 
+def pack_fp6(codes) -> np.ndarray:
+    """Pack 6-bit codes along the last axis as a little-endian bit stream: element i
+    occupies bits 6i .. 6i+5 of the row, so 4 elements fill 3 bytes (the FP4 nibble
+    order, element 2j in the low nibble, is the same rule at 4 bits)."""
+    c = np.asarray(codes).astype(np.uint32) & 0x3F
+    assert c.shape[-1] % 4 == 0
+    g = c.reshape(c.shape[:-1] + (c.shape[-1] // 4, 4))
+    word = g[..., 0] | (g[..., 1] << 6) | (g[..., 2] << 12) | (g[..., 3] << 18)     # 24 bits
+    out = np.stack([word & 0xFF, (word >> 8) & 0xFF, (word >> 16) & 0xFF], axis=-1)
+    return out.reshape(c.shape[:-1] + (c.shape[-1] * 3 // 4,)).astype(np.uint8)
+
+
+def unpack_fp6(packed) -> np.ndarray:
+    p = np.asarray(packed).astype(np.uint32)
+    assert p.shape[-1] % 3 == 0
+    g = p.reshape(p.shape[:-1] + (p.shape[-1] // 3, 3))
+    word = g[..., 0] | (g[..., 1] << 8) | (g[..., 2] << 16)
+    out = np.stack([(word >> (6 * k)) & 0x3F for k in range(4)], axis=-1)
+    return out.reshape(p.shape[:-1] + (p.shape[-1] * 4 // 3,)).astype(np.uint8)
+
+
+def pack_codes(codes, fmt) -> np.ndarray:
+    """Storage form of a code array: FP4 and FP6 packed along the last axis, FP8 as is."""
+    f = fmt_of(fmt)
+    if f.bits == 4:
+        return pack_fp4(codes)
+    if f.bits == 6:
+        return pack_fp6(codes)
+    return np.asarray(codes).astype(np.uint8)
+
+
+def unpack_codes(packed, fmt) -> np.ndarray:
+    f = fmt_of(fmt)
+    if f.bits == 4:
+        return unpack_fp4(packed)
+    if f.bits == 6:
+        return unpack_fp6(packed)
+    return np.asarray(packed).astype(np.uint8)
+
+
 def quantize_rowwise(x, fmt, rule, hadamard_mask=None):
     """Row-wise MX quantization of a 2-D FP32 array [R][C], blocks of 32 along C.
 
-    Returns (codes [R][C] uint8 - or [R][C/2] packed for E2M1 -, scales [R][C/32]).
+    Returns (codes [R][C] uint8 - or [R][C/2] packed for E2M1, [R][3C/4] for FP6 -,
+    scales [R][C/32]).
     With ``hadamard_mask`` (a 32-bit int), each block is first passed through the
     fixed-sign 32-point Hadamard transform of ``oracle.hadamard``.
     """
@@ -115,10 +156,7 @@ def quantize_rowwise(x, fmt, rule, hadamard_mask=None):
         from .hadamard import hadamard32
         blocks = hadamard32(blocks, hadamard_mask)
     codes, scales = quantize_blocks(blocks, f, rule)
-    codes = codes.reshape(R, C)
-    if f.name == "e2m1":
-        codes = pack_fp4(codes)
-    return codes, scales
+    return pack_codes(codes.reshape(R, C), f), scales
 
 
 def quantize_colwise_t(x, fmt, rule, hadamard_mask=None):
@@ -150,12 +188,12 @@ def dequantize_exact(codes, scales, fmt, packed_fp4=True) -> np.ndarray:
     """Exact dequantized values V^_i = Q_i * X as float64 ([UE8M0] section 2 of the
     first part: decoding an E8M0 scale is an exponent shift).
 
-    ``codes`` are [R][C] (or [R][C/2] packed E2M1), ``scales`` [R][C/32].
+    ``codes`` are [R][C] (or packed: [R][C/2] E2M1, [R][3C/4] FP6), ``scales`` [R][C/32].
     """
     f = fmt_of(fmt)
     c = np.asarray(codes)
-    if f.name == "e2m1" and packed_fp4:
-        c = unpack_fp4(c)
+    if f.bits < 8 and packed_fp4:
+        c = unpack_codes(c, f)
     R, C = c.shape
     vals = decode(c, f).reshape(R, C // BLOCK, BLOCK)
     sc = e8m0_decode(scales).reshape(R, C // BLOCK, 1)

@@ -22,9 +22,17 @@ def table_from_torch(name: str) -> np.ndarray:
     return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(dt).to(torch.float64).numpy()
 
 
+# FP6 magnitudes in code order, written from the format definitions (OCP MX):
+# subnormals M * 2^(1 - bias - mbits), normals (1 + M / 2^mbits) * 2^(E - bias).
+E2M3_MAGNITUDES = [m / 8 for m in range(8)] + [(1 + m / 8) * 2.0 ** e for e in range(0, 3) for m in range(8)]
+E3M2_MAGNITUDES = [m / 16 for m in range(4)] + [(1 + m / 4) * 2.0 ** e for e in range(-2, 5) for m in range(4)]
+BITS = {"e4m3": 8, "e5m2": 8, "e2m1": 4, "e2m3": 6, "e3m2": 6}
+
+
 def table(name: str) -> np.ndarray:
-    if name == "e2m1":
-        mags = np.array(E2M1_MAGNITUDES)
+    small = {"e2m1": E2M1_MAGNITUDES, "e2m3": E2M3_MAGNITUDES, "e3m2": E3M2_MAGNITUDES}
+    if name in small:
+        mags = np.array(small[name])
         return np.concatenate([mags, -mags])
     return table_from_torch(name)
 
@@ -36,7 +44,7 @@ def nearest_even_codes(values: np.ndarray, name: str) -> np.ndarray:
     Works on |v| over the sorted positive finite codes, then restores the sign.
     """
     tab = table(name)
-    nbits = 4 if name == "e2m1" else 8
+    nbits = BITS[name]
     half = 1 << (nbits - 1)
     pos_codes = np.arange(half)
     pos_vals = tab[:half]
@@ -94,7 +102,7 @@ def scan_ceil_exponent(amax: Fraction, name: str) -> int:
 def frac_nearest_code(v: Fraction, name: str) -> int:
     """Nearest-even finite code of an exact rational, saturating, by scanning all codes."""
     tab = table(name)
-    nbits = 4 if name == "e2m1" else 8
+    nbits = BITS[name]
     half = 1 << (nbits - 1)
     best = None
     a = abs(v)
@@ -127,7 +135,7 @@ def frac_quantize_block(block, name: str, rule: str):
     for xv, xf in zip(block, xs):
         c = frac_nearest_code(xf / Fraction(2) ** e, name)
         if xf == 0 and np.signbit(xv):
-            c |= (8 if name == "e2m1" else 128)
+            c |= 1 << (BITS[name] - 1)
         codes.append(c)
     return codes, scale
 

@@ -78,13 +78,52 @@ def test_decode_e2m1_table():
     assert np.signbit(ours[8])
 
 
-@pytest.mark.parametrize("name", ["e4m3", "e5m2", "e2m1"])
+@pytest.mark.parametrize("name", ["e2m3", "e3m2"])
+def test_decode_fp6_tables(name):
+    ours = F.decode(np.arange(64), name)
+    mags = pins.E2M3_MAGNITUDES if name == "e2m3" else pins.E3M2_MAGNITUDES
+    assert list(ours[:32]) == mags and list(-ours[32:]) == mags
+    assert np.signbit(ours[32])
+    # the OCP extremes: E2M3 max 7.5, smallest subnormal 0.125; E3M2 max 28, 0.0625
+    f = F.FORMATS[name]
+    assert (f.max_value, f.min_subnormal) == ((7.5, 0.125) if name == "e2m3" else (28.0, 0.0625))
+
+
+def test_fp6_packing_is_a_little_endian_bit_stream():
+    from oracle import mx
+    # codes 1, 2, 3, 4 -> 24-bit word 1 | 2 << 6 | 3 << 12 | 4 << 18 = 0x103081
+    assert list(mx.pack_fp6(np.array([1, 2, 3, 4]))) == [0x81, 0x30, 0x10]
+    assert list(mx.pack_fp6(np.array([0x3F, 0, 0, 0x3F]))) == [0x3F, 0x00, 0xFC]
+    g = np.random.default_rng(9)
+    c = g.integers(0, 64, size=(5, 64)).astype(np.uint8)
+    p = mx.pack_fp6(c)
+    assert p.shape == (5, 48) and np.array_equal(mx.unpack_fp6(p), c)
+    # bit i of the stream is bit i % 6 of element i // 6
+    stream = np.unpackbits(p[0], bitorder="little")
+    assert np.array_equal(stream.reshape(64, 6), np.unpackbits(c[0][:, None], axis=1, bitorder="little")[:, :6])
+
+
+def test_planted_big_endian_fp6_packing_is_caught(monkeypatch):
+    from oracle import mx
+
+    def wrong(codes):
+        c = np.asarray(codes).astype(np.uint32) & 0x3F
+        g = c.reshape(c.shape[:-1] + (c.shape[-1] // 4, 4))
+        word = (g[..., 0] << 18) | (g[..., 1] << 12) | (g[..., 2] << 6) | g[..., 3]
+        out = np.stack([(word >> 16) & 0xFF, (word >> 8) & 0xFF, word & 0xFF], axis=-1)
+        return out.reshape(c.shape[:-1] + (c.shape[-1] * 3 // 4,)).astype(np.uint8)
+    monkeypatch.setattr(mx, "pack_fp6", wrong)
+    with pytest.raises(AssertionError):
+        test_fp6_packing_is_a_little_endian_bit_stream()
+
+
+@pytest.mark.parametrize("name", ["e4m3", "e5m2", "e2m1", "e2m3", "e3m2"])
 def test_code_enumeration(name):
     f = F.FORMATS[name]
     n = 1 << f.bits
     d = F.decode(np.arange(n), f)
     fin = np.isfinite(d)
-    expected_finite = {"e4m3": 254, "e5m2": 248, "e2m1": 16}[name]
+    expected_finite = {"e4m3": 254, "e5m2": 248, "e2m1": 16, "e2m3": 64, "e3m2": 64}[name]
     assert fin.sum() == expected_finite
     # decode -> encode is the identity on every non-NaN code (Inf saturates)
     e = F.encode(d[fin], f)
@@ -111,12 +150,12 @@ def check_encoder_vs_bruteforce(encode, name, values) -> bool:
     return bool(np.array_equal(a, b))
 
 
-@pytest.mark.parametrize("name", ["e4m3", "e5m2", "e2m1"])
+@pytest.mark.parametrize("name", ["e4m3", "e5m2", "e2m1", "e2m3", "e3m2"])
 def test_encode_all_bf16_patterns_at_many_scales(name):
     assert check_encoder_vs_bruteforce(F.encode, name, _bf16_times_scales())
 
 
-@pytest.mark.parametrize("name", ["e4m3", "e5m2", "e2m1"])
+@pytest.mark.parametrize("name", ["e4m3", "e5m2", "e2m1", "e2m3", "e3m2"])
 def test_encode_midpoints_and_neighbours(name):
     f = F.FORMATS[name]
     d = F.decode(np.arange(1 << (f.bits - 1)), f)
@@ -129,7 +168,7 @@ def test_encode_midpoints_and_neighbours(name):
     assert check_encoder_vs_bruteforce(F.encode, name, vals)
 
 
-@pytest.mark.parametrize("name", ["e4m3", "e5m2", "e2m1"])
+@pytest.mark.parametrize("name", ["e4m3", "e5m2", "e2m1", "e2m3", "e3m2"])
 def test_encode_random_fp32_bits(name):
     g = np.random.default_rng(7)
     bits = g.integers(0, 1 << 32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
@@ -157,6 +196,14 @@ def test_encode_e2m1_ties():
     got = F.decode(F.encode(vals, "e2m1"), "e2m1")
     assert list(got) == expect
     assert np.signbit(got[-2])
+
+
+def test_encode_fp6_ties_and_specials():
+    # halfway cases go to the even code; NaN -> largest magnitude with its sign; no Inf
+    got = F.decode(F.encode(np.array([0.0625, 0.1875, 7.25, 7.75, 100.0, -np.inf, np.nan]), "e2m3"), "e2m3")
+    assert list(got[:5]) == [0.0, 0.25, 7.0, 7.5, 7.5] and got[5] == -7.5 and got[6] == 7.5
+    got = F.decode(F.encode(np.array([0.03125, 26.0, 30.0, -1e9]), "e3m2"), "e3m2")
+    assert list(got) == [0.0, 24.0, 28.0, -28.0]
 
 
 def test_encode_specials():

@@ -10,7 +10,7 @@ from oracle import formats as F
 from oracle import mx
 from tests import pins
 
-FMTS = ["e4m3", "e5m2", "e2m1"]
+FMTS = ["e4m3", "e5m2", "e2m1", "e2m3", "e3m2"]
 RULES = ["floor", "ceil"]
 
 
@@ -119,16 +119,16 @@ def test_power_of_two_equivariance_and_sign_symmetry(name, rule):
     f = F.FORMATS[name]
     for x in _inputs():
         q, s = mx.quantize_rowwise(x, f, rule)
+        q = mx.unpack_codes(q, f)
         for j in (-3, 5):
             q2, s2 = mx.quantize_rowwise((x * np.float32(2.0 ** j)).astype(np.float32), f, rule)
             ok = (s > 20) & (s < 230) & (s2 > 0)       # away from the clamps
             assert np.array_equal(s2[ok].astype(int), s[ok].astype(int) + j)
-            rows_ok = np.repeat(ok, 32 // (2 if name == "e2m1" else 1), axis=1)
-            assert np.array_equal(q2[rows_ok], q[rows_ok])
+            rows_ok = np.repeat(ok, 32, axis=1)
+            assert np.array_equal(mx.unpack_codes(q2, f)[rows_ok], q[rows_ok])
         qn, sn = mx.quantize_rowwise(-x, f, rule)
         assert np.array_equal(sn, s)
-        flip = 0x88 if name == "e2m1" else 0x80
-        assert np.array_equal(qn, q ^ flip)
+        assert np.array_equal(mx.unpack_codes(qn, f), q ^ f.sign_bit)
 
 
 @pytest.mark.parametrize("name", FMTS)
@@ -140,8 +140,7 @@ def test_permutation_within_block(name, rule):
     xp = x.reshape(16, 4, 32)[:, :, perm].reshape(16, 128)
     q, s = mx.quantize_rowwise(x, f, rule)
     qp, sp = mx.quantize_rowwise(xp, f, rule)
-    if name == "e2m1":
-        q, qp = mx.unpack_fp4(q), mx.unpack_fp4(qp)
+    q, qp = mx.unpack_codes(q, f), mx.unpack_codes(qp, f)
     assert np.array_equal(s, sp)
     assert np.array_equal(q.reshape(16, 4, 32)[:, :, perm], qp.reshape(16, 4, 32))
 
@@ -196,7 +195,7 @@ def test_dequantize_exact_against_fraction(name):
     scales = g.integers(0, 255, size=(8, 2)).astype(np.uint8)
     scales[0, 0] = 0
     scales[1, 1] = 254
-    packed = mx.pack_fp4(codes) if name == "e2m1" else codes
+    packed = mx.pack_codes(codes, name)
     d = mx.dequantize_exact(packed, scales, name)
     for i in range(8):
         for j in range(64):
