@@ -277,7 +277,14 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
     bsr = R * C * 2 + R * C * 4 + R * C // 2 + R * C // 32
     res["sr_mxfp4_rowwise_bf16_8192x4096"] = {"us": round(tsr * 1e6, 2), "GB/s": round(bsr / tsr / 1e9, 1),
                                               "hbm_frac": round(bsr / tsr / 1e9 / HBM_PEAK_GBS, 4)}
-    del gx, words, sq, ss
+    # MXFP6 E3M2 row-wise of the same gradient (codes packed 4 per 3 bytes)
+    fq = torch.empty((R, C * 3 // 4), dtype=torch.uint8, device=dev)
+    tf6 = time_calls(lambda: mxa.check(lib.mx_quantize(gx.data_ptr(), 1, R, C, 32, 4, 1, 0, 0, 0, fq.data_ptr(),
+                                                       ss.data_ptr(), None, sp)), 32, 4, stream, torch)
+    bf6 = R * C * 2 + R * C * 3 // 4 + R * C // 32
+    res["mxfp6_e3m2_rowwise_bf16_8192x4096"] = {"us": round(tf6 * 1e6, 2), "GB/s": round(bf6 / tf6 / 1e9, 1),
+                                                "hbm_frac": round(bf6 / tf6 / 1e9 / HBM_PEAK_GBS, 4)}
+    del gx, words, sq, ss, fq
     # Hadamard + column-wise MXFP4 quantization of both operands, then the MXFP4 GEMM
     g_bits, x_bits, mask = workloads.cfg5()
     G, X = up_bf16(g_bits), up_bf16(x_bits)

@@ -37,7 +37,7 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 # ---------------------------------------------------------------- enums (include/mx.h)
-FMT = {"e4m3": 0, "e5m2": 1, "e2m1": 2}
+FMT = {"e4m3": 0, "e5m2": 1, "e2m1": 2, "e2m3": 3, "e3m2": 4}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 RULE = {"floor": 0, "ceil": 1}
 ORIENT = {"row": 0, "col": 1}
@@ -125,8 +125,12 @@ def _check_2d(x):
 
 
 def code_cols(n: int, fmt: str) -> int:
-    """Bytes per row of n element codes (FP4 packs two per byte)."""
-    return n // 2 if fmt == "e2m1" else n
+    """Bytes per row of n element codes (FP4 packs two per byte, FP6 four per three bytes)."""
+    if fmt == "e2m1":
+        return n // 2
+    if fmt in ("e2m3", "e3m2"):
+        return n * 3 // 4
+    return n
 
 
 def mx_quantize(x, fmt="e4m3", rule="ceil", orient="row", hadamard_mask=None, amax=False):
@@ -135,7 +139,7 @@ def mx_quantize(x, fmt="e4m3", rule="ceil", orient="row", hadamard_mask=None, am
     amax=True returns max |x| (NaN ignored) in a fresh 1-element tensor; pass a
     tensor instead to max-accumulate into it (running amax).
 
-    orient='row': q [R][C] (FP4 [R][C/2]), scales [R][C/32].
+    orient='row': q [R][C] (FP4 [R][C/2], FP6 [R][3C/4]), scales [R][C/32].
     orient='col': q [C][R] (FP4 [C][R/2]), scales [C][R/32] (transposed storage).
     """
     _check_2d(x)

@@ -39,6 +39,20 @@ __device__ __forceinline__ float decode_scaled(uint32_t code, int sexp) {
     const int ex = ef ? int(ef) - 17 : -16;
     const float m = ldexpf(float(sig), ex + sexp);
     return neg ? -m : m;
+  } else if constexpr (F == E2M3) {   // bias 1, 3 mantissa bits, no specials
+    const uint32_t ef = (code >> 3) & 3u, mf = code & 7u;
+    const bool neg = (code & 0x20u) != 0;
+    const int sig = ef ? int(8u + mf) : int(mf);
+    const int ex = ef ? int(ef) - 4 : -3;
+    const float m = ldexpf(float(sig), ex + sexp);
+    return neg ? -m : m;
+  } else if constexpr (F == E3M2) {   // bias 3, 2 mantissa bits, no specials
+    const uint32_t ef = (code >> 2) & 7u, mf = code & 3u;
+    const bool neg = (code & 0x20u) != 0;
+    const int sig = ef ? int(4u + mf) : int(mf);
+    const int ex = ef ? int(ef) - 5 : -4;
+    const float m = ldexpf(float(sig), ex + sexp);
+    return neg ? -m : m;
   } else {
     const uint32_t ef = (code >> 1) & 3u, mf = code & 1u;
     const bool neg = (code & 0x8u) != 0;
@@ -66,6 +80,23 @@ __device__ __forceinline__ void decode8(const uint8_t* __restrict__ q, int64_t e
       c[j] = (w.x >> (8 * j)) & 0xFFu;
       c[4 + j] = (w.y >> (8 * j)) & 0xFFu;
     }
+  } else if constexpr (Fmt_<F>::kBits == 6) {
+    // 6 bytes at elem * 3 / 4: 4-byte aligned for even chunks, 2-byte aligned for odd
+    const uint8_t* p = q + elem / 8 * 6;
+    uint32_t lo, hi;
+    if (((elem / 8) & 1) == 0) {
+      lo = *reinterpret_cast<const uint32_t*>(p);
+      hi = *reinterpret_cast<const uint16_t*>(p + 4);
+    } else {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(p + 2);
+      lo = uint32_t(*reinterpret_cast<const uint16_t*>(p)) | (w << 16);
+      hi = w >> 16;
+    }
+#pragma unroll
+    for (int j = 0; j < 5; ++j) c[j] = (lo >> (6 * j)) & 0x3Fu;
+    c[5] = (lo >> 30) | ((hi & 0xFu) << 2);
+    c[6] = (hi >> 4) & 0x3Fu;
+    c[7] = (hi >> 10) & 0x3Fu;
   } else {
     const uint32_t w = *reinterpret_cast<const uint32_t*>(q + elem / 2);
 #pragma unroll
@@ -181,9 +212,11 @@ using namespace mxk;
 extern "C" mx_status_t mx_dequantize(const uint8_t* q, const uint8_t* scales, int64_t rows, int64_t cols, int block,
                                      mx_elem_t fmt, mx_orient_t orient, void* out, mx_dtype_t out_dtype,
                                      hipStream_t stream) {
-  if (fmt != MX_E4M3 && fmt != MX_E5M2 && fmt != MX_E2M1) return MX_ERR_UNSUPPORTED;
+  const bool fp6 = fmt == MX_E2M3 || fmt == MX_E3M2;
+  if (fmt != MX_E4M3 && fmt != MX_E5M2 && fmt != MX_E2M1 && !fp6) return MX_ERR_UNSUPPORTED;
   if (out_dtype != MX_F32 && out_dtype != MX_BF16) return MX_ERR_UNSUPPORTED;
   if (orient != MX_ROWWISE && orient != MX_COLWISE_T) return MX_ERR_UNSUPPORTED;
+  if (fp6 && orient != MX_ROWWISE) return MX_ERR_UNSUPPORTED;   // MXFP6 is stored row-wise only
   if (block != 32) return MX_ERR_UNSUPPORTED;
   if (rows < 0 || cols < 0 || rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31)) return MX_ERR_SHAPE;
   if (orient == MX_ROWWISE && cols % 32 != 0) return MX_ERR_SHAPE;
@@ -198,6 +231,10 @@ extern "C" mx_status_t mx_dequantize(const uint8_t* q, const uint8_t* scales, in
                             : deq_dispatch<E4M3, false>(q, scales, rows, cols, col, out, stream);
     case MX_E5M2: return bf ? deq_dispatch<E5M2, true>(q, scales, rows, cols, col, out, stream)
                             : deq_dispatch<E5M2, false>(q, scales, rows, cols, col, out, stream);
+    case MX_E2M3: return bf ? deq_dispatch<E2M3, true>(q, scales, rows, cols, false, out, stream)
+                            : deq_dispatch<E2M3, false>(q, scales, rows, cols, false, out, stream);
+    case MX_E3M2: return bf ? deq_dispatch<E3M2, true>(q, scales, rows, cols, false, out, stream)
+                            : deq_dispatch<E3M2, false>(q, scales, rows, cols, false, out, stream);
     default: return bf ? deq_dispatch<E2M1, true>(q, scales, rows, cols, col, out, stream)
                        : deq_dispatch<E2M1, false>(q, scales, rows, cols, col, out, stream);
   }

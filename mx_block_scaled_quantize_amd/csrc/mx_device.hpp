@@ -15,7 +15,7 @@
 
 namespace mxk {
 
-enum Fmt : int { E4M3 = 0, E5M2 = 1, E2M1 = 2 };
+enum Fmt : int { E4M3 = 0, E5M2 = 1, E2M1 = 2, E2M3 = 3, E3M2 = 4 };
 enum InType : int { IN_F32 = 0, IN_BF16 = 1, IN_F16 = 2 };
 enum Rule : int { FLOOR = 0, CEIL = 1 };
 
@@ -54,6 +54,28 @@ template <> struct Fmt_<E2M1> {
   static constexpr int kShift = 22;
   static constexpr uint32_t kRebias = (127u - 1u) << 1;
   static constexpr uint32_t kNan = 0x7u;             // no NaN: largest magnitude
+};
+template <> struct Fmt_<E2M3> {
+  static constexpr int kBits = 6;
+  static constexpr int kEmax = 2;                    // 7.5 = 1.875 * 2^2
+  static constexpr uint32_t kMaxFrac = 0x700000u;    // fraction of 1.875
+  static constexpr uint32_t kMaxBits = 0x40F00000u;  // 7.5f
+  static constexpr uint32_t kMinNormBits = 0x3F800000u;  // 1.0
+  static constexpr uint32_t kSubMagicBits = 0x49800000u; // 2^20: ulp 2^-3
+  static constexpr int kShift = 20;
+  static constexpr uint32_t kRebias = (127u - 1u) << 3;
+  static constexpr uint32_t kNan = 0x1Fu;            // no NaN: largest magnitude
+};
+template <> struct Fmt_<E3M2> {
+  static constexpr int kBits = 6;
+  static constexpr int kEmax = 4;                    // 28 = 1.75 * 2^4
+  static constexpr uint32_t kMaxFrac = 0x600000u;
+  static constexpr uint32_t kMaxBits = 0x41E00000u;  // 28.0f
+  static constexpr uint32_t kMinNormBits = 0x3E800000u;  // 2^-2
+  static constexpr uint32_t kSubMagicBits = 0x49000000u; // 2^19: ulp 2^-4
+  static constexpr int kShift = 21;
+  static constexpr uint32_t kRebias = (127u - 3u) << 2;
+  static constexpr uint32_t kNan = 0x1Fu;
 };
 
 // Round-to-nearest-even, saturating cast of an FP32 value to format F.

@@ -779,6 +779,8 @@ extern "C" mx_status_t mx_quantize(const void* x, mx_dtype_t in, int64_t rows, i
                                    mx_elem_t fmt, mx_scale_rule_t rule, mx_orient_t orient, int hadamard,
                                    uint32_t hadamard_sign_mask, uint8_t* q, uint8_t* scales, float* amax_out,
                                    hipStream_t stream) {
+  if (fmt == MX_E2M3 || fmt == MX_E3M2)
+    return fp6_quantize(x, in, rows, cols, block, fmt, rule, orient, hadamard, q, scales, amax_out, stream);
   if (mx_status_t st = check_common_quant(in, rows, cols, block, fmt, rule); st != MX_OK) return st;
   if (orient != MX_ROWWISE && orient != MX_COLWISE_T) return MX_ERR_UNSUPPORTED;
   const int64_t n = rows * cols;
