@@ -387,12 +387,25 @@ def _pmc_mean(path, kernel_substr, counter):
 
 GEMM_PROFILES = {
     # kernel name substring -> (file, title, FLOPs per launch, dense peak TFLOP/s)
-    "gemm256_kernel<0, 0, true>": ("gemm256_kernel_mxfp8_8192x14336x4096.md",
-                                   "MXFP8 E4M3 GEMM, A 8192x4096 . (W 14336x4096)^T, BF16 out",
-                                   2.0 * 8192 * 14336 * 4096, FP8_PEAK_TFLOPS),
-    "gemm256_kernel<2, 2, true>": ("gemm256_kernel_mxfp4_4096x4096x8192.md",
-                                   "MXFP4 E2M1 GEMM, dW = (1/32) Gq^T Xq, 4096x4096, K = 8192, BF16 out",
-                                   2.0 * 4096 * 4096 * 8192, FP4_PEAK_TFLOPS),
+    "gemm256_kernel<0, 0, true, false, false, false, false>": (
+        "gemm256_kernel_mxfp8_8192x14336x4096.md", "MXFP8 E4M3 GEMM, A 8192x4096 . (W 14336x4096)^T, BF16 out",
+        2.0 * 8192 * 14336 * 4096, FP8_PEAK_TFLOPS),
+    "gemm256_kernel<2, 2, true, false, false, false, false>": (
+        "gemm256_kernel_mxfp4_4096x4096x8192.md",
+        "MXFP4 E2M1 GEMM, dW = (1/32) Gq^T Xq, 4096x4096, K = 8192, BF16 out",
+        2.0 * 4096 * 4096 * 8192, FP4_PEAK_TFLOPS),
+    "gemm256_kernel<0, 0, true, false, false, false, true>": (
+        "gemm256_kernel_mxfp8_requant_e4m3_8192x14336x4096.md",
+        "MXFP8 E4M3 GEMM 8192x4096 . (14336x4096)^T, FP32 result re-quantized to MXFP8 E4M3 in the epilogue",
+        2.0 * 8192 * 14336 * 4096, FP8_PEAK_TFLOPS),
+    "gemm256_kernel<0, 0, true, true, false, false, false>": (
+        "gemm256_kernel_mm_fp8_nt_8192x14336x4096.md",
+        "per-tensor FP8 E4M3 mm_fp8, x 8192x4096 @ w.t() (w 14336x4096 K-contiguous), BF16 bias, BF16 out",
+        2.0 * 8192 * 14336 * 4096, FP8_PEAK_TFLOPS),
+    "gemm256_kernel<0, 0, true, true, false, true, false>": (
+        "gemm256_kernel_mm_fp8_nn_8192x14336x4096.md",
+        "per-tensor FP8 E4M3 mm_fp8, x 8192x4096 @ wT (wT 4096x14336 N-contiguous, LDS transpose reads), BF16 bias",
+        2.0 * 8192 * 14336 * 4096, FP8_PEAK_TFLOPS),
 }
 
 
