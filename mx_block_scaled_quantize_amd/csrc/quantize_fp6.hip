@@ -8,11 +8,19 @@
 // little-endian bit stream along the row (element i at bits 6i .. 6i+5), so a
 // block is 24 bytes and 8 elements are 6 bytes.
 //
-// Kernel: flat over the row-wise blocks (contiguous in row-major input): a lane
-// owns 8 elements (one 16-byte BF16/FP16 load, two for FP32), a quad owns a
-// block and takes its amax with two DPP steps.  The element cast is the exact
-// integer RNE + saturation encoder applied to v * 2^-e (a power-of-two multiply,
-// exact wherever the result can matter).
+// Kernels, flat over the row-wise blocks (contiguous in row-major input):
+//   rowwise_bf16_kernel  BF16 input: a lane owns a whole block (64 bytes in, 24
+//     out) and converts it with one V_CVT_SCALEF32_PK32_{FP6,BF6}_BF16.  An
+//     in-bounds probe over every BF16 value at block scales 2^-124 .. 2^125 found
+//     these converts equal to RNE(v / 2^e) on the E2M3 / E3M2 grids, saturating
+//     beyond the largest magnitude, elements in bit-stream order.  (The FP32-input
+//     converts differ on some values, so FP32 and FP16 inputs do not use them.)
+//     Blocks with NaN/Inf, or with e = -127 (not a normal FP32 scale), take the
+//     integer encoder below.
+//   rowwise_kernel  FP32 / FP16 input: a lane owns 8 elements, a quad owns a block
+//     and takes its amax with two DPP steps; the cast is the exact integer RNE +
+//     saturation encoder on v * 2^-e (a power-of-two multiply, exact wherever the
+//     result can matter).
 
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
@@ -81,6 +89,104 @@ __global__ __launch_bounds__(kThreads) void rowwise_kernel(const void* __restric
   }
 }
 
+typedef __bf16 v32bf_t __attribute__((ext_vector_type(32)));
+typedef unsigned int v16u_t __attribute__((ext_vector_type(16)));
+typedef unsigned int v6u_t __attribute__((ext_vector_type(6)));
+constexpr int kUnrollB = 2;
+
+template <int F, int R, bool AMAX>
+__global__ __launch_bounds__(kThreads) void rowwise_bf16_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
+                                                                uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
+                                                                uint32_t* __restrict__ amax_out) {
+  uint32_t tmax = 0;
+#pragma unroll
+  for (int u = 0; u < kUnrollB; ++u) {
+    const int64_t blk = (int64_t(blockIdx.x) * kUnrollB + u) * kThreads + threadIdx.x;
+    if (blk >= nblocks) continue;
+    const uint4* src = reinterpret_cast<const uint4*>(x + blk * 32);
+    v16u_t d;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 t = src[k];
+      d[4 * k] = t.x;
+      d[4 * k + 1] = t.y;
+      d[4 * k + 2] = t.z;
+      d[4 * k + 3] = t.w;
+    }
+    // block amax of the 32 magnitudes as FP32 bit patterns (NaN > Inf > finite)
+    uint32_t mp = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) mp = pk_umax16(mp, d[k] & 0x7FFF7FFFu);
+    const uint32_t bmax = umax((mp & 0xFFFFu) << 16, mp & 0xFFFF0000u);
+    if constexpr (AMAX) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        tmax = umax(tmax, abs_bits_no_nan(__uint_as_float(d[k] << 16)));
+        tmax = umax(tmax, abs_bits_no_nan(__uint_as_float(d[k] & 0xFFFF0000u)));
+      }
+    }
+    const bool nonfinite = bmax >= 0x7F800000u;
+    const int e = nonfinite ? 0 : shared_exponent<F, R>(bmax);
+    uint32_t w[6];
+    if (!nonfinite && e > -127) {
+      const float scale = __uint_as_float(uint32_t(127 + e) << 23);
+      const v32bf_t xv = __builtin_bit_cast(v32bf_t, d);
+      v6u_t r;
+      if constexpr (F == E2M3) r = __builtin_bit_cast(v6u_t, __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(xv, scale));
+      else r = __builtin_bit_cast(v6u_t, __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(xv, scale));
+#pragma unroll
+      for (int k = 0; k < 6; ++k) w[k] = r[k];
+    } else {
+      const float mul = pow2_neg(e);
+      uint64_t acc = 0;
+      int nb = 0, wi = 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t bits = (i & 1) ? (d[i >> 1] & 0xFFFF0000u) : (d[i >> 1] << 16);
+        const uint32_t c = nonfinite ? (Fmt_<F>::kNan | ((bits >> 31) << 5)) : encode_rne_sat<F>(__uint_as_float(bits) * mul);
+        acc |= uint64_t(c) << nb;
+        nb += 6;
+        if (nb >= 32) {
+          w[wi++] = uint32_t(acc);
+          acc >>= 32;
+          nb -= 32;
+        }
+      }
+    }
+    // 24 bytes at 24 * blk: 8-byte aligned
+    uint2* dst = reinterpret_cast<uint2*>(q + blk * 24);
+    dst[0] = make_uint2(w[0], w[1]);
+    dst[1] = make_uint2(w[2], w[3]);
+    dst[2] = make_uint2(w[4], w[5]);
+    scales[blk] = uint8_t(nonfinite ? 0xFFu : uint32_t(e + 127));
+  }
+  if constexpr (AMAX) {
+    __shared__ uint32_t red[kThreads / 64];
+    tmax = wave_max(tmax);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = tmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t mm = red[0];
+#pragma unroll
+      for (int k = 1; k < kThreads / 64; ++k) mm = umax(mm, red[k]);
+      if (mm) atomic_max_u32(amax_out, mm);
+    }
+  }
+}
+
+template <int F, int R>
+static mx_status_t launch_bf16(const void* x, int64_t n, uint8_t* q, uint8_t* s, uint32_t* amax, hipStream_t st) {
+  const int64_t nblocks = n / 32;
+  const int64_t per = int64_t(kThreads) * kUnrollB;
+  const dim3 grid{unsigned((nblocks + per - 1) / per)}, block{unsigned(kThreads)};
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  if (amax)
+    hipLaunchKernelGGL((rowwise_bf16_kernel<F, R, true>), grid, block, 0, st, xb, nblocks, q, s, amax);
+  else
+    hipLaunchKernelGGL((rowwise_bf16_kernel<F, R, false>), grid, block, 0, st, xb, nblocks, q, s, amax);
+  return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
 template <int IN, int F, int R>
 static mx_status_t launch(const void* x, int64_t n, uint8_t* q, uint8_t* s, uint32_t* amax, hipStream_t st) {
   const int64_t nchunks = n / 8;
@@ -96,7 +202,7 @@ static mx_status_t launch(const void* x, int64_t n, uint8_t* q, uint8_t* s, uint
 template <int F, int R>
 static mx_status_t by_input(mx_dtype_t in, const void* x, int64_t n, uint8_t* q, uint8_t* s, uint32_t* amax,
                             hipStream_t st) {
-  if (in == MX_BF16) return launch<IN_BF16, F, R>(x, n, q, s, amax, st);
+  if (in == MX_BF16) return launch_bf16<F, R>(x, n, q, s, amax, st);
   if (in == MX_F16) return launch<IN_F16, F, R>(x, n, q, s, amax, st);
   return launch<IN_F32, F, R>(x, n, q, s, amax, st);
 }

@@ -44,10 +44,14 @@ def test_fp6_rowwise_parity(dtype, fmt, rule):
 
 @pytest.mark.parametrize("fmt", FP6)
 @pytest.mark.parametrize("rule", RULES)
-def test_fp6_every_bf16_pattern_and_specials(fmt, rule):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fp6_every_bf16_pattern_and_specials(fmt, rule, dtype):
+    """Every finite BF16 value in blocks sweeping the exponent range, plus special
+    blocks; BF16 input runs the hardware-convert kernel, FP32 the integer encoder."""
     blocks = np.concatenate([workloads.all_bf16_blocks(), workloads.special_blocks()])
-    x32 = blocks.reshape(-1, 32)
-    q, s = mxa.mx_quantize(upload_f32(x32), fmt, rule, "row")
+    x = make_input(blocks.reshape(-1, 32), dtype)
+    x32 = f32_of_input(x)
+    q, s = mxa.mx_quantize(x, fmt, rule, "row")
     wq, ws = omx.quantize_rowwise(x32, fmt, rule)
     assert_bytes_equal(host(s), ws, "scales")
     assert_bytes_equal(host(q), wq, "codes")
