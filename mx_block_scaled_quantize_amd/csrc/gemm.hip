@@ -283,7 +283,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// gemm256_kernel: the large-shape path (M, N multiples of 256, K of 1024).
+// gemm256_kernel: the large-shape path (K a multiple of 1024; any M, N, a partial last
+// tile row / column reading zeros past the matrix and storing only inside it).
 //
 // One workgroup of 4 waves owns a 256 x 256 output tile; each wave owns a
 // 128 x 128 quarter held as 4 x 4 MFMA accumulators (256 FP32 per lane, in
@@ -739,9 +740,12 @@ __device__ __forceinline__ void requant_quarter(const v16f (&acc)[4][4], float a
         v[4 * c + 3] = x.w;
       }
 #pragma unroll
-      for (int c = 0; c < 32; ++c) tmax = umax(tmax, abs_bits_no_nan(v[c]));
+      if (row0 + 32 * i + row < g.M && col0 + 32 * blk < g.N)
+#pragma unroll
+        for (int c = 0; c < 32; ++c) tmax = umax(tmax, abs_bits_no_nan(v[c]));
       const int64_t r = row0 + 32 * i + row;
-      requant_block32<FC, RC>(v, g.qc + r * qpitch + (col0 + 32 * blk) * kBits / 8, g.sc + r * nb + col0 / 32 + blk);
+      if (r < g.M && col0 + 32 * blk < g.N)   // partial last tile row / column
+        requant_block32<FC, RC>(v, g.qc + r * qpitch + (col0 + 32 * blk) * kBits / 8, g.sc + r * nb + col0 / 32 + blk);
     }
     wave_lds_fence();   // the tile is read before the next one overwrites it
   }
@@ -765,19 +769,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   const uint8_t* A = g.a + int64_t(blockIdx.y) * g.batch_a;
   const uint8_t* B = g.b + int64_t(blockIdx.y) * g.batch_b;
 
+  // rows (columns) of the tile inside the matrix: the last tile row / column may be
+  // partial; the resources end there, so loads beyond return zeros (K-contiguous) or,
+  // M/N-contiguous, the next K-row's leading codes (which only reach outputs beyond
+  // M / N, never stored) and zeros past the end of the matrix
+  const int rows_a = int(min(int64_t(kTile), g.M - int64_t(tm) * kTile));
+  const int rows_b = int(min(int64_t(kTile), g.N - int64_t(tn) * kTile));
   Ctx c;
   if constexpr (TA)   // columns tm * 256 .. + 255 of every K-row
-    c.a = make_rsrc(A + int64_t(tm) * kTile, uint32_t(int64_t(K - 1) * lda + kTile));
+    c.a = make_rsrc(A + int64_t(tm) * kTile, uint32_t(int64_t(K - 1) * lda + rows_a));
   else
-    c.a = make_rsrc(A + int64_t(tm) * kTile * kbytes, uint32_t(kTile * kbytes));
+    c.a = make_rsrc(A + int64_t(tm) * kTile * kbytes, uint32_t(rows_a * kbytes));
   if constexpr (TB)
-    c.b = make_rsrc(B + int64_t(tn) * kTile, uint32_t(int64_t(K - 1) * ldb + kTile));
+    c.b = make_rsrc(B + int64_t(tn) * kTile, uint32_t(int64_t(K - 1) * ldb + rows_b));
   else
-    c.b = make_rsrc(B + int64_t(tn) * kTile * kbytes, uint32_t(kTile * kbytes));
+    c.b = make_rsrc(B + int64_t(tn) * kTile * kbytes, uint32_t(rows_b * kbytes));
   c.z = make_rsrc(A, 0);
   if constexpr (!PT) {
-    c.sa = make_rsrc(g.sa + int64_t(tm) * kTile * kblocks, uint32_t(kTile * kblocks));
-    c.sb = make_rsrc(g.sb + int64_t(tn) * kTile * kblocks, uint32_t(kTile * kblocks));
+    c.sa = make_rsrc(g.sa + int64_t(tm) * kTile * kblocks, uint32_t(rows_a * kblocks));
+    c.sb = make_rsrc(g.sb + int64_t(tn) * kTile * kblocks, uint32_t(rows_b * kblocks));
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -885,7 +895,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint2 bw = make_uint2(0, 0);
-        if (PT && g.bias) bw = *reinterpret_cast<const uint2*>(g.bias + col0 + 32 * j + 8 * q + 4 * h);
+        if (PT && g.bias && col0 + 32 * j + 8 * q + 4 * h < g.N)
+          bw = *reinterpret_cast<const uint2*>(g.bias + col0 + 32 * j + 8 * q + 4 * h);
         bias[j][q][0] = __uint_as_float(bw.x << 16);
         bias[j][q][1] = __uint_as_float(bw.x & 0xFFFF0000u);
         bias[j][q][2] = __uint_as_float(bw.y << 16);
@@ -919,7 +930,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
     for (int it = 0; it < 32; ++it) {
       const int row = 4 * it + (lane >> 4);
       const uint4 v = *reinterpret_cast<const uint4*>(ep + row * 256 + 16 * (u ^ (row & 15)));
-      *reinterpret_cast<uint4*>(C + (row0 + row) * ldc + col0 + 8 * u) = v;
+      if (row0 + row < g.M && col0 + 8 * u < g.N)   // N % 8 == 0: a piece is wholly in or out
+        *reinterpret_cast<uint4*>(C + (row0 + row) * ldc + col0 + 8 * u) = v;
     }
   } else {
     float* C = static_cast<float*>(g.c) + int64_t(blockIdx.y) * g.batch_c;
@@ -930,6 +942,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t off = (row0 + 32 * i + rr) * ldc + col0 + 32 * j + 8 * q + 4 * h;
+          if (row0 + 32 * i + rr < g.M && col0 + 32 * j + 8 * q + 4 * h < g.N)   // N % 4 == 0
           *reinterpret_cast<float4*>(C + off) =
               make_float4(alpha * acc[i][j][4 * q], alpha * acc[i][j][4 * q + 1], alpha * acc[i][j][4 * q + 2],
                           alpha * acc[i][j][4 * q + 3]);
@@ -956,12 +969,13 @@ static mx_status_t gemm_dispatch(const uint8_t* a, const uint8_t* sa, const uint
   g.ldb = FB == E2M1 ? K / 2 : K;
   g.ldc = ldc;
   g.alpha = alpha;
-  const bool big = M % t256::kTile == 0 && N % t256::kTile == 0 && K % t256::kMinK == 0 && K > 0 && K <= (int64_t(1) << 22) &&
-                   (M / t256::kTile) * (N / t256::kTile) < (int64_t(1) << 31) && !misaligned(a) && !misaligned(b) &&
-                   !misaligned(sa) && !misaligned(sb) && !misaligned(c) && (ldc * esize) % 16 == 0;
+  const int64_t tm256 = (M + t256::kTile - 1) / t256::kTile, tn256 = (N + t256::kTile - 1) / t256::kTile;
+  const bool big = N % (BF ? 8 : 4) == 0 && K % t256::kMinK == 0 && K > 0 && K <= (int64_t(1) << 22) &&
+                   tm256 * tn256 < (int64_t(1) << 31) && !misaligned(a) && !misaligned(b) && !misaligned(sa) &&
+                   !misaligned(sb) && !misaligned(c) && (ldc * esize) % 16 == 0;
   if (big) {
-    g.tiles_m = int(M / t256::kTile);
-    g.tiles_n = int(N / t256::kTile);
+    g.tiles_m = int(tm256);
+    g.tiles_n = int(tn256);
     hipLaunchKernelGGL((t256::gemm256_kernel<FA, FB, BF, false, false, false>), dim3(unsigned(g.tiles_m * g.tiles_n)),
                        dim3(t256::kThreads), 0, st, g);
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
@@ -978,14 +992,16 @@ static mx_status_t gemm_dispatch(const uint8_t* a, const uint8_t* sa, const uint
 template <int F, bool TA, bool TB>
 static mx_status_t mm_launch(GemmArgs g, int64_t batch, hipStream_t st) {
   constexpr int64_t kTile = t256::kTile;
-  const bool big = g.M % kTile == 0 && g.N % kTile == 0 && g.K % t256::kMinK == 0 && g.K > 0 &&
-                   g.K <= (int64_t(1) << 22) && (g.M / kTile) * (g.N / kTile) < (int64_t(1) << 31) &&
+  const int64_t tm256 = (g.M + kTile - 1) / kTile, tn256 = (g.N + kTile - 1) / kTile;
+  // M/N-contiguous operands are fetched in 16-byte chunks of each K-row: rows must stay 16-byte aligned
+  const bool big = g.N % 8 == 0 && (!TA || g.M % 16 == 0) && (!TB || g.N % 16 == 0) && g.K % t256::kMinK == 0 &&
+                   g.K > 0 && g.K <= (int64_t(1) << 22) && tm256 * tn256 < (int64_t(1) << 31) &&
                    g.K * g.lda < (int64_t(1) << 31) && g.K * g.ldb < (int64_t(1) << 31) && !misaligned(g.a) &&
                    !misaligned(g.b) && !misaligned(g.c) && (g.batch_a % 16) == 0 && (g.batch_b % 16) == 0 &&
                    (reinterpret_cast<uintptr_t>(g.bias) & 7u) == 0;
   if (big) {
-    g.tiles_m = int(g.M / kTile);
-    g.tiles_n = int(g.N / kTile);
+    g.tiles_m = int(tm256);
+    g.tiles_n = int(tn256);
     hipLaunchKernelGGL((t256::gemm256_kernel<F, F, true, true, TA, TB>),
                        dim3(unsigned(g.tiles_m * g.tiles_n), unsigned(batch)), dim3(t256::kThreads), 0, st, g);
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
@@ -1006,13 +1022,12 @@ static mx_status_t mm_layouts(const GemmArgs& g, bool ta, bool tb, int64_t batch
 template <int FA, int FB>
 static mx_status_t requant_dispatch(GemmArgs g, hipStream_t st) {
   const int64_t M = g.M, N = g.N, K = g.K;
-  const bool big = M % t256::kTile == 0 && N % t256::kTile == 0 && K % t256::kMinK == 0 && K > 0 &&
-                   K <= (int64_t(1) << 22) && (M / t256::kTile) * (N / t256::kTile) < (int64_t(1) << 31) &&
-                   !misaligned(g.a) && !misaligned(g.b) && !misaligned(g.sa) && !misaligned(g.sb) &&
-                   (reinterpret_cast<uintptr_t>(g.sc) & 3u) == 0;
+  const int64_t tm256 = (M + t256::kTile - 1) / t256::kTile, tn256 = (N + t256::kTile - 1) / t256::kTile;
+  const bool big = K % t256::kMinK == 0 && K > 0 && K <= (int64_t(1) << 22) && tm256 * tn256 < (int64_t(1) << 31) &&
+                   !misaligned(g.a) && !misaligned(g.b) && !misaligned(g.sa) && !misaligned(g.sb);
   if (big) {
-    g.tiles_m = int(M / t256::kTile);
-    g.tiles_n = int(N / t256::kTile);
+    g.tiles_m = int(tm256);
+    g.tiles_n = int(tn256);
     hipLaunchKernelGGL((t256::gemm256_kernel<FA, FB, true, false, false, false, true>),
                        dim3(unsigned(g.tiles_m * g.tiles_n)), dim3(t256::kThreads), 0, st, g);
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
