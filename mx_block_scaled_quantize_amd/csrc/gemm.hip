@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// gemm256_kernel: the large-shape path (K a multiple of 1024; any M, N, a partial last
+// gemm256_kernel: the large-shape path (K a multiple of 512, or of 128 per-tensor; any M, N, a partial last
 // tile row / column reading zeros past the matrix and storing only inside it).
 //
 // One workgroup of 4 waves owns a 256 x 256 output tile; each wave owns a
@@ -339,7 +339,8 @@ constexpr int kPairRow = 2 * kRow;            // K-contiguous row of a stage pai
 constexpr int kPairLoads = kPairOp / 1024 / 4;   // 1 KiB DMA instructions per wave per operand per pair
 constexpr int kCodeGroup = kPairLoads;        // vector-memory instructions per wave per stage (both operands)
 constexpr int kKbPerScale = 16;               // K-blocks per scale stage
-constexpr int kMinK = 1024;                   // K granule of this path (two scale stages)
+constexpr int kMxK = 512;                     // K granule with MX scales: whole scale stages (16 K-blocks)
+constexpr int kPtK = 128;                     // K granule of the per-tensor mode: whole stage pairs
 constexpr int kMnPitch = kTile;               // M/N-contiguous stage: bytes per K-row
 
 __shared__ __attribute__((aligned(1024))) uint8_t g_pair0[2 * kPairOp];   // stages 4n, 4n + 1: [A | B]
@@ -839,14 +840,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   Regs r;
 
-  // prologue: code stages 0..3, scale stages 0 and 1 (T >= 16, nsuper >= 2)
+  // prologue: code stages 0..3, scale stages 0 and 1 (T >= 2 and even, nsuper >= 1); stages
+  // and scale stages past the end of K load zeros from the empty resource, and so do the
+  // dead stages of the last unrolled body, so their MFMAs add nothing
   // same op pattern as the loop (pair, its scale stage if any, one prefetch) so that
   // the first boundaries' wait counts hold; the prologue's prefetches are empty
   if constexpr (!PT) issue_scales<0>(c, 0, wave, true);
-  issue_pair<0, 1, TA, TB>(c, 0, wave, true, true);
+  issue_pair<0, 1, TA, TB>(c, 0, wave, true, true);   // T >= 2
   issue_prefetch<TA, TB>(c, 0, wave, false);
-  issue_pair<2, 3, TA, TB>(c, 2, wave, true, true);
-  if constexpr (!PT) issue_scales<1>(c, 1, wave, true);
+  issue_pair<2, 3, TA, TB>(c, 2, wave, 2 < T, 3 < T);
+  if constexpr (!PT) issue_scales<1>(c, 1, wave, 1 < nsuper);
   issue_prefetch<TA, TB>(c, 0, wave, false);
   // scale stage 0 and code stage 0 landed; the pair order interleaves stages 0 and 1
   // instruction by instruction, so wait for both: what may stay in flight is stages
@@ -970,7 +973,7 @@ static mx_status_t gemm_dispatch(const uint8_t* a, const uint8_t* sa, const uint
   g.ldc = ldc;
   g.alpha = alpha;
   const int64_t tm256 = (M + t256::kTile - 1) / t256::kTile, tn256 = (N + t256::kTile - 1) / t256::kTile;
-  const bool big = N % (BF ? 8 : 4) == 0 && K % t256::kMinK == 0 && K > 0 && K <= (int64_t(1) << 22) &&
+  const bool big = N % (BF ? 8 : 4) == 0 && K % t256::kMxK == 0 && K > 0 && K <= (int64_t(1) << 22) &&
                    tm256 * tn256 < (int64_t(1) << 31) && !misaligned(a) && !misaligned(b) && !misaligned(sa) &&
                    !misaligned(sb) && !misaligned(c) && (ldc * esize) % 16 == 0;
   if (big) {
@@ -994,7 +997,7 @@ static mx_status_t mm_launch(GemmArgs g, int64_t batch, hipStream_t st) {
   constexpr int64_t kTile = t256::kTile;
   const int64_t tm256 = (g.M + kTile - 1) / kTile, tn256 = (g.N + kTile - 1) / kTile;
   // M/N-contiguous operands are fetched in 16-byte chunks of each K-row: rows must stay 16-byte aligned
-  const bool big = g.N % 8 == 0 && (!TA || g.M % 16 == 0) && (!TB || g.N % 16 == 0) && g.K % t256::kMinK == 0 &&
+  const bool big = g.N % 8 == 0 && (!TA || g.M % 16 == 0) && (!TB || g.N % 16 == 0) && g.K % t256::kPtK == 0 &&
                    g.K > 0 && g.K <= (int64_t(1) << 22) && tm256 * tn256 < (int64_t(1) << 31) &&
                    g.K * g.lda < (int64_t(1) << 31) && g.K * g.ldb < (int64_t(1) << 31) && !misaligned(g.a) &&
                    !misaligned(g.b) && !misaligned(g.c) && (g.batch_a % 16) == 0 && (g.batch_b % 16) == 0 &&
@@ -1023,7 +1026,7 @@ template <int FA, int FB>
 static mx_status_t requant_dispatch(GemmArgs g, hipStream_t st) {
   const int64_t M = g.M, N = g.N, K = g.K;
   const int64_t tm256 = (M + t256::kTile - 1) / t256::kTile, tn256 = (N + t256::kTile - 1) / t256::kTile;
-  const bool big = K % t256::kMinK == 0 && K > 0 && K <= (int64_t(1) << 22) && tm256 * tn256 < (int64_t(1) << 31) &&
+  const bool big = K % t256::kMxK == 0 && K > 0 && K <= (int64_t(1) << 22) && tm256 * tn256 < (int64_t(1) << 31) &&
                    !misaligned(g.a) && !misaligned(g.b) && !misaligned(g.sa) && !misaligned(g.sb);
   if (big) {
     g.tiles_m = int(tm256);

@@ -66,13 +66,15 @@ def test_gemm_small_parity(fa, fb, shape):
     assert og.rel_frobenius(bf16_to_f64(c16), bf16_to_f64(og.f64_to_bf16_bits(ref))) <= BF16_TOL
 
 
-# Shapes on the 256 x 256-tile LDS-DMA path (K a multiple of 1024, N of 8):
+# Shapes on the 256 x 256-tile LDS-DMA path (K a multiple of 512, N of 8):
 # one tile at the minimum K; 6 tiles (no XCD regrouping); 8 tiles (regrouped
 # across XCDs, one tile column); a wide tile row at K = 3 * 1024 (odd number of
 # 16-K-block scale stages per unrolled pass).
 TILED_SHAPES = [(256, 256, 1024), (512, 768, 2048), (2048, 256, 1024), (256, 1024, 3072),
                 # ragged last tile row / column (rows past M, N read as zeros, stores masked)
-                (300, 264, 1024), (520, 1000, 2048)]
+                (300, 264, 1024), (520, 1000, 2048),
+                # K of 512 / 1536: the last unrolled body has stages past K (they load zeros)
+                (256, 512, 512), (264, 256, 1536)]
 
 
 @pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2"),

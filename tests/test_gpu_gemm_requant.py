@@ -41,7 +41,8 @@ def check(shape, fa, fb, fc, rc, alpha, seed):
     return qa, sa, qb, sb, c32
 
 
-SHAPES = [(256, 256, 1024), (512, 768, 2048), (300, 288, 1024), (200, 160, 96), (64, 96, 64), (1, 32, 32)]
+SHAPES = [(256, 256, 1024), (512, 768, 2048), (300, 288, 1024), (256, 256, 512), (200, 160, 96), (64, 96, 64),
+          (1, 32, 32)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)

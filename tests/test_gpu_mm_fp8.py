@@ -89,7 +89,8 @@ def test_mm_fp8_small_parity(fmt, ta, tb, shape):
 
 
 # 256 x 256-tile path shapes: one tile at the minimum K; 6 tiles; one wide tile row at K = 3 * 1024
-TILED = [(256, 256, 1024), (512, 768, 2048), (256, 1024, 3072), (272, 400, 1024)]   # last: ragged tiles
+TILED = [(256, 256, 1024), (512, 768, 2048), (256, 1024, 3072), (272, 400, 1024),   # ragged tiles
+         (256, 256, 128), (512, 256, 640)]                                                # K past the last pair
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
