@@ -51,8 +51,9 @@ extern "C" {
  * (max 6).  E2M3 (max 7.5) and E3M2 (max 28) are the FP6 members of the MX family
  * ([UE8M0] names MXFP8/6/4); they have no specials and are stored as a
  * little-endian bit stream along the row (element i at bits 6i .. 6i+5: 32
- * elements in 24 bytes).  FP6 is offered by mx_quantize (row-wise, no Hadamard)
- * and mx_dequantize (row-wise); the other entry points return MX_ERR_UNSUPPORTED. */
+ * elements in 24 bytes).  FP6 is offered by mx_quantize (no Hadamard),
+ * mx_quantize_dual and mx_dequantize; the other entry points return
+ * MX_ERR_UNSUPPORTED. */
 typedef enum { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M1 = 2, MX_E2M3 = 3, MX_E3M2 = 4 } mx_elem_t;
 
 /* Storage type of a floating-point tensor argument. */
@@ -99,8 +100,8 @@ typedef enum {
  * Q_i = RNE + saturating cast of V_i / 2^e to `fmt`.  A block holding NaN or
  * +-Inf gets scale code 255 and every Q_i set to the format's NaN with the
  * input's sign (E2M1, E2M3 and E3M2, having no NaN: the largest magnitude, +-6,
- * +-7.5, +-28).  -0 keeps its sign.  E2M3 / E3M2 (MXFP6): MX_ROWWISE only,
- * hadamard == 0; q is [rows][cols * 3 / 4].
+ * +-7.5, +-28).  -0 keeps its sign.  E2M3 / E3M2 (MXFP6): hadamard == 0; q is
+ * [rows][cols * 3 / 4] (MX_ROWWISE) or [cols][rows * 3 / 4] (MX_COLWISE_T).
  *
  * hadamard != 0 first replaces each block by H32 * diag(s) * V, where s_j = -1
  * when bit j of `hadamard_sign_mask` is set and H32 is the unnormalised

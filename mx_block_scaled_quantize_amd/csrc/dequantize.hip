@@ -216,7 +216,6 @@ extern "C" mx_status_t mx_dequantize(const uint8_t* q, const uint8_t* scales, in
   if (fmt != MX_E4M3 && fmt != MX_E5M2 && fmt != MX_E2M1 && !fp6) return MX_ERR_UNSUPPORTED;
   if (out_dtype != MX_F32 && out_dtype != MX_BF16) return MX_ERR_UNSUPPORTED;
   if (orient != MX_ROWWISE && orient != MX_COLWISE_T) return MX_ERR_UNSUPPORTED;
-  if (fp6 && orient != MX_ROWWISE) return MX_ERR_UNSUPPORTED;   // MXFP6 is stored row-wise only
   if (block != 32) return MX_ERR_UNSUPPORTED;
   if (rows < 0 || cols < 0 || rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31)) return MX_ERR_SHAPE;
   if (orient == MX_ROWWISE && cols % 32 != 0) return MX_ERR_SHAPE;
@@ -231,10 +230,10 @@ extern "C" mx_status_t mx_dequantize(const uint8_t* q, const uint8_t* scales, in
                             : deq_dispatch<E4M3, false>(q, scales, rows, cols, col, out, stream);
     case MX_E5M2: return bf ? deq_dispatch<E5M2, true>(q, scales, rows, cols, col, out, stream)
                             : deq_dispatch<E5M2, false>(q, scales, rows, cols, col, out, stream);
-    case MX_E2M3: return bf ? deq_dispatch<E2M3, true>(q, scales, rows, cols, false, out, stream)
-                            : deq_dispatch<E2M3, false>(q, scales, rows, cols, false, out, stream);
-    case MX_E3M2: return bf ? deq_dispatch<E3M2, true>(q, scales, rows, cols, false, out, stream)
-                            : deq_dispatch<E3M2, false>(q, scales, rows, cols, false, out, stream);
+    case MX_E2M3: return bf ? deq_dispatch<E2M3, true>(q, scales, rows, cols, col, out, stream)
+                            : deq_dispatch<E2M3, false>(q, scales, rows, cols, col, out, stream);
+    case MX_E3M2: return bf ? deq_dispatch<E3M2, true>(q, scales, rows, cols, col, out, stream)
+                            : deq_dispatch<E3M2, false>(q, scales, rows, cols, col, out, stream);
     default: return bf ? deq_dispatch<E2M1, true>(q, scales, rows, cols, col, out, stream)
                        : deq_dispatch<E2M1, false>(q, scales, rows, cols, col, out, stream);
   }

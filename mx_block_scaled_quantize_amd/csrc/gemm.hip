@@ -740,13 +740,12 @@ __device__ __forceinline__ void requant_quarter(const v16f (&acc)[4][4], float a
         v[4 * c + 2] = x.z;
         v[4 * c + 3] = x.w;
       }
-#pragma unroll
-      if (row0 + 32 * i + row < g.M && col0 + 32 * blk < g.N)
+      const int64_t r = row0 + 32 * i + row;
+      if (r < g.M && col0 + 32 * blk < g.N) {   // partial last tile row / column
 #pragma unroll
         for (int c = 0; c < 32; ++c) tmax = umax(tmax, abs_bits_no_nan(v[c]));
-      const int64_t r = row0 + 32 * i + row;
-      if (r < g.M && col0 + 32 * blk < g.N)   // partial last tile row / column
         requant_block32<FC, RC>(v, g.qc + r * qpitch + (col0 + 32 * blk) * kBits / 8, g.sc + r * nb + col0 / 32 + blk);
+      }
     }
     wave_lds_fence();   // the tile is read before the next one overwrites it
   }

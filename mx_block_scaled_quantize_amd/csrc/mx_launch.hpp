@@ -25,5 +25,9 @@ inline mx_status_t check_common_quant(mx_dtype_t in, int64_t rows, int64_t cols,
 mx_status_t fp6_quantize(const void* x, mx_dtype_t in, int64_t rows, int64_t cols, int block, mx_elem_t fmt,
                          mx_scale_rule_t rule, mx_orient_t orient, int hadamard, uint8_t* q, uint8_t* scales,
                          float* amax_out, hipStream_t stream);
+// Dual (row-wise + column-wise) MXFP6 quantization (quantize_fp6.hip), reached from mx_quantize_dual.
+mx_status_t fp6_quantize_dual(const void* x, mx_dtype_t in, int64_t rows, int64_t cols, int block, mx_elem_t fmt,
+                              mx_scale_rule_t rule, uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT,
+                              uint8_t* s_colT, float* amax_out, hipStream_t stream);
 
 }  // namespace mxk

@@ -802,6 +802,8 @@ extern "C" mx_status_t mx_quantize(const void* x, mx_dtype_t in, int64_t rows, i
 extern "C" mx_status_t mx_quantize_dual(const void* x, mx_dtype_t in, int64_t rows, int64_t cols, int block,
                                         mx_elem_t fmt, mx_scale_rule_t rule, uint8_t* q_row, uint8_t* s_row,
                                         uint8_t* q_colT, uint8_t* s_colT, float* amax_out, hipStream_t stream) {
+  if (fmt == MX_E2M3 || fmt == MX_E3M2)
+    return fp6_quantize_dual(x, in, rows, cols, block, fmt, rule, q_row, s_row, q_colT, s_colT, amax_out, stream);
   if (mx_status_t st = check_common_quant(in, rows, cols, block, fmt, rule); st != MX_OK) return st;
   const int64_t n = rows * cols;
   if (n > 0 && (!x || !q_row || !s_row || !q_colT || !s_colT)) return MX_ERR_NULL;

@@ -207,21 +207,222 @@ static mx_status_t by_input(mx_dtype_t in, const void* x, int64_t n, uint8_t* q,
   return launch<IN_F32, F, R>(x, n, q, s, amax, st);
 }
 
+// ---------------------------------------------------------------------------
+// Column-wise and dual MXFP6: a workgroup stages a 128-row x 64-column tile in LDS
+// (coalesced 16-byte loads), then each of its 256 threads encodes one column block
+// (32 rows of one column; threads 4 c .. 4 c + 3 cover the 4 blocks of column c, so
+// they write its 96 contiguous output bytes) and, for the dual layout, one row block
+// (32 contiguous values of a staged row).
+// ---------------------------------------------------------------------------
+constexpr int kTR = 128, kTC = 64;
+template <int IN> struct TileWord { using T = uint16_t; };
+template <> struct TileWord<IN_F32> { using T = float; };
+
+template <int IN>
+__device__ __forceinline__ float tile_value(typename TileWord<IN>::T w) {
+  if constexpr (IN == IN_F32) return w;
+  else if constexpr (IN == IN_BF16) return __uint_as_float(uint32_t(w) << 16);
+  else return f16_bits_to_f32(w);
+}
+
+// Encode one block of 32 values (v: the FP32 values; bf: their BF16 bit pairs, used
+// only for BF16 input) into 6 code words; returns the scale code.
+template <int IN, int F, int R>
+__device__ __forceinline__ uint32_t encode_block32(const float (&v)[32], const uint32_t (&bf)[16], uint32_t (&w)[6]) {
+  uint32_t bmax = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) bmax = umax(bmax, abs_bits(v[i]));
+  const bool nonfinite = bmax >= 0x7F800000u;
+  const int e = nonfinite ? 0 : shared_exponent<F, R>(bmax);
+  if constexpr (IN == IN_BF16) {
+    if (!nonfinite && e > -127) {
+      const float scale = __uint_as_float(uint32_t(127 + e) << 23);
+      v16u_t d;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) d[k] = bf[k];
+      const v32bf_t xv = __builtin_bit_cast(v32bf_t, d);
+      v6u_t r;
+      if constexpr (F == E2M3) r = __builtin_bit_cast(v6u_t, __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(xv, scale));
+      else r = __builtin_bit_cast(v6u_t, __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(xv, scale));
+#pragma unroll
+      for (int k = 0; k < 6; ++k) w[k] = r[k];
+      return uint32_t(e + 127);
+    }
+  }
+  const float mul = pow2_neg(e);
+  uint64_t acc = 0;
+  int nb = 0, wi = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t c = nonfinite ? (Fmt_<F>::kNan | ((__float_as_uint(v[i]) >> 31) << 5)) : encode_rne_sat<F>(v[i] * mul);
+    acc |= uint64_t(c) << nb;
+    nb += 6;
+    if (nb >= 32) {
+      w[wi++] = uint32_t(acc);
+      acc >>= 32;
+      nb -= 32;
+    }
+  }
+  return nonfinite ? 0xFFu : uint32_t(e + 127);
+}
+
+// 24 code bytes at an 8-byte aligned address
+__device__ __forceinline__ void store24(uint8_t* dst, const uint32_t (&w)[6]) {
+  uint2* d = reinterpret_cast<uint2*>(dst);
+  d[0] = make_uint2(w[0], w[1]);
+  d[1] = make_uint2(w[2], w[3]);
+  d[2] = make_uint2(w[4], w[5]);
+}
+
+template <int IN, int F, int R, bool DUAL, bool AMAX>
+__global__ __launch_bounds__(kThreads) void tile_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                        int tiles_c, uint8_t* __restrict__ q_row,
+                                                        uint8_t* __restrict__ s_row, uint8_t* __restrict__ q_col,
+                                                        uint8_t* __restrict__ s_col, uint32_t* __restrict__ amax_out) {
+  using W = typename TileWord<IN>::T;
+  constexpr int kPitch = kTC + 2;   // elements per staged row (an odd number of dwords apart for 2-byte W)
+  __shared__ W t[kTR][kPitch];
+  const int tid = threadIdx.x;
+  const int64_t r0 = int64_t(blockIdx.x / tiles_c) * kTR;
+  const int64_t c0 = int64_t(blockIdx.x % tiles_c) * kTC;
+  // ---- stage: 16-byte pieces (8 elements of 2-byte input, 4 of FP32), zero outside the matrix
+  constexpr int kPer = 16 / int(sizeof(W));
+  constexpr int kPieces = kTR * kTC / kPer;
+#pragma unroll
+  for (int k = 0; k < kPieces / kThreads; ++k) {
+    const int id = tid + kThreads * k, row = id / (kTC / kPer), pc = id % (kTC / kPer);
+    const int64_t gr = r0 + row, gc = c0 + pc * kPer;
+    uint4 d = make_uint4(0, 0, 0, 0);
+    if (gr < rows && gc < cols)
+      d = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) + (gr * cols + gc) * int64_t(sizeof(W)));
+    const W* e = reinterpret_cast<const W*>(&d);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) t[row][pc * kPer + j] = e[j];
+  }
+  __syncthreads();
+  uint32_t tmax = 0;
+  // ---- column block: column c, rows 32 b .. 32 b + 31 of the tile
+  {
+    const int c = tid >> 2, b = tid & 3;
+    const int64_t gc = c0 + c, gr = r0 + 32 * b;
+    if (gc < cols && gr < rows) {
+      float v[32];
+      uint32_t bf[16];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        v[i] = tile_value<IN>(t[32 * b + i][c]);
+        tmax = umax(tmax, abs_bits_no_nan(v[i]));
+      }
+      if constexpr (IN == IN_BF16) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) bf[k] = uint32_t(t[32 * b + 2 * k][c]) | (uint32_t(t[32 * b + 2 * k + 1][c]) << 16);
+      }
+      uint32_t w[6];
+      const uint32_t sc = encode_block32<IN, F, R>(v, bf, w);
+      store24(q_col + gc * (rows / 32 * 24) + (gr / 32) * 24, w);
+      s_col[gc * (rows / 32) + gr / 32] = uint8_t(sc);
+    }
+  }
+  // ---- row block (dual): row r, columns 32 h .. 32 h + 31 of the tile
+  if constexpr (DUAL) {
+    const int r = tid >> 1, h = tid & 1;
+    const int64_t gr = r0 + r, gc = c0 + 32 * h;
+    if (gr < rows && gc < cols) {
+      float v[32];
+      uint32_t bf[16];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = tile_value<IN>(t[r][32 * h + i]);
+      if constexpr (IN == IN_BF16) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) bf[k] = uint32_t(t[r][32 * h + 2 * k]) | (uint32_t(t[r][32 * h + 2 * k + 1]) << 16);
+      }
+      uint32_t w[6];
+      const uint32_t sc = encode_block32<IN, F, R>(v, bf, w);
+      store24(q_row + gr * (cols / 32 * 24) + (gc / 32) * 24, w);
+      s_row[gr * (cols / 32) + gc / 32] = uint8_t(sc);
+    }
+  }
+  if constexpr (AMAX) {
+    __shared__ uint32_t red[kThreads / 64];
+    tmax = wave_max(tmax);
+    if ((tid & 63) == 0) red[tid >> 6] = tmax;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t mm = red[0];
+#pragma unroll
+      for (int k = 1; k < kThreads / 64; ++k) mm = umax(mm, red[k]);
+      if (mm) atomic_max_u32(amax_out, mm);
+    }
+  }
+}
+
+template <int IN, int F, int R, bool DUAL>
+static mx_status_t launch_tiles(const void* x, int64_t rows, int64_t cols, uint8_t* qr, uint8_t* sr, uint8_t* qc,
+                                uint8_t* sc, uint32_t* amax, hipStream_t st) {
+  const int64_t tr = (rows + kTR - 1) / kTR, tc = (cols + kTC - 1) / kTC;
+  const dim3 grid{unsigned(tr * tc)}, block{unsigned(kThreads)};
+  if (amax)
+    hipLaunchKernelGGL((tile_kernel<IN, F, R, DUAL, true>), grid, block, 0, st, x, rows, cols, int(tc), qr, sr, qc, sc,
+                       amax);
+  else
+    hipLaunchKernelGGL((tile_kernel<IN, F, R, DUAL, false>), grid, block, 0, st, x, rows, cols, int(tc), qr, sr, qc,
+                       sc, amax);
+  return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+template <int F, int R, bool DUAL>
+static mx_status_t tiles_by_input(mx_dtype_t in, const void* x, int64_t rows, int64_t cols, uint8_t* qr, uint8_t* sr,
+                                  uint8_t* qc, uint8_t* sc, uint32_t* amax, hipStream_t st) {
+  if (in == MX_BF16) return launch_tiles<IN_BF16, F, R, DUAL>(x, rows, cols, qr, sr, qc, sc, amax, st);
+  if (in == MX_F16) return launch_tiles<IN_F16, F, R, DUAL>(x, rows, cols, qr, sr, qc, sc, amax, st);
+  return launch_tiles<IN_F32, F, R, DUAL>(x, rows, cols, qr, sr, qc, sc, amax, st);
+}
+
+template <bool DUAL>
+static mx_status_t tiles(mx_elem_t fmt, mx_scale_rule_t rule, mx_dtype_t in, const void* x, int64_t rows,
+                         int64_t cols, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* sc, uint32_t* amax,
+                         hipStream_t st) {
+  const bool ceil = rule == MX_SCALE_CEIL;
+  if (fmt == MX_E2M3)
+    return ceil ? tiles_by_input<E2M3, CEIL, DUAL>(in, x, rows, cols, qr, sr, qc, sc, amax, st)
+                : tiles_by_input<E2M3, FLOOR, DUAL>(in, x, rows, cols, qr, sr, qc, sc, amax, st);
+  return ceil ? tiles_by_input<E3M2, CEIL, DUAL>(in, x, rows, cols, qr, sr, qc, sc, amax, st)
+              : tiles_by_input<E3M2, FLOOR, DUAL>(in, x, rows, cols, qr, sr, qc, sc, amax, st);
+}
+
 }  // namespace fp6
+
+mx_status_t fp6_quantize_dual(const void* x, mx_dtype_t in, int64_t rows, int64_t cols, int block, mx_elem_t fmt,
+                              mx_scale_rule_t rule, uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT,
+                              uint8_t* s_colT, float* amax_out, hipStream_t stream) {
+  if (in != MX_F32 && in != MX_BF16 && in != MX_F16) return MX_ERR_UNSUPPORTED;
+  if (rule != MX_SCALE_FLOOR && rule != MX_SCALE_CEIL) return MX_ERR_UNSUPPORTED;
+  if (block != 32) return MX_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0 || rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31)) return MX_ERR_SHAPE;
+  if (rows % 32 != 0 || cols % 32 != 0) return MX_ERR_SHAPE;
+  if (rows * cols == 0) return MX_OK;
+  if (!x || !q_row || !s_row || !q_colT || !s_colT) return MX_ERR_NULL;
+  if (misaligned(x) || misaligned(q_row) || misaligned(q_colT)) return MX_ERR_ALIGN;
+  return fp6::tiles<true>(fmt, rule, in, x, rows, cols, q_row, s_row, q_colT, s_colT,
+                          reinterpret_cast<uint32_t*>(amax_out), stream);
+}
 
 mx_status_t fp6_quantize(const void* x, mx_dtype_t in, int64_t rows, int64_t cols, int block, mx_elem_t fmt,
                          mx_scale_rule_t rule, mx_orient_t orient, int hadamard, uint8_t* q, uint8_t* scales,
                          float* amax_out, hipStream_t stream) {
   if (in != MX_F32 && in != MX_BF16 && in != MX_F16) return MX_ERR_UNSUPPORTED;
   if (rule != MX_SCALE_FLOOR && rule != MX_SCALE_CEIL) return MX_ERR_UNSUPPORTED;
-  if (block != 32 || orient != MX_ROWWISE || hadamard != 0) return MX_ERR_UNSUPPORTED;
+  if (block != 32 || (orient != MX_ROWWISE && orient != MX_COLWISE_T) || hadamard != 0) return MX_ERR_UNSUPPORTED;
   if (rows < 0 || cols < 0 || rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31)) return MX_ERR_SHAPE;
-  if (cols % 32 != 0) return MX_ERR_SHAPE;
+  if (orient == MX_ROWWISE && cols % 32 != 0) return MX_ERR_SHAPE;
+  if (orient == MX_COLWISE_T && (rows % 32 != 0 || cols % 8 != 0)) return MX_ERR_SHAPE;
   const int64_t n = rows * cols;
   if (n == 0) return MX_OK;
   if (!x || !q || !scales) return MX_ERR_NULL;
   if (misaligned(x) || misaligned(q)) return MX_ERR_ALIGN;
   uint32_t* am = reinterpret_cast<uint32_t*>(amax_out);
+  if (orient == MX_COLWISE_T)
+    return fp6::tiles<false>(fmt, rule, in, x, rows, cols, nullptr, nullptr, q, scales, am, stream);
   const bool ceil = rule == MX_SCALE_CEIL;
   if (fmt == MX_E2M3)
     return ceil ? fp6::by_input<E2M3, CEIL>(in, x, n, q, scales, am, stream)

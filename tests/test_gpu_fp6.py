@@ -103,15 +103,63 @@ def test_fp6_full_size_sampled_rows():
     assert_bytes_equal(qh[rows], wq, "codes")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("fmt", FP6)
+@pytest.mark.parametrize("rule", RULES)
+def test_fp6_colwise_and_dual_parity(dtype, fmt, rule):
+    # ragged tiles: 160 rows (one full and one partial 128-row tile), 200 / 96 columns
+    for shape, seed, kind in (((160, 200), 67, "wide"), ((96, 96), 68, "rows"), ((288, 416), 69, "normal")):
+        x = make_input(workloads.random_tensor(shape, seed, kind), dtype)
+        xs = f32_of_input(x)
+        q, s, a = mxa.mx_quantize(x, fmt, rule, "col", amax=True)
+        wq, ws = omx.quantize_colwise_t(xs, fmt, rule)
+        assert_bytes_equal(host(s), ws, f"{shape} col scales")
+        assert_bytes_equal(host(q), wq, f"{shape} col codes")
+        assert host(a)[0] == omx.tensor_amax(xs)
+        if shape[1] % 32 == 0:
+            qr, sr, qc, sc, a = mxa.mx_quantize_dual(x, fmt, rule, amax=True)
+            wqr, wsr, wqc, wsc = omx.quantize_dual(xs, fmt, rule)
+            assert_bytes_equal(host(sr), wsr, f"{shape} dual row scales")
+            assert_bytes_equal(host(qr), wqr, f"{shape} dual row codes")
+            assert_bytes_equal(host(sc), wsc, f"{shape} dual col scales")
+            assert_bytes_equal(host(qc), wqc, f"{shape} dual col codes")
+            assert host(a)[0] == omx.tensor_amax(xs)
+
+
+@pytest.mark.parametrize("fmt", FP6)
+def test_fp6_dual_special_blocks(fmt):
+    blocks = workloads.special_blocks()
+    x32 = np.zeros((64, 64), np.float32)
+    x32[:18, :32] = blocks
+    x32[32:64, 32:50] = blocks.T
+    x32[40, :] = np.nan
+    x32[:, 60] = -np.inf
+    for dtype in ("f32", "bf16"):
+        x = make_input(x32, dtype)
+        xs = f32_of_input(x)
+        qr, sr, qc, sc = mxa.mx_quantize_dual(x, fmt, "ceil")
+        wqr, wsr, wqc, wsc = omx.quantize_dual(xs, fmt, "ceil")
+        for got, want, what in ((sr, wsr, "row scales"), (qr, wqr, "row codes"), (sc, wsc, "col scales"),
+                                (qc, wqc, "col codes")):
+            assert_bytes_equal(host(got), want, f"{dtype} {what}")
+
+
+@pytest.mark.parametrize("fmt", FP6)
+def test_fp6_colwise_dequantize(fmt):
+    g = np.random.default_rng(70)
+    rows, cols = 96, 136
+    codes = g.integers(0, 64, size=(cols, rows)).astype(np.uint8)      # stored transposed
+    scales = g.integers(0, 256, size=(cols, rows // 32)).astype(np.uint8)
+    packed = omx.pack_fp6(codes)
+    out = host(mxa.mx_dequantize(upload_u8(packed), upload_u8(scales), rows, cols, fmt, "col", torch.float32))
+    assert_float_equal(out, omx.dequantize(packed, scales, fmt).T, "col dequant")
+
+
 def test_fp6_unsupported_paths_raise():
     x = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
-    for call in (lambda: mxa.mx_quantize(x, "e2m3", "ceil", "col"),
-                 lambda: mxa.mx_quantize(x, "e2m3", "ceil", "row", hadamard_mask=1),
-                 lambda: mxa.mx_quantize_dual(x, "e3m2"),
-                 lambda: mxa.mx_dequantize(torch.zeros((64, 48), dtype=torch.uint8, device="cuda"),
-                                           torch.zeros((64, 2), dtype=torch.uint8, device="cuda"), 64, 64, "e2m3",
-                                           "col")):
-        with pytest.raises(ValueError):
-            call()
+    with pytest.raises(ValueError):
+        mxa.mx_quantize(x, "e2m3", "ceil", "row", hadamard_mask=1)
+    with pytest.raises(ValueError):
+        mxa.mx_quantize_dual(torch.zeros((64, 48), dtype=torch.bfloat16, device="cuda"), "e3m2")
     q, s = mxa.mx_quantize(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), "e2m3", "ceil", "row")
     assert q.shape == (0, 48)
