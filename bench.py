@@ -284,7 +284,16 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
     bf6 = R * C * 2 + R * C * 3 // 4 + R * C // 32
     res["mxfp6_e3m2_rowwise_bf16_8192x4096"] = {"us": round(tf6 * 1e6, 2), "GB/s": round(bf6 / tf6 / 1e9, 1),
                                                 "hbm_frac": round(bf6 / tf6 / 1e9 / HBM_PEAK_GBS, 4)}
-    del gx, words, sq, ss, fq
+    # MXFP6 E3M2 dual (row-wise + column-wise from one read)
+    fqc = torch.empty((C, R * 3 // 4), dtype=torch.uint8, device=dev)
+    fsc = torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
+    tf6d = time_calls(lambda: mxa.check(lib.mx_quantize_dual(gx.data_ptr(), 1, R, C, 32, 4, 1, fq.data_ptr(),
+                                                             ss.data_ptr(), fqc.data_ptr(), fsc.data_ptr(), None, sp)),
+                      32, 4, stream, torch)
+    bf6d = R * C * 2 + 2 * (R * C * 3 // 4 + R * C // 32)
+    res["mxfp6_e3m2_dual_bf16_8192x4096"] = {"us": round(tf6d * 1e6, 2), "GB/s": round(bf6d / tf6d / 1e9, 1),
+                                             "hbm_frac": round(bf6d / tf6d / 1e9 / HBM_PEAK_GBS, 4)}
+    del gx, words, sq, ss, fq, fqc, fsc
     # Hadamard + column-wise MXFP4 quantization of both operands, then the MXFP4 GEMM
     g_bits, x_bits, mask = workloads.cfg5()
     G, X = up_bf16(g_bits), up_bf16(x_bits)
