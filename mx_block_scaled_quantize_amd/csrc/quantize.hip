@@ -31,6 +31,8 @@
 //   The per-tensor kernels end with the delayed-scaling fold done by the last
 //   workgroup to finish (atomic ticket).
 
+#include <mutex>
+
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
 
@@ -679,20 +681,28 @@ static mx_status_t rowwise_dispatch(const void* x, int64_t n, uint8_t* q, uint8_
 // kernel and device): the strip kernels run as one such wave of persistent
 // workgroups that walk the supertiles (measured ~6-10% faster than one
 // workgroup per supertile, whose launch rounds load and compute in lockstep).
+// The cache is keyed by the kernel's address: instances of one kernel template
+// share a signature but not their register and LDS footprints.
 template <typename K>
 static int64_t resident_workgroups(K kernel, int threads) {
-  static int64_t cached[16] = {};
+  struct Entry { const void* fn; int dev; int64_t n; };
+  static Entry cache[64];
+  static int used = 0;
+  static std::mutex mu;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
-  if (cached[dev] == 0) {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || cus <= 0 ||
-        per_cu <= 0)
-      return 0;
-    cached[dev] = int64_t(cus) * per_cu;
-  }
-  return cached[dev];
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  const void* fn = reinterpret_cast<const void*>(kernel);
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (cache[i].fn == fn && cache[i].dev == dev) return cache[i].n;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || cus <= 0 ||
+      per_cu <= 0)
+    return 0;
+  const int64_t n = int64_t(cus) * per_cu;
+  if (used < 64) cache[used++] = Entry{fn, dev, n};
+  return n;
 }
 
 template <typename K>

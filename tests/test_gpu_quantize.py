@@ -117,7 +117,9 @@ def test_colwise_hadamard(fmt):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("rule", RULES)
 def test_dual_parity_ragged(dtype, fmt, rule):
-    for shape, seed in (((96, 160), 26), ((288, 416), 27)):
+    # tiles of 128 x 128 with ragged right and bottom edges; (256, 992) gives a
+    # tile count divisible by 8 (the XCD-grouped tile order)
+    for shape, seed in (((96, 160), 26), ((288, 416), 27), ((256, 992), 28), ((320, 544), 29)):
         x32 = workloads.random_tensor(shape, seed, "rows")
         x = make_input(x32, dtype)
         xs = f32_of_input(x)
@@ -142,14 +144,16 @@ def test_dual_matches_single_orientation_calls():
         assert torch.equal(qc, q2) and torch.equal(sc, s2)
 
 
-def test_special_blocks_dual():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_special_blocks_dual(dtype):
     blocks = workloads.special_blocks()          # [18][32]
     x32 = np.zeros((64, 64), np.float32)
     x32[:18, :32] = blocks                      # as row blocks
     x32[32:64, 32:50] = blocks.T                # as column blocks
     x32[40, :] = np.nan
     x32[:, 60] = -np.inf
-    x = make_input(x32, "f32")
+    x = make_input(x32, dtype)
+    x32 = f32_of_input(x)
     for fmt in FMTS:
         for rule in RULES:
             qr, sr, qc, sc, a = mxa.mx_quantize_dual(x, fmt, rule, amax=True)
