@@ -80,7 +80,7 @@ typedef enum { MX_ROWWISE = 0, MX_COLWISE_T = 1 } mx_orient_t;
 typedef enum { FP8_ROW = 0, FP8_TRANSPOSED = 1, FP8_DUAL = 2 } fp8_layout_t;
 
 /* Size of the delayed-scaling ring state of fp8_quantize_delayed, in FP32 words. */
-#define MX_RING_TICKET_WORDS 1024
+#define MX_RING_TICKET_WORDS 4096
 #define MX_RING_WORDS(hist_len) ((hist_len) + 4 + MX_RING_TICKET_WORDS)
 
 typedef enum {
@@ -145,7 +145,7 @@ mx_status_t mx_quantize_dual(const void* x, mx_dtype_t in, int64_t rows, int64_t
  * where s is the dequantization scale (x ~ q * s), m = 1/s is the multiplier the
  * cast uses, and the amax, ticket and counter words are scratch that must read 0
  * before the first call (initialise the buffer to hist = 0, s = m = 1, the rest
- * 0); every call leaves them 0 again.  The counter words hold 32 groups of
+ * 0); every call leaves them 0 again.  The counter words hold 128 groups of
  * (max, ticket) pairs, one group per 128-byte line, that spread the
  * per-workgroup ticket over several cache lines, because atomics on one line
  * serialize; the first hist_len + 4 words are the page's

@@ -45,7 +45,7 @@ LAYOUT = {"row": 0, "transposed": 1, "dual": 2}
 STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN", 4: "MX_ERR_UNSUPPORTED",
           5: "MX_ERR_LAUNCH", 6: "MX_ERR_ARG"}
 DEFAULT_FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
-RING_TICKET_WORDS = 1024        # MX_RING_TICKET_WORDS
+RING_TICKET_WORDS = 4096        # MX_RING_TICKET_WORDS
 
 
 def ring_words(hist_len: int) -> int:

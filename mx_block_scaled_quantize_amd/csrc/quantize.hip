@@ -211,7 +211,7 @@ struct RingArgs {
 // The fold is reached through a two-level ticket taken by every workgroup
 // (thread 0):
 //   1. as soon as the workgroup knows its max |x|, it posts it to the max word
-//      of its group (workgroup id modulo 32) -- an atomic max, sent only when
+//      of its group (workgroup id modulo 128) -- an atomic max, sent only when
 //      an atomic read shows that it can raise the word (the word only grows);
 //   2. after its stores, it increments its group's ticket, an increment that
 //      depends on the value step 1 returned, so it is issued only after that
@@ -225,7 +225,7 @@ struct RingArgs {
 // load) while different lines proceed in parallel, so every group sits on a
 // 128-byte line of its own, and splitting the chain keeps the round trips
 // behind the workgroup's stores instead of after them.
-constexpr unsigned kTicketGroups = 32;
+constexpr unsigned kTicketGroups = 128;
 constexpr unsigned kTicketStride = MX_RING_TICKET_WORDS / kTicketGroups;   // 32 words = 128 bytes
 static_assert(kTicketStride >= 2, "a group needs a max and a ticket word");
 
@@ -657,6 +657,97 @@ __global__ __launch_bounds__(64 * kStripWaves) void strip_kernel(StripArgs a) {
   }
 }
 
+__device__ __forceinline__ uint32_t u4_word(const uint4& u, int d) {
+  return d == 0 ? u.x : d == 1 ? u.y : d == 2 ? u.z : u.w;
+}
+
+// ---------------------------------------------------------------------------
+// Per-tensor FP8 cast of a BF16 tensor, transposed output only
+// ---------------------------------------------------------------------------
+// A workgroup of 4 waves takes a 128 x 128 tile, each wave a 64 x 64 quarter in
+// which lane (g, h) holds rows 8h .. 8h+7 of columns 8g .. 8g+7 (8 loads of 16
+// bytes, each load instruction reading 8 rows x 128 bytes).  A lane's 8 rows of
+// a column convert to 8 contiguous bytes of the transposed output; they are
+// staged in LDS so that the tile leaves as 16-byte pieces of whole 128-byte
+// lines (a 64-byte piece per column and wave would cost ~15% of the write
+// bandwidth).  The input never goes through LDS.  Every workgroup then takes
+// the two-level ring ticket; the last one folds the history.
+constexpr int kPtTile = 128, kPtWave = 64;
+
+template <int F>
+__global__ __launch_bounds__(256) void pt_col_bf16_kernel(StripArgs a, int tiles_c) {
+  __shared__ __attribute__((aligned(16))) uint8_t qc_lds[kPtTile * kPtTile];   // [tile column][tile row]
+  __shared__ uint32_t red[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane & 7, h = lane >> 3;
+  bool pt_slow;
+  const float mult = ring_multiplier(a.ring, pt_slow);
+  const RingTicket tk = ring_ticket(a.ring, blockIdx.x, gridDim.x);
+  const int t = blockIdx.x;
+  const int64_t tr = int64_t(t / tiles_c) * kPtTile, tc = int64_t(t % tiles_c) * kPtTile;
+  const int wro = (wave >> 1) * kPtWave, wco = (wave & 1) * kPtWave;       // wave offset in the tile
+  // rows are a multiple of 32 and cols of 8: a lane's 8 x 8 block is in or out
+  const bool ok = tr + wro + 8 * h < a.rows && tc + wco + 8 * g < a.cols;
+  uint32_t tmax = 0;
+  if (ok) {
+    // the wave's origin is uniform: a scalar base plus a 32-bit lane offset
+    // (the host keeps 64 * cols * 2 below 2^32)
+    const uint8_t* xb = static_cast<const uint8_t*>(a.x) + ((tr + wro) * a.cols + tc + wco) * 2;
+    const uint32_t cols = uint32_t(a.cols);
+    uint4 raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4_t v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(xb + (uint32_t(8 * h + i) * cols + uint32_t(8 * g)) * 2u));
+      raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      // max |x| of columns 2d (low half) and 2d+1 (high half) over the lane's 8 rows
+      uint32_t mp = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mp = pk_umax16(mp, u4_word(raw[i], d) & 0x7FFF7FFFu);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t cmax = k ? (mp & 0xFFFF0000u) : (mp << 16);
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t x = u4_word(raw[i], d);
+          v[i] = __uint_as_float(k ? (x & 0xFFFF0000u) : (x << 16));
+        }
+        if (cmax <= 0x7F800000u) {
+          tmax = umax(tmax, cmax);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) tmax = umax(tmax, abs_bits_no_nan(v[i]));
+        }
+        uint32_t w[2];
+        pt_encode_f32<F, 8>(v, mult, pt_slow ? 0x7FFFFFFFu : cmax, w);
+        *reinterpret_cast<u32x2_t*>(qc_lds + (wco + 8 * g + 2 * d + k) * kPtTile + wro + 8 * h) = u32x2_t{w[0], w[1]};
+      }
+    }
+  }
+  const uint32_t wm = wave_max(tmax);
+  if (lane == 0) red[wave] = wm;
+  __syncthreads();
+  // post the workgroup's max now; the dependent ticket is taken after the stores
+  uint32_t posted = 0;
+  if (threadIdx.x == 0) posted = ring_post_max(tk, umax(umax(red[0], red[1]), umax(red[2], red[3])));
+  // transposed codes: 8 consecutive threads per 128-byte line (column c, 128 rows)
+#pragma unroll
+  for (int it = 0; it < kPtTile * kPtTile / 16 / 256; ++it) {
+    const int item = threadIdx.x + 256 * it;
+    const int c = item >> 3, pc = item & 7;
+    if (tc + c < a.cols && tr + 16 * pc < a.rows) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qc_lds + c * kPtTile + 16 * pc);
+      *reinterpret_cast<uint4*>(a.q_col + (tc + c) * a.rows + tr + 16 * pc) = v;
+    }
+  }
+  if (threadIdx.x == 0) ring_finish(a.ring, tk, posted, gridDim.x);
+}
+
 template <typename K, typename... Args>
 static mx_status_t launch(K kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
   hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
@@ -775,7 +866,13 @@ template <int IN, int F, int R> struct PtOp {
       return MX_ERR_UNSUPPORTED;
     } else {
       if (layout == FP8_ROW) return pt_row_dispatch<IN, F>(a.x, a.rows * a.cols, a.q_row, a.ring, st);
-      if (layout == FP8_TRANSPOSED) return strip_dispatch<IN, F, R, PT_COL>(a, false, false, st);
+      if (layout == FP8_TRANSPOSED) {
+        const int64_t tiles_c = (a.cols + kPtTile - 1) / kPtTile;
+        const int64_t ntiles = tiles_c * ((a.rows + kPtTile - 1) / kPtTile);
+        if (IN == IN_BF16 && ntiles > 0 && ntiles < (int64_t(1) << 31) && a.cols < (int64_t(1) << 25))
+          return launch(pt_col_bf16_kernel<F>, dim3{unsigned(ntiles)}, dim3{256u}, st, a, int(tiles_c));
+        return strip_dispatch<IN, F, R, PT_COL>(a, false, false, st);
+      }
       return strip_dispatch<IN, F, R, PT_DUAL>(a, false, false, st);
     }
   }

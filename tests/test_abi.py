@@ -51,7 +51,7 @@ def test_header_compiles_as_c():
 
 
 def test_version_and_status_strings():
-    assert lib.mx_abi_version() == 100
+    assert lib.mx_abi_version() == 101
     for code in range(7):
         assert lib.mx_status_str(code).decode().startswith(mxa.STATUS[code])
 

@@ -266,20 +266,30 @@ def test_delayed_resume_from_saved_ring():
     assert torch.equal(saved, ring)
 
 
-def test_delayed_margin_and_nonfinite():
+@pytest.mark.parametrize("dtype,layout,shape", [("f32", "dual", (64, 64)), ("bf16", "transposed", (64, 64)),
+                                                ("bf16", "transposed", (160, 200))])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_delayed_margin_and_nonfinite(dtype, layout, shape, fmt):
+    fp8_max = 448.0 if fmt == "e4m3" else 57344.0
     ring = mxa.new_ring(4)
     oring = odl.Ring(4)
-    x32 = workloads.random_tensor((64, 64), 41, "normal") * 50
-    x32[5, 5] = np.inf
-    x32[6, 6] = np.nan
-    for t, margin in enumerate([2.0, 0.5, 1.0]):
-        y = x32 if t != 1 else np.zeros_like(x32)
-        x = upload_f32(y)
-        q, qT = mxa.fp8_quantize_delayed(x, ring, t, "e5m2", "dual", 57344.0, margin)
-        wq, wqT, _ = odl.quantize_delayed(y, "e5m2", oring, t, 57344.0, margin)
-        assert_bytes_equal(host(q), wq, "q")
-        assert_bytes_equal(host(qT), wqT, "qT")
-        assert_float_equal(host(ring), oring.as_array(mxa.RING_TICKET_WORDS), "ring")
+    x_nan = workloads.random_tensor(shape, 41, "normal") * 50
+    x_nan[6, 6] = np.nan                 # ignored by the amax: the fold goes ahead
+    x_inf = x_nan.copy()
+    x_inf[5, 5] = np.inf                 # an infinite amax: s and m are kept
+    x_inf[40, 7] = -np.inf
+    # margins 1e30 and 1e-30 make the multiplier huge (every code saturates) and tiny
+    steps = [(x_nan, 2.0), (np.zeros_like(x_nan), 0.5), (x_nan, 1e30), (x_nan, 1e-30), (x_inf, 1.0),
+             (x_nan, 1.0), (x_inf, 3.0), (x_nan, 1.0)]
+    for t, (y, margin) in enumerate(steps):
+        x = make_input(y, dtype)
+        ys = f32_of_input(x)
+        q, qT = mxa.fp8_quantize_delayed(x, ring, t % 4, fmt, layout, fp8_max, margin)
+        wq, wqT, _ = odl.quantize_delayed(ys, fmt, oring, t % 4, fp8_max, margin)
+        if q is not None:
+            assert_bytes_equal(host(q), wq, f"step {t} q")
+        assert_bytes_equal(host(qT), wqT, f"step {t} qT")
+        assert_float_equal(host(ring), oring.as_array(mxa.RING_TICKET_WORDS), f"step {t} ring")
 
 
 # ---------------------------------------------------------------- full-size workloads (sampled)
