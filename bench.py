@@ -214,6 +214,25 @@ def time_calls(fn, n, warm, stream, torch):
     return e0.elapsed_time(e1) / n / 1e3
 
 
+# Memory-bound legs rotate through enough buffer sets that one call's data is
+# long gone from the 256 MiB last-level cache when it comes round again.
+CACHE_DEFEAT_BYTES = 768 << 20
+
+
+def time_rotating(make_set, call, per_call_bytes, n, warm, stream, torch):
+    """time_calls over ceil(768 MiB / per_call_bytes) (2..16) buffer sets used in turn."""
+    k = max(2, min(16, -(-CACHE_DEFEAT_BYTES // per_call_bytes)))
+    sets = [make_set(i) for i in range(k)]
+    idx = [0]
+
+    def fn():
+        call(sets[idx[0] % k], idx[0])
+        idx[0] += 1
+    t = time_calls(fn, n, warm, stream, torch)
+    del sets
+    return t, k
+
+
 def bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=10):
     """MXFP8 E4M3 GEMM 8192 x 4096 . (14336 x 4096)^T, BF16 out (quantized operands resident)."""
     M, N, K = 8192, 14336, 4096
@@ -253,65 +272,86 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
     # per-tensor delayed scaling, BF16 8192 x 4096 -> transposed FP8, ring of 16
     R, C = 8192, 4096
     xs = [up_bf16(workloads.cfg3_step("act", t)) for t in range(2)]
-    qT = torch.empty((C, R), dtype=torch.uint8, device=dev)
     ring = mxa.new_ring(16, dev)
-    cnt = [0]
-
-    def delayed():
-        t = cnt[0]
-        cnt[0] += 1
-        lib.fp8_quantize_delayed(xs[t % 2].data_ptr(), 1, R, C, 0, 1, None, qT.data_ptr(), ring.data_ptr(), 16,
-                                 t % 16, 448.0, 1.0, None, sp)
-    t3 = time_calls(delayed, 32, 4, stream, torch)
     b3 = R * C * 2 + R * C + 80
+
+    def d_set(i):
+        return dict(x=xs[i % 2] if i < 2 else xs[i % 2].clone(), qT=torch.empty((C, R), dtype=torch.uint8, device=dev))
+
+    def delayed(st, t):
+        mxa.check(lib.fp8_quantize_delayed(st["x"].data_ptr(), 1, R, C, 0, 1, None, st["qT"].data_ptr(),
+                                           ring.data_ptr(), 16, t % 16, 448.0, 1.0, None, sp))
+    t3, k3 = time_rotating(d_set, delayed, b3, 32, 4, stream, torch)
     res["delayed_fp8_transposed_bf16_8192x4096"] = {"us": round(t3 * 1e6, 2), "GB/s": round(b3 / t3 / 1e9, 1),
-                                                    "hbm_frac": round(b3 / t3 / 1e9 / HBM_PEAK_GBS, 4)}
-    del xs, qT
+                                                    "hbm_frac": round(b3 / t3 / 1e9 / HBM_PEAK_GBS, 4),
+                                                    "buffer_sets": k3}
+    del xs
     # stochastic-rounding MXFP4 row-wise of a BF16 8192 x 4096 gradient, one uint32 word per element
     gx = up_bf16(workloads.cfg2(R, C))
     words = torch.from_numpy(workloads.random_words((R, C), 47).view(np.int32)).to(dev)
-    sq = torch.empty((R, C // 2), dtype=torch.uint8, device=dev)
-    ss = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
-    tsr = time_calls(lambda: mxa.check(lib.mx_quantize_sr(gx.data_ptr(), 1, R, C, 32, 2, 1, words.data_ptr(),
-                                                          sq.data_ptr(), ss.data_ptr(), None, sp)), 32, 4, stream, torch)
     bsr = R * C * 2 + R * C * 4 + R * C // 2 + R * C // 32
+
+    def sr_set(i):
+        return dict(x=gx if i == 0 else gx.clone(), w=words if i == 0 else words.clone(),
+                    q=torch.empty((R, C // 2), dtype=torch.uint8, device=dev),
+                    s=torch.empty((R, C // 32), dtype=torch.uint8, device=dev))
+    tsr, ksr = time_rotating(sr_set, lambda st, t: mxa.check(lib.mx_quantize_sr(
+        st["x"].data_ptr(), 1, R, C, 32, 2, 1, st["w"].data_ptr(), st["q"].data_ptr(), st["s"].data_ptr(), None, sp)),
+        bsr, 32, 4, stream, torch)
     res["sr_mxfp4_rowwise_bf16_8192x4096"] = {"us": round(tsr * 1e6, 2), "GB/s": round(bsr / tsr / 1e9, 1),
-                                              "hbm_frac": round(bsr / tsr / 1e9 / HBM_PEAK_GBS, 4)}
+                                              "hbm_frac": round(bsr / tsr / 1e9 / HBM_PEAK_GBS, 4),
+                                              "buffer_sets": ksr}
+    del words
     # MXFP6 E3M2 row-wise of the same gradient (codes packed 4 per 3 bytes)
-    fq = torch.empty((R, C * 3 // 4), dtype=torch.uint8, device=dev)
-    tf6 = time_calls(lambda: mxa.check(lib.mx_quantize(gx.data_ptr(), 1, R, C, 32, 4, 1, 0, 0, 0, fq.data_ptr(),
-                                                       ss.data_ptr(), None, sp)), 32, 4, stream, torch)
     bf6 = R * C * 2 + R * C * 3 // 4 + R * C // 32
+
+    def f6_set(i):
+        return dict(x=gx if i == 0 else gx.clone(), q=torch.empty((R, C * 3 // 4), dtype=torch.uint8, device=dev),
+                    s=torch.empty((R, C // 32), dtype=torch.uint8, device=dev),
+                    qc=torch.empty((C, R * 3 // 4), dtype=torch.uint8, device=dev),
+                    sc=torch.empty((C, R // 32), dtype=torch.uint8, device=dev))
+    tf6, kf6 = time_rotating(f6_set, lambda st, t: mxa.check(lib.mx_quantize(
+        st["x"].data_ptr(), 1, R, C, 32, 4, 1, 0, 0, 0, st["q"].data_ptr(), st["s"].data_ptr(), None, sp)),
+        bf6, 32, 4, stream, torch)
     res["mxfp6_e3m2_rowwise_bf16_8192x4096"] = {"us": round(tf6 * 1e6, 2), "GB/s": round(bf6 / tf6 / 1e9, 1),
-                                                "hbm_frac": round(bf6 / tf6 / 1e9 / HBM_PEAK_GBS, 4)}
+                                                "hbm_frac": round(bf6 / tf6 / 1e9 / HBM_PEAK_GBS, 4),
+                                                "buffer_sets": kf6}
     # MXFP6 E3M2 dual (row-wise + column-wise from one read)
-    fqc = torch.empty((C, R * 3 // 4), dtype=torch.uint8, device=dev)
-    fsc = torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
-    tf6d = time_calls(lambda: mxa.check(lib.mx_quantize_dual(gx.data_ptr(), 1, R, C, 32, 4, 1, fq.data_ptr(),
-                                                             ss.data_ptr(), fqc.data_ptr(), fsc.data_ptr(), None, sp)),
-                      32, 4, stream, torch)
     bf6d = R * C * 2 + 2 * (R * C * 3 // 4 + R * C // 32)
+    tf6d, kf6d = time_rotating(f6_set, lambda st, t: mxa.check(lib.mx_quantize_dual(
+        st["x"].data_ptr(), 1, R, C, 32, 4, 1, st["q"].data_ptr(), st["s"].data_ptr(), st["qc"].data_ptr(),
+        st["sc"].data_ptr(), None, sp)), bf6d, 32, 4, stream, torch)
     res["mxfp6_e3m2_dual_bf16_8192x4096"] = {"us": round(tf6d * 1e6, 2), "GB/s": round(bf6d / tf6d / 1e9, 1),
-                                             "hbm_frac": round(bf6d / tf6d / 1e9 / HBM_PEAK_GBS, 4)}
-    del gx, words, sq, ss, fq, fqc, fsc
+                                             "hbm_frac": round(bf6d / tf6d / 1e9 / HBM_PEAK_GBS, 4),
+                                             "buffer_sets": kf6d}
+    del gx
     # Hadamard + column-wise MXFP4 quantization of both operands, then the MXFP4 GEMM
     g_bits, x_bits, mask = workloads.cfg5()
     G, X = up_bf16(g_bits), up_bf16(x_bits)
-    gq = torch.empty((4096, 4096), dtype=torch.uint8, device=dev)
-    gs = torch.empty((4096, 256), dtype=torch.uint8, device=dev)
-    xq = torch.empty_like(gq)
-    xsc = torch.empty_like(gs)
-
-    def quant5():
-        lib.mx_quantize(G.data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, gq.data_ptr(), gs.data_ptr(), None, sp)
-        lib.mx_quantize(X.data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, xq.data_ptr(), xsc.data_ptr(), None, sp)
-    t5q = time_calls(quant5, 20, 3, stream, torch)
     b5 = 2 * (8192 * 4096 * 2 + 4096 * 4096 + 4096 * 256)
+
+    def h_set(i):
+        return dict(G=G if i == 0 else G.clone(), X=X if i == 0 else X.clone(),
+                    gq=torch.empty((4096, 4096), dtype=torch.uint8, device=dev),
+                    gs=torch.empty((4096, 256), dtype=torch.uint8, device=dev),
+                    xq=torch.empty((4096, 4096), dtype=torch.uint8, device=dev),
+                    xs=torch.empty((4096, 256), dtype=torch.uint8, device=dev))
+
+    def quant5(st, t):
+        mxa.check(lib.mx_quantize(st["G"].data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, st["gq"].data_ptr(),
+                                  st["gs"].data_ptr(), None, sp))
+        mxa.check(lib.mx_quantize(st["X"].data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, st["xq"].data_ptr(),
+                                  st["xs"].data_ptr(), None, sp))
+    t5q, k5 = time_rotating(h_set, quant5, b5, 20, 3, stream, torch)
     res["hadamard_mxfp4_colwise_quant_2x_bf16_8192x4096"] = {"us": round(t5q * 1e6, 2),
                                                               "GB/s": round(b5 / t5q / 1e9, 1),
-                                                              "hbm_frac": round(b5 / t5q / 1e9 / HBM_PEAK_GBS, 4)}
+                                                              "hbm_frac": round(b5 / t5q / 1e9 / HBM_PEAK_GBS, 4),
+                                                              "buffer_sets": k5}
+    st0 = h_set(0)
+    quant5(st0, 0)
+    gq, gs, xq, xsc = st0["gq"], st0["gs"], st0["xq"], st0["xs"]
     res["mxfp4_gemm_4096x4096x8192"] = time_gemm_fp4(lib, sp, stream, dev, gq, gs, xq, xsc, torch, 10)
-    del G, X, gq, gs, xq, xsc
+    del G, X, gq, gs, xq, xsc, st0
     res.update(bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
     res.update(bench_gemm_requant(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
     return res
