@@ -73,7 +73,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--mode", choices=["full", "dual", "gemm", "copy"], default="full")
+    ap.add_argument("--mode", choices=["full", "dual", "delayed", "gemm", "copy"], default="full")
+    ap.add_argument("--workload", choices=["dual", "delayed"], default="dual",
+                    help="which kernel --summarize describes")
     ap.add_argument("--summarize", metavar="OUT_MD")
     ap.add_argument("--summarize-gemm", metavar="OUT_DIR")
     ap.add_argument("--pmc-gemm")
@@ -118,6 +120,23 @@ def main():
         t = time_calls(lambda: dst.copy_(src), args.steps, args.warmup, stream, torch)
         print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "us": round(t * 1e6, 2),
                           "GB/s": round(2 * n / t / 1e9, 1)}), flush=True)
+        return
+    if args.mode == "delayed":
+        R, C = 8192, 4096
+        xs = [up_bf16(workloads.cfg3_step("act", t)) for t in range(2)]
+        ring = mxa.new_ring(16, dev)
+        b3 = R * C * 2 + R * C + 80
+
+        def d_set(i):
+            return dict(x=xs[i % 2] if i < 2 else xs[i % 2].clone(),
+                        qT=torch.empty((C, R), dtype=torch.uint8, device=dev))
+
+        def delayed(st, t):
+            mxa.check(lib.fp8_quantize_delayed(st["x"].data_ptr(), 1, R, C, 0, 1, None, st["qT"].data_ptr(),
+                                               ring.data_ptr(), 16, t % 16, 448.0, 1.0, None, sp))
+        t3, k3 = time_rotating(d_set, delayed, b3, args.steps, args.warmup, stream, torch)
+        print(json.dumps({"mode": "delayed", "us": round(t3 * 1e6, 2), "GB/s": round(b3 / t3 / 1e9, 1),
+                          "buffer_sets": k3}), flush=True)
         return
     if args.mode == "gemm":
         print(json.dumps({"mode": "gemm", "gemm": bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np,
@@ -510,9 +529,14 @@ def summarize(args):
     f_scale, w_scale = copy_bytes_kib / cf, copy_bytes_kib / cw
     fetch_b = kf * f_scale * 1024
     write_b = kw * w_scale * 1024
-    algo = 8192 * 4096 * 2 + 2 * 8192 * 4096 + 2 * (8192 * 4096 // 32) + 4
+    if args.workload == "dual":
+        algo = 8192 * 4096 * 2 + 2 * 8192 * 4096 + 2 * (8192 * 4096 // 32) + 4
+        title = "MXFP8 E4M3 dual quantization, BF16 8192x4096, round-up scale, amax"
+    else:
+        algo = 8192 * 4096 * 2 + 8192 * 4096 + 80
+        title = "per-tensor delayed-scaling FP8 E4M3 cast, BF16 8192x4096 -> transposed codes, ring of 16"
     lines = [
-        f"# {args.kernel} -- MXFP8 E4M3 dual quantization, BF16 8192x4096, round-up scale, amax",
+        f"# {args.kernel} -- {title}",
         "",
         f"command: {args.command}",
         "",
