@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0         # dense FP8 / MXFP8 MFMA
 FP4_PEAK_TFLOPS = 10100.0        # dense MXFP4 MFMA
+FP6_PEAK_TFLOPS = 10100.0        # dense MXFP6 MFMA
 METRIC = "MX quantize GB/s (% HBM peak); MXFP8 GEMM TFLOP/s (% FP8 MFMA peak)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "strip_kernel_dual_mxfp8_bf16_8192x4096.md")
 
@@ -373,7 +374,23 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
     del G, X, gq, gs, xq, xsc, st0
     res.update(bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
     res.update(bench_gemm_requant(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
+    res.update(bench_gemm_fp6(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
     return res
+
+
+def bench_gemm_fp6(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=5):
+    """The cfg4 GEMM shape with both operands quantized row-wise to MXFP6 E2M3
+    (round-up scale), BF16 out, on the 128 x 128-tile path."""
+    M, N, K = 8192, 14336, 4096
+    a_bits, w_bits = workloads.cfg4()
+    qa, sa = mxa.mx_quantize(up_bf16(a_bits), "e2m3", "ceil", "row")
+    qw, sw = mxa.mx_quantize(up_bf16(w_bits), "e2m3", "ceil", "row")
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    t = time_calls(lambda: mxa.check(lib.mx_gemm(qa.data_ptr(), sa.data_ptr(), 3, qw.data_ptr(), sw.data_ptr(), 3, M, N,
+                                                 K, 1.0, c.data_ptr(), 1, N, sp)), steps, 1, stream, torch)
+    f = 2.0 * M * N * K
+    return {"mxfp6_e2m3_gemm_8192x14336x4096": {"us": round(t * 1e6, 2), "TFLOP/s": round(f / t / 1e12, 1),
+                                                "mfma_frac": round(f / t / 1e12 / FP6_PEAK_TFLOPS, 4)}}
 
 
 def bench_gemm_requant(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=10):

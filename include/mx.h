@@ -215,12 +215,13 @@ mx_status_t mx_quantize_sr(const void* x, mx_dtype_t in, int64_t rows, int64_t c
  * codes and scales of both operands and accumulates in FP32):
  *   C[m][n] = alpha * sum_k (Qa[m][k] 2^(sa[m][k/32]-127)) (Qb[n][k] 2^(sb[n][k/32]-127))
  * with FP32 accumulation, then one rounding to `c_dtype` (BF16 or F32).
- *   a  [M][K] codes (E2M1: [M][K/2]), sa [M][K/32];
- *   b  [N][K] codes (E2M1: [N][K/2]), sb [N][K/32]  -- B^T, K-contiguous ("NT");
+ *   a  [M][K] codes (E2M1: [M][K/2]; E2M3 / E3M2: [M][3K/4] bit streams), sa [M][K/32];
+ *   b  [N][K] codes (likewise), sb [N][K/32]  -- B^T, K-contiguous ("NT");
  *   c  [M][ldc] output rows, ldc >= N; c needs only the alignment of its element
  *      type (it may be a column slice of a wider matrix).
- * fmt_a / fmt_b: both FP8 (E4M3 / E5M2, any mix) or both E2M1.
- * Shapes: K % 32 == 0 (K == 0 writes zeros); any M, N >= 0.
+ * fmt_a / fmt_b: both FP8 (E4M3 / E5M2, any mix), both FP6 (E2M3 / E3M2, any mix;
+ * packed as mx_quantize writes them) or both E2M1.
+ * Shapes: K % 32 == 0, and K % 64 == 0 for FP6 (K == 0 writes zeros); any M, N >= 0.
  * Accumulation: the matrix unit sums the FP8 products of each MFMA step with a
  * fixed-point alignment of limited width, not with IEEE FP32 rounding after
  * every product; the FP32 result is within a few 2^-12 of the largest product

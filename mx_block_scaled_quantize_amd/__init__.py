@@ -188,12 +188,21 @@ def mx_quantize_sr(x, rand, rule="ceil", amax=False):
     return (q, s) if a is None else (q, s, a)
 
 
+def _k_of(a, fmt):
+    """Elements per row of a [rows][code bytes] operand: E2M1 packs 2 per byte, FP6 4 per 3 bytes."""
+    if fmt == "e2m1":
+        return a.shape[1] * 2
+    if fmt in ("e2m3", "e3m2"):
+        return a.shape[1] * 4 // 3
+    return a.shape[1]
+
+
 def mx_gemm_requant(a, sa, b, sb, fmt_a="e4m3", fmt_b="e4m3", alpha=1.0, fmt_c="e4m3", rule_c="ceil", amax=False):
     """C32 = fl32(alpha * deq(A) deq(B)^T), re-quantized row-wise to MX in the GEMM
     epilogue.  Returns (q [M][N] (E2M1: [M][N/2]), scales [M][N/32]) or (q, scales, amax)."""
     M = a.shape[0]
     N = b.shape[0]
-    K = a.shape[1] * (2 if fmt_a == "e2m1" else 1)
+    K = _k_of(a, fmt_a)
     fc = _lookup(FMT, fmt_c, "format")
     q = torch.empty((M, N // 2 if fmt_c == "e2m1" else N), dtype=torch.uint8, device=a.device)
     s = torch.empty((M, N // 32), dtype=torch.uint8, device=a.device)
@@ -246,7 +255,7 @@ def mx_gemm(a, sa, b, sb, fmt_a="e4m3", fmt_b="e4m3", alpha=1.0, out_dtype=torch
     """C = alpha * deq(A) deq(B)^T with A [M][K], B [N][K] codes (K-contiguous)."""
     M = a.shape[0]
     N = b.shape[0]
-    K = a.shape[1] * (2 if fmt_a == "e2m1" else 1)
+    K = _k_of(a, fmt_a)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
     check(lib.mx_gemm(_ptr(a), _ptr(sa), _lookup(FMT, fmt_a, "format"), _ptr(b), _ptr(sb),

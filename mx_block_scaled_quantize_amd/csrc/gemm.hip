@@ -35,7 +35,14 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kBM = 128, kBN = 128, kBK = 128;
 constexpr int kGemmThreads = 256;
 
-template <int FA> struct OpBytes { static constexpr int kRow = FA == E2M1 ? kBK / 2 : kBK; };
+// Code bytes of k elements: FP4 two per byte, FP6 four per three bytes.
+template <int F> constexpr bool kIsFp6 = F == E2M3 || F == E3M2;
+template <int F>
+__host__ __device__ constexpr int64_t code_bytes(int64_t k) {
+  return F == E2M1 ? k / 2 : kIsFp6<F> ? k / 4 * 3 : k;
+}
+
+template <int FA> struct OpBytes { static constexpr int kRow = int(code_bytes<FA>(kBK)); };
 
 // Arguments of both GEMM kernels.  C[p] = alpha op(A[p]) op(B[p])^T where A is
 // [M][K] and B is [N][K] as the MFMA consumes them.  An operand is stored either
@@ -67,10 +74,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 
 // Operand-format field of the scaled MFMA: 0 FP8 E4M3, 1 FP8 E5M2, 2 FP6 E2M3,
 // 3 FP6 E3M2, 4 FP4 E2M1.
-template <int F> struct MfmaFmt { static constexpr int kCode = F == E4M3 ? 0 : F == E5M2 ? 1 : 4; };
+template <int F> struct MfmaFmt {
+  static constexpr int kCode = F == E4M3 ? 0 : F == E5M2 ? 1 : F == E2M3 ? 2 : F == E3M2 ? 3 : 4;
+};
 
 // One lane's operand for K-step kk (64 K-values) of a row staged in LDS; h = lane / 32.
 //   FP4: the lane holds the 32 codes of K-block 2*kk + h (16 contiguous bytes).
+//   FP6: likewise, the 24 bytes of K-block 2*kk + h (its codes as a little-endian
+//        bit stream, element i at bits 6i .. 6i+5) in dwords 0..5.
 //   FP8: the lane holds K = 16h .. 16h+15 of the step in bytes 0..15 and
 //        K = 32 + 16h .. 32 + 16h + 15 in bytes 16..31, i.e. half of each of the
 //        step's two K-blocks; the scale register of lane (row + 32 kb) still
@@ -80,6 +91,10 @@ __device__ __forceinline__ v8i load_operand(const uint8_t* row, int kk, int h) {
   if constexpr (F == E2M1) {
     const uint4 x = *reinterpret_cast<const uint4*>(row + kk * 32 + h * 16);
     return v8i{int(x.x), int(x.y), int(x.z), int(x.w), 0, 0, 0, 0};
+  } else if constexpr (kIsFp6<F>) {
+    const uint2* p = reinterpret_cast<const uint2*>(row + kk * 48 + h * 24);
+    const uint2 x = p[0], y = p[1], z = p[2];
+    return v8i{int(x.x), int(x.y), int(y.x), int(y.y), int(z.x), int(z.y), 0, 0};
   } else {
     const uint4 x = *reinterpret_cast<const uint4*>(row + kk * 64 + h * 16);
     const uint4 y = *reinterpret_cast<const uint4*>(row + kk * 64 + 32 + h * 16);
@@ -121,7 +136,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
   const uint8_t* __restrict__ B = g.b + int64_t(blockIdx.y) * g.batch_b;
   const uint8_t* __restrict__ SA = g.sa;
   const uint8_t* __restrict__ SB = g.sb;
-  const int64_t kbytesA = FA == E2M1 ? K / 2 : K, kbytesB = FB == E2M1 ? K / 2 : K;
+  const int64_t kbytesA = code_bytes<FA>(K), kbytesB = code_bytes<FB>(K);
   const int64_t kblocks = K / 32;
 
   v16f acc[2][2];
@@ -147,7 +162,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
       for (int i = tid; i < kBM * kChA; i += kGemmThreads) {
         const int r = i / kChA, ch = i % kChA;
         const int64_t gr = m0 + r;
-        const int64_t kb = (FA == E2M1 ? k0 / 2 : k0) + ch * 16;
+        const int64_t kb = code_bytes<FA>(k0) + ch * 16;
         uint4 d = make_uint4(0, 0, 0, 0);
         if (gr < M && kb < kbytesA) d = *reinterpret_cast<const uint4*>(A + gr * g.lda + kb);
         *reinterpret_cast<uint4*>(&sA[r * kPitchA + ch * 16]) = d;
@@ -163,7 +178,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
       for (int i = tid; i < kBN * kChB; i += kGemmThreads) {
         const int r = i / kChB, ch = i % kChB;
         const int64_t gr = n0 + r;
-        const int64_t kb = (FB == E2M1 ? k0 / 2 : k0) + ch * 16;
+        const int64_t kb = code_bytes<FB>(k0) + ch * 16;
         uint4 d = make_uint4(0, 0, 0, 0);
         if (gr < N && kb < kbytesB) d = *reinterpret_cast<const uint4*>(B + gr * g.ldb + kb);
         *reinterpret_cast<uint4*>(&sB[r * kPitchB + ch * 16]) = d;
@@ -967,20 +982,23 @@ static mx_status_t gemm_dispatch(const uint8_t* a, const uint8_t* sa, const uint
   g.M = M;
   g.N = N;
   g.K = K;
-  g.lda = FA == E2M1 ? K / 2 : K;
-  g.ldb = FB == E2M1 ? K / 2 : K;
+  g.lda = code_bytes<FA>(K);
+  g.ldb = code_bytes<FB>(K);
   g.ldc = ldc;
   g.alpha = alpha;
-  const int64_t tm256 = (M + t256::kTile - 1) / t256::kTile, tn256 = (N + t256::kTile - 1) / t256::kTile;
-  const bool big = N % (BF ? 8 : 4) == 0 && K % t256::kMxK == 0 && K > 0 && K <= (int64_t(1) << 22) &&
-                   tm256 * tn256 < (int64_t(1) << 31) && !misaligned(a) && !misaligned(b) && !misaligned(sa) &&
-                   !misaligned(sb) && !misaligned(c) && (ldc * esize) % 16 == 0;
-  if (big) {
-    g.tiles_m = int(tm256);
-    g.tiles_n = int(tn256);
-    hipLaunchKernelGGL((t256::gemm256_kernel<FA, FB, BF, false, false, false>), dim3(unsigned(g.tiles_m * g.tiles_n)),
-                       dim3(t256::kThreads), 0, st, g);
-    return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+  // FP6 operands run on the 128 x 128 path only (the 256 path stages 64-byte K-slices)
+  if constexpr (!kIsFp6<FA> && !kIsFp6<FB>) {
+    const int64_t tm256 = (M + t256::kTile - 1) / t256::kTile, tn256 = (N + t256::kTile - 1) / t256::kTile;
+    const bool big = N % (BF ? 8 : 4) == 0 && K % t256::kMxK == 0 && K > 0 && K <= (int64_t(1) << 22) &&
+                     tm256 * tn256 < (int64_t(1) << 31) && !misaligned(a) && !misaligned(b) && !misaligned(sa) &&
+                     !misaligned(sb) && !misaligned(c) && (ldc * esize) % 16 == 0;
+    if (big) {
+      g.tiles_m = int(tm256);
+      g.tiles_n = int(tn256);
+      hipLaunchKernelGGL((t256::gemm256_kernel<FA, FB, BF, false, false, false>),
+                         dim3(unsigned(g.tiles_m * g.tiles_n)), dim3(t256::kThreads), 0, st, g);
+      return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+    }
   }
   g.tiles_m = int((M + kBM - 1) / kBM);
   g.tiles_n = int((N + kBN - 1) / kBN);
@@ -1050,6 +1068,10 @@ static mx_status_t gemm_formats(int fa, int fb, const uint8_t* a, const uint8_t*
   if (fa == E5M2 && fb == E4M3) return gemm_dispatch<E5M2, E4M3, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
   if (fa == E5M2 && fb == E5M2) return gemm_dispatch<E5M2, E5M2, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
   if (fa == E2M1 && fb == E2M1) return gemm_dispatch<E2M1, E2M1, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
+  if (fa == E2M3 && fb == E2M3) return gemm_dispatch<E2M3, E2M3, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
+  if (fa == E2M3 && fb == E3M2) return gemm_dispatch<E2M3, E3M2, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
+  if (fa == E3M2 && fb == E2M3) return gemm_dispatch<E3M2, E2M3, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
+  if (fa == E3M2 && fb == E3M2) return gemm_dispatch<E3M2, E3M2, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
   return MX_ERR_UNSUPPORTED;
 }
 
@@ -1061,9 +1083,12 @@ extern "C" mx_status_t mx_gemm(const uint8_t* a, const uint8_t* sa, mx_elem_t fm
                                const uint8_t* sb, mx_elem_t fmt_b, int64_t M, int64_t N, int64_t K, float alpha,
                                void* c, mx_dtype_t c_dtype, int64_t ldc, hipStream_t stream) {
   const bool f8a = fmt_a == MX_E4M3 || fmt_a == MX_E5M2, f8b = fmt_b == MX_E4M3 || fmt_b == MX_E5M2;
-  if (!((f8a && f8b) || (fmt_a == MX_E2M1 && fmt_b == MX_E2M1))) return MX_ERR_UNSUPPORTED;
+  const bool f6a = fmt_a == MX_E2M3 || fmt_a == MX_E3M2, f6b = fmt_b == MX_E2M3 || fmt_b == MX_E3M2;
+  if (!((f8a && f8b) || (f6a && f6b) || (fmt_a == MX_E2M1 && fmt_b == MX_E2M1))) return MX_ERR_UNSUPPORTED;
   if (c_dtype != MX_BF16 && c_dtype != MX_F32) return MX_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return MX_ERR_SHAPE;
+  // FP6 rows of K codes are K * 3 / 4 bytes, read in 16-byte chunks
+  if (f6a && K % 64 != 0) return MX_ERR_SHAPE;
   if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return MX_ERR_SHAPE;
   if (ldc < N) return MX_ERR_SHAPE;
   if (M == 0 || N == 0) return MX_OK;

@@ -135,6 +135,8 @@ def test_mx_gemm_argument_errors():
     f = lib.mx_gemm
     # (a, sa, fa, b, sb, fb, M, N, K, alpha, c, c_dtype, ldc, stream)
     assert f(FAKE, FAKE, 0, FAKE, FAKE, 2, 64, 64, 64, 1.0, FAKE, 1, 64, None) == UNSUP   # FP8 x FP4
+    assert f(FAKE, FAKE, 3, FAKE, FAKE, 0, 64, 64, 64, 1.0, FAKE, 1, 64, None) == UNSUP   # FP6 x FP8
+    assert f(FAKE, FAKE, 3, FAKE, FAKE, 4, 64, 64, 96, 1.0, FAKE, 1, 64, None) == SHAPE   # FP6: K % 64
     assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 48, 1.0, FAKE, 1, 64, None) == SHAPE   # K % 32
     assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, FAKE, 1, 60, None) == SHAPE   # ldc < N
     assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, FAKE, 2, 64, None) == UNSUP   # F16 out

@@ -66,6 +66,44 @@ def test_gemm_small_parity(fa, fb, shape):
     assert og.rel_frobenius(bf16_to_f64(c16), bf16_to_f64(og.f64_to_bf16_bits(ref))) <= BF16_TOL
 
 
+@pytest.mark.parametrize("fa,fb", [("e2m3", "e2m3"), ("e3m2", "e2m3"), ("e2m3", "e3m2"), ("e3m2", "e3m2")])
+@pytest.mark.parametrize("shape", [(128, 128, 128), (200, 136, 192), (64, 300, 512), (1, 7, 64), (256, 384, 1024)])
+def test_gemm_fp6_parity(fa, fb, shape):
+    """MXFP6 operands (bit-stream packed as mx_quantize writes them) on the
+    128 x 128 path; a K of 192 ends on a half K-step."""
+    M, N, K = shape
+    qa, sa, qb, sb = quantized_operands(M, N, K, fa, fb, seed=M + N + K + 1)
+    args = (upload_u8(qa), upload_u8(sa), upload_u8(qb), upload_u8(sb), fa, fb, 0.75)
+    c32 = host(mxa.mx_gemm(*args, out_dtype=torch.float32))
+    ref = check_fp32(c32, qa, sa, fa, qb, sb, fb, alpha=0.75)
+    c16 = host(mxa.mx_gemm(*args, out_dtype=torch.bfloat16))
+    assert og.rel_frobenius(bf16_to_f64(c16), bf16_to_f64(og.f64_to_bf16_bits(ref))) <= BF16_TOL
+
+
+def test_gemm_fp6_integer_exact():
+    """Operands whose products and sums are exact in FP32 (small integers on the
+    E2M3 grid at scale 2^0) give the exact integer product."""
+    g = np.random.default_rng(71)
+    M, N, K = 64, 96, 256
+    A = g.integers(-7, 8, size=(M, K)).astype(np.float32) / 1.0
+    B = g.integers(-7, 8, size=(N, K)).astype(np.float32)
+    A[:, ::32] = 7.0                                  # every block's amax is 7 -> scale 2^0 under CEIL (max 7.5)
+    B[:, ::32] = -7.0
+    qa, sa = omx.quantize_rowwise(A, "e2m3", "ceil")
+    qb, sb = omx.quantize_rowwise(B, "e2m3", "ceil")
+    assert (sa == 127).all() and (sb == 127).all()
+    c = host(mxa.mx_gemm(upload_u8(qa), upload_u8(sa), upload_u8(qb), upload_u8(sb), "e2m3", "e2m3", 1.0,
+                         out_dtype=torch.float32))
+    assert np.array_equal(c, (A.astype(np.float64) @ B.astype(np.float64).T).astype(np.float32))
+
+
+def test_gemm_fp6_bad_k_raises():
+    q = torch.zeros((64, 72), dtype=torch.uint8, device="cuda")       # K = 96: not a multiple of 64
+    s = torch.zeros((64, 3), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        mxa.mx_gemm(q, s, q, s, "e2m3", "e2m3")
+
+
 # Shapes on the 256 x 256-tile LDS-DMA path (K a multiple of 512, N of 8):
 # one tile at the minimum K; 6 tiles (no XCD regrouping); 8 tiles (regrouped
 # across XCDs, one tile column); a wide tile row at K = 3 * 1024 (odd number of
