@@ -40,7 +40,7 @@ FP8_PEAK_TFLOPS = 5000.0         # dense FP8 / MXFP8 MFMA
 FP4_PEAK_TFLOPS = 10100.0        # dense MXFP4 MFMA
 FP6_PEAK_TFLOPS = 10100.0        # dense MXFP6 MFMA
 METRIC = "MX quantize GB/s (% HBM peak); MXFP8 GEMM TFLOP/s (% FP8 MFMA peak)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "strip_kernel_dual_mxfp8_bf16_8192x4096.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dual_bf16_kernel_mxfp8_bf16_8192x4096.md")
 
 
 def kernel_source_hash() -> str:
@@ -86,7 +86,7 @@ def main():
     ap.add_argument("--copy-fetch")
     ap.add_argument("--copy-write")
     ap.add_argument("--command", default="")
-    ap.add_argument("--kernel", default="strip_kernel<1, 0, 1, 0, false, true>")
+    ap.add_argument("--kernel", default="dual_bf16_kernel<0, 1, true>")
     args = ap.parse_args()
     if args.summarize_gemm:
         summarize_gemm(args)

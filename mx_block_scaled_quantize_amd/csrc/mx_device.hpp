@@ -188,6 +188,9 @@ __device__ __forceinline__ uint32_t abs_bits_no_nan(float v) {
 // DPP quad permutations: [1,0,3,2] and [2,3,0,1].
 constexpr int kQuadXor1 = 0xB1;
 constexpr int kQuadXor2 = 0x4E;
+// DPP rotations by 4 and 8 lanes within each 16-lane row (row_ror).
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
@@ -463,6 +466,12 @@ __device__ __forceinline__ void pt_encode_f32(const float (&v)[N], float m, uint
 // max over the two halves of a packed pair of 16-bit magnitudes
 __device__ __forceinline__ uint32_t pk_umax16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(v2u16_t, a),
+                                                                __builtin_bit_cast(v2u16_t, b)));
+}
+
+// min of the two halves of packed pairs of 16-bit magnitudes
+__device__ __forceinline__ uint32_t pk_umin16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(v2u16_t, a),
                                                                 __builtin_bit_cast(v2u16_t, b)));
 }
 

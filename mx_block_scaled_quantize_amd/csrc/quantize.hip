@@ -661,6 +661,221 @@ __device__ __forceinline__ uint32_t u4_word(const uint4& u, int d) {
   return d == 0 ? u.x : d == 1 ? u.y : d == 2 ? u.z : u.w;
 }
 
+// Max |x| of 8 BF16 values as an FP32 bit pattern (a NaN makes it > 0x7F800000).
+__device__ __forceinline__ uint32_t bf16_chunk_absmax(const uint4& c) {
+  const uint32_t k = 0x7FFF7FFFu;
+  const uint32_t m = pk_umax16(pk_umax16(c.x & k, c.y & k), pk_umax16(c.z & k, c.w & k));
+  return umax(m & 0xFFFFu, m >> 16) << 16;
+}
+
+// ---------------------------------------------------------------------------
+// Register-resident MX dual quantizer for BF16 input
+// ---------------------------------------------------------------------------
+// A workgroup of 4 waves takes a 128 x 128 tile, each wave a 64 x 64 quarter in
+// which a lane holds rows 8h .. 8h+7 of columns 8g .. 8g+7 (8 loads of 16
+// bytes, each load instruction reading 8 rows x 128 bytes; the input never goes
+// through LDS).  A row-wise block (32 columns) sits in a quad and a column-wise
+// block (32 rows) in 4 lanes of one 16-lane row, so both block maxima are DPP
+// steps.  Both code outputs are staged in LDS and leave as 16-byte pieces of
+// whole 128-byte lines; the scales are gathered in LDS and leave as one dword
+// per row and per column.  The converter handles the round-up rule on finite
+// blocks inline; every other block (non-finite, round-down rule, e = -127) goes
+// through an out-of-line general encoder, which keeps the register count of the
+// common path at 4 waves per SIMD.  (Waves that take the general encoder are
+// slow: it is kept for non-finite blocks and blocks with a subnormal amax.)
+constexpr int kDualTile = 128, kDualWave = 64;
+
+// General MX encoding of 8 BF16 values of one block (element order, pairs
+// low half first) whose max |x| bit pattern is bmax.  Out of line: rare.
+template <int F, int R>
+__device__ __attribute__((noinline)) uint2 dual_encode8_general(uint4 c, uint32_t bmax) {
+  float v[8];
+  const uint32_t w4[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = __uint_as_float(w4[j] << 16);
+    v[2 * j + 1] = __uint_as_float(w4[j] & 0xFFFF0000u);
+  }
+  uint32_t w[Words<F, 8>::kN];
+  mx_encode_f32<F, R, 8>(v, bmax, w);
+  if constexpr (Words<F, 8>::kN == 2) return make_uint2(w[0], w[1]);
+  else return make_uint2(w[0], 0u);
+}
+
+// Per-tensor amax of a BF16 chunk holding a NaN (which the amax ignores).  Out of line: rare.
+__device__ __attribute__((noinline)) uint32_t dual_amax_nan_chunk(uint4 c) {
+  const uint32_t w4[4] = {c.x, c.y, c.z, c.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m = umax(m, abs_bits_no_nan(__uint_as_float(w4[j] << 16)));
+    m = umax(m, abs_bits_no_nan(__uint_as_float(w4[j] & 0xFFFF0000u)));
+  }
+  return m;
+}
+
+// Codes of 8 BF16 values (4 pairs, element order) of a block with max bmax; sets the scale code.
+// Inline: finite blocks with e > -127 under either rule (the round-down rule
+// first clamps each magnitude to max_elem * 2^e, exact in BF16 since every
+// format maximum is a BF16 value, so the converter cannot overflow:
+// sat(RNE(v)) = RNE(clamp(v))), and all-zero blocks (+-0 codes, scale 0).  A
+// wave that leaves the inline path costs several microseconds of tail, so only
+// non-finite blocks and blocks with a subnormal amax take the general encoder.
+template <int F, int R>
+__device__ __forceinline__ uint2 dual_encode8(const uint32_t (&p)[4], uint32_t bmax, uint32_t& scale_code) {
+  constexpr int kB = Fmt_<F>::kBits;
+  const int e = shared_exponent<F, R>(bmax);
+  if (bmax < 0x7F800000u && e > -127) {
+    uint32_t q[4] = {p[0], p[1], p[2], p[3]};
+    if constexpr (R == FLOOR) {
+      const uint32_t lim = (Fmt_<F>::kMaxBits >> 16) + (uint32_t(e) << 7);     // BF16 bits of max * 2^e
+      const uint32_t limp = (lim & 0xFFFFu) * 0x10001u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = (p[i] & 0x80008000u) | pk_umin16(p[i] & 0x7FFF7FFFu, limp);
+    }
+    uint32_t w[Words<F, 8>::kN];
+    cvt_values_bf16<F, 8>(q, __uint_as_float(uint32_t(127 + e) << 23), w);
+    scale_code = uint32_t(e + 127);
+    if constexpr (Words<F, 8>::kN == 2) return make_uint2(w[0], w[1]);
+    else return make_uint2(w[0], 0u);
+  }
+  if (bmax == 0u) {
+    // +-0 codes: each element's sign bit in the top bit of its code
+    scale_code = 0;
+    if constexpr (kB == 8) {
+      uint32_t b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b[i] = ((p[i] >> 8) & 0x80u) | ((p[i] >> 16) & 0x8000u);
+      return make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+    } else {
+      uint32_t x = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x |= (((p[i] >> 12) & 0x8u) | ((p[i] >> 24) & 0x80u)) << (8 * i);
+      return make_uint2(x, 0u);
+    }
+  }
+  scale_code = bmax >= 0x7F800000u ? 0xFFu : uint32_t(e + 127);
+  return dual_encode8_general<F, R>(make_uint4(p[0], p[1], p[2], p[3]), bmax);
+}
+
+template <int F, int R, bool AMAX>
+__global__ __launch_bounds__(256) void dual_bf16_kernel(StripArgs a, int tiles_c) {
+  constexpr int kB = Fmt_<F>::kBits;
+  constexpr int kLine = kDualTile * kB / 8;                          // code bytes per tile row / column
+  __shared__ __attribute__((aligned(16))) uint8_t qr_lds[kDualTile * kLine];   // [tile row][tile column]
+  __shared__ __attribute__((aligned(16))) uint8_t qc_lds[kDualTile * kLine];   // [tile column][tile row]
+  __shared__ uint32_t srow_lds[kDualTile], scol_lds[kDualTile];                 // 4 scale codes per row / column
+  __shared__ uint32_t red[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // lane bits 0-1 and 4 give g, bits 2-3 and 5 give h
+  const int g = (lane & 3) | ((lane >> 2) & 4), h = ((lane >> 2) & 3) | ((lane >> 3) & 4), lane_q = lane & 3;
+  const int t = blockIdx.x;
+  const int64_t tr = int64_t(t / tiles_c) * kDualTile, tc = int64_t(t % tiles_c) * kDualTile;
+  const int wro = (wave >> 1) * kDualWave, wco = (wave & 1) * kDualWave;
+  uint8_t* const srl = reinterpret_cast<uint8_t*>(srow_lds) + wro * 4 + (wave & 1) * 2;
+  uint8_t* const scl = reinterpret_cast<uint8_t*>(scol_lds) + wco * 4 + (wave >> 1) * 2;
+  // rows and cols are multiples of 32: a quad (row blocks) and the lanes
+  // h = 4k .. 4k+3 (column blocks) are entirely in or out of range
+  const bool ok = tr + wro + 8 * h < a.rows && tc + wco + 8 * g < a.cols;
+  uint32_t tmax = 0;
+  if (ok) {
+    // the wave's origin is uniform: a scalar base plus a 32-bit lane offset
+    // (the host keeps 64 * cols * 2 below 2^32)
+    const uint8_t* xb = static_cast<const uint8_t*>(a.x) + ((tr + wro) * a.cols + tc + wco) * 2;
+    const uint32_t cols = uint32_t(a.cols);
+    uint4 raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4_t v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(xb + (uint32_t(8 * h + i) * cols + uint32_t(8 * g)) * 2u));
+      raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    // ---- row-wise half
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t m = bf16_chunk_absmax(raw[i]);
+      if constexpr (AMAX) tmax = umax(tmax, m <= 0x7F800000u ? m : dual_amax_nan_chunk(raw[i]));
+      const uint32_t p[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+      uint32_t sc;
+      const uint2 w = dual_encode8<F, R>(p, quad_max(m), sc);
+      if (lane_q == 0) srl[(8 * h + i) * 4 + (g >> 2)] = uint8_t(sc);
+      uint8_t* const d = qr_lds + (wro + 8 * h + i) * kLine + (wco + 8 * g) * kB / 8;
+      if constexpr (kB == 8) *reinterpret_cast<u32x2_t*>(d) = u32x2_t{w.x, w.y};
+      else *reinterpret_cast<uint32_t*>(d) = w.x;
+    }
+    // ---- column-wise half: dword d holds columns 2d (low halves) and 2d+1
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t mp = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mp = pk_umax16(mp, u4_word(raw[i], d) & 0x7FFF7FFFu);
+      mp = pk_umax16(mp, dpp_u32<kRowRor4>(mp));
+      mp = pk_umax16(mp, dpp_u32<kRowRor8>(mp));
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t sel = k ? 0x07060302u : 0x05040100u;
+        uint32_t p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_perm(u4_word(raw[2 * i + 1], d), u4_word(raw[2 * i], d), sel);
+        uint32_t sc;
+        const uint2 w = dual_encode8<F, R>(p, k ? (mp & 0xFFFF0000u) : (mp << 16), sc);
+        const int c = 8 * g + 2 * d + k;                     // column within the wave quarter
+        uint8_t* const dst = qc_lds + (wco + c) * kLine + (wro + 8 * h) * kB / 8;
+        if constexpr (kB == 8) *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{w.x, w.y};
+        else *reinterpret_cast<uint32_t*>(dst) = w.x;
+        if ((h & 3) == 0) scl[c * 4 + (h >> 2)] = uint8_t(sc);
+      }
+    }
+  }
+  if constexpr (AMAX) {
+    const uint32_t wm = wave_max(tmax);
+    if (lane == 0) red[wave] = wm;
+  }
+  __syncthreads();
+  // ---- codes: 16-byte pieces, kLine / 16 consecutive threads per line; a piece
+  // (16 FP8 or 32 FP4 codes) is entirely in or out of range
+#pragma unroll
+  for (int it = 0; it < kDualTile * kLine / 16 / 256; ++it) {
+    const int item = threadIdx.x + 256 * it;
+    const int r = item / (kLine / 16), pc = item % (kLine / 16);
+    const int64_t e = pc * 16 * 8 / kB;                              // first element of the piece
+    if (tr + r < a.rows && tc + e < a.cols) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qr_lds + r * kLine + pc * 16);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(a.q_row + ((tr + r) * a.cols + tc) * kB / 8 + pc * 16));
+    }
+    if (tc + r < a.cols && tr + e < a.rows) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qc_lds + r * kLine + pc * 16);
+      *reinterpret_cast<uint4*>(a.q_col + ((tc + r) * a.rows + tr) * kB / 8 + pc * 16) = v;
+    }
+  }
+  // ---- scales: thread j < 128 writes tile row j's 4 row scales, thread 128 + j
+  // tile column j's 4 column scales (fewer, byte by byte, on a ragged edge)
+  {
+    const int j = threadIdx.x & (kDualTile - 1);
+    const bool col_side = threadIdx.x >= kDualTile;
+    const int64_t line = col_side ? tc + j : tr + j;
+    const int64_t lines = col_side ? a.cols : a.rows;
+    const int64_t other0 = col_side ? tr : tc, other = col_side ? a.rows : a.cols;
+    if (line < lines) {
+      const uint32_t v = col_side ? scol_lds[j] : srow_lds[j];
+      uint8_t* dst = (col_side ? a.s_col : a.s_row) + line * (other >> 5) + (other0 >> 5);
+      const int64_t nb = (other - other0) >> 5;
+      if (nb >= 4 && (reinterpret_cast<uintptr_t>(dst) & 3u) == 0) {
+        *reinterpret_cast<uint32_t*>(dst) = v;
+      } else {
+        for (int b = 0; b < 4 && b < nb; ++b) dst[b] = uint8_t(v >> (8 * b));
+      }
+    }
+  }
+  if constexpr (AMAX) {
+    if (threadIdx.x == 0) {
+      const uint32_t mm = umax(umax(red[0], red[1]), umax(red[2], red[3]));
+      if (mm) atomic_max_u32(a.amax_out, mm);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Per-tensor FP8 cast of a BF16 tensor, transposed output only
 // ---------------------------------------------------------------------------
@@ -857,6 +1072,15 @@ template <int IN, int F, int R> struct ColOp {
 };
 template <int IN, int F, int R> struct DualOp {
   static mx_status_t run(StripArgs& a, bool amax, hipStream_t st) {
+    if constexpr (IN == IN_BF16) {
+      const int64_t tiles_c = (a.cols + kDualTile - 1) / kDualTile;
+      const int64_t ntiles = tiles_c * ((a.rows + kDualTile - 1) / kDualTile);
+      if (ntiles > 0 && ntiles < (int64_t(1) << 31) && a.cols < (int64_t(1) << 25)) {
+        const dim3 grid{unsigned(ntiles)}, block{256u};
+        return amax ? launch(dual_bf16_kernel<F, R, true>, grid, block, st, a, int(tiles_c))
+                    : launch(dual_bf16_kernel<F, R, false>, grid, block, st, a, int(tiles_c));
+      }
+    }
     return strip_dispatch<IN, F, R, MX_DUAL>(a, false, amax, st);
   }
 };
