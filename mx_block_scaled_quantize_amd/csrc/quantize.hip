@@ -877,6 +877,184 @@ __global__ __launch_bounds__(256) void dual_bf16_kernel(StripArgs a, int tiles_c
 }
 
 // ---------------------------------------------------------------------------
+// Register-resident MX column-wise quantizer for BF16 input (optionally with the
+// fixed-sign 32-point Hadamard transform along each column block)
+// ---------------------------------------------------------------------------
+// A workgroup takes 32 * W rows x 128 columns, wave w the 32-row strip w (W = 4
+// for FP8, 8 for FP4, so that a tile column is one 128-byte line of codes).  A
+// lane holds rows 8q .. 8q+7 (q = lane & 3) of columns 8g .. 8g+7 (g = lane / 4):
+// 8 loads of 16 bytes, each load instruction reading 4 rows x 256 bytes.  A
+// column block (32 rows) is a quad, so its maximum is two DPP steps and the
+// Hadamard transform is the quad butterfly (spans 1, 2, 4 in the lane, 8 and 16
+// across it).  The transposed codes are staged in LDS and leave as 16-byte
+// pieces of whole column lines; the W scales of a column leave as one store.
+
+// General MX encoding of 8 FP32 values of one block (non-finite or subnormal
+// amax).  Out of line: rare.
+template <int F, int R>
+__device__ __attribute__((noinline)) uint2 col_encode8_general(float4 lo, float4 hi, uint32_t bmax) {
+  const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  uint32_t w[Words<F, 8>::kN];
+  mx_encode_f32<F, R, 8>(v, bmax, w);
+  if constexpr (Words<F, 8>::kN == 2) return make_uint2(w[0], w[1]);
+  else return make_uint2(w[0], 0u);
+}
+
+// Codes of 8 FP32 values of a block with max |.| bit pattern bmax; sets the scale code.
+template <int F, int R>
+__device__ __forceinline__ uint2 col_encode8_f32(const float (&v)[8], uint32_t bmax, uint32_t& scale_code) {
+  const int e = shared_exponent<F, R>(bmax);
+  if (bmax < 0x7F800000u && e > -127) {
+    uint32_t w[Words<F, 8>::kN];
+    mx_encode_given<F, R, 8>(v, false, e, w);
+    scale_code = uint32_t(e + 127);
+    if constexpr (Words<F, 8>::kN == 2) return make_uint2(w[0], w[1]);
+    else return make_uint2(w[0], 0u);
+  }
+  if (bmax == 0u) {
+    // +-0 codes: each element's sign bit in the top bit of its code
+    scale_code = 0;
+    uint32_t c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = (__float_as_uint(v[j]) >> 31) << (Fmt_<F>::kBits - 1);
+    uint32_t w[Words<F, 8>::kN];
+    pack_codes<F, 8>(c, w);
+    if constexpr (Words<F, 8>::kN == 2) return make_uint2(w[0], w[1]);
+    else return make_uint2(w[0], 0u);
+  }
+  scale_code = bmax >= 0x7F800000u ? 0xFFu : uint32_t(e + 127);
+  return col_encode8_general<F, R>(make_float4(v[0], v[1], v[2], v[3]), make_float4(v[4], v[5], v[6], v[7]), bmax);
+}
+
+template <int F> struct ColTile { static constexpr int kWaves = Fmt_<F>::kBits == 4 ? 8 : 4; };
+
+template <int F, int R, bool HAD, bool AMAX>
+__global__ __launch_bounds__(64 * ColTile<F>::kWaves) void col_bf16_kernel(StripArgs a, int tiles_c) {
+  constexpr int kB = Fmt_<F>::kBits;
+  constexpr int kW = ColTile<F>::kWaves;
+  constexpr int kRows = 32 * kW;                                     // tile rows
+  constexpr int kLine = kRows * kB / 8;                              // code bytes per tile column: 128
+  constexpr int kThreads = 64 * kW;
+  __shared__ __attribute__((aligned(16))) uint8_t qc_lds[kDualTile * kLine];   // [tile column][tile row]
+  __shared__ __attribute__((aligned(8))) uint8_t scol_lds[kDualTile * kW];      // W scale codes per column
+  __shared__ uint32_t red[kW];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane & 3, g = lane >> 2;
+  const int t = blockIdx.x;
+  const int64_t tr = int64_t(t / tiles_c) * kRows, tc = int64_t(t % tiles_c) * kDualTile;
+  const int wro = wave * 32;
+  uint8_t* const scl = scol_lds + wave;
+  // rows are a multiple of 32 and cols of 8: a quad (a column block) and a
+  // lane's 8 columns are entirely in or out of range
+  const bool ok = tr + wro < a.rows && tc + 8 * g < a.cols;
+  uint32_t tmax = 0;
+  if (ok) {
+    // the wave's origin is uniform: a scalar base plus a 32-bit lane offset
+    // (the host keeps 32 * cols * 2 below 2^32)
+    const uint8_t* xb = static_cast<const uint8_t*>(a.x) + ((tr + wro) * a.cols + tc) * 2;
+    const uint32_t cols = uint32_t(a.cols);
+    uint4 raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4_t v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(xb + (uint32_t(8 * q + i) * cols + uint32_t(8 * g)) * 2u));
+      raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    // dword d holds columns 2d (low halves) and 2d+1
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t mp = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mp = pk_umax16(mp, u4_word(raw[i], d) & 0x7FFF7FFFu);
+      if constexpr (AMAX) {
+        const uint32_t m2 = umax(mp << 16, mp & 0xFFFF0000u);
+        if (m2 <= 0x7F800000u) {
+          tmax = umax(tmax, m2);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; i += 4)
+            tmax = umax(tmax, dual_amax_nan_chunk(make_uint4(u4_word(raw[i], d), u4_word(raw[i + 1], d),
+                                                             u4_word(raw[i + 2], d), u4_word(raw[i + 3], d))));
+        }
+      }
+      if constexpr (!HAD) {
+        mp = pk_umax16(mp, dpp_u32<kQuadXor1>(mp));
+        mp = pk_umax16(mp, dpp_u32<kQuadXor2>(mp));
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        uint32_t sc;
+        uint2 w;
+        if constexpr (HAD) {
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t x = u4_word(raw[i], d);
+            v[i] = __uint_as_float(k ? (x & 0xFFFF0000u) : (x << 16));
+          }
+          hadamard32_quad(v, a.had_mask, q);
+          uint32_t m = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) m = umax(m, abs_bits(v[i]));
+          w = col_encode8_f32<F, R>(v, quad_max(m), sc);
+        } else {
+          const uint32_t sel = k ? 0x07060302u : 0x05040100u;
+          uint32_t p[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_perm(u4_word(raw[2 * i + 1], d), u4_word(raw[2 * i], d), sel);
+          w = dual_encode8<F, R>(p, k ? (mp & 0xFFFF0000u) : (mp << 16), sc);
+        }
+        const int c = 8 * g + 2 * d + k;                     // column within the tile
+        uint8_t* const dst = qc_lds + c * kLine + (wro + 8 * q) * kB / 8;
+        if constexpr (kB == 8) *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{w.x, w.y};
+        else *reinterpret_cast<uint32_t*>(dst) = w.x;
+        if (q == 0) scl[c * kW] = uint8_t(sc);
+      }
+    }
+  }
+  if constexpr (AMAX) {
+    const uint32_t wm = wave_max(tmax);
+    if (lane == 0) red[wave] = wm;
+  }
+  __syncthreads();
+  // ---- transposed codes: 16-byte pieces (16 FP8 or 32 FP4 codes of one column),
+  // each entirely in or out of range
+#pragma unroll
+  for (int it = 0; it < kDualTile * kLine / 16 / kThreads; ++it) {
+    const int item = threadIdx.x + kThreads * it;
+    const int c = item / (kLine / 16), pc = item % (kLine / 16);
+    if (tc + c < a.cols && tr + pc * 16 * 8 / kB < a.rows) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qc_lds + c * kLine + pc * 16);
+      *reinterpret_cast<uint4*>(a.q_col + ((tc + c) * a.rows + tr) * kB / 8 + pc * 16) = v;
+    }
+  }
+  // ---- column scales: thread j < 128 writes tile column j's W scales (fewer,
+  // byte by byte, on a ragged bottom edge)
+  if (threadIdx.x < kDualTile) {
+    const int j = threadIdx.x;
+    if (tc + j < a.cols) {
+      uint8_t* dst = a.s_col + (tc + j) * (a.rows >> 5) + (tr >> 5);
+      const int64_t nb = (a.rows - tr) >> 5;
+      if (nb >= kW && (reinterpret_cast<uintptr_t>(dst) & (kW - 1)) == 0) {
+        if constexpr (kW == 8) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(scol_lds + j * kW);
+        else *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(scol_lds + j * kW);
+      } else {
+        for (int b = 0; b < kW && b < nb; ++b) dst[b] = scol_lds[j * kW + b];
+      }
+    }
+  }
+  if constexpr (AMAX) {
+    if (threadIdx.x == 0) {
+      uint32_t mm = red[0];
+#pragma unroll
+      for (int w = 1; w < kW; ++w) mm = umax(mm, red[w]);
+      if (mm) atomic_max_u32(a.amax_out, mm);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Per-tensor FP8 cast of a BF16 tensor, transposed output only
 // ---------------------------------------------------------------------------
 // A workgroup of 4 waves takes a 128 x 128 tile, each wave a 64 x 64 quarter in
@@ -1067,6 +1245,19 @@ template <int IN, int F, int R> struct RowOp {
 };
 template <int IN, int F, int R> struct ColOp {
   static mx_status_t run(StripArgs& a, bool had, bool amax, hipStream_t st) {
+    if constexpr (IN == IN_BF16) {
+      constexpr int kRows = 32 * ColTile<F>::kWaves;
+      const int64_t tiles_c = (a.cols + kDualTile - 1) / kDualTile;
+      const int64_t ntiles = tiles_c * ((a.rows + kRows - 1) / kRows);
+      if (ntiles > 0 && ntiles < (int64_t(1) << 31) && a.cols < (int64_t(1) << 25)) {
+        const dim3 grid{unsigned(ntiles)}, block{unsigned(64 * ColTile<F>::kWaves)};
+        if (had)
+          return amax ? launch(col_bf16_kernel<F, R, true, true>, grid, block, st, a, int(tiles_c))
+                      : launch(col_bf16_kernel<F, R, true, false>, grid, block, st, a, int(tiles_c));
+        return amax ? launch(col_bf16_kernel<F, R, false, true>, grid, block, st, a, int(tiles_c))
+                    : launch(col_bf16_kernel<F, R, false, false>, grid, block, st, a, int(tiles_c));
+      }
+    }
     return strip_dispatch<IN, F, R, MX_COL>(a, had, amax, st);
   }
 };

@@ -165,6 +165,36 @@ def test_special_blocks_dual(dtype):
             assert host(a)[0] == omx.tensor_amax(x32)
 
 
+@pytest.mark.parametrize("had", [False, True])
+def test_special_blocks_colwise_bf16(had):
+    """Column-wise BF16 quantization of zero, subnormal, extreme and non-finite
+    column blocks, with and without the Hadamard transform."""
+    blocks = workloads.special_blocks()          # [18][32]
+    x32 = np.zeros((96, 64), np.float32)
+    x32[32:64, 8:26] = blocks.T                 # as column blocks
+    x32[70, :] = np.nan
+    x32[:, 60] = -np.inf
+    x = make_input(x32, "bf16")
+    xs = f32_of_input(x)
+    mask = 0x2468_ACE1 if had else None
+    for fmt in FMTS:
+        for rule in RULES:
+            q, s, a = mxa.mx_quantize(x, fmt, rule, "col", hadamard_mask=mask, amax=True)
+            wq, ws = omx.quantize_colwise_t(xs, fmt, rule, hadamard_mask=mask)
+            assert_bytes_equal(host(s), ws, f"{fmt} {rule} scales")
+            gq = host(q)
+            if had:
+                # the butterflies turn a block holding NaN into NaNs whose sign
+                # IEEE 754 leaves open: non-finite blocks compare without sign bits
+                sign = np.uint8(0x88 if fmt == "e2m1" else 0x80)
+                per_scale = gq.shape[1] // ws.shape[1]
+                nonfinite = np.repeat(ws == 0xFF, per_scale, axis=1)
+                gq = np.where(nonfinite, gq & ~sign, gq)
+                wq = np.where(nonfinite, wq & ~sign, wq)
+            assert_bytes_equal(gq, wq, f"{fmt} {rule} codes")
+            assert host(a)[0] == omx.tensor_amax(xs)
+
+
 def test_empty_inputs():
     x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
     q, s, a = mxa.mx_quantize(x, "e4m3", "ceil", "row", amax=True)
