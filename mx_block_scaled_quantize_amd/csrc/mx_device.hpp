@@ -253,8 +253,9 @@ __device__ __forceinline__ void hadamard32_inlane(float (&v)[32], uint32_t mask)
 // q with lane q^1 and q^2, where the lower lane keeps a + b and the upper lane
 // computes a - b with a = the lower lane's value (the same FP32 operations).
 __device__ __forceinline__ void hadamard32_quad(float (&v)[8], uint32_t mask, int q) {
+  const uint32_t lm = mask >> (8 * q);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = ((mask >> (8 * q + j)) & 1u) ? -v[j] : v[j];
+  for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((lm >> j) & 1u) << 31));
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -266,20 +267,21 @@ __device__ __forceinline__ void hadamard32_quad(float (&v)[8], uint32_t mask, in
       }
     }
   }
+  // the upper lane adds its own value negated: p + (-v) is p - v exactly
   {
-    const bool upper = (q & 1) != 0;
+    const uint32_t neg = (q & 1) ? 0x80000000u : 0u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float p = dpp_f32<kQuadXor1>(v[i]);
-      v[i] = upper ? (p - v[i]) : (v[i] + p);
+      v[i] = p + __uint_as_float(__float_as_uint(v[i]) ^ neg);
     }
   }
   {
-    const bool upper = (q & 2) != 0;
+    const uint32_t neg = (q & 2) ? 0x80000000u : 0u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float p = dpp_f32<kQuadXor2>(v[i]);
-      v[i] = upper ? (p - v[i]) : (v[i] + p);
+      v[i] = p + __uint_as_float(__float_as_uint(v[i]) ^ neg);
     }
   }
 }
