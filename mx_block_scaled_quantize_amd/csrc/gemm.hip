@@ -147,11 +147,51 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+  // K-contiguous operands (the MX GEMM and per-tensor NT): the next K-step's
+  // codes and scales are loaded into registers while the current step's MFMAs
+  // run, then written to LDS between the two barriers
+  constexpr int kChA = kRowA / 16, kChB = kRowB / 16;
+  constexpr int kNA = (kBM * kChA + kGemmThreads - 1) / kGemmThreads;
+  constexpr int kNB = (kBN * kChB + kGemmThreads - 1) / kGemmThreads;
+  constexpr int kNS = (kBM * 4 + kGemmThreads - 1) / kGemmThreads;
+  uint4 ra[kNA], rb[kNB];
+  uint8_t rsa[kNS], rsb[kNS];
+  auto fetch = [&](int64_t k0) {
+    if constexpr (!TA) {
+#pragma unroll
+      for (int u = 0; u < kNA; ++u) {
+        const int i = tid + u * kGemmThreads, r = i / kChA, ch = i % kChA;
+        const int64_t gr = m0 + r, kb = code_bytes<FA>(k0) + ch * 16;
+        ra[u] = make_uint4(0, 0, 0, 0);
+        if (i < kBM * kChA && gr < M && kb < kbytesA) ra[u] = *reinterpret_cast<const uint4*>(A + gr * g.lda + kb);
+      }
+    }
+    if constexpr (!TB) {
+#pragma unroll
+      for (int u = 0; u < kNB; ++u) {
+        const int i = tid + u * kGemmThreads, r = i / kChB, ch = i % kChB;
+        const int64_t gr = n0 + r, kb = code_bytes<FB>(k0) + ch * 16;
+        rb[u] = make_uint4(0, 0, 0, 0);
+        if (i < kBN * kChB && gr < N && kb < kbytesB) rb[u] = *reinterpret_cast<const uint4*>(B + gr * g.ldb + kb);
+      }
+    }
+    if constexpr (!PT) {
+#pragma unroll
+      for (int u = 0; u < kNS; ++u) {
+        const int i = tid + u * kGemmThreads, r = i >> 2, kb = i & 3;
+        const int64_t gk = k0 / 32 + kb;
+        rsa[u] = (m0 + r < M && gk < kblocks) ? SA[(m0 + r) * kblocks + gk] : uint8_t(127);
+        rsb[u] = (n0 + r < N && gk < kblocks) ? SB[(n0 + r) * kblocks + gk] : uint8_t(127);
+      }
+    }
+  };
+  if (K > 0) fetch(0);
+
   for (int64_t k0 = 0; k0 < K; k0 += kBK) {
-    // ---- stage codes: 16-byte chunks, zero past the matrix (K-contiguous rows are
-    // whole 16-byte chunks: K is a multiple of 16); an M- / N-contiguous operand is
-    // gathered byte by byte, consecutive lanes on consecutive rows of the tile
-    constexpr int kChA = kRowA / 16, kChB = kRowB / 16;
+    // ---- stage codes: the prefetched 16-byte chunks (zero past the matrix:
+    // K-contiguous rows are whole 16-byte chunks, K being a multiple of 16); an
+    // M- / N-contiguous operand is gathered byte by byte, consecutive lanes on
+    // consecutive rows of the tile
     if constexpr (TA) {
       for (int i = tid; i < kBM * kBK; i += kGemmThreads) {
         const int r = i % kBM, kk = i / kBM;
@@ -159,13 +199,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
         sA[r * kPitchA + kk] = (gr < M && gk < K) ? A[gk * g.lda + gr] : uint8_t(0);
       }
     } else {
-      for (int i = tid; i < kBM * kChA; i += kGemmThreads) {
-        const int r = i / kChA, ch = i % kChA;
-        const int64_t gr = m0 + r;
-        const int64_t kb = code_bytes<FA>(k0) + ch * 16;
-        uint4 d = make_uint4(0, 0, 0, 0);
-        if (gr < M && kb < kbytesA) d = *reinterpret_cast<const uint4*>(A + gr * g.lda + kb);
-        *reinterpret_cast<uint4*>(&sA[r * kPitchA + ch * 16]) = d;
+#pragma unroll
+      for (int u = 0; u < kNA; ++u) {
+        const int i = tid + u * kGemmThreads;
+        if (i < kBM * kChA) *reinterpret_cast<uint4*>(&sA[(i / kChA) * kPitchA + (i % kChA) * 16]) = ra[u];
       }
     }
     if constexpr (TB) {
@@ -175,29 +212,25 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
         sB[r * kPitchB + kk] = (gr < N && gk < K) ? B[gk * g.ldb + gr] : uint8_t(0);
       }
     } else {
-      for (int i = tid; i < kBN * kChB; i += kGemmThreads) {
-        const int r = i / kChB, ch = i % kChB;
-        const int64_t gr = n0 + r;
-        const int64_t kb = code_bytes<FB>(k0) + ch * 16;
-        uint4 d = make_uint4(0, 0, 0, 0);
-        if (gr < N && kb < kbytesB) d = *reinterpret_cast<const uint4*>(B + gr * g.ldb + kb);
-        *reinterpret_cast<uint4*>(&sB[r * kPitchB + ch * 16]) = d;
+#pragma unroll
+      for (int u = 0; u < kNB; ++u) {
+        const int i = tid + u * kGemmThreads;
+        if (i < kBN * kChB) *reinterpret_cast<uint4*>(&sB[(i / kChB) * kPitchB + (i % kChB) * 16]) = rb[u];
       }
     }
-    // ---- stage scales: 4 K-blocks per row, 2^0 (code 127) past the matrix
+    // ---- scales: 4 K-blocks per row, 2^0 (code 127) past the matrix
     if constexpr (!PT) {
-      for (int i = tid; i < kBM * 4; i += kGemmThreads) {
-        const int r = i >> 2, kb = i & 3;
-        const int64_t gr = m0 + r, gk = k0 / 32 + kb;
-        sSA[i] = (gr < M && gk < kblocks) ? SA[gr * kblocks + gk] : uint8_t(127);
-      }
-      for (int i = tid; i < kBN * 4; i += kGemmThreads) {
-        const int r = i >> 2, kb = i & 3;
-        const int64_t gr = n0 + r, gk = k0 / 32 + kb;
-        sSB[i] = (gr < N && gk < kblocks) ? SB[gr * kblocks + gk] : uint8_t(127);
+#pragma unroll
+      for (int u = 0; u < kNS; ++u) {
+        const int i = tid + u * kGemmThreads;
+        if (i < kBM * 4) {
+          sSA[i] = rsa[u];
+          sSB[i] = rsb[u];
+        }
       }
     }
     __syncthreads();
+    if (k0 + kBK < K) fetch(k0 + kBK);
 
     // ---- two MFMA K-steps of 64; lane l feeds row l%32, K-block (2*kk + l/32)
 #pragma unroll
