@@ -425,7 +425,16 @@ __device__ __forceinline__ void mx_encode_given(const float (&v)[N], bool nonfin
       cvt_values_f32<F, N>(v, scale, w);
     }
   } else {
-    // e = -127: 2^-127 is not a normal FP32 scale operand; use the integer encoder
+    // e = -127: an all-zero group converts at scale 1 (+-0 gives +-0 codes at
+    // any scale), which keeps its wave off the slow integer encoder
+    uint32_t any = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) any |= abs_bits(v[j]);
+    if (any == 0u) {
+      cvt_values_f32<F, N>(v, 1.0f, w);
+      return;
+    }
+    // otherwise 2^-127 is not a normal FP32 scale operand; use the integer encoder
     const float mul = pow2_neg(e);
     uint32_t c[N];
 #pragma unroll

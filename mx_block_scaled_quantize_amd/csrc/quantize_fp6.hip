@@ -128,8 +128,10 @@ __global__ __launch_bounds__(kThreads) void rowwise_bf16_kernel(const uint16_t* 
     const bool nonfinite = bmax >= 0x7F800000u;
     const int e = nonfinite ? 0 : shared_exponent<F, R>(bmax);
     uint32_t w[6];
-    if (!nonfinite && e > -127) {
-      const float scale = __uint_as_float(uint32_t(127 + e) << 23);
+    // an all-zero block (e = -127) converts too: +-0 gives +-0 at any scale, and
+    // keeping it off the integer encoder keeps its wave off the launch's tail
+    if (!nonfinite && (e > -127 || bmax == 0u)) {
+      const float scale = bmax == 0u ? 1.0f : __uint_as_float(uint32_t(127 + e) << 23);
       const v32bf_t xv = __builtin_bit_cast(v32bf_t, d);
       v6u_t r;
       if constexpr (F == E2M3) r = __builtin_bit_cast(v6u_t, __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(xv, scale));
@@ -235,8 +237,9 @@ __device__ __forceinline__ uint32_t encode_block32(const float (&v)[32], const u
   const bool nonfinite = bmax >= 0x7F800000u;
   const int e = nonfinite ? 0 : shared_exponent<F, R>(bmax);
   if constexpr (IN == IN_BF16) {
-    if (!nonfinite && e > -127) {
-      const float scale = __uint_as_float(uint32_t(127 + e) << 23);
+    // an all-zero block converts too (+-0 gives +-0 at any scale)
+    if (!nonfinite && (e > -127 || bmax == 0u)) {
+      const float scale = bmax == 0u ? 1.0f : __uint_as_float(uint32_t(127 + e) << 23);
       v16u_t d;
 #pragma unroll
       for (int k = 0; k < 16; ++k) d[k] = bf[k];
