@@ -381,6 +381,228 @@ static mx_status_t tiles_by_input(mx_dtype_t in, const void* x, int64_t rows, in
   return launch_tiles<IN_F32, F, R, DUAL>(x, rows, cols, qr, sr, qc, sc, amax, st);
 }
 
+// ---------------------------------------------------------------------------
+// Register-resident MXFP6 dual quantizer for BF16 input
+// ---------------------------------------------------------------------------
+// The layout of the MXFP8 dual kernel: a workgroup of 4 waves takes a 128 x 128
+// tile, each wave a 64 x 64 quarter in which a lane holds rows 8h .. 8h+7 of
+// columns 8g .. 8g+7 (8 loads of 16 bytes).  A row block (32 columns) sits in a
+// quad and a column block (32 rows) in 4 lanes of one 16-lane DPP row, so both
+// block maxima are DPP steps.  The 32-element FP6 converter encodes each element
+// from its own value and the block scale, so a lane converts just its 8 values
+// (the other 24 inputs zero) and keeps the first 6 bytes of the stream: its 8
+// codes, in place in the block's little-endian bit stream.  Codes are staged in
+// LDS (96 bytes per tile row / column) and leave as 8-byte pieces of whole
+// lines; scales leave as one dword per row and per column.
+constexpr int kD6Tile = 128, kD6Wave = 64;
+constexpr int kD6Line = kD6Tile * 6 / 8;     // 96 code bytes per tile row / column
+
+__device__ __forceinline__ uint32_t d6_word(const uint4& u, int d) {
+  return d == 0 ? u.x : d == 1 ? u.y : d == 2 ? u.z : u.w;
+}
+
+// 48 code bits of 8 BF16 values (4 pairs, element order) at the given scale.
+template <int F>
+__device__ __forceinline__ uint2 d6_convert8(const uint32_t (&p)[4], float scale) {
+  v16u_t d;
+  d[0] = p[0]; d[1] = p[1]; d[2] = p[2]; d[3] = p[3];
+#pragma unroll
+  for (int k = 4; k < 16; ++k) d[k] = 0u;
+  const v32bf_t xv = __builtin_bit_cast(v32bf_t, d);
+  v6u_t r;
+  if constexpr (F == E2M3) r = __builtin_bit_cast(v6u_t, __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(xv, scale));
+  else r = __builtin_bit_cast(v6u_t, __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(xv, scale));
+  return make_uint2(r[0], r[1] & 0xFFFFu);
+}
+
+// 48 code bits of 8 BF16 values of a block that is non-finite (largest
+// magnitude with each input's sign) or has a subnormal amax (integer encoder
+// on v * 2^-e).  Out of line: rare.
+template <int F>
+__device__ __attribute__((noinline)) uint2 d6_encode8_general(uint4 c, int e, int nonfinite) {
+  const uint32_t w4[4] = {c.x, c.y, c.z, c.w};
+  const float mul = pow2_neg(e);
+  uint64_t acc = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t bits = (i & 1) ? (w4[i >> 1] & 0xFFFF0000u) : (w4[i >> 1] << 16);
+    const uint32_t code = nonfinite ? (Fmt_<F>::kNan | ((bits >> 31) << 5))
+                                    : encode_rne_sat<F>(__uint_as_float(bits) * mul);
+    acc |= uint64_t(code & 0x3Fu) << (6 * i);
+  }
+  return make_uint2(uint32_t(acc), uint32_t(acc >> 32));
+}
+
+template <int F, int R>
+__device__ __forceinline__ uint2 d6_encode8(const uint32_t (&p)[4], uint32_t bmax, uint32_t& scale_code) {
+  const bool nonfinite = bmax >= 0x7F800000u;
+  const int e = nonfinite ? 0 : shared_exponent<F, R>(bmax);
+  // the converter saturates: both rules go straight in; an all-zero block
+  // converts at scale 1 (+-0 gives +-0)
+  if (!nonfinite && (e > -127 || bmax == 0u)) {
+    scale_code = uint32_t(e + 127);
+    return d6_convert8<F>(p, bmax == 0u ? 1.0f : __uint_as_float(uint32_t(127 + e) << 23));
+  }
+  scale_code = nonfinite ? 0xFFu : uint32_t(e + 127);
+  return d6_encode8_general<F>(make_uint4(p[0], p[1], p[2], p[3]), e, nonfinite ? 1 : 0);
+}
+
+// 6 bytes at a 2-byte aligned LDS address
+__device__ __forceinline__ void d6_put6(uint8_t* dst, uint2 w) {
+  uint16_t* d = reinterpret_cast<uint16_t*>(dst);
+  d[0] = uint16_t(w.x);
+  d[1] = uint16_t(w.x >> 16);
+  d[2] = uint16_t(w.y);
+}
+
+__device__ __forceinline__ uint32_t d6_absmax(const uint4& c) {
+  const uint32_t k = 0x7FFF7FFFu;
+  const uint32_t m = pk_umax16(pk_umax16(c.x & k, c.y & k), pk_umax16(c.z & k, c.w & k));
+  return umax(m & 0xFFFFu, m >> 16) << 16;
+}
+
+template <int F, int R, bool AMAX>
+__global__ __launch_bounds__(256) void dual_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                        int tiles_c, uint8_t* __restrict__ q_row,
+                                                        uint8_t* __restrict__ s_row, uint8_t* __restrict__ q_col,
+                                                        uint8_t* __restrict__ s_col, uint32_t* __restrict__ amax_out) {
+  __shared__ __attribute__((aligned(16))) uint8_t qr_lds[kD6Tile * kD6Line];   // [tile row][96 B]
+  __shared__ __attribute__((aligned(16))) uint8_t qc_lds[kD6Tile * kD6Line];   // [tile column][96 B]
+  __shared__ uint32_t srow_lds[kD6Tile], scol_lds[kD6Tile];
+  __shared__ uint32_t red[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // lane bits 0-1 and 4 give g, bits 2-3 and 5 give h
+  const int g = (lane & 3) | ((lane >> 2) & 4), h = ((lane >> 2) & 3) | ((lane >> 3) & 4), lane_q = lane & 3;
+  const int t = blockIdx.x;
+  const int64_t tr = int64_t(t / tiles_c) * kD6Tile, tc = int64_t(t % tiles_c) * kD6Tile;
+  const int wro = (wave >> 1) * kD6Wave, wco = (wave & 1) * kD6Wave;
+  uint8_t* const srl = reinterpret_cast<uint8_t*>(srow_lds) + wro * 4 + (wave & 1) * 2;
+  uint8_t* const scl = reinterpret_cast<uint8_t*>(scol_lds) + wco * 4 + (wave >> 1) * 2;
+  // rows and cols are multiples of 32: a quad and the lanes h = 4k .. 4k+3 are in or out together
+  const bool ok = tr + wro + 8 * h < rows && tc + wco + 8 * g < cols;
+  uint32_t tmax = 0;
+  if (ok) {
+    // a scalar base plus a 32-bit lane offset (the host keeps 64 * cols * 2 below 2^32)
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(x) + ((tr + wro) * cols + tc + wco) * 2;
+    const uint32_t c32 = uint32_t(cols);
+    uint4 raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4_t v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(xb + (uint32_t(8 * h + i) * c32 + uint32_t(8 * g)) * 2u));
+      raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    // ---- row-wise half: lane q of a quad holds elements 8q .. 8q+7 of the block
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t m = d6_absmax(raw[i]);
+      if constexpr (AMAX) {
+        if (m <= 0x7F800000u) {
+          tmax = umax(tmax, m);
+        } else {
+          const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            tmax = umax(tmax, abs_bits_no_nan(__uint_as_float(w4[j] << 16)));
+            tmax = umax(tmax, abs_bits_no_nan(__uint_as_float(w4[j] & 0xFFFF0000u)));
+          }
+        }
+      }
+      const uint32_t p[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+      uint32_t sc;
+      const uint2 w = d6_encode8<F, R>(p, quad_max(m), sc);
+      if (lane_q == 0) srl[(8 * h + i) * 4 + (g >> 2)] = uint8_t(sc);
+      d6_put6(qr_lds + (wro + 8 * h + i) * kD6Line + 6 * ((wco >> 3) + g), w);
+    }
+    // ---- column-wise half: dword d holds columns 2d (low halves) and 2d+1
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t mp = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mp = pk_umax16(mp, d6_word(raw[i], d) & 0x7FFF7FFFu);
+      mp = pk_umax16(mp, dpp_u32<kRowRor4>(mp));
+      mp = pk_umax16(mp, dpp_u32<kRowRor8>(mp));
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t sel = k ? 0x07060302u : 0x05040100u;
+        uint32_t p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          p[i] = __builtin_amdgcn_perm(d6_word(raw[2 * i + 1], d), d6_word(raw[2 * i], d), sel);
+        uint32_t sc;
+        const uint2 w = d6_encode8<F, R>(p, k ? (mp & 0xFFFF0000u) : (mp << 16), sc);
+        const int c = 8 * g + 2 * d + k;                     // column within the wave quarter
+        d6_put6(qc_lds + (wco + c) * kD6Line + 6 * ((wro >> 3) + h), w);
+        if ((h & 3) == 0) scl[c * 4 + (h >> 2)] = uint8_t(sc);
+      }
+    }
+  }
+  if constexpr (AMAX) {
+    const uint32_t wm = wave_max(tmax);
+    if (lane == 0) red[wave] = wm;
+  }
+  __syncthreads();
+  // ---- codes: 8-byte pieces, 12 per 96-byte line; 3 pieces are one block, so a
+  // ragged edge (whole 32-element blocks) stays exact
+  {
+    const int64_t row_pitch = cols / 32 * 24, col_pitch = rows / 32 * 24;
+#pragma unroll
+    for (int it = 0; it < kD6Tile * 12 / 256; ++it) {
+      const int item = threadIdx.x + 256 * it;
+      const int r = item / 12, pc = item % 12;
+      const int64_t e = int64_t(pc / 3) * 32;                        // first element of the piece's block
+      if (tr + r < rows && tc + e < cols)
+        *reinterpret_cast<uint2*>(q_row + (tr + r) * row_pitch + (tc / 32) * 24 + 8 * pc) =
+            *reinterpret_cast<const uint2*>(qr_lds + r * kD6Line + 8 * pc);
+      if (tc + r < cols && tr + e < rows)
+        *reinterpret_cast<uint2*>(q_col + (tc + r) * col_pitch + (tr / 32) * 24 + 8 * pc) =
+            *reinterpret_cast<const uint2*>(qc_lds + r * kD6Line + 8 * pc);
+    }
+  }
+  // ---- scales: thread j < 128 writes tile row j's 4 row scales, thread 128 + j
+  // tile column j's 4 column scales (fewer, byte by byte, on a ragged edge)
+  {
+    const int j = threadIdx.x & (kD6Tile - 1);
+    const bool col_side = threadIdx.x >= kD6Tile;
+    const int64_t line = col_side ? tc + j : tr + j;
+    const int64_t lines = col_side ? cols : rows;
+    const int64_t other0 = col_side ? tr : tc, other = col_side ? rows : cols;
+    if (line < lines) {
+      const uint32_t v = col_side ? scol_lds[j] : srow_lds[j];
+      uint8_t* dst = (col_side ? s_col : s_row) + line * (other >> 5) + (other0 >> 5);
+      const int64_t nb = (other - other0) >> 5;
+      if (nb >= 4 && (reinterpret_cast<uintptr_t>(dst) & 3u) == 0) {
+        *reinterpret_cast<uint32_t*>(dst) = v;
+      } else {
+        for (int b = 0; b < 4 && b < nb; ++b) dst[b] = uint8_t(v >> (8 * b));
+      }
+    }
+  }
+  if constexpr (AMAX) {
+    if (threadIdx.x == 0) {
+      const uint32_t mm = umax(umax(red[0], red[1]), umax(red[2], red[3]));
+      if (mm) atomic_max_u32(amax_out, mm);
+    }
+  }
+}
+
+template <int F, int R>
+static mx_status_t launch_dual_bf16(const void* x, int64_t rows, int64_t cols, uint8_t* qr, uint8_t* sr,
+                                    uint8_t* qc, uint8_t* sc, uint32_t* amax, hipStream_t st) {
+  const int64_t tiles_c = (cols + kD6Tile - 1) / kD6Tile;
+  const int64_t ntiles = tiles_c * ((rows + kD6Tile - 1) / kD6Tile);
+  const dim3 grid{unsigned(ntiles)}, block{256u};
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  if (amax)
+    hipLaunchKernelGGL((dual_bf16_kernel<F, R, true>), grid, block, 0, st, xb, rows, cols, int(tiles_c), qr, sr, qc,
+                       sc, amax);
+  else
+    hipLaunchKernelGGL((dual_bf16_kernel<F, R, false>), grid, block, 0, st, xb, rows, cols, int(tiles_c), qr, sr, qc,
+                       sc, amax);
+  return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
 template <bool DUAL>
 static mx_status_t tiles(mx_elem_t fmt, mx_scale_rule_t rule, mx_dtype_t in, const void* x, int64_t rows,
                          int64_t cols, uint8_t* qr, uint8_t* sr, uint8_t* qc, uint8_t* sc, uint32_t* amax,
@@ -406,8 +628,17 @@ mx_status_t fp6_quantize_dual(const void* x, mx_dtype_t in, int64_t rows, int64_
   if (rows * cols == 0) return MX_OK;
   if (!x || !q_row || !s_row || !q_colT || !s_colT) return MX_ERR_NULL;
   if (misaligned(x) || misaligned(q_row) || misaligned(q_colT)) return MX_ERR_ALIGN;
-  return fp6::tiles<true>(fmt, rule, in, x, rows, cols, q_row, s_row, q_colT, s_colT,
-                          reinterpret_cast<uint32_t*>(amax_out), stream);
+  uint32_t* am = reinterpret_cast<uint32_t*>(amax_out);
+  const int64_t ntiles = ((cols + fp6::kD6Tile - 1) / fp6::kD6Tile) * ((rows + fp6::kD6Tile - 1) / fp6::kD6Tile);
+  if (in == MX_BF16 && ntiles < (int64_t(1) << 31) && cols < (int64_t(1) << 25)) {
+    const bool ceil = rule == MX_SCALE_CEIL;
+    if (fmt == MX_E2M3)
+      return ceil ? fp6::launch_dual_bf16<E2M3, CEIL>(x, rows, cols, q_row, s_row, q_colT, s_colT, am, stream)
+                  : fp6::launch_dual_bf16<E2M3, FLOOR>(x, rows, cols, q_row, s_row, q_colT, s_colT, am, stream);
+    return ceil ? fp6::launch_dual_bf16<E3M2, CEIL>(x, rows, cols, q_row, s_row, q_colT, s_colT, am, stream)
+                : fp6::launch_dual_bf16<E3M2, FLOOR>(x, rows, cols, q_row, s_row, q_colT, s_colT, am, stream);
+  }
+  return fp6::tiles<true>(fmt, rule, in, x, rows, cols, q_row, s_row, q_colT, s_colT, am, stream);
 }
 
 mx_status_t fp6_quantize(const void* x, mx_dtype_t in, int64_t rows, int64_t cols, int block, mx_elem_t fmt,

@@ -137,11 +137,12 @@ def test_fp6_dual_special_blocks(fmt):
     for dtype in ("f32", "bf16"):
         x = make_input(x32, dtype)
         xs = f32_of_input(x)
-        qr, sr, qc, sc = mxa.mx_quantize_dual(x, fmt, "ceil")
-        wqr, wsr, wqc, wsc = omx.quantize_dual(xs, fmt, "ceil")
-        for got, want, what in ((sr, wsr, "row scales"), (qr, wqr, "row codes"), (sc, wsc, "col scales"),
-                                (qc, wqc, "col codes")):
-            assert_bytes_equal(host(got), want, f"{dtype} {what}")
+        for rule in ("floor", "ceil"):
+            qr, sr, qc, sc = mxa.mx_quantize_dual(x, fmt, rule)
+            wqr, wsr, wqc, wsc = omx.quantize_dual(xs, fmt, rule)
+            for got, want, what in ((sr, wsr, "row scales"), (qr, wqr, "row codes"), (sc, wsc, "col scales"),
+                                    (qc, wqc, "col codes")):
+                assert_bytes_equal(host(got), want, f"{dtype} {rule} {what}")
 
 
 @pytest.mark.parametrize("fmt", FP6)
