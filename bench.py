@@ -124,7 +124,7 @@ def main():
         return
     if args.mode == "delayed":
         R, C = 8192, 4096
-        xs = [up_bf16(workloads.cfg3_step("act", t)) for t in range(2)]
+        xs = [up_bf16(workloads.delayed_step("act", t)) for t in range(2)]
         ring = mxa.new_ring(16, dev)
         b3 = R * C * 2 + R * C + 80
 
@@ -152,7 +152,7 @@ def main():
     # ------------------------------------------------------------------ headline: dual quantize
     R, C = 8192, 4096
     algo_bytes = R * C * 2 + 2 * R * C + 2 * (R * C // 32) + 4      # 136,314,884
-    x0 = up_bf16(workloads.cfg2())
+    x0 = up_bf16(workloads.activation_bf16())
     nsets = 8
     sets = []
     for i in range(nsets):
@@ -256,7 +256,7 @@ def time_rotating(make_set, call, per_call_bytes, n, warm, stream, torch):
 def bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=10):
     """MXFP8 E4M3 GEMM 8192 x 4096 . (14336 x 4096)^T, BF16 out (quantized operands resident)."""
     M, N, K = 8192, 14336, 4096
-    a_bits, w_bits = workloads.cfg4()
+    a_bits, w_bits = workloads.mlp_operands()
     qa, sa = mxa.mx_quantize(up_bf16(a_bits), "e4m3", "ceil", "row")
     qw, sw = mxa.mx_quantize(up_bf16(w_bits), "e4m3", "ceil", "row")
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -278,7 +278,7 @@ def bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=1
 def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
     res = {}
     # row-wise quantize + dequantize, FP32 256 x 1024, round-down rule
-    x = torch.from_numpy(workloads.cfg1()).to(dev)
+    x = torch.from_numpy(workloads.wide_range_f32()).to(dev)
     q = torch.empty((256, 1024), dtype=torch.uint8, device=dev)
     s = torch.empty((256, 32), dtype=torch.uint8, device=dev)
     d = torch.empty((256, 1024), dtype=torch.float32, device=dev)
@@ -291,7 +291,7 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
     res["dequant_f32_256x1024"] = {"us": round(td * 1e6, 2), "GB/s": round(b1 / td / 1e9, 1)}
     # per-tensor delayed scaling, BF16 8192 x 4096 -> transposed FP8, ring of 16
     R, C = 8192, 4096
-    xs = [up_bf16(workloads.cfg3_step("act", t)) for t in range(2)]
+    xs = [up_bf16(workloads.delayed_step("act", t)) for t in range(2)]
     ring = mxa.new_ring(16, dev)
     b3 = R * C * 2 + R * C + 80
 
@@ -307,7 +307,7 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
                                                     "buffer_sets": k3}
     del xs
     # stochastic-rounding MXFP4 row-wise of a BF16 8192 x 4096 gradient, one uint32 word per element
-    gx = up_bf16(workloads.cfg2(R, C))
+    gx = up_bf16(workloads.activation_bf16(R, C))
     words = torch.from_numpy(workloads.random_words((R, C), 47).view(np.int32)).to(dev)
     bsr = R * C * 2 + R * C * 4 + R * C // 2 + R * C // 32
 
@@ -346,7 +346,7 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
                                              "buffer_sets": kf6d}
     del gx
     # Hadamard + column-wise MXFP4 quantization of both operands, then the MXFP4 GEMM
-    g_bits, x_bits, mask = workloads.cfg5()
+    g_bits, x_bits, mask = workloads.weight_grad_operands()
     G, X = up_bf16(g_bits), up_bf16(x_bits)
     b5 = 2 * (8192 * 4096 * 2 + 4096 * 4096 + 4096 * 256)
 
@@ -379,10 +379,10 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
 
 
 def bench_gemm_fp6(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=5):
-    """The cfg4 GEMM shape with both operands quantized row-wise to MXFP6 E2M3
+    """The 8192 x 14336 x 4096 MLP GEMM shape with both operands quantized row-wise to MXFP6 E2M3
     (round-up scale), BF16 out, on the 128 x 128-tile path."""
     M, N, K = 8192, 14336, 4096
-    a_bits, w_bits = workloads.cfg4()
+    a_bits, w_bits = workloads.mlp_operands()
     qa, sa = mxa.mx_quantize(up_bf16(a_bits), "e2m3", "ceil", "row")
     qw, sw = mxa.mx_quantize(up_bf16(w_bits), "e2m3", "ceil", "row")
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -394,10 +394,10 @@ def bench_gemm_fp6(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=5
 
 
 def bench_gemm_requant(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=10):
-    """The cfg4 MXFP8 GEMM with its FP32 result re-quantized to MXFP8 E4M3 (round-up
+    """The MXFP8 GEMM 8192 x 4096 . (14336 x 4096)^T with its FP32 result re-quantized to MXFP8 E4M3 (round-up
     scale) in the epilogue: codes [8192][14336] + scales instead of a BF16 matrix."""
     M, N, K = 8192, 14336, 4096
-    a_bits, w_bits = workloads.cfg4()
+    a_bits, w_bits = workloads.mlp_operands()
     qa, sa = mxa.mx_quantize(up_bf16(a_bits), "e4m3", "ceil", "row")
     qw, sw = mxa.mx_quantize(up_bf16(w_bits), "e4m3", "ceil", "row")
     qc = torch.empty((M, N), dtype=torch.uint8, device=dev)
@@ -419,7 +419,7 @@ def bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=10)
     'nt': w as stored [N][K] (x @ w.t(), K-contiguous); 'nn': its transposed copy
     [K][N] (N-contiguous, read through the LDS transpose)."""
     M, N, K = 8192, 14336, 4096
-    a_bits, w_bits = workloads.cfg4()
+    a_bits, w_bits = workloads.mlp_operands()
     x, w = up_bf16(a_bits), up_bf16(w_bits)
     rx, rw = mxa.new_ring(16, dev), mxa.new_ring(16, dev)
     for step in range(2):
@@ -453,7 +453,7 @@ def time_gemm_fp4(lib, sp, stream, dev, gq, gs, xq, xsc, torch, steps):
 
 def bench_gemm_fp4(lib, sp, stream, dev, up_bf16, workloads, torch, steps=10):
     """The MXFP4 weight-gradient GEMM alone, on the Hadamard + MXFP4 column-wise operands."""
-    g_bits, x_bits, mask = workloads.cfg5()
+    g_bits, x_bits, mask = workloads.weight_grad_operands()
     G, X = up_bf16(g_bits), up_bf16(x_bits)
     gq = torch.empty((4096, 4096), dtype=torch.uint8, device=dev)
     gs = torch.empty((4096, 256), dtype=torch.uint8, device=dev)
@@ -584,7 +584,7 @@ def cpu_baseline(workloads, np, target_s=10.0):
     tensor); the rate of the largest strip is reported."""
     from oracle import mx as omx
     cols = 4096
-    xb_all = workloads.cfg2()
+    xb_all = workloads.activation_bf16()
     rows, spent, rate, dt = 256, 0.0, None, 0.0
     while True:
         xs = workloads.bf16_to_f32(xb_all[:rows])

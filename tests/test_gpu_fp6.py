@@ -94,7 +94,7 @@ def test_fp6_roundtrip_error_bound(fmt):
 
 def test_fp6_full_size_sampled_rows():
     """BF16 8192 x 4096 activation to MXFP6 E3M2: sampled rows against the oracle."""
-    bits = workloads.cfg2(8192, 4096)
+    bits = workloads.activation_bf16(8192, 4096)
     q, s = mxa.mx_quantize(upload_bf16_bits(bits), "e3m2", "ceil", "row")
     qh, sh = host(q), host(s)
     rows = np.concatenate([[0, 8191], np.random.default_rng(66).choice(8192, 30, replace=False)])

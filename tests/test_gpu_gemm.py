@@ -195,10 +195,10 @@ def test_gemm_ldc_and_k_zero():
     assert st == 0 and (host(c) == 0).all()               # empty sum
 
 
-def test_cfg4_mxfp8_gemm_full_size_sampled():
+def test_mlp_mxfp8_gemm_full_size_sampled():
     """A 8192 x 4096 activations, W 14336 x 4096 weights, both MXFP8 E4M3 with the
     round-up rule along K, BF16 out; 48 x 48 sampled outputs against the oracle."""
-    a_bits, w_bits = workloads.cfg4()
+    a_bits, w_bits = workloads.mlp_operands()
     qa, sa = mxa.mx_quantize(upload_bf16_bits(a_bits), "e4m3", "ceil", "row")
     qw, sw = mxa.mx_quantize(upload_bf16_bits(w_bits), "e4m3", "ceil", "row")
     c = mxa.mx_gemm(qa, sa, qw, sw, "e4m3", "e4m3", 1.0, out_dtype=torch.bfloat16)
@@ -215,10 +215,10 @@ def test_cfg4_mxfp8_gemm_full_size_sampled():
     assert og.rel_frobenius(got, ref) <= 4e-3                  # BF16 output rounding only
 
 
-def test_cfg5_hadamard_mxfp4_wgrad_full_size_sampled():
+def test_hadamard_mxfp4_wgrad_full_size_sampled():
     """G, X BF16 8192 tokens x 4096: fixed-sign Hadamard + column-wise MXFP4
     quantization along tokens, then dW = (1/32) Gq^T Xq with BF16 out."""
-    g_bits, x_bits, mask = workloads.cfg5()
+    g_bits, x_bits, mask = workloads.weight_grad_operands()
     gq, gs = mxa.mx_quantize(upload_bf16_bits(g_bits), "e2m1", "ceil", "col", hadamard_mask=mask)
     xq, xs = mxa.mx_quantize(upload_bf16_bits(x_bits), "e2m1", "ceil", "col", hadamard_mask=mask)
     dw = mxa.mx_gemm(gq, gs, xq, xs, "e2m1", "e2m1", 1.0 / 32, out_dtype=torch.bfloat16)

@@ -79,7 +79,7 @@ def test_requant_full_size_sampled_rows():
     """The MLP up-projection (8192 x 4096 x (14336 x 4096)^T) re-quantized to MXFP8 E4M3:
     sampled rows against the oracle quantizer of the FP32 result."""
     M, N, K = 8192, 14336, 4096
-    a_bits, w_bits = workloads.cfg4()
+    a_bits, w_bits = workloads.mlp_operands()
     xa = torch.from_numpy(a_bits.view(np.int16)).view(torch.bfloat16).cuda()
     xw = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).cuda()
     qa, sa = mxa.mx_quantize(xa, "e4m3", "ceil", "row")

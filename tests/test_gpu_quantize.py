@@ -31,7 +31,7 @@ def make_input(x32: np.ndarray, dtype: str) -> torch.Tensor:
 
 def small_inputs():
     return {
-        "cfg1": workloads.cfg1(96, 256),
+        "wide_range": workloads.wide_range_f32(96, 256),
         "wide": workloads.random_tensor((64, 320), 21, "wide"),
         "rows": workloads.random_tensor((160, 96), 22, "rows"),
     }
@@ -135,7 +135,7 @@ def test_dual_parity_ragged(dtype, fmt, rule):
 def test_dual_matches_single_orientation_calls():
     """Page-3 style orientation check: the one-read dual output equals the
     row-wise call and the column-wise call byte for byte."""
-    x = upload_bf16_bits(workloads.cfg2(256, 384))
+    x = upload_bf16_bits(workloads.activation_bf16(256, 384))
     for fmt in FMTS:
         qr, sr, qc, sc = mxa.mx_quantize_dual(x, fmt, "ceil")
         q1, s1 = mxa.mx_quantize(x, fmt, "ceil", "row")
@@ -244,11 +244,11 @@ def test_dequantize_parity(fmt, orient, out_dtype):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_quantize_dequantize_roundtrip_cfg1(fmt):
-    x = upload_f32(workloads.cfg1())
+def test_quantize_dequantize_roundtrip_wide_range_f32(fmt):
+    x = upload_f32(workloads.wide_range_f32())
     q, s = mxa.mx_quantize(x, fmt, "floor", "row")
     d = mxa.mx_dequantize(q, s, 256, 1024, fmt, "row")
-    wq, ws = omx.quantize_rowwise(workloads.cfg1(), fmt, "floor")
+    wq, ws = omx.quantize_rowwise(workloads.wide_range_f32(), fmt, "floor")
     assert_bytes_equal(host(q), wq, "codes")
     assert_float_equal(host(d), omx.dequantize(wq, ws, fmt), "roundtrip")
 
@@ -261,11 +261,11 @@ def test_delayed_sequence_small(fmt, layout):
     """32 successive steps on one ring (length 16): codes, amax and the whole
     ring state equal the host fold after every step."""
     stream = "act" if fmt == "e4m3" else "grad"
-    fp8_max = workloads.CFG3_FP8_MAX[stream]
+    fp8_max = workloads.DELAYED_FP8_MAX[stream]
     ring = mxa.new_ring(16)
     oring = odl.Ring(16)
     for t in range(32):
-        xb = workloads.cfg3_step(stream, t, rows=96, cols=160)
+        xb = workloads.delayed_step(stream, t, rows=96, cols=160)
         x = upload_bf16_bits(xb)
         xs = workloads.bf16_to_f32(xb)
         q, qT, a = mxa.fp8_quantize_delayed(x, ring, t % 16, fmt, layout, fp8_max, 1.0, amax=True)
@@ -287,10 +287,10 @@ def test_delayed_resume_from_saved_ring():
     for t in range(24):
         if t == 16:
             saved = ring.clone()
-        x = upload_bf16_bits(workloads.cfg3_step("act", t, rows=64, cols=64))
+        x = upload_bf16_bits(workloads.delayed_step("act", t, rows=64, cols=64))
         outs.append(mxa.fp8_quantize_delayed(x, ring, t % 16, "e4m3", "transposed")[1])
     for t in range(16, 24):
-        x = upload_bf16_bits(workloads.cfg3_step("act", t, rows=64, cols=64))
+        x = upload_bf16_bits(workloads.delayed_step("act", t, rows=64, cols=64))
         qT = mxa.fp8_quantize_delayed(x, saved, t % 16, "e4m3", "transposed")[1]
         assert torch.equal(qT, outs[t])
     assert torch.equal(saved, ring)
@@ -324,10 +324,10 @@ def test_delayed_margin_and_nonfinite(dtype, layout, shape, fmt):
 
 # ---------------------------------------------------------------- full-size workloads (sampled)
 
-def test_cfg2_dual_full_size_sampled():
+def test_activation_dual_full_size_sampled():
     """BF16 8192 x 4096, E4M3, round-up rule, dual + amax, in the bench's launch
     configuration; the oracle checks 64 sampled rows and 4 sampled 32-row strips."""
-    xb = workloads.cfg2()
+    xb = workloads.activation_bf16()
     x = upload_bf16_bits(xb)
     qr, sr, qc, sc, a = mxa.mx_quantize_dual(x, "e4m3", "ceil", amax=True)
     g = np.random.default_rng(5)
@@ -347,16 +347,16 @@ def test_cfg2_dual_full_size_sampled():
     assert (host(sr) == 0).sum() >= 16 and (sc_h == 0).sum() >= 16
 
 
-def test_cfg3_delayed_full_size_first_steps():
+def test_delayed_full_size_first_steps():
     """BF16 8192 x 4096 delayed scaling, both streams, 3 steps each: ring state
     exact, sampled transposed codes exact."""
     g = np.random.default_rng(6)
     for stream, fmt in (("act", "e4m3"), ("grad", "e5m2")):
-        fp8_max = workloads.CFG3_FP8_MAX[stream]
+        fp8_max = workloads.DELAYED_FP8_MAX[stream]
         ring = mxa.new_ring(16)
         oring = odl.Ring(16)
         for t in range(3):
-            xb = workloads.cfg3_step(stream, t)
+            xb = workloads.delayed_step(stream, t)
             x = upload_bf16_bits(xb)
             m_before = np.float32(oring.m)
             _, qT, a = mxa.fp8_quantize_delayed(x, ring, t % 16, fmt, "transposed", fp8_max, 1.0, amax=True)

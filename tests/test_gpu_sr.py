@@ -88,7 +88,7 @@ def test_sr_threshold_boundaries():
 
 def test_sr_cfg_size_sampled_rows():
     """The bench workload (BF16 8192 x 4096 gradient): sampled rows against the oracle."""
-    x_bits = workloads.cfg2(8192, 4096)
+    x_bits = workloads.activation_bf16(8192, 4096)
     r = workloads.random_words((8192, 4096), 47)
     x = upload_bf16_bits(x_bits)
     q, s = mxa.mx_quantize_sr(x, upload_words(r), "ceil")

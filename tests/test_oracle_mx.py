@@ -109,8 +109,8 @@ def test_nonfinite_blocks(name):
 # ---------------------------------------------------------------- invariants on larger inputs
 
 def _inputs():
-    return [workloads.cfg1(64, 256), workloads.random_tensor((64, 256), 3, "wide"),
-            workloads.bf16_to_f32(workloads.cfg2(64, 128))]
+    return [workloads.wide_range_f32(64, 256), workloads.random_tensor((64, 256), 3, "wide"),
+            workloads.bf16_to_f32(workloads.activation_bf16(64, 128))]
 
 
 @pytest.mark.parametrize("name", FMTS)
@@ -170,7 +170,7 @@ def test_idempotence_and_error_bound(name, rule):
 
 
 def test_scale_bytes_per_element():
-    x = workloads.cfg1(32, 256)
+    x = workloads.wide_range_f32(32, 256)
     for name in FMTS:
         q, s = mx.quantize_rowwise(x, name, "ceil")
         assert s.size * 32 == x.size

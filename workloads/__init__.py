@@ -36,7 +36,7 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 # Workload recipes
 # ----------------------------------------------------------------------------
 
-def cfg1(rows: int = 256, cols: int = 1024, seed: int = 1) -> np.ndarray:
+def wide_range_f32(rows: int = 256, cols: int = 1024, seed: int = 1) -> np.ndarray:
     """FP32 [rows][cols]: N(0,1) * 2^u_row with u_row ~ U(-20, 20); 1% of the
     entries replaced by +-U(1e3, 1e4); then 4 random 32-element row blocks set to +0."""
     g = rng(seed)
@@ -53,7 +53,7 @@ def cfg1(rows: int = 256, cols: int = 1024, seed: int = 1) -> np.ndarray:
     return x.astype(np.float32)
 
 
-def cfg2(rows: int = 8192, cols: int = 4096, seed: int = 2) -> np.ndarray:
+def activation_bf16(rows: int = 8192, cols: int = 4096, seed: int = 2) -> np.ndarray:
     """BF16 bits [rows][cols]: N(0,1) * 2^u_col with u_col ~ U(-8, 8) per column
     (channel); 0.1% of entries multiplied by 300; zero blocks: 16 aligned 32x32
     tiles, 16 row-only 1x32 and 16 column-only 32x1 blocks (fewer if small)."""
@@ -77,11 +77,11 @@ def cfg2(rows: int = 8192, cols: int = 4096, seed: int = 2) -> np.ndarray:
     return to_bf16_bits(x)
 
 
-CFG3_FP8_MAX = {"act": 448.0, "grad": 57344.0}
-CFG3_FMT = {"act": "e4m3", "grad": "e5m2"}
+DELAYED_FP8_MAX = {"act": 448.0, "grad": 57344.0}
+DELAYED_FMT = {"act": "e4m3", "grad": "e5m2"}
 
 
-def cfg3_step(stream: str, t: int, rows: int = 8192, cols: int = 4096, seed: int = 3) -> np.ndarray:
+def delayed_step(stream: str, t: int, rows: int = 8192, cols: int = 4096, seed: int = 3) -> np.ndarray:
     """BF16 bits for delayed-scaling step t of stream 'act' or 'grad':
     N(0,1) * 2^(sin(t/4) * 6), a fresh draw per (stream, step)."""
     sidx = {"act": 0, "grad": 1}[stream]
@@ -90,7 +90,7 @@ def cfg3_step(stream: str, t: int, rows: int = 8192, cols: int = 4096, seed: int
     return to_bf16_bits(x)
 
 
-def cfg4(M: int = 8192, N: int = 14336, K: int = 4096, seed: int = 4):
+def mlp_operands(M: int = 8192, N: int = 14336, K: int = 4096, seed: int = 4):
     """GEMM operands: activations A = BF16 N(0,1) [M][K], weights W = BF16
     N(0, 0.02) [N][K] (the K-contiguous B^T of an MLP up-projection)."""
     a = to_bf16_bits(rng(seed, 0).standard_normal((M, K)))
@@ -98,7 +98,7 @@ def cfg4(M: int = 8192, N: int = 14336, K: int = 4096, seed: int = 4):
     return a, w
 
 
-def cfg5(tokens: int = 8192, width: int = 4096, seed: int = 5):
+def weight_grad_operands(tokens: int = 8192, width: int = 4096, seed: int = 5):
     """Weight-gradient operands: G = BF16 N(0, 1e-3) [tokens][width],
     X = BF16 N(0,1) [tokens][width], and a 32-bit sign mask."""
     g = to_bf16_bits(rng(seed, 0).standard_normal((tokens, width)) * 1e-3)
