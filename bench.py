@@ -27,6 +27,7 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline] 
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -44,10 +45,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dual_bf16_kernel_mxfp8_bf16_8192x
 
 
 def kernel_source_hash() -> str:
+    """Hash of the quantizer sources with comments and blank space removed, so that
+    a comment-only edit keeps a counter summary valid and any code edit voids it."""
     h = hashlib.sha256()
     for f in ("quantize.hip", "mx_device.hpp"):
-        with open(os.path.join(ROOT, "mx_block_scaled_quantize_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "mx_block_scaled_quantize_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -8,7 +8,8 @@
 // MX block (k = 32) maps onto one lane's operand and its scale register.
 //
 // Operand layouts (K-contiguous "NT"): A [M][K] codes, sa [M][K/32];
-// B^T [N][K] codes, sb [N][K/32]; FP4 codes are packed two per byte.
+// B^T [N][K] codes, sb [N][K/32]; FP4 codes are packed two per byte, FP6 codes
+// as a little-endian 6-bit stream along the row (24 bytes per block).
 //
 // The same kernels serve the per-tensor FP8 GEMM of the AstrAI fp8.py page
 // (mm_fp8: C = op(a) op(b) * scale + bias, BF16 out): every block scale is
@@ -21,6 +22,9 @@
 // (rows padded by 16 bytes so that the 8 lanes of a ds_read_b128 phase hit
 // distinct banks), scales staged next to the codes.  Rows / K-blocks beyond
 // the matrix are filled with code 0 and scale 2^0, which contribute nothing.
+// The next K-step's codes and scales are loaded into registers right after a
+// step is staged, so the loads run under that step's MFMAs.  This kernel serves
+// every shape the 256 x 256 kernel below does not take, and all FP6 operands.
 
 #include "mx_device.hpp"
 #include "mx_launch.hpp"

@@ -25,11 +25,25 @@
 //                   independent strips in flight per CU.  Workgroup ids are
 //                   mapped so that the 4 strips that share the 128-byte lines of
 //                   the transposed output run on the same XCD (ids are handed
-//                   to the 8 XCDs round-robin).  Used for MX dual, MX
-//                   column-wise (optionally with the in-lane Hadamard transform)
-//                   and the per-tensor transposed / dual outputs.
-//   The per-tensor kernels end with the delayed-scaling fold done by the last
-//   workgroup to finish (atomic ticket).
+//                   to the 8 XCDs round-robin).  Used for FP32 / FP16 inputs
+//                   (MX dual, MX column-wise with or without the Hadamard
+//                   transform, per-tensor transposed / dual outputs) and for
+//                   BF16 tensors too large for the tiled kernels below.
+//   BF16 input has register-resident kernels that never stage the input in LDS:
+//   dual_bf16_kernel    MX dual.  A 256-thread workgroup takes a 128 x 128 tile;
+//                       each lane holds an 8 x 8 patch, so a row block is one
+//                       quad of lanes (DPP max) and a column block is 4 lanes
+//                       of a DPP row (row_ror max).  Both code copies are
+//                       staged in LDS and leave as 16-byte pieces of whole
+//                       128-byte lines; the scales leave as dwords.
+//   col_bf16_kernel     MX column-wise (optionally after the 32-point Hadamard
+//                       transform, butterflies across the quad), same staging
+//                       of the transposed codes; 256-row tiles for FP4 so that
+//                       a column's output line is whole.
+//   pt_col_bf16_kernel  per-tensor FP8 cast, transposed output only.
+//   The per-tensor kernels end with the delayed-scaling fold, done by the last
+//   workgroup to finish (two-level ring ticket: a ticket per group of
+//   workgroups, then one over the groups).
 
 #include <mutex>
 

@@ -1,4 +1,4 @@
-// Row-wise MXFP6 (E2M3, E3M2) quantization for gfx950.
+// MXFP6 (E2M3, E3M2) quantization for gfx950: row-wise, column-wise and dual.
 //
 // "EU8M0 FP8" article, MX definition paragraph: the MX family shares the E8M0
 // block scale over k = 32 elements; MXFP6 is its 6-bit member.  Scale rule,
@@ -15,12 +15,22 @@
 //     these converts equal to RNE(v / 2^e) on the E2M3 / E3M2 grids, saturating
 //     beyond the largest magnitude, elements in bit-stream order.  (The FP32-input
 //     converts differ on some values, so FP32 and FP16 inputs do not use them.)
-//     Blocks with NaN/Inf, or with e = -127 (not a normal FP32 scale), take the
+//     All-zero blocks convert at scale 1 (+-0 gives +-0).  Blocks with NaN/Inf,
+//     or with a nonzero amax and e = -127 (not a normal FP32 scale), take the
 //     integer encoder below.
 //   rowwise_kernel  FP32 / FP16 input: a lane owns 8 elements, a quad owns a block
 //     and takes its amax with two DPP steps; the cast is the exact integer RNE +
 //     saturation encoder on v * 2^-e (a power-of-two multiply, exact wherever the
 //     result can matter).
+// Tiled kernels, for the column-wise copy (blocks run down the columns):
+//   tile_kernel      any input type, column-wise or dual: a tile is staged in
+//     LDS and each lane encodes whole 32-element blocks (the BF16 converter or
+//     the integer encoder, as above).
+//   dual_bf16_kernel BF16 dual, register resident: a lane holds an 8 x 8 patch,
+//     so a row block is a quad and a column block is 4 lanes of a DPP row; each
+//     lane converts its own 8 values with the 32-element converter (the other
+//     slots zero) and keeps its 6 bytes.  Both copies are staged in LDS as
+//     96-byte lines (128 elements) and leave as 8-byte pieces.
 
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
