@@ -52,8 +52,8 @@ extern "C" {
  * ([UE8M0] names MXFP8/6/4); they have no specials and are stored as a
  * little-endian bit stream along the row (element i at bits 6i .. 6i+5: 32
  * elements in 24 bytes).  FP6 is offered by mx_quantize (no Hadamard),
- * mx_quantize_dual and mx_dequantize; the other entry points return
- * MX_ERR_UNSUPPORTED. */
+ * mx_quantize_dual, mx_dequantize and mx_gemm (as both operands); the other
+ * entry points return MX_ERR_UNSUPPORTED for it. */
 typedef enum { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M1 = 2, MX_E2M3 = 3, MX_E3M2 = 4 } mx_elem_t;
 
 /* Storage type of a floating-point tensor argument. */
@@ -242,9 +242,9 @@ mx_status_t mx_gemm(const uint8_t* a, const uint8_t* sa, mx_elem_t fmt_a,
  *   qc        [M][N] codes (E2M1: [M][N/2] packed), 16-byte aligned;
  *   sc        [M][N/32] E8M0 scales;
  *   amax_out  optional max-accumulator of |C32| (NaN excluded), as for mx_quantize.
- * Operands as mx_gemm.  Shapes: K % 32 == 0, N % 32 == 0, any M.
- * Errors: as mx_gemm, plus MX_ERR_UNSUPPORTED for fmt_c / rule_c and MX_ERR_NULL for
- * qc / sc. */
+ * Operands as mx_gemm, FP8 or FP4 only.  Shapes: K % 32 == 0, N % 32 == 0, any M.
+ * Errors: as mx_gemm, plus MX_ERR_UNSUPPORTED for FP6 operands and for fmt_c / rule_c,
+ * and MX_ERR_NULL for qc / sc. */
 mx_status_t mx_gemm_requant(const uint8_t* a, const uint8_t* sa, mx_elem_t fmt_a,
                             const uint8_t* b, const uint8_t* sb, mx_elem_t fmt_b,
                             int64_t M, int64_t N, int64_t K, float alpha,

@@ -107,6 +107,8 @@ def test_fp8_quantize_delayed_argument_errors():
         a[i] = v
         return f(*a)
     assert call(4, 2) == UNSUP          # E2M1 has no per-tensor path
+    assert call(4, 3) == UNSUP          # nor E2M3 / E3M2
+    assert call(4, 4) == UNSUP
     assert call(5, 9) == UNSUP
     assert call(8, None) == NULL        # ring
     assert call(9, 0) == ARG            # hist_len
@@ -151,6 +153,8 @@ def test_mm_fp8_argument_errors():
     f = lib.mm_fp8
     # (a, b, fmt, batch, M, N, K, a_batched, b_batched, trans_a, trans_b, scale, bias, c, stream)
     assert f(FAKE, FAKE, 2, 1, 64, 64, 64, 0, 0, 0, 0, FAKE, None, FAKE, None) == UNSUP   # FP4 is not FP8
+    assert f(FAKE, FAKE, 3, 1, 64, 64, 64, 0, 0, 0, 0, FAKE, None, FAKE, None) == UNSUP   # nor FP6
+    assert f(FAKE, FAKE, 4, 1, 64, 64, 64, 0, 0, 0, 0, FAKE, None, FAKE, None) == UNSUP
     assert f(FAKE, FAKE, 0, 1, 64, 64, 40, 0, 0, 0, 0, FAKE, None, FAKE, None) == SHAPE   # K % 16
     assert f(FAKE, FAKE, 0, 70000, 64, 64, 64, 1, 1, 0, 0, FAKE, None, FAKE, None) == SHAPE   # batch limit
     assert f(FAKE, FAKE, 0, 1, -1, 64, 64, 0, 0, 0, 0, FAKE, None, FAKE, None) == SHAPE
@@ -169,6 +173,9 @@ def test_mx_gemm_requant_argument_errors():
     # (a, sa, fa, b, sb, fb, M, N, K, alpha, fc, rc, qc, sc, amax, stream)
     assert f(FAKE, FAKE, 0, FAKE, FAKE, 2, 64, 64, 64, 1.0, 0, 1, FAKE, FAKE, None, None) == UNSUP   # FP8 x FP4
     assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, 3, 1, FAKE, FAKE, None, None) == UNSUP   # output format
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, 4, 1, FAKE, FAKE, None, None) == UNSUP   # E3M2 output
+    assert f(FAKE, FAKE, 3, FAKE, FAKE, 3, 64, 64, 64, 1.0, 0, 1, FAKE, FAKE, None, None) == UNSUP   # FP6 operands
+    assert f(FAKE, FAKE, 3, FAKE, FAKE, 4, 64, 64, 64, 1.0, 0, 1, FAKE, FAKE, None, None) == UNSUP
     assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, 0, 2, FAKE, FAKE, None, None) == UNSUP   # rule
     assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 48, 64, 1.0, 0, 1, FAKE, FAKE, None, None) == SHAPE   # N % 32
     assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 48, 1.0, 0, 1, FAKE, FAKE, None, None) == SHAPE   # K % 32
@@ -182,6 +189,8 @@ def test_mx_quantize_sr_argument_errors():
     f = lib.mx_quantize_sr
     # (x, in, rows, cols, block, fmt, rule, rand, q, scales, amax, stream)
     assert f(FAKE, 1, 64, 64, 32, 0, 1, FAKE, FAKE, FAKE, None, None) == UNSUP     # E4M3: SR is MXFP4 only
+    assert f(FAKE, 1, 64, 64, 32, 3, 1, FAKE, FAKE, FAKE, None, None) == UNSUP     # E2M3
+    assert f(FAKE, 1, 64, 64, 32, 4, 1, FAKE, FAKE, FAKE, None, None) == UNSUP     # E3M2
     assert f(FAKE, 1, 64, 48, 32, 2, 1, FAKE, FAKE, FAKE, None, None) == SHAPE
     assert f(FAKE, 1, 64, 64, 16, 2, 1, FAKE, FAKE, FAKE, None, None) == UNSUP     # block must be 32
     assert f(FAKE, 1, 64, 64, 32, 2, 1, None, FAKE, FAKE, None, None) == NULL      # no random words
