@@ -18,9 +18,9 @@
 // N) contiguous is handled in the kernel (no transposed copy).
 //
 // gemm_kernel: 128 x 128 output tile per workgroup, 4 waves in a 2 x 2 grid
-// with a 64 x 64 sub-tile (2 x 2 MFMA tiles) each, K-steps of 128 staged in LDS
-// (rows padded by 16 bytes so that the 8 lanes of a ds_read_b128 phase hit
-// distinct banks), scales staged next to the codes.  Rows / K-blocks beyond
+// with a 64 x 64 sub-tile (2 x 2 MFMA tiles) each, K-steps of 128 (256 for
+// FP6 x FP6) staged in LDS (rows padded by 16 bytes so that the 8 lanes of a
+// ds_read_b128 phase hit distinct banks), scales staged next to the codes.  Rows / K-blocks beyond
 // the matrix are filled with code 0 and scale 2^0, which contribute nothing.
 // The next K-step's codes and scales are loaded into registers right after a
 // step is staged, so the loads run under that step's MFMAs.  This kernel serves
@@ -45,8 +45,6 @@ template <int F>
 __host__ __device__ constexpr int64_t code_bytes(int64_t k) {
   return F == E2M1 ? k / 2 : kIsFp6<F> ? k / 4 * 3 : k;
 }
-
-template <int FA> struct OpBytes { static constexpr int kRow = int(code_bytes<FA>(kBK)); };
 
 // Arguments of both GEMM kernels.  C[p] = alpha op(A[p]) op(B[p])^T where A is
 // [M][K] and B is [N][K] as the MFMA consumes them.  An operand is stored either
@@ -122,14 +120,19 @@ __device__ __forceinline__ void requant_block32(const float (&v)[32], uint8_t* _
 }
 
 template <int FA, int FB, bool BF16OUT, bool PT, bool TA, bool TB, bool RQ = false>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
-  constexpr int kRowA = OpBytes<FA>::kRow, kRowB = OpBytes<FB>::kRow;
+__global__ __launch_bounds__(kGemmThreads)
+__attribute__((amdgpu_waves_per_eu((kIsFp6<FA> && kIsFp6<FB>) ? 2 : 1))) void gemm_kernel(const GemmArgs g) {
+  // FP6 x FP6 takes K-steps of 256 (four MFMA steps per pair of barriers; a
+  // 128-step stages only 96 bytes per row); every other pair 128
+  constexpr int kStep = (kIsFp6<FA> && kIsFp6<FB>) ? 2 * kBK : kBK;
+  constexpr int kSB = kStep / 32;                                   // scales per row and step
+  constexpr int kRowA = int(code_bytes<FA>(kStep)), kRowB = int(code_bytes<FB>(kStep));
   constexpr int kPitchA = kRowA + 16, kPitchB = kRowB + 16;
   static_assert(!(TA || TB) || (PT && FA != E2M1 && FB != E2M1), "M/N-contiguous operands: per-tensor FP8 only");
   __shared__ __attribute__((aligned(16))) uint8_t sA[kBM * kPitchA];
   __shared__ __attribute__((aligned(16))) uint8_t sB[kBN * kPitchB];
-  __shared__ uint8_t sSA[kBM * 4];
-  __shared__ uint8_t sSB[kBN * 4];
+  __shared__ uint8_t sSA[kBM * kSB];
+  __shared__ uint8_t sSB[kBN * kSB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
   constexpr int kChA = kRowA / 16, kChB = kRowB / 16;
   constexpr int kNA = (kBM * kChA + kGemmThreads - 1) / kGemmThreads;
   constexpr int kNB = (kBN * kChB + kGemmThreads - 1) / kGemmThreads;
-  constexpr int kNS = (kBM * 4 + kGemmThreads - 1) / kGemmThreads;
+  constexpr int kNS = (kBM * kSB + kGemmThreads - 1) / kGemmThreads;
   uint4 ra[kNA], rb[kNB];
   uint8_t rsa[kNS], rsb[kNS];
   auto fetch = [&](int64_t k0) {
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
     if constexpr (!PT) {
 #pragma unroll
       for (int u = 0; u < kNS; ++u) {
-        const int i = tid + u * kGemmThreads, r = i >> 2, kb = i & 3;
+        const int i = tid + u * kGemmThreads, r = i / kSB, kb = i % kSB;
         const int64_t gk = k0 / 32 + kb;
         rsa[u] = (m0 + r < M && gk < kblocks) ? SA[(m0 + r) * kblocks + gk] : uint8_t(127);
         rsb[u] = (n0 + r < N && gk < kblocks) ? SB[(n0 + r) * kblocks + gk] : uint8_t(127);
@@ -191,13 +194,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
   };
   if (K > 0) fetch(0);
 
-  for (int64_t k0 = 0; k0 < K; k0 += kBK) {
+  for (int64_t k0 = 0; k0 < K; k0 += kStep) {
     // ---- stage codes: the prefetched 16-byte chunks (zero past the matrix:
     // K-contiguous rows are whole 16-byte chunks, K being a multiple of 16); an
     // M- / N-contiguous operand is gathered byte by byte, consecutive lanes on
     // consecutive rows of the tile
     if constexpr (TA) {
-      for (int i = tid; i < kBM * kBK; i += kGemmThreads) {
+      for (int i = tid; i < kBM * kStep; i += kGemmThreads) {
         const int r = i % kBM, kk = i / kBM;
         const int64_t gr = m0 + r, gk = k0 + kk;
         sA[r * kPitchA + kk] = (gr < M && gk < K) ? A[gk * g.lda + gr] : uint8_t(0);
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
       }
     }
     if constexpr (TB) {
-      for (int i = tid; i < kBN * kBK; i += kGemmThreads) {
+      for (int i = tid; i < kBN * kStep; i += kGemmThreads) {
         const int r = i % kBN, kk = i / kBN;
         const int64_t gr = n0 + r, gk = k0 + kk;
         sB[r * kPitchB + kk] = (gr < N && gk < K) ? B[gk * g.ldb + gr] : uint8_t(0);
@@ -222,23 +225,23 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
         if (i < kBN * kChB) *reinterpret_cast<uint4*>(&sB[(i / kChB) * kPitchB + (i % kChB) * 16]) = rb[u];
       }
     }
-    // ---- scales: 4 K-blocks per row, 2^0 (code 127) past the matrix
+    // ---- scales: kSB K-blocks per row, 2^0 (code 127) past the matrix
     if constexpr (!PT) {
 #pragma unroll
       for (int u = 0; u < kNS; ++u) {
         const int i = tid + u * kGemmThreads;
-        if (i < kBM * 4) {
+        if (i < kBM * kSB) {
           sSA[i] = rsa[u];
           sSB[i] = rsb[u];
         }
       }
     }
     __syncthreads();
-    if (k0 + kBK < K) fetch(k0 + kBK);
+    if (k0 + kStep < K) fetch(k0 + kStep);
 
-    // ---- two MFMA K-steps of 64; lane l feeds row l%32, K-block (2*kk + l/32)
+    // ---- MFMA K-steps of 64; lane l feeds row l%32, K-block (2*kk + l/32)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < kStep / 64; ++kk) {
       const int kblk = 2 * kk + (lane >> 5);
       v8i a[2], b[2];
       int sa[2], sb[2];
@@ -248,8 +251,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
         const int rb = wn * 64 + t * 32 + (lane & 31);
         a[t] = load_operand<FA>(&sA[ra * kPitchA], kk, lane >> 5);
         b[t] = load_operand<FB>(&sB[rb * kPitchB], kk, lane >> 5);
-        sa[t] = PT ? 127 : sSA[ra * 4 + kblk];
-        sb[t] = PT ? 127 : sSB[rb * 4 + kblk];
+        sa[t] = PT ? 127 : sSA[ra * kSB + kblk];
+        sb[t] = PT ? 127 : sSB[rb * kSB + kblk];
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
