@@ -67,10 +67,12 @@ def test_gemm_small_parity(fa, fb, shape):
 
 
 @pytest.mark.parametrize("fa,fb", [("e2m3", "e2m3"), ("e3m2", "e2m3"), ("e2m3", "e3m2"), ("e3m2", "e3m2")])
-@pytest.mark.parametrize("shape", [(128, 128, 128), (200, 136, 192), (64, 300, 512), (1, 7, 64), (256, 384, 1024)])
+@pytest.mark.parametrize("shape", [(128, 128, 128), (200, 136, 192), (64, 300, 512), (1, 7, 64), (256, 384, 1024),
+                                   (96, 160, 320), (130, 258, 704)])   # whole K-steps of 256, then a partial one
 def test_gemm_fp6_parity(fa, fb, shape):
     """MXFP6 operands (bit-stream packed as mx_quantize writes them) on the
-    128 x 128 path; a K of 192 ends on a half K-step."""
+    128 x 128 path, whose FP6 K-steps are 256 long: K of 64, 128, 192, 320 and
+    704 end on a partial step, zero-filled past K."""
     M, N, K = shape
     qa, sa, qb, sb = quantized_operands(M, N, K, fa, fb, seed=M + N + K + 1)
     args = (upload_u8(qa), upload_u8(sa), upload_u8(qb), upload_u8(sb), fa, fb, 0.75)
