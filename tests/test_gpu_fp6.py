@@ -107,8 +107,10 @@ def test_fp6_full_size_sampled_rows():
 @pytest.mark.parametrize("fmt", FP6)
 @pytest.mark.parametrize("rule", RULES)
 def test_fp6_colwise_and_dual_parity(dtype, fmt, rule):
-    # ragged tiles: 160 rows (one full and one partial 128-row tile), 200 / 96 columns
-    for shape, seed, kind in (((160, 200), 67, "wide"), ((96, 96), 68, "rows"), ((288, 416), 69, "normal")):
+    # ragged tiles: 160 rows (one full and one partial 128-row tile), 200 / 224 / 96 columns;
+    # a single 32 x 32 block
+    for shape, seed, kind in (((160, 200), 67, "wide"), ((96, 96), 68, "rows"), ((288, 416), 69, "normal"),
+                              ((160, 224), 70, "wide"), ((32, 32), 71, "normal")):
         x = make_input(workloads.random_tensor(shape, seed, kind), dtype)
         xs = f32_of_input(x)
         q, s, a = mxa.mx_quantize(x, fmt, rule, "col", amax=True)
