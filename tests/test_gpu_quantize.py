@@ -90,27 +90,30 @@ def test_rowwise_hadamard(fmt):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("rule", RULES)
 def test_colwise_parity_ragged(dtype, fmt, rule):
-    # 160 rows (one full and one partial 128-row tile), 200 columns (not a multiple of 32)
-    x32 = workloads.random_tensor((160, 200), 24, "wide")
-    x = make_input(x32, dtype)
-    xs = f32_of_input(x)
-    q, s, a = mxa.mx_quantize(x, fmt, rule, "col", amax=True)
-    wq, ws = omx.quantize_colwise_t(xs, fmt, rule)
-    assert_bytes_equal(host(s), ws, "scales")
-    assert_bytes_equal(host(q), wq, "codes")
-    assert host(a)[0] == omx.tensor_amax(xs)
+    # 160 rows (one full and one partial 128-row tile), 200 columns (not a multiple
+    # of 32); 288 rows (a full 256-row FP4 tile and a partial one); one 32 x 32 block
+    for shape, seed in (((160, 200), 24), ((288, 72), 30), ((32, 32), 31)):
+        x32 = workloads.random_tensor(shape, seed, "wide")
+        x = make_input(x32, dtype)
+        xs = f32_of_input(x)
+        q, s, a = mxa.mx_quantize(x, fmt, rule, "col", amax=True)
+        wq, ws = omx.quantize_colwise_t(xs, fmt, rule)
+        assert_bytes_equal(host(s), ws, f"{shape} scales")
+        assert_bytes_equal(host(q), wq, f"{shape} codes")
+        assert host(a)[0] == omx.tensor_amax(xs)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_colwise_hadamard(fmt):
     mask = 0x1357_9BDF
-    x32 = workloads.random_tensor((256, 136), 25, "normal")
-    x = make_input(x32, "bf16")
-    xs = f32_of_input(x)
-    q, s = mxa.mx_quantize(x, fmt, "ceil", "col", hadamard_mask=mask)
-    wq, ws = omx.quantize_colwise_t(xs, fmt, "ceil", hadamard_mask=mask)
-    assert_bytes_equal(host(s), ws, "scales")
-    assert_bytes_equal(host(q), wq, "codes")
+    for shape, seed in (((256, 136), 25), ((544, 72), 32)):
+        x32 = workloads.random_tensor(shape, seed, "normal")
+        x = make_input(x32, "bf16")
+        xs = f32_of_input(x)
+        q, s = mxa.mx_quantize(x, fmt, "ceil", "col", hadamard_mask=mask)
+        wq, ws = omx.quantize_colwise_t(xs, fmt, "ceil", hadamard_mask=mask)
+        assert_bytes_equal(host(s), ws, f"{shape} scales")
+        assert_bytes_equal(host(q), wq, f"{shape} codes")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
@@ -119,7 +122,7 @@ def test_colwise_hadamard(fmt):
 def test_dual_parity_ragged(dtype, fmt, rule):
     # tiles of 128 x 128 with ragged right and bottom edges; (256, 992) gives a
     # tile count divisible by 8 (the XCD-grouped tile order)
-    for shape, seed in (((96, 160), 26), ((288, 416), 27), ((256, 992), 28), ((320, 544), 29)):
+    for shape, seed in (((96, 160), 26), ((288, 416), 27), ((256, 992), 28), ((320, 544), 29), ((32, 32), 33)):
         x32 = workloads.random_tensor(shape, seed, "rows")
         x = make_input(x32, dtype)
         xs = f32_of_input(x)
