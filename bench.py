@@ -151,7 +151,9 @@ def main():
                           "gemm_fp4": bench_gemm_fp4(lib, sp, stream, dev, up_bf16, workloads, torch, args.steps),
                           "mm_fp8": bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, args.steps),
                           "requant": bench_gemm_requant(lib, sp, stream, dev, up_bf16, mxa, workloads, torch,
-                                                        args.steps)}),
+                                                        args.steps),
+                          "gemm_fp6": bench_gemm_fp6(lib, sp, stream, dev, up_bf16, mxa, workloads, torch,
+                                                     args.steps)}),
               flush=True)
         return
 
@@ -497,6 +499,10 @@ GEMM_PROFILES = {
         "gemm256_kernel_mm_fp8_nn_8192x14336x4096.md",
         "per-tensor FP8 E4M3 mm_fp8, x 8192x4096 @ wT (wT 4096x14336 N-contiguous, LDS transpose reads), BF16 bias",
         2.0 * 8192 * 14336 * 4096, FP8_PEAK_TFLOPS),
+    "gemm_kernel<3, 3, true, false, false, false, false>": (
+        "gemm_kernel_mxfp6_e2m3_8192x14336x4096.md",
+        "MXFP6 E2M3 GEMM 8192x4096 . (14336x4096)^T, both operands bit-stream packed, BF16 out (128x128 path)",
+        2.0 * 8192 * 14336 * 4096, FP6_PEAK_TFLOPS),
 }
 
 
