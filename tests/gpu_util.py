@@ -1,6 +1,7 @@
 """Helpers for the GPU parity tests: uploads, downloads and mismatch reports."""
 
 import numpy as np
+import pytest
 import torch
 
 
@@ -59,3 +60,13 @@ def assert_float_equal(got: np.ndarray, want: np.ndarray, what: str):
         bad = np.argwhere(~same)
         first = [(tuple(int(i) for i in b), float(got[tuple(b)]), float(want[tuple(b)])) for b in bad[:8]]
         raise AssertionError(f"{what}: {len(bad)} of {got.size} differ; first (index, gpu, oracle): {first}")
+
+
+def import_library():
+    """The package under test.  Where a GPU is present a missing or unloadable
+    libmx.so is an error, so the GPU tests cannot pass by being skipped; without
+    a GPU (where they are deselected anyway) the module is skipped."""
+    if torch.cuda.is_available():
+        import mx_block_scaled_quantize_amd as mxa
+        return mxa
+    return pytest.importorskip("mx_block_scaled_quantize_amd")

@@ -9,12 +9,12 @@ import torch
 import workloads
 from oracle import formats as F
 from oracle import mx as omx
-from tests.gpu_util import (assert_bytes_equal, assert_float_equal, f32_of_input, host, upload_bf16_bits,
-                            upload_f16_from_f32, upload_f32, upload_u8)
+from tests.gpu_util import (assert_bytes_equal, assert_float_equal, f32_of_input, host, import_library,
+                            upload_bf16_bits, upload_f16_from_f32, upload_f32, upload_u8)
 
 pytestmark = pytest.mark.gpu
 
-mxa = pytest.importorskip("mx_block_scaled_quantize_amd")
+mxa = import_library()
 
 FP6 = ["e2m3", "e3m2"]
 RULES = ["floor", "ceil"]

@@ -19,11 +19,11 @@ import torch
 import workloads
 from oracle import gemm as og
 from oracle import mx as omx
-from tests.gpu_util import assert_bytes_equal, host, upload_bf16_bits, upload_f32, upload_u8
+from tests.gpu_util import assert_bytes_equal, host, upload_bf16_bits, upload_f32, upload_u8, import_library
 
 pytestmark = pytest.mark.gpu
 
-mxa = pytest.importorskip("mx_block_scaled_quantize_amd")
+mxa = import_library()
 
 FP32_TOL = 1e-3
 BF16_TOL = 1e-3

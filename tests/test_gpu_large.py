@@ -10,11 +10,11 @@ import torch
 from oracle import formats as F
 from oracle import gemm as og
 from oracle import mx as omx
-from tests.gpu_util import assert_bytes_equal, host
+from tests.gpu_util import assert_bytes_equal, host, import_library
 
 pytestmark = pytest.mark.gpu
 
-mxa = pytest.importorskip("mx_block_scaled_quantize_amd")
+mxa = import_library()
 
 
 def bf16_host_f32(t: torch.Tensor) -> np.ndarray:

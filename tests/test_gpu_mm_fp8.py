@@ -17,11 +17,11 @@ import torch
 import workloads
 from oracle import formats as ofmt
 from oracle import gemm as og
-from tests.gpu_util import assert_bytes_equal, host, upload_bf16_bits, upload_u8
+from tests.gpu_util import assert_bytes_equal, host, upload_bf16_bits, upload_u8, import_library
 
 pytestmark = pytest.mark.gpu
 
-mxa = pytest.importorskip("mx_block_scaled_quantize_amd")
+mxa = import_library()
 
 BF16_TOL = 1e-3
 ELEM_REL = 2.0 ** -10

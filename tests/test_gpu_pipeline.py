@@ -12,11 +12,11 @@ import workloads
 from oracle import delayed as odl
 from oracle import formats as ofmt
 from oracle import gemm as og
-from tests.gpu_util import host, upload_bf16_bits
+from tests.gpu_util import host, upload_bf16_bits, import_library
 
 pytestmark = pytest.mark.gpu
 
-mxa = pytest.importorskip("mx_block_scaled_quantize_amd")
+mxa = import_library()
 
 
 @pytest.mark.parametrize("shape", [(256, 384, 512), (512, 512, 1024)])

@@ -10,12 +10,12 @@ import workloads
 from oracle import delayed as odl
 from oracle import formats as F
 from oracle import mx as omx
-from tests.gpu_util import (assert_bytes_equal, assert_float_equal, f32_of_input, host, upload_bf16_bits,
-                            upload_f16_from_f32, upload_f32, upload_u8)
+from tests.gpu_util import (assert_bytes_equal, assert_float_equal, f32_of_input, host, import_library,
+                            upload_bf16_bits, upload_f16_from_f32, upload_f32, upload_u8)
 
 pytestmark = pytest.mark.gpu
 
-mxa = pytest.importorskip("mx_block_scaled_quantize_amd")
+mxa = import_library()
 
 FMTS = ["e4m3", "e5m2", "e2m1"]
 RULES = ["floor", "ceil"]

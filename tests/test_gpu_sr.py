@@ -9,11 +9,12 @@ import torch
 import workloads
 from oracle import mx as omx
 from oracle import sr as osr
-from tests.gpu_util import assert_bytes_equal, f32_of_input, host, upload_bf16_bits, upload_f16_from_f32, upload_f32
+from tests.gpu_util import (assert_bytes_equal, f32_of_input, host, import_library, upload_bf16_bits,
+                            upload_f16_from_f32, upload_f32)
 
 pytestmark = pytest.mark.gpu
 
-mxa = pytest.importorskip("mx_block_scaled_quantize_amd")
+mxa = import_library()
 
 RULES = ["floor", "ceil"]
 
