@@ -44,17 +44,23 @@ METRIC = "MX quantize GB/s (% HBM peak); MXFP8 GEMM TFLOP/s (% FP8 MFMA peak)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dual_bf16_kernel_mxfp8_bf16_8192x4096.md")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the quantizer sources with comments and blank space removed, so that
-    a comment-only edit keeps a counter summary valid and any code edit voids it."""
+def code_digest(texts) -> str:
+    """Hash of C++ source texts with comments and blank space removed, so that a
+    comment-only edit keeps a counter summary valid and any code edit voids it."""
     h = hashlib.sha256()
-    for f in ("quantize.hip", "mx_device.hpp"):
-        with open(os.path.join(ROOT, "mx_block_scaled_quantize_amd", "csrc", f)) as fh:
-            text = fh.read()
+    for text in texts:
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def kernel_source_hash() -> str:
+    texts = []
+    for f in ("quantize.hip", "mx_device.hpp"):
+        with open(os.path.join(ROOT, "mx_block_scaled_quantize_amd", "csrc", f)) as fh:
+            texts.append(fh.read())
+    return code_digest(texts)
 
 
 def measured_traffic():
