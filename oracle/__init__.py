@@ -38,7 +38,11 @@ Parity status: every public function is pinned by the CPU tests in
 independent library routines, invariants).  The pages print no worked numeric
 example, so no function is pinned to printed input/output pairs; the printed
 constants (E4M3 max 448, min 2^-9, E8M0 range, k = 32, 8 scale bits per block)
-are pinned in ``tests/golden/``.
+are pinned in ``tests/golden/``.  The packed storage of the sub-byte formats
+(E2M1 two per byte, element 2j in the low nibble; FP6 as a little-endian bit
+stream) is a reading, since the pages define no packing; it is pinned by
+hand-written literal bytes, and a planted high-nibble-first (FP4) or
+big-endian (FP6) packer must fail those pins.
 """
 
 from . import formats, mx, delayed, hadamard, gemm, sr  # noqa: F401

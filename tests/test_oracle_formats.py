@@ -89,6 +89,52 @@ def test_decode_fp6_tables(name):
     assert (f.max_value, f.min_subnormal) == ((7.5, 0.125) if name == "e2m3" else (28.0, 0.0625))
 
 
+def test_fp4_packing_is_a_little_endian_nibble_stream():
+    """E2M1 codes are packed two per byte, element 2j in the low nibble of byte j:
+    the same little-endian bit-stream rule as FP6, at 4 bits (the pages are silent
+    on the packing; this pins the reading, literal bytes written out by hand)."""
+    from oracle import mx
+    # codes 0x1, 0x2, 0xF, 0x0 -> bytes 0x21 (element 0 low, element 1 high), 0x0F
+    assert list(mx.pack_fp4(np.array([0x1, 0x2, 0xF, 0x0]))) == [0x21, 0x0F]
+    assert list(mx.pack_fp4(np.array([0x8, 0x7, 0x0, 0xC]))) == [0x78, 0xC0]
+    assert list(mx.unpack_fp4(np.array([0x21, 0x0F], dtype=np.uint8))) == [0x1, 0x2, 0xF, 0x0]
+    g = np.random.default_rng(8)
+    c = g.integers(0, 16, size=(5, 64)).astype(np.uint8)
+    p = mx.pack_fp4(c)
+    assert p.shape == (5, 32) and np.array_equal(mx.unpack_fp4(p), c)
+    # bit i of the stream is bit i % 4 of element i // 4
+    stream = np.unpackbits(p[0], bitorder="little")
+    assert np.array_equal(stream.reshape(64, 4), np.unpackbits(c[0][:, None], axis=1, bitorder="little")[:, :4])
+    # through the block quantizer: a block 1, -2, 6, 0.5, 0, ... (amax 6, scale 2^0) gives
+    # E2M1 codes 0x2, 0xC, 0x7, 0x1, 0, ... -> bytes 0xC2, 0x17, 0x00 ...
+    x = np.zeros((1, 32), np.float32)
+    x[0, :4] = [1.0, -2.0, 6.0, 0.5]
+    q, s = mx.quantize_rowwise(x, "e2m1", "ceil")
+    assert list(s[0]) == [127]
+    assert list(q[0]) == [0xC2, 0x17] + [0] * 14
+
+
+def test_planted_high_nibble_first_fp4_packing_is_caught(monkeypatch):
+    """A consistent pack / unpack pair with element 2j in the HIGH nibble passes
+    every round-trip check; the literal-byte pin must still reject it."""
+    from oracle import mx
+
+    def wrong_pack(codes):
+        c = np.asarray(codes).astype(np.uint8)
+        return (((c[..., 0::2] & 0xF) << 4) | (c[..., 1::2] & 0xF)).astype(np.uint8)
+
+    def wrong_unpack(packed):
+        p = np.asarray(packed).astype(np.uint8)
+        out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+        out[..., 0::2] = p >> 4
+        out[..., 1::2] = p & 0xF
+        return out
+    monkeypatch.setattr(mx, "pack_fp4", wrong_pack)
+    monkeypatch.setattr(mx, "unpack_fp4", wrong_unpack)
+    with pytest.raises(AssertionError):
+        test_fp4_packing_is_a_little_endian_nibble_stream()
+
+
 def test_fp6_packing_is_a_little_endian_bit_stream():
     from oracle import mx
     # codes 1, 2, 3, 4 -> 24-bit word 1 | 2 << 6 | 3 << 12 | 4 << 18 = 0x103081
