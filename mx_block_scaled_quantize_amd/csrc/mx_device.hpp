@@ -287,6 +287,17 @@ __device__ __forceinline__ void hadamard32_quad(float (&v)[8], uint32_t mask, in
 }
 
 
+// A NaN made by the transform's additions has no sign that IEEE 754 fixes (the
+// FP32 adders here and other hardware may differ), so the Hadamard paths clear
+// the sign bit of every NaN they encode; Inf and finite values keep theirs.
+// Only called on blocks already known to hold a non-finite value.
+template <int N>
+__device__ __forceinline__ void clear_nan_signs(float (&v)[N]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = abs_bits(v[j]) > 0x7F800000u ? __uint_as_float(abs_bits(v[j])) : v[j];
+}
+
+
 // ---------------------------------------------------------------------------
 // gfx950 scaled pair converts (V_CVT_SCALEF32_PK_{FP8,BF8,FP4}_{F32,BF16}).
 // Measured against the CPU oracle on every BF16 value at several scales: for

@@ -16,7 +16,10 @@ reading taken here:
 * every addition is one FP32 operation rounded to nearest even, in exactly that
   order (so a GPU doing the same additions reproduces the bits);
 * both GEMM operands get the same transform along the reduction axis; since
-  H32 H32^T = 32 I, the GEMM multiplies its result by alpha = 1/32.
+  H32 H32^T = 32 I, the GEMM multiplies its result by alpha = 1/32;
+* a NaN produced by the additions (from a NaN input, or Inf - Inf) has no sign
+  that IEEE 754 fixes, so every NaN leaving the transform has its sign bit
+  cleared; Inf and finite results keep their signs.
 """
 
 import numpy as np
@@ -41,4 +44,5 @@ def hadamard32(blocks, sign_mask: int) -> np.ndarray:
                 v[..., i] = a + b          # float32 + float32 -> float32, RNE
                 v[..., i + h] = a - b
         h *= 2
-    return v
+    bits = v.view(np.uint32)
+    return np.where(np.isnan(v), (bits & np.uint32(0x7FFFFFFF)).view(np.float32), v)

@@ -61,6 +61,46 @@ def test_hadamard_mask_zero_is_plain_fwht_and_identity_twice():
     assert np.array_equal(y, 32 * x)
 
 
+def test_hadamard_nonfinite_signs():
+    """Non-finite inputs: an Inf propagates as +-Inf with the signs of its column
+    of H32 (an IEEE-defined sign); a NaN, or Inf - Inf, makes NaNs, which leave
+    the transform with a clear sign bit whatever the input NaN's sign."""
+    H = scipy.linalg.hadamard(32)
+    x = np.zeros((3, 32), np.float32)
+    x[0, 5] = np.inf                             # column 5 of H32, times +Inf
+    x[1, 9] = -np.float32(np.nan)                # a NaN with its sign bit set
+    x[2, 3], x[2, 4] = np.inf, np.inf            # +Inf +- Inf: NaN where H32's signs differ
+    y = hadamard.hadamard32(x, 0)
+    assert np.array_equal(y[0], np.where(H[:, 5] > 0, np.inf, -np.inf).astype(np.float32))
+    assert np.isnan(y[1]).all() and not np.signbit(y[1]).any()
+    differ = H[:, 3] != H[:, 4]
+    assert np.isnan(y[2][differ]).all() and not np.signbit(y[2][differ]).any()
+    assert np.array_equal(y[2][~differ], np.where(H[~differ, 3] > 0, np.inf, -np.inf).astype(np.float32))
+    # through the MX quantizer: a NaN block's codes are the positive NaN code (E2M1: +6)
+    q, s = mx.quantize_rowwise(x[1:2], "e4m3", "ceil", hadamard_mask=0xFFFFFFFF)
+    assert list(s[0]) == [0xFF] and (q == 0x7F).all()
+    q, s = mx.quantize_rowwise(x[1:2], "e2m1", "ceil", hadamard_mask=0)
+    assert list(s[0]) == [0xFF] and (mx.unpack_fp4(q) == 0x7).all()
+
+
+def test_planted_nan_sign_passthrough_is_caught(monkeypatch):
+    """An oracle that leaves the sign of the NaNs numpy's additions produce must
+    fail the pin above (numpy keeps the input NaN's sign bit through a + b)."""
+    def passthrough(blocks, sign_mask):
+        v = hadamard.sign_flip(blocks, sign_mask).copy()
+        h = 1
+        while h < 32:
+            for i in range(32):
+                if i & h == 0:
+                    a, b = v[..., i].copy(), v[..., i + h].copy()
+                    v[..., i], v[..., i + h] = a + b, a - b
+            h *= 2
+        return v
+    monkeypatch.setattr(hadamard, "hadamard32", passthrough)
+    with pytest.raises(AssertionError):
+        test_hadamard_nonfinite_signs()
+
+
 # ---------------------------------------------------------------- GEMM
 
 def _quantized_pair(M, N, K, fa, fb, rule="ceil", seed=0):
