@@ -79,9 +79,11 @@ typedef enum { MX_ROWWISE = 0, MX_COLWISE_T = 1 } mx_orient_t;
  * quantize_dual): q [rows][cols], qT [cols][rows], or both from one read. */
 typedef enum { FP8_ROW = 0, FP8_TRANSPOSED = 1, FP8_DUAL = 2 } fp8_layout_t;
 
-/* Size of the delayed-scaling ring state of fp8_quantize_delayed, in FP32 words. */
-#define MX_RING_TICKET_WORDS 4096
-#define MX_RING_WORDS(hist_len) ((hist_len) + 4 + MX_RING_TICKET_WORDS)
+/* Size of the delayed-scaling ring state of fp8_quantize_delayed, in FP32 words
+ * ([FP8PY] quantize() docstring: ring_state is [hist n | scale | legacy | amax | done]). */
+#define MX_RING_WORDS(hist_len) ((hist_len) + 4)
+/* Size of the optional ticket scratch of fp8_quantize_delayed, in uint32 words. */
+#define MX_TICKET_WORDS 4096
 
 typedef enum {
   MX_OK = 0,
@@ -140,17 +142,25 @@ mx_status_t mx_quantize_dual(const void* x, mx_dtype_t in, int64_t rows, int64_t
 /* Per-tensor FP8 quantization with delayed scaling ([FP8PY] quantize /
  * quantize_dual with ring_state, and its commit message).
  *
- * ring: caller-owned FP32 device buffer of MX_RING_WORDS(hist_len) words,
- *   [hist[0..hist_len-1] | s | m | amax | ticket | MX_RING_TICKET_WORDS counters]
- * where s is the dequantization scale (x ~ q * s), m = 1/s is the multiplier the
- * cast uses, and the amax, ticket and counter words are scratch that must read 0
- * before the first call (initialise the buffer to hist = 0, s = m = 1, the rest
- * 0); every call leaves them 0 again.  The counter words hold 128 groups of
- * (max, ticket) pairs, one group per 128-byte line, that spread the
- * per-workgroup ticket over several cache lines, because atomics on one line
- * serialize; the first hist_len + 4 words are the page's
- * [hist | scale | legacy | amax | done].  The buffer must be 128-byte aligned
- * past those first words for the spreading to pay off (any alignment is correct).
+ * ring: caller-owned FP32 device buffer of MX_RING_WORDS(hist_len) = hist_len + 4
+ *   words, the page's [hist n | scale | legacy | amax | done]:
+ *     hist[0 .. hist_len-1]  the amax history;
+ *     s       the dequantization scale (x ~ q * s);
+ *     m       ("legacy") the multiplier the cast uses, m = 1 / s;
+ *     amax    scratch that must read 0 before the first call;
+ *     ticket  (uint32 bits) scratch that must read 0 before the first call.
+ *   Initialise it to hist = 0, s = m = 1, amax = ticket = 0; every call leaves the
+ *   amax and ticket words 0 again.  4-byte aligned.
+ * ticket_scratch: optional (NULL allowed) caller-owned uint32 device buffer of
+ *   MX_TICKET_WORDS words, all 0 before the first call and left 0 by every call.
+ *   It holds 128 groups of (max, ticket) pairs, one group per 128-byte line,
+ *   that spread the per-workgroup ticket over many cache lines, because atomics
+ *   on one line serialize.  With NULL every workgroup takes its ticket on the
+ *   ring's own amax and ticket words, and the launch caps the grid at a few
+ *   hundred persistent workgroups to bound that queue; the codes and the ring
+ *   are the same either way, only the time differs.  4-byte aligned (128-byte
+ *   alignment keeps each group on one line).  One scratch buffer may serve many
+ *   rings, but not two calls in flight at once.
  *
  * Each call: y = fl32(x * m) with the m the ring holds at launch, q = RNE +
  * saturating cast of y to `fmt` (Inf saturates, NaN gives NaN), written as
@@ -158,8 +168,8 @@ mx_status_t mx_quantize_dual(const void* x, mx_dtype_t in, int64_t rows, int64_t
  * atomic ticket) then sets hist[hist_idx] = a, h = max(hist), and when
  * 0 < h < Inf publishes s = fl32(fl32(h / fp8_max) / margin), m = fl32(1 / s)
  * (correctly rounded FP32 divisions); otherwise s and m stay.  The next call on
- * the same ring sees the new m.  Calls sharing a ring must be ordered (same
- * stream or explicit events).
+ * the same ring sees the new m.  Calls sharing a ring (or a ticket scratch)
+ * must be ordered (same stream or explicit events).
  *
  *   fmt      MX_E4M3 or MX_E5M2.
  *   q, qT    outputs: q [rows][cols] for FP8_ROW, qT [cols][rows] for
@@ -167,11 +177,16 @@ mx_status_t mx_quantize_dual(const void* x, mx_dtype_t in, int64_t rows, int64_t
  *   hist_len 1..4096; 0 <= hist_idx < hist_len; fp8_max and margin finite > 0.
  *   amax_out optional: receives a.
  * Shapes: FP8_ROW needs cols % 8 == 0; FP8_TRANSPOSED and FP8_DUAL need
- * rows % 32 == 0 and cols % 8 == 0.  An empty input still folds (a = 0). */
+ * rows % 32 == 0 and cols % 8 == 0.  An empty input still folds (a = 0).
+ * Errors, returned before any launch: MX_ERR_UNSUPPORTED (in, fmt, layout),
+ * MX_ERR_SHAPE, MX_ERR_NULL (ring, or an output or x the layout needs),
+ * MX_ERR_ARG (hist_len, hist_idx, fp8_max, margin), MX_ERR_ALIGN (x, q, qT not
+ * 16-byte aligned; ring or ticket_scratch not 4-byte aligned); MX_ERR_LAUNCH. */
 mx_status_t fp8_quantize_delayed(const void* x, mx_dtype_t in, int64_t rows, int64_t cols,
                                  mx_elem_t fmt, fp8_layout_t layout, uint8_t* q, uint8_t* qT,
                                  float* ring, int hist_len, int hist_idx, float fp8_max,
-                                 float margin, float* amax_out, hipStream_t stream);
+                                 float margin, float* amax_out, uint32_t* ticket_scratch,
+                                 hipStream_t stream);
 
 /* MX dequantization ([UE8M0] first part, section 2: decoding an E8M0 scale is an
  * exponent shift): out = Q_i * 2^(c - 127), computed exactly and rounded once to

@@ -12,7 +12,7 @@ The functions carry the names of the C entry points declared in
 
     mx_quantize(x, fmt, rule, orient, hadamard_mask=None, amax=False)
     mx_quantize_dual(x, fmt, rule, amax=False)
-    fp8_quantize_delayed(x, ring, hist_idx, fmt, layout, fp8_max, margin, amax=False)
+    fp8_quantize_delayed(x, ring, hist_idx, fmt, layout, fp8_max, margin, amax=False, tickets=None)
     mx_dequantize(q, scales, rows, cols, fmt, orient, out_dtype)
     mx_gemm(a, sa, b, sb, fmt_a, fmt_b, alpha, out_dtype)
     mx_quantize_sr(x, rand, rule, amax=False)
@@ -45,17 +45,17 @@ LAYOUT = {"row": 0, "transposed": 1, "dual": 2}
 STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN", 4: "MX_ERR_UNSUPPORTED",
           5: "MX_ERR_LAUNCH", 6: "MX_ERR_ARG"}
 DEFAULT_FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
-RING_TICKET_WORDS = 4096        # MX_RING_TICKET_WORDS
+TICKET_WORDS = 4096             # MX_TICKET_WORDS
 
 
 def ring_words(hist_len: int) -> int:
-    """MX_RING_WORDS(hist_len): [hist | s | m | amax | ticket | ticket counters]."""
-    return hist_len + 4 + RING_TICKET_WORDS
+    """MX_RING_WORDS(hist_len): [hist | s | m | amax | ticket]."""
+    return hist_len + 4
 
 _p, _i64, _i32, _u32, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32, ctypes.c_float
 lib.mx_quantize.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _u32, _p, _p, _p, _p]
 lib.mx_quantize_dual.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p]
-lib.fp8_quantize_delayed.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _p, _p, _p, _i32, _i32, _f32, _f32, _p, _p]
+lib.fp8_quantize_delayed.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _p, _p, _p, _i32, _i32, _f32, _f32, _p, _p, _p]
 lib.mx_dequantize.argtypes = [_p, _p, _i64, _i64, _i32, _i32, _i32, _p, _i32, _p]
 lib.mx_gemm.argtypes = [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64, _f32, _p, _i32, _i64, _p]
 lib.mx_quantize_sr.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p]
@@ -214,20 +214,32 @@ def mx_gemm_requant(a, sa, b, sb, fmt_a="e4m3", fmt_b="e4m3", alpha=1.0, fmt_c="
 
 
 def new_ring(hist_len: int, device="cuda") -> torch.Tensor:
-    """A fresh delayed-scaling ring: [hist (zeros) | s = 1 | m = 1 | amax = 0 | ticket = 0 | counters = 0]."""
+    """A fresh delayed-scaling ring: [hist (zeros) | s = 1 | m = 1 | amax = 0 | ticket = 0]."""
     r = torch.zeros(ring_words(hist_len), dtype=torch.float32, device=device)
     r[hist_len] = 1.0
     r[hist_len + 1] = 1.0
     return r
 
 
-def fp8_quantize_delayed(x, ring, hist_idx, fmt="e4m3", layout="transposed", fp8_max=None, margin=1.0, amax=False):
+def new_tickets(device="cuda") -> torch.Tensor:
+    """Zeroed ticket scratch for fp8_quantize_delayed (MX_TICKET_WORDS uint32 words).
+    Every call leaves it zero, so one buffer serves any number of ordered calls."""
+    return torch.zeros(TICKET_WORDS, dtype=torch.int32, device=device)
+
+
+def fp8_quantize_delayed(x, ring, hist_idx, fmt="e4m3", layout="transposed", fp8_max=None, margin=1.0, amax=False,
+                         tickets=None):
     """Per-tensor FP8 cast with the ring's multiplier, then the on-device ring
-    fold.  Returns (q or None, qT or None[, amax])."""
+    fold.  ``tickets`` (from new_tickets) spreads the workgroups' ticket over
+    many cache lines; None takes it on the ring's own words (same result, slower
+    on large tensors).  Returns (q or None, qT or None[, amax])."""
     _check_2d(x)
     R, C = x.shape
-    if ring.dtype != torch.float32 or ring.dim() != 1 or not ring.is_contiguous():
-        raise ValueError("ring must be a contiguous 1-D float32 tensor")
+    if ring.dtype != torch.float32 or ring.dim() != 1 or not ring.is_contiguous() or ring.numel() < 5:
+        raise ValueError("ring must be a contiguous 1-D float32 tensor of hist_len + 4 words")
+    if tickets is not None and (tickets.element_size() != 4 or tickets.numel() < TICKET_WORDS
+                                or not tickets.is_contiguous()):
+        raise ValueError("tickets must be a contiguous tensor of MX_TICKET_WORDS 32-bit words")
     lay = _lookup(LAYOUT, layout, "layout")
     f = _lookup(FMT, fmt, "format")
     if fp8_max is None:
@@ -236,9 +248,8 @@ def fp8_quantize_delayed(x, ring, hist_idx, fmt="e4m3", layout="transposed", fp8
     qT = torch.empty((C, R), dtype=torch.uint8, device=x.device) if layout != "row" else None
     a = torch.empty(1, dtype=torch.float32, device=x.device) if amax else None
     check(lib.fp8_quantize_delayed(_ptr(x), _lookup(DTYPE, x.dtype, "dtype"), R, C, f, lay, _ptr(q), _ptr(qT),
-                                   _ptr(ring), ring.numel() - 4 - RING_TICKET_WORDS, int(hist_idx), float(fp8_max),
-                                   float(margin),
-                                   _ptr(a), _stream(x)))
+                                   _ptr(ring), ring.numel() - 4, int(hist_idx), float(fp8_max), float(margin),
+                                   _ptr(a), _ptr(tickets), _stream(x)))
     return (q, qT, a) if amax else (q, qT)
 
 

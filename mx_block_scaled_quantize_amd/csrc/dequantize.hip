@@ -252,4 +252,4 @@ extern "C" const char* mx_status_str(mx_status_t s) {
   return "unknown mx_status_t";
 }
 
-extern "C" int mx_abi_version(void) { return 101; }
+extern "C" int mx_abi_version(void) { return 200; }

@@ -148,6 +148,9 @@ __device__ __forceinline__ uint32_t row_chunk_mx(const uint4 (&c)[ChunkWords<IN>
     for (int j = 0; j < 8; ++j) m = umax(m, abs_bits(v[j]));
   }
   const uint32_t bmax = quad_max(m);
+  if constexpr (HAD) {
+    if (bmax >= 0x7F800000u) clear_nan_signs(v);
+  }
   if constexpr (IN == IN_BF16 && R == CEIL && !HAD) {
     // no element exceeds the format maximum under the round-up rule: convert the
     // BF16 pairs directly
@@ -216,44 +219,55 @@ __global__ __launch_bounds__(kRowThreads) void rowwise_kernel(const void* __rest
 // Delayed-scaling ring fold, run by the last workgroup of a per-tensor kernel
 // ---------------------------------------------------------------------------
 struct RingArgs {
-  float* ring;          // [hist | s | m | amax | ticket]
+  float* ring;          // [hist | s | m | amax | ticket], hist_len + 4 words
+  uint32_t* tickets;    // optional spread-ticket scratch (MX_TICKET_WORDS words), or null
   int hist_len, hist_idx;
   float fp8_max, margin;
   float* amax_out;      // optional copy of this call's amax
 };
 
-// The fold is reached through a two-level ticket taken by every workgroup
-// (thread 0):
+// The fold is reached through a ticket taken by every workgroup (thread 0).
+// With ticket scratch it is two-level:
 //   1. as soon as the workgroup knows its max |x|, it posts it to the max word
 //      of its group (workgroup id modulo 128) -- an atomic max, sent only when
 //      an atomic read shows that it can raise the word (the word only grows);
-//   2. after its stores, it increments its group's ticket, an increment that
-//      depends on the value step 1 returned, so it is issued only after that
-//      max has been performed (or found to be covered);
+//   2. it increments its group's ticket, an increment whose operand depends on
+//      the value step 1 returned and on the multiplier the workgroup read, so
+//      it is issued only after that max has been performed (or found to be
+//      covered) and after the multiplier has been read;
 //   3. the group's last arrival reads the group max (an RMW), clears the group
 //      words, posts the group max to the top amax word and takes a top ticket
 //      (again dependent RMWs);
 //   4. the last top ticket reads the overall max, folds it into the history,
 //      publishes s and m = 1/s and clears the top words.
+// Without scratch, steps 1-2 use the ring's own amax and ticket words and the
+// first arrival at step 2 that completes the count goes straight to step 4.
 // Atomics on one cache line serialize (about 12 ns each on MI355X, more under
 // load) while different lines proceed in parallel, so every group sits on a
-// 128-byte line of its own, and splitting the chain keeps the round trips
-// behind the workgroup's stores instead of after them.
+// 128-byte line of its own; the single-word mode is kept to few workgroups by
+// the launch (persistent grids, see kNullTicketGrid).
 constexpr unsigned kTicketGroups = 128;
-constexpr unsigned kTicketStride = MX_RING_TICKET_WORDS / kTicketGroups;   // 32 words = 128 bytes
+constexpr unsigned kTicketStride = MX_TICKET_WORDS / kTicketGroups;   // 32 words = 128 bytes
 static_assert(kTicketStride >= 2, "a group needs a max and a ticket word");
+// Grid cap of the per-tensor kernels when the caller passes no ticket scratch:
+// every workgroup then takes its ticket on one word.
+constexpr int64_t kNullTicketGrid = 512;
 
 struct RingTicket {
   uint32_t* gmax;
   uint32_t* gctr;
   unsigned members;    // workgroups in this group
+  bool two_level;
 };
 
 __device__ __forceinline__ RingTicket ring_ticket(const RingArgs& r, unsigned wg, unsigned num_wg) {
-  uint32_t* scratch = reinterpret_cast<uint32_t*>(r.ring + r.hist_len + 4);
+  if (r.tickets == nullptr) {
+    uint32_t* top = reinterpret_cast<uint32_t*>(r.ring + r.hist_len + 2);
+    return RingTicket{top, top + 1, num_wg, false};
+  }
   const unsigned g = wg % kTicketGroups;
-  return RingTicket{scratch + g * kTicketStride, scratch + g * kTicketStride + 1,
-                    num_wg / kTicketGroups + (g < num_wg % kTicketGroups ? 1u : 0u)};
+  return RingTicket{r.tickets + g * kTicketStride, r.tickets + g * kTicketStride + 1,
+                    num_wg / kTicketGroups + (g < num_wg % kTicketGroups ? 1u : 0u), true};
 }
 
 // step 1: returns the value the ticket increment will depend on
@@ -263,23 +277,38 @@ __device__ __forceinline__ uint32_t ring_post_max(const RingTicket& t, uint32_t 
   return __hip_atomic_fetch_max(t.gmax, wg_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// steps 2-4
-__device__ __forceinline__ void ring_finish(const RingArgs& r, const RingTicket& t, uint32_t posted,
+// 0, produced by an instruction that reads v: an operand built from it makes the
+// consumer wait until v's load has returned (a data dependency the compiler cannot fold).
+__device__ __forceinline__ uint32_t zero_after(uint32_t v) {
+  uint32_t z;
+  asm volatile("v_and_b32 %0, 0, %1" : "=v"(z) : "v"(v));
+  return z;
+}
+
+// Ticket increment of a posted value (never 0xFFFFFFFF, a NaN-free magnitude:
+// the increment is always 1) that also depends on the multiplier bits.
+__device__ __forceinline__ uint32_t ticket_inc(uint32_t posted, float mult) {
+  return (posted == 0xFFFFFFFFu ? 2u : 1u) + zero_after(__float_as_uint(mult));
+}
+
+// steps 2-4 (mult: the multiplier this workgroup read from the ring)
+__device__ __forceinline__ void ring_finish(const RingArgs& r, const RingTicket& t, uint32_t posted, float mult,
                                             unsigned num_wg) {
-  // posted never holds 0xFFFFFFFF (a NaN-free magnitude): every increment is 1
-  const uint32_t tg = __hip_atomic_fetch_add(t.gctr, posted == 0xFFFFFFFFu ? 2u : 1u, __ATOMIC_RELAXED,
+  const uint32_t tg = __hip_atomic_fetch_add(t.gctr, ticket_inc(posted, mult), __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
   if (tg != t.members - 1) return;
-  const uint32_t gm = __hip_atomic_fetch_or(t.gmax, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(t.gmax, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(t.gctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint32_t* amax_slot = reinterpret_cast<uint32_t*>(r.ring + r.hist_len + 2);
   uint32_t* ticket = reinterpret_cast<uint32_t*>(r.ring + r.hist_len + 3);
-  const uint32_t tm = __hip_atomic_fetch_max(amax_slot, gm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const unsigned ngroups = num_wg < kTicketGroups ? num_wg : kTicketGroups;
-  const uint32_t tt = __hip_atomic_fetch_add(ticket, tm == 0xFFFFFFFFu ? 2u : 1u, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-  if (tt != ngroups - 1) return;
+  if (t.two_level) {
+    const uint32_t gm = __hip_atomic_fetch_or(t.gmax, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(t.gmax, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(t.gctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t tm = __hip_atomic_fetch_max(amax_slot, gm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned ngroups = num_wg < kTicketGroups ? num_wg : kTicketGroups;
+    const uint32_t tt = __hip_atomic_fetch_add(ticket, tm == 0xFFFFFFFFu ? 2u : 1u, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+    if (tt != ngroups - 1) return;
+  }
   const uint32_t ab = __hip_atomic_fetch_or(amax_slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const float amax = __uint_as_float(ab);
   float* hist = r.ring;
@@ -334,34 +363,36 @@ __global__ __launch_bounds__(kPtRowThreads) void pt_row_kernel(const void* __res
   bool slow;
   const float mult = ring_multiplier(r, slow);
   uint32_t tmax = 0;
-  const int64_t b = int64_t(blockIdx.x) * kPtRowThreads * kRowUnroll;
-  uint4 raw[kRowUnroll][kW];
-#pragma unroll
-  for (int u = 0; u < kRowUnroll; ++u) {
-    const int64_t c = b + u * kPtRowThreads + threadIdx.x;
-#pragma unroll
-    for (int k = 0; k < kW; ++k) raw[u][k] = make_uint4(0, 0, 0, 0);
-    if (c < nchunks) load_chunk_nt<IN>(x, c * 8, raw[u]);
-  }
-  uint32_t w[kRowUnroll][Words<F, 8>::kN];
-#pragma unroll
-  for (int u = 0; u < kRowUnroll; ++u) {
-    float v[8];
-    widen_chunk<IN>(raw[u], v);
-    const uint32_t m = chunk_absmax<IN>(raw[u], v);
-    tmax = amax_update(tmax, m, v);
-    pt_encode_f32<F, 8>(v, mult, slow ? 0x7FFFFFFFu : m, w[u]);
-  }
   const RingTicket tk = ring_ticket(r, blockIdx.x, gridDim.x);
-  const uint32_t bm = block_max<kPtRowThreads>(tmax);
-  uint32_t posted = 0;
-  if (threadIdx.x == 0) posted = ring_post_max(tk, bm);
+  // one block of kPtRowThreads * kRowUnroll chunks per iteration; the grid covers
+  // the input in one pass unless the launch caps it (no ticket scratch)
+  for (int64_t b = int64_t(blockIdx.x) * kPtRowThreads * kRowUnroll; b < nchunks;
+       b += int64_t(gridDim.x) * kPtRowThreads * kRowUnroll) {
+    uint4 raw[kRowUnroll][kW];
 #pragma unroll
-  for (int u = 0; u < kRowUnroll; ++u) {
-    const int64_t c = b + u * kPtRowThreads + threadIdx.x;
-    if (c < nchunks) store_row8<F>(q, c * 8, w[u]);
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int64_t c = b + u * kPtRowThreads + threadIdx.x;
+#pragma unroll
+      for (int k = 0; k < kW; ++k) raw[u][k] = make_uint4(0, 0, 0, 0);
+      if (c < nchunks) load_chunk_nt<IN>(x, c * 8, raw[u]);
+    }
+    uint32_t w[kRowUnroll][Words<F, 8>::kN];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      float v[8];
+      widen_chunk<IN>(raw[u], v);
+      const uint32_t m = chunk_absmax<IN>(raw[u], v);
+      tmax = amax_update(tmax, m, v);
+      pt_encode_f32<F, 8>(v, mult, slow ? 0x7FFFFFFFu : m, w[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int64_t c = b + u * kPtRowThreads + threadIdx.x;
+      if (c < nchunks) store_row8<F>(q, c * 8, w[u]);
+    }
   }
-  if (threadIdx.x == 0) ring_finish(r, tk, posted, gridDim.x);
+  const uint32_t bm = block_max<kPtRowThreads>(tmax);
+  if (threadIdx.x == 0) ring_finish(r, tk, ring_post_max(tk, bm), mult, gridDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -466,6 +497,7 @@ __device__ __forceinline__ uint32_t col_encode(const typename LdsWord<IN>::T* __
     cmax = 0;
 #pragma unroll
     for (int i = 0; i < 32; ++i) cmax = umax(cmax, abs_bits(cv[i]));
+    if (cmax >= 0x7F800000u) clear_nan_signs(cv);
     return mx_encode_f32<F, R, 32>(cv, cmax, w);
   } else {
     // the scale (or the per-tensor multiplier) is known: convert 16 values at a time
@@ -656,7 +688,7 @@ __global__ __launch_bounds__(64 * kStripWaves) void strip_kernel(StripArgs a) {
 
   if constexpr (kPT) {
     // an empty input runs no supertile: post nothing, still take the ticket
-    if (threadIdx.x == 0) ring_finish(a.ring, tk, posted, gridDim.x);
+    if (threadIdx.x == 0) ring_finish(a.ring, tk, posted, mult, gridDim.x);
   } else if constexpr (AMAX) {
     // ---- per-tensor amax: one (conditional) atomic per workgroup
     const uint32_t m = wave_max(tmax);
@@ -903,11 +935,12 @@ __global__ __launch_bounds__(256) void dual_bf16_kernel(StripArgs a, int tiles_c
 // across it).  The transposed codes are staged in LDS and leave as 16-byte
 // pieces of whole column lines; the W scales of a column leave as one store.
 
-// General MX encoding of 8 FP32 values of one block (non-finite or subnormal
-// amax).  Out of line: rare.
+// General MX encoding of 8 FP32 values of one transformed block (non-finite or
+// subnormal amax; NaNs made by the transform get a clear sign bit).  Out of line: rare.
 template <int F, int R>
 __device__ __attribute__((noinline)) uint2 col_encode8_general(float4 lo, float4 hi, uint32_t bmax) {
-  const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  if (bmax >= 0x7F800000u) clear_nan_signs(v);
   uint32_t w[Words<F, 8>::kN];
   mx_encode_f32<F, R, 8>(v, bmax, w);
   if constexpr (Words<F, 8>::kN == 2) return make_uint2(w[0], w[1]);
@@ -1082,7 +1115,7 @@ __global__ __launch_bounds__(64 * ColTile<F>::kWaves) void col_bf16_kernel(Strip
 constexpr int kPtTile = 128, kPtWave = 64;
 
 template <int F>
-__global__ __launch_bounds__(256) void pt_col_bf16_kernel(StripArgs a, int tiles_c) {
+__global__ __launch_bounds__(256) void pt_col_bf16_kernel(StripArgs a, int tiles_c, int ntiles) {
   __shared__ __attribute__((aligned(16))) uint8_t qc_lds[kPtTile * kPtTile];   // [tile column][tile row]
   __shared__ uint32_t red[4];
   const int lane = threadIdx.x & 63;
@@ -1091,68 +1124,74 @@ __global__ __launch_bounds__(256) void pt_col_bf16_kernel(StripArgs a, int tiles
   bool pt_slow;
   const float mult = ring_multiplier(a.ring, pt_slow);
   const RingTicket tk = ring_ticket(a.ring, blockIdx.x, gridDim.x);
-  const int t = blockIdx.x;
-  const int64_t tr = int64_t(t / tiles_c) * kPtTile, tc = int64_t(t % tiles_c) * kPtTile;
   const int wro = (wave >> 1) * kPtWave, wco = (wave & 1) * kPtWave;       // wave offset in the tile
-  // rows are a multiple of 32 and cols of 8: a lane's 8 x 8 block is in or out
-  const bool ok = tr + wro + 8 * h < a.rows && tc + wco + 8 * g < a.cols;
-  uint32_t tmax = 0;
-  if (ok) {
-    // the wave's origin is uniform: a scalar base plus a 32-bit lane offset
-    // (the host keeps 64 * cols * 2 below 2^32)
-    const uint8_t* xb = static_cast<const uint8_t*>(a.x) + ((tr + wro) * a.cols + tc + wco) * 2;
-    const uint32_t cols = uint32_t(a.cols);
-    uint4 raw[8];
+  uint32_t tmax = 0, posted = 0;
+  // one tile per workgroup, unless the launch caps the grid (no ticket scratch)
+  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t tr = int64_t(t / tiles_c) * kPtTile, tc = int64_t(t % tiles_c) * kPtTile;
+    // rows are a multiple of 32 and cols of 8: a lane's 8 x 8 block is in or out
+    const bool ok = tr + wro + 8 * h < a.rows && tc + wco + 8 * g < a.cols;
+    if (ok) {
+      // the wave's origin is uniform: a scalar base plus a 32-bit lane offset
+      // (the host keeps 64 * cols * 2 below 2^32)
+      const uint8_t* xb = static_cast<const uint8_t*>(a.x) + ((tr + wro) * a.cols + tc + wco) * 2;
+      const uint32_t cols = uint32_t(a.cols);
+      uint4 raw[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32x4_t v = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4_t*>(xb + (uint32_t(8 * h + i) * cols + uint32_t(8 * g)) * 2u));
-      raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
+      for (int i = 0; i < 8; ++i) {
+        const u32x4_t v = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(xb + (uint32_t(8 * h + i) * cols + uint32_t(8 * g)) * 2u));
+        raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      // max |x| of columns 2d (low half) and 2d+1 (high half) over the lane's 8 rows
-      uint32_t mp = 0;
+      for (int d = 0; d < 4; ++d) {
+        // max |x| of columns 2d (low half) and 2d+1 (high half) over the lane's 8 rows
+        uint32_t mp = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) mp = pk_umax16(mp, u4_word(raw[i], d) & 0x7FFF7FFFu);
+        for (int i = 0; i < 8; ++i) mp = pk_umax16(mp, u4_word(raw[i], d) & 0x7FFF7FFFu);
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const uint32_t cmax = k ? (mp & 0xFFFF0000u) : (mp << 16);
-        float v[8];
+        for (int k = 0; k < 2; ++k) {
+          const uint32_t cmax = k ? (mp & 0xFFFF0000u) : (mp << 16);
+          float v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t x = u4_word(raw[i], d);
-          v[i] = __uint_as_float(k ? (x & 0xFFFF0000u) : (x << 16));
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t x = u4_word(raw[i], d);
+            v[i] = __uint_as_float(k ? (x & 0xFFFF0000u) : (x << 16));
+          }
+          if (cmax <= 0x7F800000u) {
+            tmax = umax(tmax, cmax);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) tmax = umax(tmax, abs_bits_no_nan(v[i]));
+          }
+          uint32_t w[2];
+          pt_encode_f32<F, 8>(v, mult, pt_slow ? 0x7FFFFFFFu : cmax, w);
+          *reinterpret_cast<u32x2_t*>(qc_lds + (wco + 8 * g + 2 * d + k) * kPtTile + wro + 8 * h) =
+              u32x2_t{w[0], w[1]};
         }
-        if (cmax <= 0x7F800000u) {
-          tmax = umax(tmax, cmax);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) tmax = umax(tmax, abs_bits_no_nan(v[i]));
-        }
-        uint32_t w[2];
-        pt_encode_f32<F, 8>(v, mult, pt_slow ? 0x7FFFFFFFu : cmax, w);
-        *reinterpret_cast<u32x2_t*>(qc_lds + (wco + 8 * g + 2 * d + k) * kPtTile + wro + 8 * h) = u32x2_t{w[0], w[1]};
       }
     }
-  }
-  const uint32_t wm = wave_max(tmax);
-  if (lane == 0) red[wave] = wm;
-  __syncthreads();
-  // post the workgroup's max now; the dependent ticket is taken after the stores
-  uint32_t posted = 0;
-  if (threadIdx.x == 0) posted = ring_post_max(tk, umax(umax(red[0], red[1]), umax(red[2], red[3])));
-  // transposed codes: 8 consecutive threads per 128-byte line (column c, 128 rows)
-#pragma unroll
-  for (int it = 0; it < kPtTile * kPtTile / 16 / 256; ++it) {
-    const int item = threadIdx.x + 256 * it;
-    const int c = item >> 3, pc = item & 7;
-    if (tc + c < a.cols && tr + 16 * pc < a.rows) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qc_lds + c * kPtTile + 16 * pc);
-      *reinterpret_cast<uint4*>(a.q_col + (tc + c) * a.rows + tr + 16 * pc) = v;
+    const bool last = t + int(gridDim.x) >= ntiles;
+    if (last) {
+      const uint32_t wm = wave_max(tmax);
+      if (lane == 0) red[wave] = wm;
     }
+    __syncthreads();
+    // post the workgroup's max now; the dependent ticket is taken after the stores
+    if (last && threadIdx.x == 0) posted = ring_post_max(tk, umax(umax(red[0], red[1]), umax(red[2], red[3])));
+    // transposed codes: 8 consecutive threads per 128-byte line (column c, 128 rows)
+#pragma unroll
+    for (int it = 0; it < kPtTile * kPtTile / 16 / 256; ++it) {
+      const int item = threadIdx.x + 256 * it;
+      const int c = item >> 3, pc = item & 7;
+      if (tc + c < a.cols && tr + 16 * pc < a.rows) {
+        const uint4 v = *reinterpret_cast<const uint4*>(qc_lds + c * kPtTile + 16 * pc);
+        *reinterpret_cast<uint4*>(a.q_col + (tc + c) * a.rows + tr + 16 * pc) = v;
+      }
+    }
+    if (!last) __syncthreads();   // the staging buffer is reused by the next tile
   }
-  if (threadIdx.x == 0) ring_finish(a.ring, tk, posted, gridDim.x);
+  if (threadIdx.x == 0) ring_finish(a.ring, tk, posted, mult, gridDim.x);
 }
 
 template <typename K, typename... Args>
@@ -1209,6 +1248,7 @@ static mx_status_t launch_strips(K kernel, const StripArgs& a, hipStream_t st) {
   int64_t g = a.supertiles;
   const int64_t resident = resident_workgroups(kernel, threads);
   if (resident > 0 && g > resident) g = resident;
+  if (a.ring.ring && !a.ring.tickets && g > kNullTicketGrid) g = kNullTicketGrid;
   if (g == 0) g = 1;   // an empty per-tensor input still folds
   return launch(kernel, dim3{unsigned(g)}, dim3{unsigned(threads)}, st, a);
 }
@@ -1233,6 +1273,7 @@ static mx_status_t pt_row_dispatch(const void* x, int64_t n, uint8_t* q, const R
   const int64_t nchunks = n / 8;
   const int64_t per = int64_t(kPtRowThreads) * kRowUnroll;
   int64_t g = (nchunks + per - 1) / per;
+  if (!r.tickets && g > kNullTicketGrid / 2) g = kNullTicketGrid / 2;   // 1024-thread workgroups
   if (g == 0) g = 1;   // an empty input still folds
   return launch(pt_row_kernel<IN, F>, dim3{unsigned(g)}, dim3{unsigned(kPtRowThreads)}, st, x, nchunks, q, r);
 }
@@ -1298,8 +1339,10 @@ template <int IN, int F, int R> struct PtOp {
       if (layout == FP8_TRANSPOSED) {
         const int64_t tiles_c = (a.cols + kPtTile - 1) / kPtTile;
         const int64_t ntiles = tiles_c * ((a.rows + kPtTile - 1) / kPtTile);
-        if (IN == IN_BF16 && ntiles > 0 && ntiles < (int64_t(1) << 31) && a.cols < (int64_t(1) << 25))
-          return launch(pt_col_bf16_kernel<F>, dim3{unsigned(ntiles)}, dim3{256u}, st, a, int(tiles_c));
+        if (IN == IN_BF16 && ntiles > 0 && ntiles < (int64_t(1) << 31) && a.cols < (int64_t(1) << 25)) {
+          const int64_t g = a.ring.tickets || ntiles <= kNullTicketGrid ? ntiles : kNullTicketGrid;
+          return launch(pt_col_bf16_kernel<F>, dim3{unsigned(g)}, dim3{256u}, st, a, int(tiles_c), int(ntiles));
+        }
         return strip_dispatch<IN, F, R, PT_COL>(a, false, false, st);
       }
       return strip_dispatch<IN, F, R, PT_DUAL>(a, false, false, st);
@@ -1357,7 +1400,7 @@ extern "C" mx_status_t mx_quantize_dual(const void* x, mx_dtype_t in, int64_t ro
 extern "C" mx_status_t fp8_quantize_delayed(const void* x, mx_dtype_t in, int64_t rows, int64_t cols,
                                             mx_elem_t fmt, fp8_layout_t layout, uint8_t* q, uint8_t* qT,
                                             float* ring, int hist_len, int hist_idx, float fp8_max, float margin,
-                                            float* amax_out, hipStream_t stream) {
+                                            float* amax_out, uint32_t* ticket_scratch, hipStream_t stream) {
   if (in != MX_F32 && in != MX_BF16 && in != MX_F16) return MX_ERR_UNSUPPORTED;
   if (fmt != MX_E4M3 && fmt != MX_E5M2) return MX_ERR_UNSUPPORTED;
   if (layout != FP8_ROW && layout != FP8_TRANSPOSED && layout != FP8_DUAL) return MX_ERR_UNSUPPORTED;
@@ -1370,8 +1413,10 @@ extern "C" mx_status_t fp8_quantize_delayed(const void* x, mx_dtype_t in, int64_
   if (n > 0 && (!x || (need_q && !q) || (need_qT && !qT))) return MX_ERR_NULL;
   if (cols % 8 != 0 || (need_qT && rows % 32 != 0)) return MX_ERR_SHAPE;
   if (n > 0 && (misaligned(x) || (need_q && misaligned(q)) || (need_qT && misaligned(qT)))) return MX_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(ring) & 3u) || (reinterpret_cast<uintptr_t>(ticket_scratch) & 3u))
+    return MX_ERR_ALIGN;
   StripArgs a{};
   a.x = x; a.rows = rows; a.cols = cols; a.q_row = q; a.q_col = qT;
-  a.ring = RingArgs{ring, hist_len, hist_idx, fp8_max, margin, amax_out};
+  a.ring = RingArgs{ring, ticket_scratch, hist_len, hist_idx, fp8_max, margin, amax_out};
   return expand<PtOp>(in, fmt, MX_SCALE_FLOOR, a, int(layout), stream);
 }

@@ -51,7 +51,7 @@ def test_header_compiles_as_c():
 
 
 def test_version_and_status_strings():
-    assert lib.mx_abi_version() == 101
+    assert lib.mx_abi_version() == 200
     for code in range(7):
         assert lib.mx_status_str(code).decode().startswith(mxa.STATUS[code])
 
@@ -99,8 +99,8 @@ def test_mx_quantize_dual_argument_errors():
 
 def test_fp8_quantize_delayed_argument_errors():
     f = lib.fp8_quantize_delayed
-    # (x, in, rows, cols, fmt, layout, q, qT, ring, hist_len, hist_idx, fp8_max, margin, amax, stream)
-    good = [FAKE, 1, 64, 64, 0, 1, FAKE, FAKE, FAKE, 16, 0, 448.0, 1.0, None, None]
+    # (x, in, rows, cols, fmt, layout, q, qT, ring, hist_len, hist_idx, fp8_max, margin, amax, tickets, stream)
+    good = [FAKE, 1, 64, 64, 0, 1, FAKE, FAKE, FAKE, 16, 0, 448.0, 1.0, None, FAKE, None]
 
     def call(i, v):
         a = list(good)
@@ -121,6 +121,17 @@ def test_fp8_quantize_delayed_argument_errors():
     assert call(3, 12) == SHAPE         # cols % 8
     assert call(7, None) == NULL        # qT for the transposed layout
     assert call(7, FAKE + 2) == ALIGN
+    assert call(8, FAKE + 2) == ALIGN   # ring words are 4-byte aligned
+    assert call(14, FAKE + 2) == ALIGN  # ticket scratch likewise
+
+
+def test_ring_layout_is_the_pages():
+    """The ring is [hist | scale | legacy | amax | done]: hist_len + 4 words, and the
+    ticket scratch a separate optional buffer."""
+    text = open(HEADER).read()
+    assert re.search(r"#define MX_RING_WORDS\(hist_len\) \(\(hist_len\) \+ 4\)", text)
+    assert re.search(r"#define MX_TICKET_WORDS 4096", text)
+    assert mxa.ring_words(16) == 20 and mxa.TICKET_WORDS == 4096
 
 
 def test_mx_dequantize_argument_errors():

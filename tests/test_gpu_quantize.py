@@ -168,33 +168,31 @@ def test_special_blocks_dual(dtype):
             assert host(a)[0] == omx.tensor_amax(x32)
 
 
+@pytest.mark.parametrize("orient", ["col", "row"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("had", [False, True])
-def test_special_blocks_colwise_bf16(had):
-    """Column-wise BF16 quantization of zero, subnormal, extreme and non-finite
-    column blocks, with and without the Hadamard transform."""
+def test_special_blocks_hadamard(had, dtype, orient):
+    """Zero, subnormal, extreme and non-finite blocks, with and without the
+    Hadamard transform, column-wise and row-wise.  Every byte is compared,
+    sign bits included: NaNs made by the transform carry a clear sign bit on
+    both sides."""
     blocks = workloads.special_blocks()          # [18][32]
     x32 = np.zeros((96, 64), np.float32)
     x32[32:64, 8:26] = blocks.T                 # as column blocks
     x32[70, :] = np.nan
     x32[:, 60] = -np.inf
-    x = make_input(x32, "bf16")
+    if orient == "row":
+        x32 = np.ascontiguousarray(x32.T)       # the same blocks as row blocks
+    x = make_input(x32, dtype)
     xs = f32_of_input(x)
     mask = 0x2468_ACE1 if had else None
+    ref = omx.quantize_colwise_t if orient == "col" else omx.quantize_rowwise
     for fmt in FMTS:
         for rule in RULES:
-            q, s, a = mxa.mx_quantize(x, fmt, rule, "col", hadamard_mask=mask, amax=True)
-            wq, ws = omx.quantize_colwise_t(xs, fmt, rule, hadamard_mask=mask)
+            q, s, a = mxa.mx_quantize(x, fmt, rule, orient, hadamard_mask=mask, amax=True)
+            wq, ws = ref(xs, fmt, rule, hadamard_mask=mask)
             assert_bytes_equal(host(s), ws, f"{fmt} {rule} scales")
-            gq = host(q)
-            if had:
-                # the butterflies turn a block holding NaN into NaNs whose sign
-                # IEEE 754 leaves open: non-finite blocks compare without sign bits
-                sign = np.uint8(0x88 if fmt == "e2m1" else 0x80)
-                per_scale = gq.shape[1] // ws.shape[1]
-                nonfinite = np.repeat(ws == 0xFF, per_scale, axis=1)
-                gq = np.where(nonfinite, gq & ~sign, gq)
-                wq = np.where(nonfinite, wq & ~sign, wq)
-            assert_bytes_equal(gq, wq, f"{fmt} {rule} codes")
+            assert_bytes_equal(host(q), wq, f"{fmt} {rule} codes")
             assert host(a)[0] == omx.tensor_amax(xs)
 
 
@@ -258,27 +256,86 @@ def test_quantize_dequantize_roundtrip_wide_range_f32(fmt):
 
 # ---------------------------------------------------------------- per-tensor delayed scaling
 
+def new_tickets(mode):
+    """Ticket scratch for a delayed-scaling test: a fresh zeroed buffer, or None
+    (the ticket is taken on the ring's own words)."""
+    return mxa.new_tickets() if mode == "scratch" else None
+
+
+def assert_ring_state(ring, tickets, oring, what):
+    """The whole ring equals the host fold; the ticket scratch reads zero again."""
+    assert ring.numel() == oring.hist.size + 4
+    assert_float_equal(host(ring), oring.as_array(), f"{what} ring")
+    if tickets is not None:
+        assert int(torch.count_nonzero(tickets)) == 0, f"{what}: ticket scratch not left zero"
+
+
+@pytest.mark.parametrize("tmode", ["scratch", "none"])
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("layout", ["row", "transposed", "dual"])
-def test_delayed_sequence_small(fmt, layout):
+def test_delayed_sequence_small(fmt, layout, tmode):
     """32 successive steps on one ring (length 16): codes, amax and the whole
-    ring state equal the host fold after every step."""
+    ring state equal the host fold after every step, with and without ticket
+    scratch."""
     stream = "act" if fmt == "e4m3" else "grad"
     fp8_max = workloads.DELAYED_FP8_MAX[stream]
     ring = mxa.new_ring(16)
+    tickets = new_tickets(tmode)
     oring = odl.Ring(16)
     for t in range(32):
         xb = workloads.delayed_step(stream, t, rows=96, cols=160)
         x = upload_bf16_bits(xb)
         xs = workloads.bf16_to_f32(xb)
-        q, qT, a = mxa.fp8_quantize_delayed(x, ring, t % 16, fmt, layout, fp8_max, 1.0, amax=True)
+        q, qT, a = mxa.fp8_quantize_delayed(x, ring, t % 16, fmt, layout, fp8_max, 1.0, amax=True, tickets=tickets)
         wq, wqT, wa = odl.quantize_delayed(xs, fmt, oring, t % 16, fp8_max, 1.0)
         if q is not None:
             assert_bytes_equal(host(q), wq, f"step {t} q")
         if qT is not None:
             assert_bytes_equal(host(qT), wqT, f"step {t} qT")
         assert host(a)[0] == wa
-        assert_float_equal(host(ring), oring.as_array(mxa.RING_TICKET_WORDS), f"step {t} ring")
+        assert_ring_state(ring, tickets, oring, f"step {t}")
+
+
+@pytest.mark.parametrize("tmode", ["scratch", "none"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("layout", ["row", "transposed", "dual"])
+def test_delayed_many_workgroups(layout, dtype, tmode):
+    """A 2304 x 4096 input: more tiles than the persistent grid of the
+    no-scratch launch (so workgroups loop over several tiles and all take their
+    ticket on one word) and, with scratch, more than one workgroup per ticket
+    group.  Four steps: codes, amax and ring exact."""
+    ring = mxa.new_ring(8)
+    tickets = new_tickets(tmode)
+    oring = odl.Ring(8)
+    for t in range(4):
+        xb = workloads.delayed_step("grad", t, rows=2304, cols=4096)
+        x = make_input(workloads.bf16_to_f32(xb), dtype)
+        xs = f32_of_input(x)
+        q, qT, a = mxa.fp8_quantize_delayed(x, ring, t % 8, "e5m2", layout, 57344.0, 1.0, amax=True, tickets=tickets)
+        wq, wqT, wa = odl.quantize_delayed(xs, "e5m2", oring, t % 8, 57344.0, 1.0)
+        if q is not None:
+            assert_bytes_equal(host(q), wq, f"step {t} q")
+        if qT is not None:
+            assert_bytes_equal(host(qT), wqT, f"step {t} qT")
+        assert host(a)[0] == wa
+        assert_ring_state(ring, tickets, oring, f"step {t}")
+
+
+def test_delayed_scratch_shared_by_two_rings():
+    """One ticket scratch serves calls on different rings in stream order; each
+    ring follows its own host fold."""
+    tickets = mxa.new_tickets()
+    rings = {s: mxa.new_ring(16) for s in ("act", "grad")}
+    orings = {s: odl.Ring(16) for s in ("act", "grad")}
+    for t in range(6):
+        for stream, fmt in (("act", "e4m3"), ("grad", "e5m2")):
+            fp8_max = workloads.DELAYED_FP8_MAX[stream]
+            xb = workloads.delayed_step(stream, t, rows=512, cols=1024)
+            _, qT = mxa.fp8_quantize_delayed(upload_bf16_bits(xb), rings[stream], t, fmt, "transposed", fp8_max,
+                                             tickets=tickets)
+            _, wqT, _ = odl.quantize_delayed(workloads.bf16_to_f32(xb), fmt, orings[stream], t, fp8_max, 1.0)
+            assert_bytes_equal(host(qT), wqT, f"{stream} step {t} qT")
+            assert_ring_state(rings[stream], tickets, orings[stream], f"{stream} step {t}")
 
 
 def test_delayed_resume_from_saved_ring():
@@ -322,51 +379,70 @@ def test_delayed_margin_and_nonfinite(dtype, layout, shape, fmt):
         if q is not None:
             assert_bytes_equal(host(q), wq, f"step {t} q")
         assert_bytes_equal(host(qT), wqT, f"step {t} qT")
-        assert_float_equal(host(ring), oring.as_array(mxa.RING_TICKET_WORDS), f"step {t} ring")
+        assert_ring_state(ring, None, oring, f"step {t}")
 
 
-# ---------------------------------------------------------------- full-size workloads (sampled)
+# ---------------------------------------------------------------- full-size workloads (complete)
 
-def test_activation_dual_full_size_sampled():
+def test_activation_dual_full_size():
     """BF16 8192 x 4096, E4M3, round-up rule, dual + amax, in the bench's launch
-    configuration; the oracle checks 64 sampled rows and 4 sampled 32-row strips."""
+    configuration: every row code and scale and every transposed column code and
+    scale against the oracle."""
     xb = workloads.activation_bf16()
     x = upload_bf16_bits(xb)
     qr, sr, qc, sc, a = mxa.mx_quantize_dual(x, "e4m3", "ceil", amax=True)
-    g = np.random.default_rng(5)
-    rows = np.sort(g.choice(8192, size=64, replace=False))
-    xs = workloads.bf16_to_f32(xb[rows])
-    wq, ws = omx.quantize_rowwise(xs, "e4m3", "ceil")
-    assert_bytes_equal(host(qr)[rows], wq, "row codes")
-    assert_bytes_equal(host(sr)[rows], ws, "row scales")
-    qc_h, sc_h = host(qc), host(sc)
-    for strip in g.choice(256, size=4, replace=False):
-        xs = workloads.bf16_to_f32(xb[32 * strip:32 * strip + 32])
-        wq, ws = omx.quantize_colwise_t(xs, "e4m3", "ceil")
-        assert_bytes_equal(qc_h[:, 32 * strip:32 * strip + 32], wq, "col codes")
-        assert_bytes_equal(sc_h[:, strip:strip + 1], ws, "col scales")
-    assert host(a)[0] == omx.tensor_amax(workloads.bf16_to_f32(xb))
+    xs = workloads.bf16_to_f32(xb)
+    wqr, wsr, wqc, wsc = omx.quantize_dual(xs, "e4m3", "ceil")
+    assert_bytes_equal(host(sr), wsr, "row scales")
+    assert_bytes_equal(host(qr), wqr, "row codes")
+    assert_bytes_equal(host(sc), wsc, "col scales")
+    assert_bytes_equal(host(qc), wqc, "col codes")
+    assert host(a)[0] == omx.tensor_amax(xs)
     # zero blocks of the recipe come out as scale code 0
-    assert (host(sr) == 0).sum() >= 16 and (sc_h == 0).sum() >= 16
+    assert (wsr == 0).sum() >= 16 and (wsc == 0).sum() >= 16
 
 
-def test_delayed_full_size_first_steps():
-    """BF16 8192 x 4096 delayed scaling, both streams, 3 steps each: ring state
-    exact, sampled transposed codes exact."""
-    g = np.random.default_rng(6)
-    for stream, fmt in (("act", "e4m3"), ("grad", "e5m2")):
-        fp8_max = workloads.DELAYED_FP8_MAX[stream]
-        ring = mxa.new_ring(16)
-        oring = odl.Ring(16)
-        for t in range(3):
-            xb = workloads.delayed_step(stream, t)
-            x = upload_bf16_bits(xb)
-            m_before = np.float32(oring.m)
-            _, qT, a = mxa.fp8_quantize_delayed(x, ring, t % 16, fmt, "transposed", fp8_max, 1.0, amax=True)
-            xs_all = workloads.bf16_to_f32(xb)
-            oring.fold(omx.tensor_amax(xs_all), t % 16, fp8_max, 1.0)
-            assert host(a)[0] == omx.tensor_amax(xs_all)
-            assert_float_equal(host(ring), oring.as_array(mxa.RING_TICKET_WORDS), f"{stream} step {t} ring")
-            cols = np.sort(g.choice(4096, size=16, replace=False))
-            want = odl.cast_per_tensor(xs_all[:, cols], m_before, fmt).T
-            assert_bytes_equal(host(qT)[cols], want, f"{stream} step {t} qT")
+@pytest.mark.parametrize("stream", ["act", "grad"])
+def test_delayed_full_size_32_steps(stream):
+    """BF16 8192 x 4096 delayed scaling, 32 steps on one ring of 16 in the bench's
+    launch configuration (ticket scratch): after every step the whole ring, the
+    ticket scratch and the amax exact; every transposed code exact at steps 0,
+    15 and 31."""
+    fmt = workloads.DELAYED_FMT[stream]
+    fp8_max = workloads.DELAYED_FP8_MAX[stream]
+    ring = mxa.new_ring(16)
+    tickets = mxa.new_tickets()
+    oring = odl.Ring(16)
+    for t in range(32):
+        xb = workloads.delayed_step(stream, t)
+        x = upload_bf16_bits(xb)
+        m_before = np.float32(oring.m)
+        _, qT, a = mxa.fp8_quantize_delayed(x, ring, t % 16, fmt, "transposed", fp8_max, 1.0, amax=True,
+                                            tickets=tickets)
+        xs = workloads.bf16_to_f32(xb)
+        amax = omx.tensor_amax(xs)
+        oring.fold(amax, t % 16, fp8_max, 1.0)
+        assert host(a)[0] == amax
+        assert_ring_state(ring, tickets, oring, f"{stream} step {t}")
+        if t in (0, 15, 31):
+            want = odl.cast_per_tensor(xs, m_before, fmt)
+            assert_bytes_equal(host(qT), np.ascontiguousarray(want.T), f"{stream} step {t} qT")
+
+
+def test_delayed_full_size_without_scratch():
+    """The same workload with the page's plain ring (no ticket scratch): three
+    steps, ring and amax exact, every code exact at the last step."""
+    ring = mxa.new_ring(16)
+    oring = odl.Ring(16)
+    for t in range(3):
+        xb = workloads.delayed_step("act", t)
+        m_before = np.float32(oring.m)
+        _, qT, a = mxa.fp8_quantize_delayed(upload_bf16_bits(xb), ring, t, "e4m3", "transposed", 448.0, 1.0,
+                                            amax=True)
+        xs = workloads.bf16_to_f32(xb)
+        amax = omx.tensor_amax(xs)
+        oring.fold(amax, t, 448.0, 1.0)
+        assert host(a)[0] == amax
+        assert_ring_state(ring, None, oring, f"step {t}")
+    want = odl.cast_per_tensor(xs, m_before, "e4m3")
+    assert_bytes_equal(host(qT), np.ascontiguousarray(want.T), "step 2 qT")
