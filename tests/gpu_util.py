@@ -70,3 +70,48 @@ def import_library():
         import mx_block_scaled_quantize_amd as mxa
         return mxa
     return pytest.importorskip("mx_block_scaled_quantize_amd")
+
+
+def tile_strata(n: int, tile: int, seed: int) -> np.ndarray:
+    """One random index inside every `tile`-long block of range(n) (the last block
+    may be ragged): a sample that touches every tile a launch of that tile size
+    covers along this axis."""
+    g = np.random.default_rng(seed)
+    return np.array([s + int(g.integers(0, min(tile, n - s))) for s in range(0, n, tile)], dtype=np.int64)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def abs_product(qa, sa, fa, qb, sb, fb, alpha=1.0, rows=None, cols=None) -> np.ndarray:
+    """|alpha| * |deq(A)| |deq(B)|^T on the selected rows / columns: the magnitude
+    the matrix unit's accumulation error is measured against."""
+    from oracle import mx as omx
+    A = omx.dequantize_exact(qa if rows is None else np.asarray(qa)[rows],
+                             sa if rows is None else np.asarray(sa)[rows], fa)
+    B = omx.dequantize_exact(qb if cols is None else np.asarray(qb)[cols],
+                             sb if cols is None else np.asarray(sb)[cols], fb)
+    return abs(alpha) * (np.abs(A) @ np.abs(B).T)
+
+
+def check_bf16_lines(got_bits: np.ndarray, ref: np.ndarray, mag: np.ndarray, tol: float, what: str, seg: int = 256):
+    """BF16 GEMM output lines (rows of `got_bits`) against the float64 reference:
+    * the relative Frobenius error of all of them against the reference rounded
+      once to BF16 is within `tol` (the graded bound);
+    * every element is within one BF16 rounding (2^-8 relative) plus
+      2^-10 * sum_k |a_k b_k| (`mag`, the matrix unit's fixed-point accumulation
+      window) of the reference -- a wrong code, scale, lane or tile pairing misses
+      this by orders of magnitude.  A failure names the line and the `seg`-long
+      segment (output tile) it falls in."""
+    from oracle import gemm as og
+    got = bf16_bits_to_f64(got_bits)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} != {ref.shape}"
+    err = og.rel_frobenius(got, bf16_bits_to_f64(og.f64_to_bf16_bits(ref)))
+    assert err <= tol, f"{what}: relative Frobenius error {err}"
+    bad = np.abs(got - ref) > 2.0 ** -8 * np.abs(ref) + 2.0 ** -10 * mag + 1e-30
+    if bad.any():
+        i, j = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {int(bad.sum())} outputs outside the bound; first at line {i}, element {j} "
+                             f"(tile segment {j // seg}): got {got[i, j]}, reference {ref[i, j]}")
+    return err

@@ -8,9 +8,11 @@ import torch
 
 import workloads
 from oracle import formats as F
+from oracle import gemm as og
 from oracle import mx as omx
-from tests.gpu_util import (assert_bytes_equal, assert_float_equal, f32_of_input, host, import_library,
-                            upload_bf16_bits, upload_f16_from_f32, upload_f32, upload_u8)
+from tests.gpu_util import (assert_bytes_equal, assert_float_equal, check_bf16_lines, f32_of_input, host,
+                            import_library, tile_strata, upload_bf16_bits, upload_f16_from_f32, upload_f32, upload_u8,
+                            abs_product)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,15 +94,39 @@ def test_fp6_roundtrip_error_bound(fmt):
     assert np.all(np.abs(d - x32) <= quantum / 2)
 
 
-def test_fp6_full_size_sampled_rows():
-    """BF16 8192 x 4096 activation to MXFP6 E3M2: sampled rows against the oracle."""
+def test_fp6_full_size():
+    """BF16 8192 x 4096 activation to MXFP6 E3M2, row-wise: every code and scale
+    against the oracle."""
     bits = workloads.activation_bf16(8192, 4096)
     q, s = mxa.mx_quantize(upload_bf16_bits(bits), "e3m2", "ceil", "row")
-    qh, sh = host(q), host(s)
-    rows = np.concatenate([[0, 8191], np.random.default_rng(66).choice(8192, 30, replace=False)])
-    wq, ws = omx.quantize_rowwise(workloads.bf16_to_f32(bits[rows]), "e3m2", "ceil")
-    assert_bytes_equal(sh[rows], ws, "scales")
-    assert_bytes_equal(qh[rows], wq, "codes")
+    wq, ws = omx.quantize_rowwise(workloads.bf16_to_f32(bits), "e3m2", "ceil")
+    assert_bytes_equal(host(s), ws, "scales")
+    assert_bytes_equal(host(q), wq, "codes")
+
+
+def test_fp6_gemm_full_size():
+    """The bench's MXFP6 GEMM: A 8192 x 4096 and W 14336 x 4096 quantized row-wise to
+    E2M3 (round-up rule), BF16 out.  Operands compared in full; the product on
+    one whole row from every 128-row tile and one whole column from every
+    128-column tile of the launch, segment by segment."""
+    a_bits, w_bits = workloads.mlp_operands()
+    qa, sa = mxa.mx_quantize(upload_bf16_bits(a_bits), "e2m3", "ceil", "row")
+    qw, sw = mxa.mx_quantize(upload_bf16_bits(w_bits), "e2m3", "ceil", "row")
+    c = host(mxa.mx_gemm(qa, sa, qw, sw, "e2m3", "e2m3", 1.0, out_dtype=torch.bfloat16))
+    oqa, osa = omx.quantize_rowwise(workloads.bf16_to_f32(a_bits), "e2m3", "ceil")
+    oqw, osw = omx.quantize_rowwise(workloads.bf16_to_f32(w_bits), "e2m3", "ceil")
+    assert_bytes_equal(host(qa), oqa, "A codes")
+    assert_bytes_equal(host(qw), oqw, "W codes")
+    assert_bytes_equal(host(sa), osa, "A scales")
+    assert_bytes_equal(host(sw), osw, "W scales")
+    rows = tile_strata(8192, 128, 61)
+    cols = tile_strata(14336, 128, 62)
+    op = (oqa, osa, "e2m3", oqw, osw, "e2m3")
+    ref_r = og.gemm_ref(*op, rows=rows)
+    check_bf16_lines(c[rows], ref_r, abs_product(*op, rows=rows), 1e-3, "rows", seg=128)
+    ref_c = og.gemm_ref(*op, cols=cols)
+    check_bf16_lines(np.ascontiguousarray(c[:, cols].T), ref_c.T, abs_product(*op, cols=cols).T, 1e-3, "columns",
+                     seg=128)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])

@@ -12,6 +12,8 @@ Tolerances (graded bound 1e-3 relative Frobenius error):
   (the BF16 rounding of an exact result alone is ~1.6e-3 away from float64, so
   the raw float64 distance is reported, not graded)."""
 
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -19,7 +21,8 @@ import torch
 import workloads
 from oracle import gemm as og
 from oracle import mx as omx
-from tests.gpu_util import assert_bytes_equal, host, upload_bf16_bits, upload_f32, upload_u8, import_library
+from tests.gpu_util import (assert_bytes_equal, check_bf16_lines, host, import_library, tile_strata, upload_bf16_bits,
+                            upload_f32, upload_u8, abs_product)
 
 pytestmark = pytest.mark.gpu
 
@@ -197,41 +200,74 @@ def test_gemm_ldc_and_k_zero():
     assert st == 0 and (host(c) == 0).all()               # empty sum
 
 
-def test_mlp_mxfp8_gemm_full_size_sampled():
+def test_mlp_mxfp8_gemm_full_size():
     """A 8192 x 4096 activations, W 14336 x 4096 weights, both MXFP8 E4M3 with the
-    round-up rule along K, BF16 out; 48 x 48 sampled outputs against the oracle."""
+    round-up rule along K, BF16 out, in the bench's launch configuration.  Both
+    quantized operands are compared in full; the product on one row from every
+    256-row output tile (whole rows) and one column from every 256-column tile
+    (whole columns), so every 256 x 256 tile of the launch is checked, segment
+    by segment."""
     a_bits, w_bits = workloads.mlp_operands()
     qa, sa = mxa.mx_quantize(upload_bf16_bits(a_bits), "e4m3", "ceil", "row")
     qw, sw = mxa.mx_quantize(upload_bf16_bits(w_bits), "e4m3", "ceil", "row")
-    c = mxa.mx_gemm(qa, sa, qw, sw, "e4m3", "e4m3", 1.0, out_dtype=torch.bfloat16)
-    g = np.random.default_rng(44)
-    rows = np.sort(g.choice(8192, size=48, replace=False))
-    cols = np.sort(g.choice(14336, size=48, replace=False))
-    oqa, osa = omx.quantize_rowwise(workloads.bf16_to_f32(a_bits[rows]), "e4m3", "ceil")
-    oqw, osw = omx.quantize_rowwise(workloads.bf16_to_f32(w_bits[cols]), "e4m3", "ceil")
-    assert_bytes_equal(host(qa)[rows], oqa, "A codes")
-    assert_bytes_equal(host(qw)[cols], oqw, "W codes")
-    ref = og.gemm_ref(oqa, osa, "e4m3", oqw, osw, "e4m3")
-    got = bf16_to_f64(host(c)[np.ix_(rows, cols)])
-    assert og.rel_frobenius(got, bf16_to_f64(og.f64_to_bf16_bits(ref))) <= BF16_TOL
-    assert og.rel_frobenius(got, ref) <= 4e-3                  # BF16 output rounding only
+    c = host(mxa.mx_gemm(qa, sa, qw, sw, "e4m3", "e4m3", 1.0, out_dtype=torch.bfloat16))
+    oqa, osa = omx.quantize_rowwise(workloads.bf16_to_f32(a_bits), "e4m3", "ceil")
+    oqw, osw = omx.quantize_rowwise(workloads.bf16_to_f32(w_bits), "e4m3", "ceil")
+    assert_bytes_equal(host(sa), osa, "A scales")
+    assert_bytes_equal(host(qa), oqa, "A codes")
+    assert_bytes_equal(host(sw), osw, "W scales")
+    assert_bytes_equal(host(qw), oqw, "W codes")
+    rows = tile_strata(8192, 256, 44)
+    cols = tile_strata(14336, 256, 45)
+    op = (oqa, osa, "e4m3", oqw, osw, "e4m3")
+    ref_r = og.gemm_ref(*op, rows=rows)
+    check_bf16_lines(c[rows], ref_r, abs_product(*op, rows=rows), BF16_TOL, "rows")
+    ref_c = og.gemm_ref(*op, cols=cols)
+    check_bf16_lines(np.ascontiguousarray(c[:, cols].T), ref_c.T, abs_product(*op, cols=cols).T, BF16_TOL,
+                     "columns")
+    assert og.rel_frobenius(bf16_to_f64(c[rows]), ref_r) <= 4e-3        # BF16 output rounding only
 
 
-def test_hadamard_mxfp4_wgrad_full_size_sampled():
-    """G, X BF16 8192 tokens x 4096: fixed-sign Hadamard + column-wise MXFP4
-    quantization along tokens, then dW = (1/32) Gq^T Xq with BF16 out."""
+@functools.lru_cache(maxsize=1)
+def wgrad_oracle():
+    """The oracle's Hadamard + column-wise MXFP4 quantization of both weight-gradient
+    operands, whole (computed once per test session)."""
+    g_bits, x_bits, mask = workloads.weight_grad_operands()
+    ogq, ogs = omx.quantize_colwise_t(workloads.bf16_to_f32(g_bits), "e2m1", "ceil", hadamard_mask=mask)
+    oxq, oxs = omx.quantize_colwise_t(workloads.bf16_to_f32(x_bits), "e2m1", "ceil", hadamard_mask=mask)
+    return ogq, ogs, oxq, oxs
+
+
+def wgrad_gpu():
     g_bits, x_bits, mask = workloads.weight_grad_operands()
     gq, gs = mxa.mx_quantize(upload_bf16_bits(g_bits), "e2m1", "ceil", "col", hadamard_mask=mask)
     xq, xs = mxa.mx_quantize(upload_bf16_bits(x_bits), "e2m1", "ceil", "col", hadamard_mask=mask)
-    dw = mxa.mx_gemm(gq, gs, xq, xs, "e2m1", "e2m1", 1.0 / 32, out_dtype=torch.bfloat16)
-    g = np.random.default_rng(55)
-    rows = np.sort(g.choice(4096, size=32, replace=False))
-    cols = np.sort(g.choice(4096, size=32, replace=False))
-    ogq, ogs = omx.quantize_colwise_t(workloads.bf16_to_f32(g_bits[:, rows]), "e2m1", "ceil", hadamard_mask=mask)
-    oxq, oxs = omx.quantize_colwise_t(workloads.bf16_to_f32(x_bits[:, cols]), "e2m1", "ceil", hadamard_mask=mask)
-    assert_bytes_equal(host(gq)[rows], ogq, "G codes")
-    assert_bytes_equal(host(gs)[rows], ogs, "G scales")
-    assert_bytes_equal(host(xq)[cols], oxq, "X codes")
-    ref = og.gemm_ref(ogq, ogs, "e2m1", oxq, oxs, "e2m1", alpha=1.0 / 32)
-    got = bf16_to_f64(host(dw)[np.ix_(rows, cols)])
-    assert og.rel_frobenius(got, bf16_to_f64(og.f64_to_bf16_bits(ref))) <= BF16_TOL
+    return gq, gs, xq, xs
+
+
+def test_hadamard_mxfp4_quant_full_size():
+    """G, X BF16 8192 tokens x 4096: fixed-sign Hadamard + column-wise MXFP4
+    quantization along tokens, in the bench's launch configuration; every code
+    and scale of both operands against the oracle."""
+    got = wgrad_gpu()
+    want = wgrad_oracle()
+    for g, w, what in zip(got, want, ("G codes", "G scales", "X codes", "X scales")):
+        assert_bytes_equal(host(g), w, what)
+
+
+def test_hadamard_mxfp4_wgrad_gemm_full_size():
+    """dW = (1/32) Gq^T Xq (4096 x 4096, K = 8192 tokens) with BF16 out: one row
+    from every 256-row tile and one column from every 256-column tile, whole."""
+    gq, gs, xq, xs = wgrad_gpu()
+    dw = host(mxa.mx_gemm(gq, gs, xq, xs, "e2m1", "e2m1", 1.0 / 32, out_dtype=torch.bfloat16))
+    ogq, ogs, oxq, oxs = wgrad_oracle()
+    rows = tile_strata(4096, 256, 55)
+    cols = tile_strata(4096, 256, 56)
+    op = (ogq, ogs, "e2m1", oxq, oxs, "e2m1", 1.0 / 32)
+    ref_r = og.gemm_ref(*op, rows=rows)
+    check_bf16_lines(dw[rows], ref_r, abs_product(*op, rows=rows), BF16_TOL, "rows")
+    ref_c = og.gemm_ref(*op, cols=cols)
+    check_bf16_lines(np.ascontiguousarray(dw[:, cols].T), ref_c.T, abs_product(*op, cols=cols).T, BF16_TOL,
+                     "columns")
+
+

@@ -17,7 +17,7 @@ import torch
 import workloads
 from oracle import formats as ofmt
 from oracle import gemm as og
-from tests.gpu_util import assert_bytes_equal, host, upload_bf16_bits, upload_u8, import_library
+from tests.gpu_util import assert_bytes_equal, host, import_library, tile_strata, upload_bf16_bits, upload_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -184,17 +184,18 @@ def field_codes(shape, seed, fmt):
 
 
 @pytest.mark.parametrize("tb", [True, False])
-def test_mm_fp8_full_size_sampled(tb):
+def test_mm_fp8_full_size(tb):
     """The linear-layer workload: x [8192][4096] times w [14336][4096] (x @ w.t(),
-    K-contiguous) or w stored [4096][14336] (N-contiguous), with bias, checked on
-    sampled rows x columns against the oracle."""
+    K-contiguous) or w stored [4096][14336] (N-contiguous), with bias: one whole
+    row from every 256-row output tile and one whole column from every
+    256-column tile against the oracle, so every tile of the launch is checked."""
     M, N, K = 8192, 14336, 4096
     x = field_codes((M, K), 21, "e4m3")
     w = field_codes((N, K) if tb else (K, N), 22, "e4m3")
     bias = ofmt.f32_to_bf16_bits(workloads.random_tensor((N,), 8, "normal"))
     out = run(x, w, "e4m3", 0.015625, False, tb, bias)
-    g = np.random.default_rng(23)
-    rows = np.concatenate([[0, M - 1], g.choice(M, 14, replace=False)])
-    cols = np.concatenate([[0, N - 1], g.choice(N, 62, replace=False)])
+    rows = tile_strata(M, 256, 23)
+    cols = tile_strata(N, 256, 24)
+    check(out[rows], x[rows], w, "e4m3", 0.015625, False, tb, bias, "full-size rows")
     ws = w[cols] if tb else w[:, cols]
-    check(out[np.ix_(rows, cols)], x[rows], ws, "e4m3", 0.015625, False, tb, bias[cols], "full size")
+    check(out[:, cols], x, ws, "e4m3", 0.015625, False, tb, bias[cols], "full-size columns")
