@@ -10,19 +10,24 @@ one); inputs are resident in HBM before the timed region.
 
 ``value`` = algorithmic bytes per step (input read + codes, scales and amax
 written) x steps / wall time of the timed region.  ``roofline.achieved`` = the
-same bytes / the kernel's own average duration (HIP events recorded around each
-launch on the stream the kernel runs on).  The MXFP8 GEMM (8192 x 4096 x 14336)
-and the other workloads are reported under ``gemm`` and ``extra``.
+same bytes / the kernel's own average duration (one HIP event pair around the K
+back-to-back launches on the stream the kernel runs on).  A second pass brackets
+every launch with its own events for the median and the 10th / 90th
+percentiles; the graphics clock comes from the committed rocprofv3 summary; a plain
+device copy of the same size gives the attainable copy roof.  The MXFP8 GEMM
+(8192 x 4096 x 14336) and the other workloads are reported under ``gemm`` and
+``extra``; the CPU oracle under ``cpu_baseline``.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline] [--no-extra]
-       python bench.py --mode dual|gemm|copy ...   (one kernel only, for profiler passes;
-                                                    'copy' is a plain 256 MiB device copy
-                                                    used to calibrate the byte counters)
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 5] [--no-cpu-baseline] [--no-extra]
+       python bench.py --mode dual|delayed|delayed_grad|col|sr|fp6dual|gemm|copy ...
+           (one workload only, for profiler passes; 'copy' is a plain 256 MiB
+            device copy used to calibrate the byte counters)
        python bench.py --summarize OUT.md --stats S.csv --fetch F.csv --write W.csv
-                       --copy-fetch CF.csv --copy-write CW.csv --command "..."
-           (turns rocprofv3 outputs into the committed profile summary)
-       python bench.py --summarize-gemm profiles --stats S.csv [--pmc-gemm P.csv] --command "..."
-           (the same for the MXFP8 and MXFP4 GEMM kernels)
+                       --copy-fetch CF.csv --copy-write CW.csv --workload W --kernel K --command "..."
+                       [--pmc P.csv ...]
+           (turns rocprofv3 outputs into a committed profile summary)
+       python bench.py --summarize-gemm profiles --stats S.csv [--pmc-gemm P.csv ...] --command "..."
+           (the same for the GEMM kernels)
 """
 
 import argparse
@@ -42,6 +47,8 @@ FP4_PEAK_TFLOPS = 10100.0        # dense MXFP4 MFMA
 FP6_PEAK_TFLOPS = 10100.0        # dense MXFP6 MFMA
 METRIC = "MX quantize GB/s (% HBM peak); MXFP8 GEMM TFLOP/s (% FP8 MFMA peak)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dual_bf16_kernel_mxfp8_bf16_8192x4096.md")
+QUANT_SOURCES = ("quantize.hip", "mx_device.hpp")
+GEMM_SOURCES = ("gemm.hip", "mx_device.hpp")
 
 
 def code_digest(texts) -> str:
@@ -55,43 +62,101 @@ def code_digest(texts) -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=QUANT_SOURCES) -> str:
     texts = []
-    for f in ("quantize.hip", "mx_device.hpp"):
+    for f in files:
         with open(os.path.join(ROOT, "mx_block_scaled_quantize_amd", "csrc", f)) as fh:
             texts.append(fh.read())
     return code_digest(texts)
 
 
+def profile_fields(path):
+    """key: value lines of a committed profile summary."""
+    vals = {}
+    if os.path.exists(path):
+        for line in open(path):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    return vals
+
+
+def profile_is_current(path, files) -> bool:
+    """True when the summary was taken on the kernel source as it stands."""
+    return profile_fields(path).get("kernel_source_hash") == kernel_source_hash(files)
+
+
 def measured_traffic():
     """HBM bytes per dual-quantize launch from the committed rocprofv3 counter
     summary, or None if absent or taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    vals = profile_fields(TRAFFIC_FILE)
+    if vals.get("kernel_source_hash") != kernel_source_hash() or "traffic_bytes_per_launch" not in vals:
         return None
-    vals = {}
-    for line in open(TRAFFIC_FILE):
-        if line.startswith("traffic_bytes_per_launch:"):
-            vals["bytes"] = float(line.split(":")[1])
-        if line.startswith("kernel_source_hash:"):
-            vals["hash"] = line.split(":")[1].strip()
-    if vals.get("hash") != kernel_source_hash() or "bytes" not in vals:
+    return float(vals["traffic_bytes_per_launch"].split()[0])
+
+
+def profile_clock(path, files):
+    """GPU clock during a kernel from a committed rocprofv3 summary (GRBM_GUI_ACTIVE
+    cycles per XCD over the kernel's duration), when it was taken on the current
+    source: the graphics clock a short kernel actually ran at, which a
+    management-library sample between launches does not see."""
+    vals = profile_fields(path)
+    if "gpu_clock_GHz_from_GRBM" not in vals:
         return None
-    return vals["bytes"]
+    return {"GHz": float(vals["gpu_clock_GHz_from_GRBM"]), "source": os.path.relpath(path, ROOT),
+            "current": vals.get("kernel_source_hash") == kernel_source_hash(files)}
+
+
+def pct(v, q):
+    """q-th percentile (nearest rank) of a sorted list."""
+    return v[min(len(v) - 1, max(0, int(round(q / 100.0 * (len(v) - 1)))))]
+
+
+def launch_distribution(fn, n, stream, torch):
+    """Per-launch durations: every launch bracketed by its own event pair."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for s, e in evs:
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(s.elapsed_time(e) * 1e3 for s, e in evs)
+    return {"median_us": round(pct(us, 50), 2), "p10_us": round(pct(us, 10), 2), "p90_us": round(pct(us, 90), 2),
+            "min_us": round(us[0], 2), "max_us": round(us[-1], 2), "launches": n}
+
+
+def copy_roof(torch, dev, stream, nbytes=64 << 20, sets=8, n=50):
+    """A plain device copy of nbytes (read nbytes, write nbytes) through rotating
+    buffer sets: the attainable streaming rate at this size."""
+    bufs = [(torch.ones(nbytes, dtype=torch.uint8, device=dev), torch.empty(nbytes, dtype=torch.uint8, device=dev))
+            for _ in range(sets)]
+    idx = [0]
+
+    def fn():
+        s, d = bufs[idx[0] % sets]
+        d.copy_(s)
+        idx[0] += 1
+    t = time_calls(fn, n, 5, stream, torch)
+    del bufs
+    return {"GB/s": round(2 * nbytes / t / 1e9, 1), "us": round(t * 1e6, 2), "bytes_read": nbytes,
+            "bytes_written": nbytes, "frac_of_spec": round(2 * nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "kind": "torch device-to-device copy_, 8 rotating buffer sets"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--mode", choices=["full", "dual", "delayed", "gemm", "copy"], default="full")
-    ap.add_argument("--workload", choices=["dual", "delayed"], default="dual",
-                    help="which kernel --summarize describes")
+    ap.add_argument("--mode", choices=["full", "dual", "delayed", "delayed_grad", "col", "sr", "fp6dual", "gemm",
+                                       "copy"], default="full")
+    ap.add_argument("--workload", default="dual", help="which workload --summarize describes")
     ap.add_argument("--summarize", metavar="OUT_MD")
     ap.add_argument("--summarize-gemm", metavar="OUT_DIR")
-    ap.add_argument("--pmc-gemm")
+    ap.add_argument("--pmc-gemm", nargs="*", default=[])
+    ap.add_argument("--pmc", nargs="*", default=[])
     ap.add_argument("--stats")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
@@ -134,22 +199,15 @@ def main():
         print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "us": round(t * 1e6, 2),
                           "GB/s": round(2 * n / t / 1e9, 1)}), flush=True)
         return
-    if args.mode == "delayed":
-        R, C = 8192, 4096
-        xs = [up_bf16(workloads.delayed_step("act", t)) for t in range(2)]
-        ring = mxa.new_ring(16, dev)
-        b3 = R * C * 2 + R * C + 80
-
-        def d_set(i):
-            return dict(x=xs[i % 2] if i < 2 else xs[i % 2].clone(),
-                        qT=torch.empty((C, R), dtype=torch.uint8, device=dev))
-
-        def delayed(st, t):
-            mxa.check(lib.fp8_quantize_delayed(st["x"].data_ptr(), 1, R, C, 0, 1, None, st["qT"].data_ptr(),
-                                               ring.data_ptr(), 16, t % 16, 448.0, 1.0, None, sp))
-        t3, k3 = time_rotating(d_set, delayed, b3, args.steps, args.warmup, stream, torch)
-        print(json.dumps({"mode": "delayed", "us": round(t3 * 1e6, 2), "GB/s": round(b3 / t3 / 1e9, 1),
-                          "buffer_sets": k3}), flush=True)
+    if args.mode in ("delayed", "delayed_grad"):
+        res = bench_delayed(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, args.steps,
+                            streams=("act",) if args.mode == "delayed" else ("grad",), with_null=False)
+        print(json.dumps({"mode": args.mode, **res}), flush=True)
+        return
+    if args.mode in ("col", "sr", "fp6dual"):
+        res = {"col": bench_wgrad_quant, "sr": bench_sr, "fp6dual": bench_fp6}[args.mode](
+            lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, args.steps)
+        print(json.dumps({"mode": args.mode, **res}), flush=True)
         return
     if args.mode == "gemm":
         print(json.dumps({"mode": "gemm", "gemm": bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np,
@@ -177,15 +235,18 @@ def main():
                          qc=torch.empty((C, R), dtype=torch.uint8, device=dev),
                          sc=torch.empty((C, R // 32), dtype=torch.uint8, device=dev),
                          a=torch.zeros(1, dtype=torch.float32, device=dev)))
+    idx = [0]
 
-    def dual(s):
+    def dual():
+        s = sets[idx[0] % nsets]
+        idx[0] += 1
         st = lib.mx_quantize_dual(s["x"].data_ptr(), 1, R, C, 32, 0, 1, s["qr"].data_ptr(), s["sr"].data_ptr(),
                                   s["qc"].data_ptr(), s["sc"].data_ptr(), s["a"].data_ptr(), sp)
         if st != 0:
             raise RuntimeError(lib.mx_status_str(st).decode())
 
     for i in range(args.warmup):
-        dual(sets[i % nsets])
+        dual()
     torch.cuda.synchronize()
     # one event pair around the K back-to-back launches on the kernel's stream:
     # their average is the kernel's average launch duration (no per-launch
@@ -194,15 +255,18 @@ def main():
     t0 = time.perf_counter()
     e0.record(stream)
     for i in range(args.steps):
-        dual(sets[i % nsets])
+        dual()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    dist = launch_distribution(dual, max(args.steps, 50), stream, torch)
     avg_kern_s = e0.elapsed_time(e1) / args.steps / 1e3
     ms_per_step = wall / args.steps * 1e3
     value = algo_bytes * args.steps / wall / 1e9
     achieved = algo_bytes / avg_kern_s / 1e9
     traffic = measured_traffic()
+    del sets
+    roof = copy_roof(torch, dev, stream)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -217,6 +281,10 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic)},
         "kernel_us": round(avg_kern_s * 1e6, 2),
+        "launch_us": dist,
+        "gpu_clock": profile_clock(TRAFFIC_FILE, QUANT_SOURCES),
+        "copy_roof": roof,
+        "frac_of_copy_roof": round(achieved / roof["GB/s"], 4),
     }
 
     # ------------------------------------------------------------------ GEMM + other workloads
@@ -253,8 +321,9 @@ def time_calls(fn, n, warm, stream, torch):
 CACHE_DEFEAT_BYTES = 768 << 20
 
 
-def time_rotating(make_set, call, per_call_bytes, n, warm, stream, torch):
-    """time_calls over ceil(768 MiB / per_call_bytes) (2..16) buffer sets used in turn."""
+def time_rotating(make_set, call, per_call_bytes, n, warm, stream, torch, dist=False):
+    """time_calls over ceil(768 MiB / per_call_bytes) (2..16) buffer sets used in turn;
+    with dist, also the per-launch distribution."""
     k = max(2, min(16, -(-CACHE_DEFEAT_BYTES // per_call_bytes)))
     sets = [make_set(i) for i in range(k)]
     idx = [0]
@@ -263,8 +332,85 @@ def time_rotating(make_set, call, per_call_bytes, n, warm, stream, torch):
         call(sets[idx[0] % k], idx[0])
         idx[0] += 1
     t = time_calls(fn, n, warm, stream, torch)
+    d = launch_distribution(fn, n, stream, torch) if dist else None
     del sets
-    return t, k
+    return (t, k, d) if dist else (t, k)
+
+
+def hbm_leg(t, nbytes, k, dist=None):
+    r = {"us": round(t * 1e6, 2), "GB/s": round(nbytes / t / 1e9, 1),
+         "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_call": nbytes, "buffer_sets": k}
+    if dist:
+        r["launch_us"] = dist
+    return r
+
+
+def bench_delayed(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=32, streams=("act", "grad"),
+                  with_null=True):
+    """Per-tensor delayed scaling, BF16 8192 x 4096 -> transposed FP8 with the ring
+    fold: the activation stream (E4M3) and the gradient stream (E5M2), each on its
+    own ring of 16 with ticket scratch; the activation stream also on the page's
+    plain ring without scratch; and the per-call cost on a small 128 x 256 tensor,
+    where the call is launch-bound (the fixed overhead per linear layer)."""
+    R, C = 8192, 4096
+    b3 = R * C * 2 + R * C + 80
+    res = {}
+    for stream_name in streams:
+        fmt = {"act": 0, "grad": 1}[stream_name]
+        fp8_max = workloads.DELAYED_FP8_MAX[stream_name]
+        xs = [up_bf16(workloads.delayed_step(stream_name, t)) for t in range(2)]
+        modes = (("scratch", True), ("no_scratch", False)) if with_null and stream_name == "act" else \
+            (("scratch", True),)
+        for mode, use_scratch in modes:
+            ring = mxa.new_ring(16, dev)
+            tickets = mxa.new_tickets(dev) if use_scratch else None
+
+            def d_set(i):
+                return dict(x=xs[i % 2] if i < 2 else xs[i % 2].clone(),
+                            qT=torch.empty((C, R), dtype=torch.uint8, device=dev))
+
+            def delayed(st, t):
+                mxa.check(lib.fp8_quantize_delayed(st["x"].data_ptr(), 1, R, C, fmt, 1, None, st["qT"].data_ptr(),
+                                                   ring.data_ptr(), 16, t % 16, fp8_max, 1.0, None,
+                                                   None if tickets is None else tickets.data_ptr(), sp))
+            t3, k3, d3 = time_rotating(d_set, delayed, b3, steps, 4, stream, torch, dist=True)
+            name = f"delayed_fp8_{mxa_fmt(fmt)}_transposed_bf16_8192x4096" + ("" if use_scratch else "_no_scratch")
+            res[name] = hbm_leg(t3, b3, k3, d3)
+        del xs
+    # per-call fixed cost: a launch-bound 128 x 256 call, ring fold included
+    x = up_bf16(workloads.delayed_step("act", 0, rows=128, cols=256))
+    qT = torch.empty((256, 128), dtype=torch.uint8, device=dev)
+    ring = mxa.new_ring(16, dev)
+    tickets = mxa.new_tickets(dev)
+    n = 200
+    calls = [0]
+
+    def small():
+        mxa.check(lib.fp8_quantize_delayed(x.data_ptr(), 1, 128, 256, 0, 1, None, qT.data_ptr(), ring.data_ptr(), 16,
+                                           calls[0] % 16, 448.0, 1.0, None, tickets.data_ptr(), sp))
+        calls[0] += 1
+    for _ in range(10):
+        small()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(n):
+        small()
+    h1 = time.perf_counter()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    res["delayed_fp8_e4m3_transposed_bf16_128x256_per_call"] = {
+        "gpu_us_per_call": round(e0.elapsed_time(e1) / n * 1e3, 2),
+        "host_enqueue_us_per_call": round((h1 - h0) / n * 1e6, 2),
+        "launch_us": launch_distribution(small, n, stream, torch),
+        "note": "back-to-back calls on one stream; the GPU time per call is the fixed cost of a call "
+                "(launch, ring fold) on a launch-bound tensor"}
+    return res
+
+
+def mxa_fmt(code):
+    return {0: "e4m3", 1: "e5m2"}[code]
 
 
 def bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=10):
@@ -283,10 +429,12 @@ def bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=1
     t = time_calls(call, steps, 2, stream, torch)
     flops = 2.0 * M * N * K
     tf = flops / t / 1e12
+    prof = os.path.join(ROOT, "profiles", "gemm256_kernel_mxfp8_8192x14336x4096.md")
     return {"workload": "MXFP8 E4M3 block-scaled GEMM 8192x4096 x (14336x4096)^T, FP32 accumulate, BF16 out",
             "value": round(tf, 1), "unit": "TFLOP/s", "ms_per_call": round(t * 1e3, 4),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / FP8_PEAK_TFLOPS, 4), "traffic": None}}
+                         "frac": round(tf / FP8_PEAK_TFLOPS, 4), "traffic": None},
+            "profile": {"file": os.path.relpath(prof, ROOT), "current": profile_is_current(prof, GEMM_SOURCES)}}
 
 
 def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
@@ -303,24 +451,25 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
     b1 = 256 * 1024 * 4 + 256 * 1024 + 256 * 32
     res["rowwise_quant_f32_256x1024"] = {"us": round(tq * 1e6, 2), "GB/s": round(b1 / tq / 1e9, 1)}
     res["dequant_f32_256x1024"] = {"us": round(td * 1e6, 2), "GB/s": round(b1 / td / 1e9, 1)}
-    # per-tensor delayed scaling, BF16 8192 x 4096 -> transposed FP8, ring of 16
+    res.update(bench_delayed(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
+    res.update(bench_sr(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch))
+    res.update(bench_fp6(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch))
+    res.update(bench_wgrad_quant(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch))
+    g_bits, x_bits, mask = workloads.weight_grad_operands()
+    st0 = wgrad_set(dev, up_bf16(g_bits), up_bf16(x_bits), torch)
+    wgrad_quant(lib, sp, mxa, st0, mask)
+    res["mxfp4_gemm_4096x4096x8192"] = time_gemm_fp4(lib, sp, stream, dev, st0["gq"], st0["gs"], st0["xq"],
+                                                     st0["xs"], torch, 10)
+    del st0
+    res.update(bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
+    res.update(bench_gemm_requant(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
+    res.update(bench_gemm_fp6(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
+    return res
+
+
+def bench_sr(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=32):
+    """Stochastic-rounding MXFP4 row-wise of a BF16 8192 x 4096 gradient, one uint32 word per element."""
     R, C = 8192, 4096
-    xs = [up_bf16(workloads.delayed_step("act", t)) for t in range(2)]
-    ring = mxa.new_ring(16, dev)
-    b3 = R * C * 2 + R * C + 80
-
-    def d_set(i):
-        return dict(x=xs[i % 2] if i < 2 else xs[i % 2].clone(), qT=torch.empty((C, R), dtype=torch.uint8, device=dev))
-
-    def delayed(st, t):
-        mxa.check(lib.fp8_quantize_delayed(st["x"].data_ptr(), 1, R, C, 0, 1, None, st["qT"].data_ptr(),
-                                           ring.data_ptr(), 16, t % 16, 448.0, 1.0, None, sp))
-    t3, k3 = time_rotating(d_set, delayed, b3, 32, 4, stream, torch)
-    res["delayed_fp8_transposed_bf16_8192x4096"] = {"us": round(t3 * 1e6, 2), "GB/s": round(b3 / t3 / 1e9, 1),
-                                                    "hbm_frac": round(b3 / t3 / 1e9 / HBM_PEAK_GBS, 4),
-                                                    "buffer_sets": k3}
-    del xs
-    # stochastic-rounding MXFP4 row-wise of a BF16 8192 x 4096 gradient, one uint32 word per element
     gx = up_bf16(workloads.activation_bf16(R, C))
     words = torch.from_numpy(workloads.random_words((R, C), 47).view(np.int32)).to(dev)
     bsr = R * C * 2 + R * C * 4 + R * C // 2 + R * C // 32
@@ -329,14 +478,16 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
         return dict(x=gx if i == 0 else gx.clone(), w=words if i == 0 else words.clone(),
                     q=torch.empty((R, C // 2), dtype=torch.uint8, device=dev),
                     s=torch.empty((R, C // 32), dtype=torch.uint8, device=dev))
-    tsr, ksr = time_rotating(sr_set, lambda st, t: mxa.check(lib.mx_quantize_sr(
+    t, k, d = time_rotating(sr_set, lambda st, i: mxa.check(lib.mx_quantize_sr(
         st["x"].data_ptr(), 1, R, C, 32, 2, 1, st["w"].data_ptr(), st["q"].data_ptr(), st["s"].data_ptr(), None, sp)),
-        bsr, 32, 4, stream, torch)
-    res["sr_mxfp4_rowwise_bf16_8192x4096"] = {"us": round(tsr * 1e6, 2), "GB/s": round(bsr / tsr / 1e9, 1),
-                                              "hbm_frac": round(bsr / tsr / 1e9 / HBM_PEAK_GBS, 4),
-                                              "buffer_sets": ksr}
-    del words
-    # MXFP6 E3M2 row-wise of the same gradient (codes packed 4 per 3 bytes)
+        bsr, steps, 4, stream, torch, dist=True)
+    return {"sr_mxfp4_rowwise_bf16_8192x4096": hbm_leg(t, bsr, k, d)}
+
+
+def bench_fp6(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=32):
+    """MXFP6 E3M2 of a BF16 8192 x 4096 tensor: row-wise, and dual (both orientations from one read)."""
+    R, C = 8192, 4096
+    gx = up_bf16(workloads.activation_bf16(R, C))
     bf6 = R * C * 2 + R * C * 3 // 4 + R * C // 32
 
     def f6_set(i):
@@ -344,52 +495,41 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
                     s=torch.empty((R, C // 32), dtype=torch.uint8, device=dev),
                     qc=torch.empty((C, R * 3 // 4), dtype=torch.uint8, device=dev),
                     sc=torch.empty((C, R // 32), dtype=torch.uint8, device=dev))
-    tf6, kf6 = time_rotating(f6_set, lambda st, t: mxa.check(lib.mx_quantize(
+    t, k, d = time_rotating(f6_set, lambda st, i: mxa.check(lib.mx_quantize(
         st["x"].data_ptr(), 1, R, C, 32, 4, 1, 0, 0, 0, st["q"].data_ptr(), st["s"].data_ptr(), None, sp)),
-        bf6, 32, 4, stream, torch)
-    res["mxfp6_e3m2_rowwise_bf16_8192x4096"] = {"us": round(tf6 * 1e6, 2), "GB/s": round(bf6 / tf6 / 1e9, 1),
-                                                "hbm_frac": round(bf6 / tf6 / 1e9 / HBM_PEAK_GBS, 4),
-                                                "buffer_sets": kf6}
-    # MXFP6 E3M2 dual (row-wise + column-wise from one read)
+        bf6, steps, 4, stream, torch, dist=True)
+    res = {"mxfp6_e3m2_rowwise_bf16_8192x4096": hbm_leg(t, bf6, k, d)}
     bf6d = R * C * 2 + 2 * (R * C * 3 // 4 + R * C // 32)
-    tf6d, kf6d = time_rotating(f6_set, lambda st, t: mxa.check(lib.mx_quantize_dual(
+    t, k, d = time_rotating(f6_set, lambda st, i: mxa.check(lib.mx_quantize_dual(
         st["x"].data_ptr(), 1, R, C, 32, 4, 1, st["q"].data_ptr(), st["s"].data_ptr(), st["qc"].data_ptr(),
-        st["sc"].data_ptr(), None, sp)), bf6d, 32, 4, stream, torch)
-    res["mxfp6_e3m2_dual_bf16_8192x4096"] = {"us": round(tf6d * 1e6, 2), "GB/s": round(bf6d / tf6d / 1e9, 1),
-                                             "hbm_frac": round(bf6d / tf6d / 1e9 / HBM_PEAK_GBS, 4),
-                                             "buffer_sets": kf6d}
-    del gx
-    # Hadamard + column-wise MXFP4 quantization of both operands, then the MXFP4 GEMM
+        st["sc"].data_ptr(), None, sp)), bf6d, steps, 4, stream, torch, dist=True)
+    res["mxfp6_e3m2_dual_bf16_8192x4096"] = hbm_leg(t, bf6d, k, d)
+    return res
+
+
+def wgrad_set(dev, G, X, torch):
+    return dict(G=G, X=X, gq=torch.empty((4096, 4096), dtype=torch.uint8, device=dev),
+                gs=torch.empty((4096, 256), dtype=torch.uint8, device=dev),
+                xq=torch.empty((4096, 4096), dtype=torch.uint8, device=dev),
+                xs=torch.empty((4096, 256), dtype=torch.uint8, device=dev))
+
+
+def wgrad_quant(lib, sp, mxa, st, mask):
+    """Hadamard + column-wise MXFP4 (round-up rule) of both weight-gradient operands."""
+    mxa.check(lib.mx_quantize(st["G"].data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, st["gq"].data_ptr(),
+                              st["gs"].data_ptr(), None, sp))
+    mxa.check(lib.mx_quantize(st["X"].data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, st["xq"].data_ptr(),
+                              st["xs"].data_ptr(), None, sp))
+
+
+def bench_wgrad_quant(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=20):
+    """Hadamard + column-wise MXFP4 quantization of both BF16 8192 x 4096 weight-gradient operands."""
     g_bits, x_bits, mask = workloads.weight_grad_operands()
     G, X = up_bf16(g_bits), up_bf16(x_bits)
     b5 = 2 * (8192 * 4096 * 2 + 4096 * 4096 + 4096 * 256)
-
-    def h_set(i):
-        return dict(G=G if i == 0 else G.clone(), X=X if i == 0 else X.clone(),
-                    gq=torch.empty((4096, 4096), dtype=torch.uint8, device=dev),
-                    gs=torch.empty((4096, 256), dtype=torch.uint8, device=dev),
-                    xq=torch.empty((4096, 4096), dtype=torch.uint8, device=dev),
-                    xs=torch.empty((4096, 256), dtype=torch.uint8, device=dev))
-
-    def quant5(st, t):
-        mxa.check(lib.mx_quantize(st["G"].data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, st["gq"].data_ptr(),
-                                  st["gs"].data_ptr(), None, sp))
-        mxa.check(lib.mx_quantize(st["X"].data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, st["xq"].data_ptr(),
-                                  st["xs"].data_ptr(), None, sp))
-    t5q, k5 = time_rotating(h_set, quant5, b5, 20, 3, stream, torch)
-    res["hadamard_mxfp4_colwise_quant_2x_bf16_8192x4096"] = {"us": round(t5q * 1e6, 2),
-                                                              "GB/s": round(b5 / t5q / 1e9, 1),
-                                                              "hbm_frac": round(b5 / t5q / 1e9 / HBM_PEAK_GBS, 4),
-                                                              "buffer_sets": k5}
-    st0 = h_set(0)
-    quant5(st0, 0)
-    gq, gs, xq, xsc = st0["gq"], st0["gs"], st0["xq"], st0["xs"]
-    res["mxfp4_gemm_4096x4096x8192"] = time_gemm_fp4(lib, sp, stream, dev, gq, gs, xq, xsc, torch, 10)
-    del G, X, gq, gs, xq, xsc, st0
-    res.update(bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
-    res.update(bench_gemm_requant(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
-    res.update(bench_gemm_fp6(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
-    return res
+    t, k, d = time_rotating(lambda i: wgrad_set(dev, G if i == 0 else G.clone(), X if i == 0 else X.clone(), torch),
+                            lambda st, i: wgrad_quant(lib, sp, mxa, st, mask), b5, steps, 3, stream, torch, dist=True)
+    return {"hadamard_mxfp4_colwise_quant_2x_bf16_8192x4096": hbm_leg(t, b5, k, d)}
 
 
 def bench_gemm_fp6(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=5):
@@ -512,9 +652,44 @@ GEMM_PROFILES = {
 }
 
 
+def _pmc_all(paths, kernel_substr):
+    """Mean per dispatch of every counter in the given --pmc CSVs for one kernel."""
+    import csv
+    acc = {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            if kernel_substr in r["Kernel_Name"]:
+                acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def _counter_lines(counters, avg_ns):
+    """Counter lines of a summary, with the derived figures the counters allow
+    (GRBM_GUI_ACTIVE is summed over the 8 XCDs; the SQ_* counters over all SIMDs)."""
+    lines = [f"{k}_per_dispatch: {v:.6g}" for k, v in sorted(counters.items())]
+    grbm = counters.get("GRBM_GUI_ACTIVE")
+    if grbm:
+        cyc = grbm / 8
+        lines.append(f"gpu_clock_GHz_from_GRBM: {cyc / avg_ns:.3f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in counters:
+            lines.append(f"mfma_busy_fraction: {counters['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 1024):.4f}")
+        if "SQ_BUSY_CYCLES" in counters:
+            lines.append(f"sq_busy_fraction: {counters['SQ_BUSY_CYCLES'] / (cyc * 8):.4f}")
+    waves = counters.get("SQ_WAVES")
+    if waves:
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR",
+                  "SQ_INSTS_MFMA"):
+            if k in counters:
+                lines.append(f"{k}_per_wave: {counters[k] / waves:.1f}")
+    if "SQ_LDS_BANK_CONFLICT" in counters and "SQ_LDS_IDX_ACTIVE" in counters and counters["SQ_LDS_IDX_ACTIVE"]:
+        lines.append(f"lds_bank_conflict_per_active_cycle: "
+                     f"{counters['SQ_LDS_BANK_CONFLICT'] / counters['SQ_LDS_IDX_ACTIVE']:.4f}")
+    return lines
+
+
 def summarize_gemm(args):
     """Profile summaries of the GEMM kernels from a rocprofv3 --stats CSV (and,
-    if given, a --pmc CSV with SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE)."""
+    if given, --pmc CSVs: MFMA busy, GRBM, LDS and wait counters)."""
     import csv
     rows = list(csv.DictReader(open(args.stats)))
     for sub, (fname, title, flops, peak) in GEMM_PROFILES.items():
@@ -530,13 +705,8 @@ def summarize_gemm(args):
                  f"flops_per_launch: {flops:.0f}", f"achieved_TFLOPs_at_avg: {tf:.1f}",
                  f"fraction_of_dense_peak_{peak:.0f}: {tf / peak:.4f}"]
         if args.pmc_gemm:
-            busy, n = _pmc_mean(args.pmc_gemm, sub, "SQ_VALU_MFMA_BUSY_CYCLES")
-            grbm, _ = _pmc_mean(args.pmc_gemm, sub, "GRBM_GUI_ACTIVE")
-            # GRBM_GUI_ACTIVE is summed over the 8 XCDs; 1024 SIMDs carry the MFMA busy cycles
-            lines += [f"SQ_VALU_MFMA_BUSY_CYCLES_per_dispatch: {busy:.4g}  (n={n})",
-                      f"GRBM_GUI_ACTIVE_per_dispatch: {grbm:.4g}",
-                      f"mfma_busy_fraction: {busy / (grbm / 8 * 1024):.4f}",
-                      f"gpu_clock_GHz_from_GRBM: {grbm / 8 / avg:.3f}"]
+            lines += _counter_lines(_pmc_all(args.pmc_gemm, sub), avg)
+        lines.append(f"kernel_source_hash: {kernel_source_hash(GEMM_SOURCES)}")
         lines.append("")
         out = os.path.join(args.summarize_gemm, fname)
         with open(out, "w") as f:
@@ -544,83 +714,160 @@ def summarize_gemm(args):
         print("\n".join(lines))
 
 
+R8, C4 = 8192, 4096
+WORKLOADS = {
+    # --workload -> (title, algorithmic bytes per launch, kernel sources)
+    "dual": ("MXFP8 E4M3 dual quantization, BF16 8192x4096, round-up scale, amax",
+             R8 * C4 * 2 + 2 * R8 * C4 + 2 * (R8 * C4 // 32) + 4, QUANT_SOURCES),
+    "delayed": ("per-tensor delayed-scaling FP8 E4M3 cast, BF16 8192x4096 -> transposed codes, ring of 16",
+                R8 * C4 * 2 + R8 * C4 + 80, QUANT_SOURCES),
+    "delayed_grad": ("per-tensor delayed-scaling FP8 E5M2 cast (gradient stream), BF16 8192x4096 -> transposed "
+                     "codes, ring of 16", R8 * C4 * 2 + R8 * C4 + 80, QUANT_SOURCES),
+    "col": ("fixed-sign Hadamard + column-wise MXFP4 E2M1 quantization of one BF16 8192x4096 weight-gradient "
+            "operand (8192 tokens), round-up scale", R8 * C4 * 2 + R8 * C4 // 2 + R8 * C4 // 32, QUANT_SOURCES),
+    "sr": ("stochastic-rounding MXFP4 row-wise, BF16 8192x4096 + one uint32 word per element",
+           R8 * C4 * 6 + R8 * C4 // 2 + R8 * C4 // 32, ("quantize_sr.hip", "mx_device.hpp")),
+    "fp6dual": ("MXFP6 E3M2 dual quantization, BF16 8192x4096, round-up scale",
+                R8 * C4 * 2 + 2 * (R8 * C4 * 3 // 4 + R8 * C4 // 32), ("quantize_fp6.hip", "mx_device.hpp")),
+}
+
+
 def summarize(args):
-    """Write the profile summary of the headline kernel from rocprofv3 CSVs.
+    """Write the profile summary of a quantizer kernel from rocprofv3 CSVs.
 
     FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by the ratio of the
     known bytes of a plain 256 MiB device copy to what the same counters read
     for it; traffic_bytes_per_launch is their scaled sum."""
     import csv
+    title, algo, sources = WORKLOADS[args.workload]
     stats = [r for r in csv.DictReader(open(args.stats)) if args.kernel in r["Name"]]
     avg_ns = float(stats[0]["AverageNs"])
     calls = int(stats[0]["Calls"])
-    copy_bytes_kib = 256 * 1024
-    cf, _ = _pmc_mean(args.copy_fetch, "copyBuffer", "FETCH_SIZE") if "copyBuffer" in open(args.copy_fetch).read() \
-        else _pmc_mean(args.copy_fetch, "elementwise", "FETCH_SIZE")
-    cw, _ = _pmc_mean(args.copy_write, "copyBuffer", "WRITE_SIZE") if "copyBuffer" in open(args.copy_write).read() \
-        else _pmc_mean(args.copy_write, "elementwise", "WRITE_SIZE")
-    kf, nf = _pmc_mean(args.fetch, args.kernel, "FETCH_SIZE")
-    kw, nw = _pmc_mean(args.write, args.kernel, "WRITE_SIZE")
-    f_scale, w_scale = copy_bytes_kib / cf, copy_bytes_kib / cw
-    fetch_b = kf * f_scale * 1024
-    write_b = kw * w_scale * 1024
-    if args.workload == "dual":
-        algo = 8192 * 4096 * 2 + 2 * 8192 * 4096 + 2 * (8192 * 4096 // 32) + 4
-        title = "MXFP8 E4M3 dual quantization, BF16 8192x4096, round-up scale, amax"
-    else:
-        algo = 8192 * 4096 * 2 + 8192 * 4096 + 80
-        title = "per-tensor delayed-scaling FP8 E4M3 cast, BF16 8192x4096 -> transposed codes, ring of 16"
-    lines = [
-        f"# {args.kernel} -- {title}",
-        "",
-        f"command: {args.command}",
-        "",
-        f"kernel_avg_ns: {avg_ns:.0f}",
-        f"kernel_calls: {calls}",
-        f"algorithmic_bytes_per_launch: {algo}",
-        f"achieved_GBps_at_avg: {algo / avg_ns:.1f}",
-        f"FETCH_SIZE_KiB_per_dispatch_raw: {kf:.1f}  (n={nf})",
-        f"WRITE_SIZE_KiB_per_dispatch_raw: {kw:.1f}  (n={nw})",
-        f"copy_calibration: 256 MiB copy reads FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB "
-        f"-> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}",
-        f"hbm_fetch_bytes_per_launch: {fetch_b:.0f}",
-        f"hbm_write_bytes_per_launch: {write_b:.0f}",
-        f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
-        f"traffic_over_algorithmic: {(fetch_b + write_b) / algo:.4f}",
-        f"kernel_source_hash: {kernel_source_hash()}",
-        "",
-    ]
+    lines = [f"# {args.kernel} -- {title}", "", f"command: {args.command}", "",
+             f"kernel_avg_ns: {avg_ns:.0f}", f"kernel_min_ns: {float(stats[0]['MinNs']):.0f}",
+             f"kernel_max_ns: {float(stats[0]['MaxNs']):.0f}", f"kernel_calls: {calls}",
+             f"algorithmic_bytes_per_launch: {algo}", f"achieved_GBps_at_avg: {algo / avg_ns:.1f}",
+             f"fraction_of_hbm_peak: {algo / avg_ns / HBM_PEAK_GBS:.4f}"]
+    if args.fetch and args.write and args.copy_fetch and args.copy_write:
+        copy_bytes_kib = 256 * 1024
+        ck = "copyBuffer" if "copyBuffer" in open(args.copy_fetch).read() else "elementwise"
+        cf, _ = _pmc_mean(args.copy_fetch, ck, "FETCH_SIZE")
+        cw, _ = _pmc_mean(args.copy_write, ck, "WRITE_SIZE")
+        kf, nf = _pmc_mean(args.fetch, args.kernel, "FETCH_SIZE")
+        kw, nw = _pmc_mean(args.write, args.kernel, "WRITE_SIZE")
+        f_scale, w_scale = copy_bytes_kib / cf, copy_bytes_kib / cw
+        fetch_b = kf * f_scale * 1024
+        write_b = kw * w_scale * 1024
+        lines += [f"FETCH_SIZE_KiB_per_dispatch_raw: {kf:.1f}  (n={nf})",
+                  f"WRITE_SIZE_KiB_per_dispatch_raw: {kw:.1f}  (n={nw})",
+                  f"copy_calibration: 256 MiB copy reads FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB "
+                  f"-> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}",
+                  f"hbm_fetch_bytes_per_launch: {fetch_b:.0f}", f"hbm_write_bytes_per_launch: {write_b:.0f}",
+                  f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
+                  f"traffic_over_algorithmic: {(fetch_b + write_b) / algo:.4f}"]
+    if args.pmc:
+        lines += _counter_lines(_pmc_all(args.pmc, args.kernel), avg_ns)
+    lines += [f"kernel_source_hash: {kernel_source_hash(sources)}", ""]
     with open(args.summarize, "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
 
 
-def cpu_baseline(workloads, np, target_s=10.0):
-    """The CPU oracle (numpy, one thread) on the same workload: dual E4M3
-    quantization + amax of leading row strips of the BF16 8192 x 4096 input,
-    growing the strip until about target_s seconds of host work (or the whole
-    tensor); the rate of the largest strip is reported."""
+def cpu_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count()}
+
+
+def _grow(run, nbytes_of, first, full, target_s):
+    """Run `run(n)` on growing leading samples (first, 2 first, ...) until about
+    target_s seconds were spent or the whole input was done; the rate of the
+    largest sample: (n, seconds, GB/s)."""
+    n, spent = first, 0.0
+    while True:
+        t0 = time.perf_counter()
+        run(n)
+        dt = time.perf_counter() - t0
+        spent += dt
+        if n >= full or spent + 2 * dt > target_s:
+            return n, dt, nbytes_of(n) / dt / 1e9, spent
+        n = min(full, 2 * n)
+
+
+def cpu_baseline(workloads, np, target_s=8.0):
+    """The CPU oracle as it stands, on bounded samples of the same workloads, on
+    the host of the GPU: the headline (dual E4M3 quantization + amax of leading
+    row strips of the BF16 8192 x 4096 input, one thread) and, under ``legs``,
+    the delayed-scaling cast with its fold, the Hadamard + MXFP4 column-wise
+    quantizer (one thread each) and the float64 GEMM reference of the MXFP8 MLP
+    product (BLAS, thread count stated)."""
+    from oracle import delayed as odl
+    from oracle import gemm as og
     from oracle import mx as omx
     cols = 4096
     xb_all = workloads.activation_bf16()
-    rows, spent, rate, dt = 256, 0.0, None, 0.0
-    while True:
+
+    def dual(rows):
         xs = workloads.bf16_to_f32(xb_all[:rows])
-        t0 = time.perf_counter()
         omx.quantize_dual(xs, "e4m3", "ceil")
         omx.tensor_amax(xs)
-        dt = time.perf_counter() - t0
-        spent += dt
-        b = rows * cols * 2 + 2 * rows * cols + 2 * (rows * cols // 32) + 4
-        rate = b / dt / 1e9
-        if rows >= 8192 or spent >= target_s:
-            break
-        rows = min(8192, rows * 2 if spent + 2 * dt < target_s * 1.5 else rows)
-        if spent + 2 * dt >= target_s * 1.5:
-            break
-    return {"value": round(rate, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} of 8192 rows of the BF16 8192x4096 input (dual E4M3 quantization + amax), "
-                      f"{dt:.1f} s for that strip, {spent:.1f} s of oracle work in total on the host CPU"}
+    dual_bytes = lambda r: r * cols * 2 + 2 * r * cols + 2 * (r * cols // 32) + 4  # noqa: E731
+    rows, dt, rate, spent = _grow(dual, dual_bytes, 256, 8192, target_s)
+    out = {"value": round(rate, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"first {rows} of 8192 rows of the BF16 8192x4096 input (dual E4M3 quantization + amax), "
+                     f"{dt:.1f} s for that strip, {spent:.1f} s of oracle work in total on the host CPU",
+           **cpu_info(), "legs": {}}
+    del xb_all
+    # delayed scaling: cast with the ring's multiplier + amax + fold, leading rows of step 0
+    xd = workloads.bf16_to_f32(workloads.delayed_step("act", 0))
+
+    def delayed(r):
+        odl.quantize_delayed(xd[:r], "e4m3", odl.Ring(16), 0, 448.0, 1.0)
+    r, dt, rate, _ = _grow(delayed, lambda r: r * cols * 3 + 80, 256, 8192, target_s / 2)
+    out["legs"]["delayed_fp8_e4m3_transposed"] = {"GB/s": round(rate, 6), "cores": 1,
+                                                  "sample": f"first {r} of 8192 rows, {dt:.2f} s"}
+    del xd
+    # Hadamard + MXFP4 column-wise: blocks run along the 8192 tokens, so samples are column strips
+    g_bits, _, mask = workloads.weight_grad_operands()
+    gx = workloads.bf16_to_f32(g_bits)
+
+    def had(c):
+        omx.quantize_colwise_t(gx[:, :c], "e2m1", "ceil", hadamard_mask=mask)
+    c, dt, rate, _ = _grow(had, lambda c: 8192 * c * 2 + 8192 * c // 2 + 8192 * c // 32, 128, 4096, target_s / 2)
+    out["legs"]["hadamard_mxfp4_colwise_one_operand"] = {"GB/s": round(rate, 6), "cores": 1,
+                                                        "sample": f"first {c} of 4096 columns (all 8192 tokens), "
+                                                                  f"{dt:.2f} s"}
+    del gx
+    # float64 GEMM reference (dequantized operands, BLAS) on leading rows of the MXFP8 MLP product
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    threads = min(16, os.cpu_count() or 1)
+    a_bits, w_bits = workloads.mlp_operands()
+    qa, sa = omx.quantize_rowwise(workloads.bf16_to_f32(a_bits[:512]), "e4m3", "ceil")
+    qw, sw = omx.quantize_rowwise(workloads.bf16_to_f32(w_bits), "e4m3", "ceil")
+    del a_bits, w_bits
+
+    def gemm(m):
+        og.gemm_ref(qa[:m], sa[:m], "e4m3", qw, sw, "e4m3")
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=threads):
+            m, dt, _, _ = _grow(gemm, lambda m: 0, 64, 512, target_s / 2)
+    else:
+        m, dt, _, _ = _grow(gemm, lambda m: 0, 64, 512, target_s / 2)
+        threads = None
+    out["legs"]["gemm_fp64_reference_mxfp8_mlp"] = {
+        "TFLOP/s": round(2.0 * m * 14336 * 4096 / dt / 1e12, 6), "threads": threads,
+        "sample": f"first {m} of 8192 output rows of the 8192x14336x4096 product (float64 BLAS on the "
+                  f"dequantized operands, dequantization included), {dt:.2f} s"}
+    return out
 
 
 if __name__ == "__main__":
