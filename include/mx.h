@@ -188,6 +188,26 @@ mx_status_t fp8_quantize_delayed(const void* x, mx_dtype_t in, int64_t rows, int
                                  float margin, float* amax_out, uint32_t* ticket_scratch,
                                  hipStream_t stream);
 
+/* fp8_quantize_delayed for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same operation, arguments and results as
+ * fp8_quantize_delayed, with the ticket scratch taken from a fixed array inside
+ * the library (MX_TICKET_WORDS uint32 words = 16 KiB per device, held by each
+ * GPU the library runs on until the process ends) instead of a caller buffer.
+ * The call allocates nothing: the array's device address is looked up once per
+ * device (hipGetSymbolAddress) on the first call made with that device current.
+ * The array is zero at load and every call leaves it zero.  Its size does not
+ * depend on the input (128 ticket groups serve any number of workgroups), so
+ * no input is rejected for its size.  All calls on one GPU share the array:
+ * calls that overlap on one GPU (different streams without ordering) race on
+ * it and must not be issued; calls ordered on one stream are safe.
+ * Errors: those of fp8_quantize_delayed, and MX_ERR_LAUNCH when the array's
+ * device address cannot be obtained. */
+mx_status_t fp8_quantize_delayed_static(const void* x, mx_dtype_t in, int64_t rows, int64_t cols,
+                                        mx_elem_t fmt, fp8_layout_t layout, uint8_t* q, uint8_t* qT,
+                                        float* ring, int hist_len, int hist_idx, float fp8_max,
+                                        float margin, float* amax_out, hipStream_t stream);
+
 /* MX dequantization ([UE8M0] first part, section 2: decoding an E8M0 scale is an
  * exponent shift): out = Q_i * 2^(c - 127), computed exactly and rounded once to
  * `out_dtype` (F32 or BF16; overflow gives +-Inf, scale 255 or a NaN code gives

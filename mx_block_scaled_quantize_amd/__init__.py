@@ -60,16 +60,19 @@ lib.mx_dequantize.argtypes = [_p, _p, _i64, _i64, _i32, _i32, _i32, _p, _i32, _p
 lib.mx_gemm.argtypes = [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64, _f32, _p, _i32, _i64, _p]
 lib.mx_quantize_sr.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p]
 lib.mm_fp8.argtypes = [_p, _p, _i32, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p]
+lib.fp8_quantize_delayed_static.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _p, _p, _p, _i32, _i32, _f32, _f32, _p,
+                                            _p]
 lib.mx_gemm_requant.argtypes = [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64, _f32, _i32, _i32, _p, _p, _p, _p]
 for _f in (lib.mx_quantize, lib.mx_quantize_dual, lib.fp8_quantize_delayed, lib.mx_dequantize, lib.mx_gemm,
-           lib.mx_quantize_sr, lib.mm_fp8, lib.mx_gemm_requant):
+           lib.mx_quantize_sr, lib.mm_fp8, lib.mx_gemm_requant, lib.fp8_quantize_delayed_static):
     _f.restype = ctypes.c_int
 lib.mx_status_str.argtypes = [ctypes.c_int]
 lib.mx_status_str.restype = ctypes.c_char_p
 lib.mx_abi_version.restype = ctypes.c_int
 
 ENTRY_POINTS = ("mx_quantize", "mx_quantize_dual", "fp8_quantize_delayed", "mx_dequantize", "mx_gemm",
-                "mx_quantize_sr", "mm_fp8", "mx_gemm_requant", "mx_status_str", "mx_abi_version")
+                "mx_quantize_sr", "mm_fp8", "mx_gemm_requant", "fp8_quantize_delayed_static", "mx_status_str",
+                "mx_abi_version")
 
 
 class MXError(RuntimeError):

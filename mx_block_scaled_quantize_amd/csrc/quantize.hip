@@ -1397,10 +1397,10 @@ extern "C" mx_status_t mx_quantize_dual(const void* x, mx_dtype_t in, int64_t ro
   return expand<DualOp>(in, fmt, rule, a, amax != nullptr, stream);
 }
 
-extern "C" mx_status_t fp8_quantize_delayed(const void* x, mx_dtype_t in, int64_t rows, int64_t cols,
-                                            mx_elem_t fmt, fp8_layout_t layout, uint8_t* q, uint8_t* qT,
-                                            float* ring, int hist_len, int hist_idx, float fp8_max, float margin,
-                                            float* amax_out, uint32_t* ticket_scratch, hipStream_t stream) {
+// Argument checks of the delayed-scaling entry points (nothing is enqueued on failure).
+static mx_status_t check_delayed(const void* x, mx_dtype_t in, int64_t rows, int64_t cols, mx_elem_t fmt,
+                                 fp8_layout_t layout, const uint8_t* q, const uint8_t* qT, const float* ring,
+                                 int hist_len, int hist_idx, float fp8_max, float margin) {
   if (in != MX_F32 && in != MX_BF16 && in != MX_F16) return MX_ERR_UNSUPPORTED;
   if (fmt != MX_E4M3 && fmt != MX_E5M2) return MX_ERR_UNSUPPORTED;
   if (layout != FP8_ROW && layout != FP8_TRANSPOSED && layout != FP8_DUAL) return MX_ERR_UNSUPPORTED;
@@ -1413,10 +1413,63 @@ extern "C" mx_status_t fp8_quantize_delayed(const void* x, mx_dtype_t in, int64_
   if (n > 0 && (!x || (need_q && !q) || (need_qT && !qT))) return MX_ERR_NULL;
   if (cols % 8 != 0 || (need_qT && rows % 32 != 0)) return MX_ERR_SHAPE;
   if (n > 0 && (misaligned(x) || (need_q && misaligned(q)) || (need_qT && misaligned(qT)))) return MX_ERR_ALIGN;
-  if ((reinterpret_cast<uintptr_t>(ring) & 3u) || (reinterpret_cast<uintptr_t>(ticket_scratch) & 3u))
-    return MX_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(ring) & 3u) return MX_ERR_ALIGN;
+  return MX_OK;
+}
+
+extern "C" mx_status_t fp8_quantize_delayed(const void* x, mx_dtype_t in, int64_t rows, int64_t cols,
+                                            mx_elem_t fmt, fp8_layout_t layout, uint8_t* q, uint8_t* qT,
+                                            float* ring, int hist_len, int hist_idx, float fp8_max, float margin,
+                                            float* amax_out, uint32_t* ticket_scratch, hipStream_t stream) {
+  if (mx_status_t st = check_delayed(x, in, rows, cols, fmt, layout, q, qT, ring, hist_len, hist_idx, fp8_max, margin);
+      st != MX_OK)
+    return st;
+  if (reinterpret_cast<uintptr_t>(ticket_scratch) & 3u) return MX_ERR_ALIGN;
   StripArgs a{};
   a.x = x; a.rows = rows; a.cols = cols; a.q_row = q; a.q_col = qT;
   a.ring = RingArgs{ring, ticket_scratch, hist_len, hist_idx, fp8_max, margin, amax_out};
   return expand<PtOp>(in, fmt, MX_SCALE_FLOOR, a, int(layout), stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the ticket scratch lives in the library
+// ---------------------------------------------------------------------------
+// One array per device (each GPU the library runs on holds its own copy until
+// the process ends).  It is zero when the code object loads and every call
+// leaves it zero again (the last workgroup of each ticket group clears its
+// words, the folding workgroup the top words), so each call finds it cleared.
+// In host code `scratch` names a host-side stand-in: only the address that
+// hipGetSymbolAddress returns for the current device is passed to kernels.
+static __device__ __align__(256) uint32_t scratch[MX_TICKET_WORDS];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+uint32_t* scratch_dev_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per device.
+uint32_t* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_dev_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    scratch_dev_ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  return scratch_dev_ptr[dev];
+}
+}  // namespace
+
+extern "C" mx_status_t fp8_quantize_delayed_static(const void* x, mx_dtype_t in, int64_t rows, int64_t cols,
+                                                   mx_elem_t fmt, fp8_layout_t layout, uint8_t* q, uint8_t* qT,
+                                                   float* ring, int hist_len, int hist_idx, float fp8_max,
+                                                   float margin, float* amax_out, hipStream_t stream) {
+  if (mx_status_t st = check_delayed(x, in, rows, cols, fmt, layout, q, qT, ring, hist_len, hist_idx, fp8_max, margin);
+      st != MX_OK)
+    return st;
+  uint32_t* t = device_scratch();
+  if (t == nullptr) return MX_ERR_LAUNCH;
+  return fp8_quantize_delayed(x, in, rows, cols, fmt, layout, q, qT, ring, hist_len, hist_idx, fp8_max, margin,
+                              amax_out, t, stream);
 }

@@ -125,6 +125,28 @@ def test_fp8_quantize_delayed_argument_errors():
     assert call(14, FAKE + 2) == ALIGN  # ticket scratch likewise
 
 
+def test_fp8_quantize_delayed_static_argument_errors():
+    """The allocation-free variant validates exactly as fp8_quantize_delayed does,
+    before it looks up its scratch array (so no device is touched here)."""
+    f = lib.fp8_quantize_delayed_static
+    good = [FAKE, 1, 64, 64, 0, 1, FAKE, FAKE, FAKE, 16, 0, 448.0, 1.0, None, None]
+
+    def call(i, v):
+        a = list(good)
+        a[i] = v
+        return f(*a)
+    assert call(4, 2) == UNSUP
+    assert call(5, 9) == UNSUP
+    assert call(8, None) == NULL
+    assert call(8, FAKE + 2) == ALIGN
+    assert call(9, 0) == ARG
+    assert call(10, 16) == ARG
+    assert call(11, 0.0) == ARG
+    assert call(2, 40) == SHAPE
+    assert call(7, None) == NULL
+    assert call(0, FAKE + 8) == ALIGN
+
+
 def test_ring_layout_is_the_pages():
     """The ring is [hist | scale | legacy | amax | done]: hist_len + 4 words, and the
     ticket scratch a separate optional buffer."""
