@@ -201,7 +201,8 @@ def main():
         return
     if args.mode in ("delayed", "delayed_grad"):
         res = bench_delayed(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, args.steps,
-                            streams=("act",) if args.mode == "delayed" else ("grad",), with_null=False)
+                            streams=("act",) if args.mode == "delayed" else ("grad",), with_null=False,
+                            with_small=False)
         print(json.dumps({"mode": args.mode, **res}), flush=True)
         return
     if args.mode in ("col", "sr", "fp6dual"):
@@ -346,7 +347,7 @@ def hbm_leg(t, nbytes, k, dist=None):
 
 
 def bench_delayed(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=32, streams=("act", "grad"),
-                  with_null=True):
+                  with_null=True, with_small=True):
     """Per-tensor delayed scaling, BF16 8192 x 4096 -> transposed FP8 with the ring
     fold: the activation stream (E4M3) and the gradient stream (E5M2), each on its
     own ring of 16 with ticket scratch; the activation stream also on the page's
@@ -377,6 +378,8 @@ def bench_delayed(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=32
             name = f"delayed_fp8_{mxa_fmt(fmt)}_transposed_bf16_8192x4096" + ("" if use_scratch else "_no_scratch")
             res[name] = hbm_leg(t3, b3, k3, d3)
         del xs
+    if not with_small:
+        return res
     # per-call fixed cost: a launch-bound 128 x 256 call, ring fold included
     x = up_bf16(workloads.delayed_step("act", 0, rows=128, cols=256))
     qT = torch.empty((256, 128), dtype=torch.uint8, device=dev)
@@ -670,11 +673,12 @@ def _counter_lines(counters, avg_ns):
     grbm = counters.get("GRBM_GUI_ACTIVE")
     if grbm:
         cyc = grbm / 8
-        lines.append(f"gpu_clock_GHz_from_GRBM: {cyc / avg_ns:.3f}")
         if "SQ_VALU_MFMA_BUSY_CYCLES" in counters:
             lines.append(f"mfma_busy_fraction: {counters['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 1024):.4f}")
-        if "SQ_BUSY_CYCLES" in counters:
-            lines.append(f"sq_busy_fraction: {counters['SQ_BUSY_CYCLES'] / (cyc * 8):.4f}")
+        # a counter pass serializes dispatches and stretches short ones, so the
+        # clock estimate is only given for kernels long against that overhead
+        if avg_ns >= 200e3:
+            lines.append(f"gpu_clock_GHz_from_GRBM: {cyc / avg_ns:.3f}")
     waves = counters.get("SQ_WAVES")
     if waves:
         for k in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR",
