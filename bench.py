@@ -242,7 +242,7 @@ def main():
         s = sets[idx[0] % nsets]
         idx[0] += 1
         st = lib.mx_quantize_dual(s["x"].data_ptr(), 1, R, C, 32, 0, 1, s["qr"].data_ptr(), s["sr"].data_ptr(),
-                                  s["qc"].data_ptr(), s["sc"].data_ptr(), s["a"].data_ptr(), sp)
+                                  s["qc"].data_ptr(), s["sc"].data_ptr(), 0, s["a"].data_ptr(), sp)
         if st != 0:
             raise RuntimeError(lib.mx_status_str(st).decode())
 
@@ -315,6 +315,17 @@ def time_calls(fn, n, warm, stream, torch):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n / 1e3
+
+
+def time_alternating(fns, n, rounds, stream, torch):
+    """Average launch durations of several variants measured in alternation
+    (A B A B ...), so that a drift of the clock under load does not favour the
+    variant measured first: {name: mean over the rounds of time_calls}."""
+    acc = {k: 0.0 for k in fns}
+    for r in range(rounds):
+        for k, fn in fns.items():
+            acc[k] += time_calls(fn, n, 2 if r == 0 else 0, stream, torch)
+    return {k: v / rounds for k, v in acc.items()}
 
 
 # Memory-bound legs rotate through enough buffer sets that one call's data is
@@ -417,26 +428,32 @@ def mxa_fmt(code):
 
 
 def bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=10):
-    """MXFP8 E4M3 GEMM 8192 x 4096 . (14336 x 4096)^T, BF16 out (quantized operands resident)."""
+    """MXFP8 E4M3 GEMM 8192 x 4096 . (14336 x 4096)^T, BF16 out (quantized operands resident), with the
+    operands' scales row-major (the headline figure) and in the GEMM layout ("gemm_scales")."""
     M, N, K = 8192, 14336, 4096
     a_bits, w_bits = workloads.mlp_operands()
-    qa, sa = mxa.mx_quantize(up_bf16(a_bits), "e4m3", "ceil", "row")
-    qw, sw = mxa.mx_quantize(up_bf16(w_bits), "e4m3", "ceil", "row")
-    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-
-    def call():
-        st = lib.mx_gemm(qa.data_ptr(), sa.data_ptr(), 0, qw.data_ptr(), sw.data_ptr(), 0, M, N, K, 1.0,
-                         c.data_ptr(), 1, N, sp)
-        if st != 0:
-            raise RuntimeError(lib.mx_status_str(st).decode())
-    t = time_calls(call, steps, 2, stream, torch)
     flops = 2.0 * M * N * K
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ops = {layout: (mxa.mx_quantize(up_bf16(a_bits), "e4m3", "ceil", "row", scale_layout=layout),
+                    mxa.mx_quantize(up_bf16(w_bits), "e4m3", "ceil", "row", scale_layout=layout))
+           for layout in ("row", "gemm")}
+
+    def call(layout):
+        (qa, sa), (qw, sw) = ops[layout]
+        return lambda: mxa.check(lib.mx_gemm(qa.data_ptr(), sa.data_ptr(), 0, qw.data_ptr(), sw.data_ptr(), 0,
+                                             mxa.SCALE_LAYOUT[layout], M, N, K, 1.0, c.data_ptr(), 1, N, sp))
+    times = time_alternating({k: call(k) for k in ops}, max(2, steps // 2), 2, stream, torch)
+    del ops
+    t = times["row"]
     tf = flops / t / 1e12
     prof = os.path.join(ROOT, "profiles", "gemm256_kernel_mxfp8_8192x14336x4096.md")
     return {"workload": "MXFP8 E4M3 block-scaled GEMM 8192x4096 x (14336x4096)^T, FP32 accumulate, BF16 out",
             "value": round(tf, 1), "unit": "TFLOP/s", "ms_per_call": round(t * 1e3, 4),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / FP8_PEAK_TFLOPS, 4), "traffic": None},
+            "gemm_scales": {"ms_per_call": round(times["gemm"] * 1e3, 4),
+                            "TFLOP/s": round(flops / times["gemm"] / 1e12, 1),
+                            "frac": round(flops / times["gemm"] / 1e12 / FP8_PEAK_TFLOPS, 4)},
             "profile": {"file": os.path.relpath(prof, ROOT), "current": profile_is_current(prof, GEMM_SOURCES)}}
 
 
@@ -448,9 +465,9 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
     s = torch.empty((256, 32), dtype=torch.uint8, device=dev)
     d = torch.empty((256, 1024), dtype=torch.float32, device=dev)
     tq = time_calls(lambda: lib.mx_quantize(x.data_ptr(), 0, 256, 1024, 32, 0, 0, 0, 0, 0, q.data_ptr(),
-                                            s.data_ptr(), None, sp), 50, 5, stream, torch)
-    td = time_calls(lambda: lib.mx_dequantize(q.data_ptr(), s.data_ptr(), 256, 1024, 32, 0, 0, d.data_ptr(), 0, sp),
-                    50, 5, stream, torch)
+                                            s.data_ptr(), 0, None, sp), 50, 5, stream, torch)
+    td = time_calls(lambda: lib.mx_dequantize(q.data_ptr(), s.data_ptr(), 256, 1024, 32, 0, 0, 0, d.data_ptr(), 0,
+                                              sp), 50, 5, stream, torch)
     b1 = 256 * 1024 * 4 + 256 * 1024 + 256 * 32
     res["rowwise_quant_f32_256x1024"] = {"us": round(tq * 1e6, 2), "GB/s": round(b1 / tq / 1e9, 1)}
     res["dequant_f32_256x1024"] = {"us": round(td * 1e6, 2), "GB/s": round(b1 / td / 1e9, 1)}
@@ -460,10 +477,11 @@ def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
     res.update(bench_wgrad_quant(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch))
     g_bits, x_bits, mask = workloads.weight_grad_operands()
     st0 = wgrad_set(dev, up_bf16(g_bits), up_bf16(x_bits), torch)
-    wgrad_quant(lib, sp, mxa, st0, mask)
-    res["mxfp4_gemm_4096x4096x8192"] = time_gemm_fp4(lib, sp, stream, dev, st0["gq"], st0["gs"], st0["xq"],
-                                                     st0["xs"], torch, 10)
-    del st0
+    st1 = wgrad_set(dev, st0["G"], st0["X"], torch)
+    wgrad_quant(lib, sp, mxa, st0, mask, 0)
+    wgrad_quant(lib, sp, mxa, st1, mask, 1)
+    res.update(time_gemm_fp4_layouts(lib, sp, stream, dev, st0, st1, torch, 10))
+    del st0, st1
     res.update(bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
     res.update(bench_gemm_requant(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
     res.update(bench_gemm_fp6(lib, sp, stream, dev, up_bf16, mxa, workloads, torch))
@@ -499,13 +517,13 @@ def bench_fp6(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=32
                     qc=torch.empty((C, R * 3 // 4), dtype=torch.uint8, device=dev),
                     sc=torch.empty((C, R // 32), dtype=torch.uint8, device=dev))
     t, k, d = time_rotating(f6_set, lambda st, i: mxa.check(lib.mx_quantize(
-        st["x"].data_ptr(), 1, R, C, 32, 4, 1, 0, 0, 0, st["q"].data_ptr(), st["s"].data_ptr(), None, sp)),
+        st["x"].data_ptr(), 1, R, C, 32, 4, 1, 0, 0, 0, st["q"].data_ptr(), st["s"].data_ptr(), 0, None, sp)),
         bf6, steps, 4, stream, torch, dist=True)
     res = {"mxfp6_e3m2_rowwise_bf16_8192x4096": hbm_leg(t, bf6, k, d)}
     bf6d = R * C * 2 + 2 * (R * C * 3 // 4 + R * C // 32)
     t, k, d = time_rotating(f6_set, lambda st, i: mxa.check(lib.mx_quantize_dual(
         st["x"].data_ptr(), 1, R, C, 32, 4, 1, st["q"].data_ptr(), st["s"].data_ptr(), st["qc"].data_ptr(),
-        st["sc"].data_ptr(), None, sp)), bf6d, steps, 4, stream, torch, dist=True)
+        st["sc"].data_ptr(), 0, None, sp)), bf6d, steps, 4, stream, torch, dist=True)
     res["mxfp6_e3m2_dual_bf16_8192x4096"] = hbm_leg(t, bf6d, k, d)
     return res
 
@@ -517,12 +535,13 @@ def wgrad_set(dev, G, X, torch):
                 xs=torch.empty((4096, 256), dtype=torch.uint8, device=dev))
 
 
-def wgrad_quant(lib, sp, mxa, st, mask):
-    """Hadamard + column-wise MXFP4 (round-up rule) of both weight-gradient operands."""
+def wgrad_quant(lib, sp, mxa, st, mask, layout=0):
+    """Hadamard + column-wise MXFP4 (round-up rule) of both weight-gradient operands
+    (scales row-major, or in the GEMM layout with layout=1)."""
     mxa.check(lib.mx_quantize(st["G"].data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, st["gq"].data_ptr(),
-                              st["gs"].data_ptr(), None, sp))
+                              st["gs"].data_ptr(), layout, None, sp))
     mxa.check(lib.mx_quantize(st["X"].data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, st["xq"].data_ptr(),
-                              st["xs"].data_ptr(), None, sp))
+                              st["xs"].data_ptr(), layout, None, sp))
 
 
 def bench_wgrad_quant(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=20):
@@ -543,7 +562,7 @@ def bench_gemm_fp6(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=5
     qa, sa = mxa.mx_quantize(up_bf16(a_bits), "e2m3", "ceil", "row")
     qw, sw = mxa.mx_quantize(up_bf16(w_bits), "e2m3", "ceil", "row")
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    t = time_calls(lambda: mxa.check(lib.mx_gemm(qa.data_ptr(), sa.data_ptr(), 3, qw.data_ptr(), sw.data_ptr(), 3, M, N,
+    t = time_calls(lambda: mxa.check(lib.mx_gemm(qa.data_ptr(), sa.data_ptr(), 3, qw.data_ptr(), sw.data_ptr(), 3, 0, M, N,
                                                  K, 1.0, c.data_ptr(), 1, N, sp)), steps, 1, stream, torch)
     f = 2.0 * M * N * K
     return {"mxfp6_e2m3_gemm_8192x14336x4096": {"us": round(t * 1e6, 2), "TFLOP/s": round(f / t / 1e12, 1),
@@ -561,7 +580,7 @@ def bench_gemm_requant(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, ste
     sc = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
 
     def call():
-        mxa.check(lib.mx_gemm_requant(qa.data_ptr(), sa.data_ptr(), 0, qw.data_ptr(), sw.data_ptr(), 0, M, N, K, 1.0,
+        mxa.check(lib.mx_gemm_requant(qa.data_ptr(), sa.data_ptr(), 0, qw.data_ptr(), sw.data_ptr(), 0, 0, M, N, K, 1.0,
                                       0, 1, qc.data_ptr(), sc.data_ptr(), None, sp))
     t = time_calls(call, steps, 2, stream, torch)
     tf = 2.0 * M * N * K / t / 1e12
@@ -599,25 +618,32 @@ def bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=10)
     return res
 
 
-def time_gemm_fp4(lib, sp, stream, dev, gq, gs, xq, xsc, torch, steps):
-    """dW = (1/32) Gq^T Xq, MXFP4 operands [4096][8192 / 2 B] (K = 8192 tokens), BF16 out."""
+def time_gemm_fp4_layouts(lib, sp, stream, dev, st_row, st_gemm, torch, steps):
+    """The MXFP4 weight-gradient GEMM on row-major scales (st_row) and on GEMM-layout scales
+    (st_gemm), measured in alternation."""
     dw = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
-    t = time_calls(lambda: lib.mx_gemm(gq.data_ptr(), gs.data_ptr(), 2, xq.data_ptr(), xsc.data_ptr(), 2, 4096,
-                                       4096, 8192, 1.0 / 32, dw.data_ptr(), 1, 4096, sp), steps, 2, stream, torch)
+
+    def call(st, layout):
+        return lambda: lib.mx_gemm(st["gq"].data_ptr(), st["gs"].data_ptr(), 2, st["xq"].data_ptr(),
+                                   st["xs"].data_ptr(), 2, layout, 4096, 4096, 8192, 1.0 / 32, dw.data_ptr(), 1, 4096,
+                                   sp)
+    t = time_alternating({"row": call(st_row, 0), "gemm": call(st_gemm, 1)}, steps, 3, stream, torch)
     f = 2.0 * 4096 * 4096 * 8192
-    return {"us": round(t * 1e6, 2), "TFLOP/s": round(f / t / 1e12, 1), "mfma_frac": round(f / t / 1e12 / FP4_PEAK_TFLOPS, 4)}
+    leg = lambda x: {"us": round(x * 1e6, 2), "TFLOP/s": round(f / x / 1e12, 1),   # noqa: E731
+                     "mfma_frac": round(f / x / 1e12 / FP4_PEAK_TFLOPS, 4)}
+    return {"mxfp4_gemm_4096x4096x8192": leg(t["row"]), "mxfp4_gemm_4096x4096x8192_gemm_scales": leg(t["gemm"])}
 
 
 def bench_gemm_fp4(lib, sp, stream, dev, up_bf16, workloads, torch, steps=10):
-    """The MXFP4 weight-gradient GEMM alone, on the Hadamard + MXFP4 column-wise operands."""
+    """The MXFP4 weight-gradient GEMM alone, on the Hadamard + MXFP4 column-wise operands, with
+    row-major and with GEMM-layout scales."""
+    import mx_block_scaled_quantize_amd as mxa
     g_bits, x_bits, mask = workloads.weight_grad_operands()
-    G, X = up_bf16(g_bits), up_bf16(x_bits)
-    gq = torch.empty((4096, 4096), dtype=torch.uint8, device=dev)
-    gs = torch.empty((4096, 256), dtype=torch.uint8, device=dev)
-    xq, xsc = torch.empty_like(gq), torch.empty_like(gs)
-    lib.mx_quantize(G.data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, gq.data_ptr(), gs.data_ptr(), None, sp)
-    lib.mx_quantize(X.data_ptr(), 1, 8192, 4096, 32, 2, 1, 1, 1, mask, xq.data_ptr(), xsc.data_ptr(), None, sp)
-    return time_gemm_fp4(lib, sp, stream, dev, gq, gs, xq, xsc, torch, steps)
+    st0 = wgrad_set(dev, up_bf16(g_bits), up_bf16(x_bits), torch)
+    st1 = wgrad_set(dev, st0["G"], st0["X"], torch)
+    wgrad_quant(lib, sp, mxa, st0, mask, 0)
+    wgrad_quant(lib, sp, mxa, st1, mask, 1)
+    return time_gemm_fp4_layouts(lib, sp, stream, dev, st0, st1, torch, steps)
 
 
 def _pmc_mean(path, kernel_substr, counter):

@@ -75,6 +75,19 @@ typedef enum { MX_SCALE_FLOOR = 0, MX_SCALE_CEIL = 1 } mx_scale_rule_t;
  *                 [cols][rows] (E2M1: [cols][rows/2]), scales [cols][rows/32]. */
 typedef enum { MX_ROWWISE = 0, MX_COLWISE_T = 1 } mx_orient_t;
 
+/* Layout of an E8M0 scale array of an operand with `lines` lines (rows of the
+ * stored codes) and kblocks = K / 32 K-blocks per line ("format-aware fusion" FP4
+ * article, section on the engineering of efficiency: quantizing producers
+ * co-designed with the scale fields and layouts their consumers read):
+ *   MX_SCALES_ROW_MAJOR: [lines][kblocks], byte (line, kb) at line * kblocks + kb;
+ *   MX_SCALES_GEMM:      [kblocks / 16][lines][16], byte (line, kb) at
+ *                        ((kb / 16) * lines + line) * 16 + kb % 16 -- the 16 scales
+ *                        one GEMM stage of 16 K-blocks needs are contiguous per
+ *                        line and the lines of a stage are contiguous, so mx_gemm
+ *                        fetches a tile's stage of scales as whole cache lines.
+ *                        Needs kblocks % 16 == 0 (K a multiple of 512). */
+typedef enum { MX_SCALES_ROW_MAJOR = 0, MX_SCALES_GEMM = 1 } mx_scale_layout_t;
+
 /* Output layout of the per-tensor FP8 quantizer ([FP8PY] quantize(transposed),
  * quantize_dual): q [rows][cols], qT [cols][rows], or both from one read. */
 typedef enum { FP8_ROW = 0, FP8_TRANSPOSED = 1, FP8_DUAL = 2 } fp8_layout_t;
@@ -114,7 +127,12 @@ typedef enum {
  *
  *   x        [rows][cols] input of type `in` (F32, BF16 or F16).
  *   block    must be 32 (MX defines k = 32 for every element type).
- *   q, scales  outputs, layouts as described at mx_orient_t.
+ *   q, scales  outputs, layouts as described at mx_orient_t; with
+ *            scale_layout == MX_SCALES_GEMM the scales are stored in the GEMM
+ *            layout (lines = rows, kblocks = cols / 32 for MX_ROWWISE; lines =
+ *            cols, kblocks = rows / 32 for MX_COLWISE_T), which needs the blocked
+ *            axis to be a multiple of 512 (MX_ERR_SHAPE otherwise) and is not
+ *            offered for E2M3 / E3M2 (MX_ERR_UNSUPPORTED).
  *   amax_out optional (NULL to skip) in/out max-accumulator: on completion it
  *            holds max(*amax_out, max |x|) over the whole input, NaN entries
  *            ignored.  It must hold a non-negative FP32 value on entry: 0 gives
@@ -125,19 +143,21 @@ typedef enum {
 mx_status_t mx_quantize(const void* x, mx_dtype_t in, int64_t rows, int64_t cols, int block,
                         mx_elem_t fmt, mx_scale_rule_t rule, mx_orient_t orient,
                         int hadamard, uint32_t hadamard_sign_mask,
-                        uint8_t* q, uint8_t* scales, float* amax_out, hipStream_t stream);
+                        uint8_t* q, uint8_t* scales, mx_scale_layout_t scale_layout,
+                        float* amax_out, hipStream_t stream);
 
 /* Dual-orientation MX quantization from a single read of x ([UE8M0] second part,
  * section 2: training keeps a row-wise and a column-wise quantized copy, and a
  * transposed MX copy must be re-quantized, not re-laid-out).  Produces exactly
  * what mx_quantize gives for MX_ROWWISE (q_row, s_row) and for MX_COLWISE_T
  * (q_colT, s_colT), plus the optional per-tensor amax (a max-accumulator, as
- * for mx_quantize).
+ * for mx_quantize).  scale_layout applies to both scale outputs (MX_SCALES_GEMM:
+ * rows % 512 == 0 and cols % 512 == 0, FP8 / FP4 only).
  * Shapes: rows % 32 == 0 and cols % 32 == 0. */
 mx_status_t mx_quantize_dual(const void* x, mx_dtype_t in, int64_t rows, int64_t cols, int block,
                              mx_elem_t fmt, mx_scale_rule_t rule,
                              uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,
-                             float* amax_out, hipStream_t stream);
+                             mx_scale_layout_t scale_layout, float* amax_out, hipStream_t stream);
 
 /* Per-tensor FP8 quantization with delayed scaling ([FP8PY] quantize /
  * quantize_dual with ring_state, and its commit message).
@@ -215,10 +235,12 @@ mx_status_t fp8_quantize_delayed_static(const void* x, mx_dtype_t in, int64_t ro
  *   MX_ROWWISE:   q [rows][cols] (E2M1 [rows][cols/2]), scales [rows][cols/32];
  *   MX_COLWISE_T: q [cols][rows] (E2M1 [cols][rows/2]), scales [cols][rows/32],
  *                 and out is still [rows][cols] (the transpose is undone).
+ * scale_layout: how `scales` is stored (MX_SCALES_GEMM: lines and kblocks as for
+ * mx_quantize; the blocked axis a multiple of 512).
  * Shapes: the blocked axis must be a multiple of 32. */
 mx_status_t mx_dequantize(const uint8_t* q, const uint8_t* scales, int64_t rows, int64_t cols,
-                          int block, mx_elem_t fmt, mx_orient_t orient, void* out,
-                          mx_dtype_t out_dtype, hipStream_t stream);
+                          int block, mx_elem_t fmt, mx_orient_t orient, mx_scale_layout_t scale_layout,
+                          void* out, mx_dtype_t out_dtype, hipStream_t stream);
 
 /* Row-wise MXFP4 with stochastic rounding ([FAF], the 37.2K tokens/s
  * configuration: row gradients quantized to MXFP4 with stochastic rounding; the
@@ -256,13 +278,15 @@ mx_status_t mx_quantize_sr(const void* x, mx_dtype_t in, int64_t rows, int64_t c
  *      type (it may be a column slice of a wider matrix).
  * fmt_a / fmt_b: both FP8 (E4M3 / E5M2, any mix), both FP6 (E2M3 / E3M2, any mix;
  * packed as mx_quantize writes them) or both E2M1.
+ * scale_layout: how sa and sb are stored; MX_SCALES_GEMM (sa with lines = M, sb
+ * with lines = N, kblocks = K / 32) needs K % 512 == 0.
  * Shapes: K % 32 == 0, and K % 64 == 0 for FP6 (K == 0 writes zeros); any M, N >= 0.
  * Accumulation: the matrix unit sums the FP8 products of each MFMA step with a
  * fixed-point alignment of limited width, not with IEEE FP32 rounding after
  * every product; the FP32 result is within a few 2^-12 of the largest product
  * of each 64-long K-step of the exact sum. */
 mx_status_t mx_gemm(const uint8_t* a, const uint8_t* sa, mx_elem_t fmt_a,
-                    const uint8_t* b, const uint8_t* sb, mx_elem_t fmt_b,
+                    const uint8_t* b, const uint8_t* sb, mx_elem_t fmt_b, mx_scale_layout_t scale_layout,
                     int64_t M, int64_t N, int64_t K, float alpha,
                     void* c, mx_dtype_t c_dtype, int64_t ldc, hipStream_t stream);
 
@@ -277,12 +301,13 @@ mx_status_t mx_gemm(const uint8_t* a, const uint8_t* sa, mx_elem_t fmt_a,
  *   qc        [M][N] codes (E2M1: [M][N/2] packed), 16-byte aligned;
  *   sc        [M][N/32] E8M0 scales;
  *   amax_out  optional max-accumulator of |C32| (NaN excluded), as for mx_quantize.
- * Operands as mx_gemm, FP8 or FP4 only.  Shapes: K % 32 == 0, N % 32 == 0, any M.
+ * Operands (and scale_layout, which applies to sa and sb; sc is row-major) as
+ * mx_gemm, FP8 or FP4 only.  Shapes: K % 32 == 0, N % 32 == 0, any M.
  * Errors: as mx_gemm, plus MX_ERR_UNSUPPORTED for FP6 operands and for fmt_c / rule_c,
  * and MX_ERR_NULL for qc / sc. */
 mx_status_t mx_gemm_requant(const uint8_t* a, const uint8_t* sa, mx_elem_t fmt_a,
                             const uint8_t* b, const uint8_t* sb, mx_elem_t fmt_b,
-                            int64_t M, int64_t N, int64_t K, float alpha,
+                            mx_scale_layout_t scale_layout, int64_t M, int64_t N, int64_t K, float alpha,
                             mx_elem_t fmt_c, mx_scale_rule_t rule_c, uint8_t* qc, uint8_t* sc,
                             float* amax_out, hipStream_t stream);
 

@@ -10,14 +10,17 @@ raises.
 The functions carry the names of the C entry points declared in
 ``include/mx.h`` and return freshly allocated output tensors:
 
-    mx_quantize(x, fmt, rule, orient, hadamard_mask=None, amax=False)
-    mx_quantize_dual(x, fmt, rule, amax=False)
+    mx_quantize(x, fmt, rule, orient, hadamard_mask=None, amax=False, scale_layout="row")
+    mx_quantize_dual(x, fmt, rule, amax=False, scale_layout="row")
     fp8_quantize_delayed(x, ring, hist_idx, fmt, layout, fp8_max, margin, amax=False, tickets=None)
-    mx_dequantize(q, scales, rows, cols, fmt, orient, out_dtype)
-    mx_gemm(a, sa, b, sb, fmt_a, fmt_b, alpha, out_dtype)
+    mx_dequantize(q, scales, rows, cols, fmt, orient, out_dtype, scale_layout="row")
+    mx_gemm(a, sa, b, sb, fmt_a, fmt_b, alpha, out_dtype, scale_layout="row")
     mx_quantize_sr(x, rand, rule, amax=False)
     mm_fp8(a, b, scale, trans_a, trans_b, bias, fmt)
-    mx_gemm_requant(a, sa, b, sb, fmt_a, fmt_b, alpha, fmt_c, rule_c, amax=False)
+    mx_gemm_requant(a, sa, b, sb, fmt_a, fmt_b, alpha, fmt_c, rule_c, amax=False, scale_layout="row")
+
+scale_layout "row" stores E8M0 scales row-major [lines][K/32]; "gemm" stores them
+in the GEMM layout [K/512][lines][16] (returned as a 3-D tensor of that shape).
 """
 
 import ctypes
@@ -41,6 +44,7 @@ FMT = {"e4m3": 0, "e5m2": 1, "e2m1": 2, "e2m3": 3, "e3m2": 4}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 RULE = {"floor": 0, "ceil": 1}
 ORIENT = {"row": 0, "col": 1}
+SCALE_LAYOUT = {"row": 0, "gemm": 1}
 LAYOUT = {"row": 0, "transposed": 1, "dual": 2}
 STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN", 4: "MX_ERR_UNSUPPORTED",
           5: "MX_ERR_LAUNCH", 6: "MX_ERR_ARG"}
@@ -53,16 +57,16 @@ def ring_words(hist_len: int) -> int:
     return hist_len + 4
 
 _p, _i64, _i32, _u32, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32, ctypes.c_float
-lib.mx_quantize.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _u32, _p, _p, _p, _p]
-lib.mx_quantize_dual.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p]
+lib.mx_quantize.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _u32, _p, _p, _i32, _p, _p]
+lib.mx_quantize_dual.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _i32, _p, _p]
 lib.fp8_quantize_delayed.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _p, _p, _p, _i32, _i32, _f32, _f32, _p, _p, _p]
-lib.mx_dequantize.argtypes = [_p, _p, _i64, _i64, _i32, _i32, _i32, _p, _i32, _p]
-lib.mx_gemm.argtypes = [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64, _f32, _p, _i32, _i64, _p]
+lib.mx_dequantize.argtypes = [_p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p, _i32, _p]
+lib.mx_gemm.argtypes = [_p, _p, _i32, _p, _p, _i32, _i32, _i64, _i64, _i64, _f32, _p, _i32, _i64, _p]
 lib.mx_quantize_sr.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p]
 lib.mm_fp8.argtypes = [_p, _p, _i32, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p]
 lib.fp8_quantize_delayed_static.argtypes = [_p, _i32, _i64, _i64, _i32, _i32, _p, _p, _p, _i32, _i32, _f32, _f32, _p,
                                             _p]
-lib.mx_gemm_requant.argtypes = [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64, _f32, _i32, _i32, _p, _p, _p, _p]
+lib.mx_gemm_requant.argtypes = [_p, _p, _i32, _p, _p, _i32, _i32, _i64, _i64, _i64, _f32, _i32, _i32, _p, _p, _p, _p]
 for _f in (lib.mx_quantize, lib.mx_quantize_dual, lib.fp8_quantize_delayed, lib.mx_dequantize, lib.mx_gemm,
            lib.mx_quantize_sr, lib.mm_fp8, lib.mx_gemm_requant, lib.fp8_quantize_delayed_static):
     _f.restype = ctypes.c_int
@@ -127,6 +131,15 @@ def _check_2d(x):
         raise ValueError("expected a contiguous 2-D tensor")
 
 
+def scale_shape(lines: int, kblocks: int, layout: str):
+    """Shape of a scale tensor: [lines][kblocks] row-major, [kblocks/16][lines][16] in the GEMM layout."""
+    if _lookup(SCALE_LAYOUT, layout, "scale layout") == 0:
+        return (lines, kblocks)
+    if kblocks % 16:
+        raise ValueError("the GEMM scale layout needs a blocked axis that is a multiple of 512")
+    return (kblocks // 16, lines, 16)
+
+
 def code_cols(n: int, fmt: str) -> int:
     """Bytes per row of n element codes (FP4 packs two per byte, FP6 four per three bytes)."""
     if fmt == "e2m1":
@@ -136,7 +149,7 @@ def code_cols(n: int, fmt: str) -> int:
     return n
 
 
-def mx_quantize(x, fmt="e4m3", rule="ceil", orient="row", hadamard_mask=None, amax=False):
+def mx_quantize(x, fmt="e4m3", rule="ceil", orient="row", hadamard_mask=None, amax=False, scale_layout="row"):
     """MX quantization of a 2-D tensor.  Returns (q, scales) or (q, scales, amax).
 
     amax=True returns max |x| (NaN ignored) in a fresh 1-element tensor; pass a
@@ -151,27 +164,28 @@ def mx_quantize(x, fmt="e4m3", rule="ceil", orient="row", hadamard_mask=None, am
     o = _lookup(ORIENT, orient, "orientation")
     qr, qc = (R, C) if orient == "row" else (C, R)
     q = torch.empty((qr, code_cols(qc, fmt)), dtype=torch.uint8, device=x.device)
-    s = torch.empty((qr, qc // 32), dtype=torch.uint8, device=x.device)
+    s = torch.empty(scale_shape(qr, qc // 32, scale_layout), dtype=torch.uint8, device=x.device)
     a = _amax_buf(amax, x.device)
     check(lib.mx_quantize(_ptr(x), _lookup(DTYPE, x.dtype, "dtype"), R, C, 32, f, _lookup(RULE, rule, "rule"), o,
                           0 if hadamard_mask is None else 1, 0 if hadamard_mask is None else int(hadamard_mask),
-                          _ptr(q), _ptr(s), _ptr(a), _stream(x)))
+                          _ptr(q), _ptr(s), SCALE_LAYOUT[scale_layout], _ptr(a), _stream(x)))
     return (q, s) if a is None else (q, s, a)
 
 
-def mx_quantize_dual(x, fmt="e4m3", rule="ceil", amax=False):
+def mx_quantize_dual(x, fmt="e4m3", rule="ceil", amax=False, scale_layout="row"):
     """Row-wise and column-wise (transposed) MX copies from one read of x.
     Returns (q_row, s_row, q_colT, s_colT[, amax])."""
     _check_2d(x)
     R, C = x.shape
     f = _lookup(FMT, fmt, "format")
     qr = torch.empty((R, code_cols(C, fmt)), dtype=torch.uint8, device=x.device)
-    sr = torch.empty((R, C // 32), dtype=torch.uint8, device=x.device)
+    sr = torch.empty(scale_shape(R, C // 32, scale_layout), dtype=torch.uint8, device=x.device)
     qc = torch.empty((C, code_cols(R, fmt)), dtype=torch.uint8, device=x.device)
-    sc = torch.empty((C, R // 32), dtype=torch.uint8, device=x.device)
+    sc = torch.empty(scale_shape(C, R // 32, scale_layout), dtype=torch.uint8, device=x.device)
     a = _amax_buf(amax, x.device)
     check(lib.mx_quantize_dual(_ptr(x), _lookup(DTYPE, x.dtype, "dtype"), R, C, 32, f, _lookup(RULE, rule, "rule"),
-                               _ptr(qr), _ptr(sr), _ptr(qc), _ptr(sc), _ptr(a), _stream(x)))
+                               _ptr(qr), _ptr(sr), _ptr(qc), _ptr(sc), SCALE_LAYOUT[scale_layout], _ptr(a),
+                               _stream(x)))
     return (qr, sr, qc, sc) if a is None else (qr, sr, qc, sc, a)
 
 
@@ -200,7 +214,8 @@ def _k_of(a, fmt):
     return a.shape[1]
 
 
-def mx_gemm_requant(a, sa, b, sb, fmt_a="e4m3", fmt_b="e4m3", alpha=1.0, fmt_c="e4m3", rule_c="ceil", amax=False):
+def mx_gemm_requant(a, sa, b, sb, fmt_a="e4m3", fmt_b="e4m3", alpha=1.0, fmt_c="e4m3", rule_c="ceil", amax=False,
+                    scale_layout="row"):
     """C32 = fl32(alpha * deq(A) deq(B)^T), re-quantized row-wise to MX in the GEMM
     epilogue.  Returns (q [M][N] (E2M1: [M][N/2]), scales [M][N/32]) or (q, scales, amax)."""
     M = a.shape[0]
@@ -211,7 +226,8 @@ def mx_gemm_requant(a, sa, b, sb, fmt_a="e4m3", fmt_b="e4m3", alpha=1.0, fmt_c="
     s = torch.empty((M, N // 32), dtype=torch.uint8, device=a.device)
     am = _amax_buf(amax, a.device)
     check(lib.mx_gemm_requant(_ptr(a), _ptr(sa), _lookup(FMT, fmt_a, "format"), _ptr(b), _ptr(sb),
-                              _lookup(FMT, fmt_b, "format"), M, N, K, float(alpha), fc, _lookup(RULE, rule_c, "rule"),
+                              _lookup(FMT, fmt_b, "format"), _lookup(SCALE_LAYOUT, scale_layout, "scale layout"),
+                              M, N, K, float(alpha), fc, _lookup(RULE, rule_c, "rule"),
                               _ptr(q), _ptr(s), _ptr(am), _stream(a)))
     return (q, s) if am is None else (q, s, am)
 
@@ -256,16 +272,18 @@ def fp8_quantize_delayed(x, ring, hist_idx, fmt="e4m3", layout="transposed", fp8
     return (q, qT, a) if amax else (q, qT)
 
 
-def mx_dequantize(q, scales, rows, cols, fmt="e4m3", orient="row", out_dtype=torch.float32):
+def mx_dequantize(q, scales, rows, cols, fmt="e4m3", orient="row", out_dtype=torch.float32, scale_layout="row"):
     """Dequantize MX codes back to a [rows][cols] tensor of out_dtype (float32 or bfloat16)."""
     out = torch.empty((rows, cols), dtype=out_dtype, device=q.device)
     check(lib.mx_dequantize(_ptr(q), _ptr(scales), rows, cols, 32, _lookup(FMT, fmt, "format"),
-                            _lookup(ORIENT, orient, "orientation"), _ptr(out), _lookup(DTYPE, out_dtype, "dtype"),
+                            _lookup(ORIENT, orient, "orientation"), _lookup(SCALE_LAYOUT, scale_layout, "scale layout"),
+                            _ptr(out), _lookup(DTYPE, out_dtype, "dtype"),
                             _stream(q)))
     return out
 
 
-def mx_gemm(a, sa, b, sb, fmt_a="e4m3", fmt_b="e4m3", alpha=1.0, out_dtype=torch.bfloat16, out=None):
+def mx_gemm(a, sa, b, sb, fmt_a="e4m3", fmt_b="e4m3", alpha=1.0, out_dtype=torch.bfloat16, out=None,
+            scale_layout="row"):
     """C = alpha * deq(A) deq(B)^T with A [M][K], B [N][K] codes (K-contiguous)."""
     M = a.shape[0]
     N = b.shape[0]
@@ -273,7 +291,8 @@ def mx_gemm(a, sa, b, sb, fmt_a="e4m3", fmt_b="e4m3", alpha=1.0, out_dtype=torch
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
     check(lib.mx_gemm(_ptr(a), _ptr(sa), _lookup(FMT, fmt_a, "format"), _ptr(b), _ptr(sb),
-                      _lookup(FMT, fmt_b, "format"), M, N, K, float(alpha), _ptr(out),
+                      _lookup(FMT, fmt_b, "format"), _lookup(SCALE_LAYOUT, scale_layout, "scale layout"), M, N, K,
+                      float(alpha), _ptr(out),
                       _lookup(DTYPE, out.dtype, "dtype"), out.stride(0), _stream(a)))
     return out
 

@@ -133,11 +133,16 @@ constexpr int kDeqThreads = 256;
 template <int F, bool BF16OUT>
 __global__ __launch_bounds__(kDeqThreads) void rowwise_deq_kernel(const uint8_t* __restrict__ q,
                                                                   const uint8_t* __restrict__ scales,
-                                                                  int64_t nchunks, void* __restrict__ out) {
+                                                                  int64_t nchunks, void* __restrict__ out,
+                                                                  int64_t lines, int64_t gemm_kblocks) {
   const int64_t chunk = int64_t(blockIdx.x) * kDeqThreads + threadIdx.x;
   if (chunk >= nchunks) return;
+  // block index chunk / 4 = line * kblocks + kb; gemm_kblocks != 0 selects the GEMM scale layout
+  const int64_t blk = chunk >> 2;
+  const uint8_t sc =
+      scales[gemm_kblocks ? scale_offset(blk / gemm_kblocks, blk % gemm_kblocks, lines, gemm_kblocks, true) : blk];
   float o[8];
-  decode8<F>(q, chunk * 8, scales[chunk >> 2], o);
+  decode8<F>(q, chunk * 8, sc, o);
   store8<BF16OUT>(out, chunk * 8, o);
 }
 
@@ -149,7 +154,7 @@ template <int F, bool BF16OUT>
 __global__ __launch_bounds__(kDeqThreads) void colwise_deq_kernel(const uint8_t* __restrict__ q,
                                                                   const uint8_t* __restrict__ scales,
                                                                   int64_t rows, int64_t cols, int tiles_r,
-                                                                  void* __restrict__ out) {
+                                                                  void* __restrict__ out, bool gemm_scales) {
   __shared__ float t[kDT][kDT + 1];
   const int tid = threadIdx.x;
   const int64_t oc0 = int64_t(blockIdx.x / tiles_r) * kDT;   // output column = stored row
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(kDeqThreads) void colwise_deq_kernel(const uint8_t*
     const int64_t c = oc0 + sr, r = or0 + ch;
     float o[8];
     if (c < cols && r < rows) {
-      decode8<F>(q, c * rows + r, scales[c * (rows >> 5) + (r >> 5)], o);
+      decode8<F>(q, c * rows + r, scales[scale_offset(c, r >> 5, cols, rows >> 5, gemm_scales)], o);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[j] = 0.0f;
@@ -194,15 +199,15 @@ static mx_status_t launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, Args
 
 template <int F, bool BF>
 static mx_status_t deq_dispatch(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols, bool colwise,
-                                void* out, hipStream_t st) {
+                                bool gemm_scales, void* out, hipStream_t st) {
   if (!colwise) {
     const int64_t nchunks = rows * cols / 8;
     return launch_k(rowwise_deq_kernel<F, BF>, dim3(unsigned((nchunks + kDeqThreads - 1) / kDeqThreads)),
-                    dim3(kDeqThreads), st, q, s, nchunks, out);
+                    dim3(kDeqThreads), st, q, s, nchunks, out, rows, gemm_scales ? cols / 32 : int64_t(0));
   }
   const int64_t tr = (rows + kDT - 1) / kDT, tc = (cols + kDT - 1) / kDT;
   return launch_k(colwise_deq_kernel<F, BF>, dim3(unsigned(tr * tc)), dim3(kDeqThreads), st, q, s, rows, cols,
-                  int(tr), out);
+                  int(tr), out, gemm_scales);
 }
 
 }  // namespace mxk
@@ -210,8 +215,8 @@ static mx_status_t deq_dispatch(const uint8_t* q, const uint8_t* s, int64_t rows
 using namespace mxk;
 
 extern "C" mx_status_t mx_dequantize(const uint8_t* q, const uint8_t* scales, int64_t rows, int64_t cols, int block,
-                                     mx_elem_t fmt, mx_orient_t orient, void* out, mx_dtype_t out_dtype,
-                                     hipStream_t stream) {
+                                     mx_elem_t fmt, mx_orient_t orient, mx_scale_layout_t scale_layout, void* out,
+                                     mx_dtype_t out_dtype, hipStream_t stream) {
   const bool fp6 = fmt == MX_E2M3 || fmt == MX_E3M2;
   if (fmt != MX_E4M3 && fmt != MX_E5M2 && fmt != MX_E2M1 && !fp6) return MX_ERR_UNSUPPORTED;
   if (out_dtype != MX_F32 && out_dtype != MX_BF16) return MX_ERR_UNSUPPORTED;
@@ -220,22 +225,25 @@ extern "C" mx_status_t mx_dequantize(const uint8_t* q, const uint8_t* scales, in
   if (rows < 0 || cols < 0 || rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31)) return MX_ERR_SHAPE;
   if (orient == MX_ROWWISE && cols % 32 != 0) return MX_ERR_SHAPE;
   if (orient == MX_COLWISE_T && (rows % 32 != 0 || cols % 8 != 0)) return MX_ERR_SHAPE;
+  if (scale_layout != MX_SCALES_ROW_MAJOR && scale_layout != MX_SCALES_GEMM) return MX_ERR_UNSUPPORTED;
+  const bool gemm_scales = scale_layout == MX_SCALES_GEMM;
+  if (gemm_scales && (orient == MX_ROWWISE ? cols : rows) % 512 != 0) return MX_ERR_SHAPE;
   if (rows * cols == 0) return MX_OK;
   if (!q || !scales || !out) return MX_ERR_NULL;
   if (misaligned(q) || misaligned(out)) return MX_ERR_ALIGN;
   const bool col = orient == MX_COLWISE_T;
   const bool bf = out_dtype == MX_BF16;
   switch (fmt) {
-    case MX_E4M3: return bf ? deq_dispatch<E4M3, true>(q, scales, rows, cols, col, out, stream)
-                            : deq_dispatch<E4M3, false>(q, scales, rows, cols, col, out, stream);
-    case MX_E5M2: return bf ? deq_dispatch<E5M2, true>(q, scales, rows, cols, col, out, stream)
-                            : deq_dispatch<E5M2, false>(q, scales, rows, cols, col, out, stream);
-    case MX_E2M3: return bf ? deq_dispatch<E2M3, true>(q, scales, rows, cols, col, out, stream)
-                            : deq_dispatch<E2M3, false>(q, scales, rows, cols, col, out, stream);
-    case MX_E3M2: return bf ? deq_dispatch<E3M2, true>(q, scales, rows, cols, col, out, stream)
-                            : deq_dispatch<E3M2, false>(q, scales, rows, cols, col, out, stream);
-    default: return bf ? deq_dispatch<E2M1, true>(q, scales, rows, cols, col, out, stream)
-                       : deq_dispatch<E2M1, false>(q, scales, rows, cols, col, out, stream);
+    case MX_E4M3: return bf ? deq_dispatch<E4M3, true>(q, scales, rows, cols, col, gemm_scales, out, stream)
+                            : deq_dispatch<E4M3, false>(q, scales, rows, cols, col, gemm_scales, out, stream);
+    case MX_E5M2: return bf ? deq_dispatch<E5M2, true>(q, scales, rows, cols, col, gemm_scales, out, stream)
+                            : deq_dispatch<E5M2, false>(q, scales, rows, cols, col, gemm_scales, out, stream);
+    case MX_E2M3: return bf ? deq_dispatch<E2M3, true>(q, scales, rows, cols, col, gemm_scales, out, stream)
+                            : deq_dispatch<E2M3, false>(q, scales, rows, cols, col, gemm_scales, out, stream);
+    case MX_E3M2: return bf ? deq_dispatch<E3M2, true>(q, scales, rows, cols, col, gemm_scales, out, stream)
+                            : deq_dispatch<E3M2, false>(q, scales, rows, cols, col, gemm_scales, out, stream);
+    default: return bf ? deq_dispatch<E2M1, true>(q, scales, rows, cols, col, gemm_scales, out, stream)
+                       : deq_dispatch<E2M1, false>(q, scales, rows, cols, col, gemm_scales, out, stream);
   }
 }
 

@@ -70,6 +70,7 @@ struct GemmArgs {
   uint8_t* sc;
   uint32_t* amax;
   int fc, rc;                   // element format and scale rule of the re-quantization
+  bool gemm_scales;             // sa / sb in the GEMM scale layout ([K/512][rows][16]) instead of row-major
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
@@ -187,8 +188,8 @@ __attribute__((amdgpu_waves_per_eu((kIsFp6<FA> && kIsFp6<FB>) ? 2 : 1))) void ge
       for (int u = 0; u < kNS; ++u) {
         const int i = tid + u * kGemmThreads, r = i / kSB, kb = i % kSB;
         const int64_t gk = k0 / 32 + kb;
-        rsa[u] = (m0 + r < M && gk < kblocks) ? SA[(m0 + r) * kblocks + gk] : uint8_t(127);
-        rsb[u] = (n0 + r < N && gk < kblocks) ? SB[(n0 + r) * kblocks + gk] : uint8_t(127);
+        rsa[u] = (m0 + r < M && gk < kblocks) ? SA[scale_offset(m0 + r, gk, M, kblocks, g.gemm_scales)] : uint8_t(127);
+        rsb[u] = (n0 + r < N && gk < kblocks) ? SB[scale_offset(n0 + r, gk, N, kblocks, g.gemm_scales)] : uint8_t(127);
       }
     }
   };
@@ -499,6 +500,7 @@ struct Ctx {
   uint32_t js_a, js_b;             // K-contiguous: bytes between the rows of DMA instructions j and j + 1
   uint32_t step_a, step_b;         // bytes between consecutive stages (M/N-contiguous operands)
   uint32_t sc_off;                 // lane's byte offset of its scale row (row 64 wave + lane)
+  uint32_t sc_step_a, sc_step_b;   // bytes between consecutive scale stages of a row
   int rd_a, rd_b;                  // lane's read base inside a stage object (row-tile 0)
   int c0, c1;                      // lane's swizzled chunk offsets: chunk h and chunk h + 2
   int tp_a, tp_b;                  // M/N-contiguous: lane's swizzled chunk byte offset (row-tile 0)
@@ -542,8 +544,8 @@ __device__ __forceinline__ void issue_pair(const Ctx& c, int t, int wave, bool l
 constexpr int kScaleOps = 2;
 template <int U>
 __device__ __forceinline__ void issue_scales(const Ctx& c, int u, int wave, bool live) {
-  dma<16>(live ? c.sa : c.z, c.sc_off, uint32_t(16 * u), &scales<U>()[0][64 * wave][0]);
-  dma<16>(live ? c.sb : c.z, c.sc_off, uint32_t(16 * u), &scales<U>()[1][64 * wave][0]);
+  dma<16>(live ? c.sa : c.z, c.sc_off, uint32_t(u) * c.sc_step_a, &scales<U>()[0][64 * wave][0]);
+  dma<16>(live ? c.sb : c.z, c.sc_off, uint32_t(u) * c.sc_step_b, &scales<U>()[1][64 * wave][0]);
 }
 
 // L2 prefetch of the 128-byte line column holding stages s and s + 1 (s even) for
@@ -841,8 +843,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
     c.b = make_rsrc(B + int64_t(tn) * kTile * kbytes, uint32_t(rows_b * kbytes));
   c.z = make_rsrc(A, 0);
   if constexpr (!PT) {
-    c.sa = make_rsrc(g.sa + int64_t(tm) * kTile * kblocks, uint32_t(rows_a * kblocks));
-    c.sb = make_rsrc(g.sb + int64_t(tn) * kTile * kblocks, uint32_t(rows_b * kblocks));
+    if (g.gemm_scales) {
+      // [K/512][rows][16]: the tile's 16-byte rows of scale stage u start u * rows * 16 bytes in
+      // (the host keeps rows * K / 32 below 2^31); rows past the tile's last one read other rows'
+      // scales, which only meet zero codes and reach outputs that are never stored
+      const int64_t oa = int64_t(tm) * kTile * 16, ob = int64_t(tn) * kTile * 16;
+      c.sa = make_rsrc(g.sa + oa, uint32_t(g.M * kblocks - oa));
+      c.sb = make_rsrc(g.sb + ob, uint32_t(g.N * kblocks - ob));
+      c.sc_step_a = uint32_t(g.M) * 16u;
+      c.sc_step_b = uint32_t(g.N) * 16u;
+    } else {
+      c.sa = make_rsrc(g.sa + int64_t(tm) * kTile * kblocks, uint32_t(rows_a * kblocks));
+      c.sb = make_rsrc(g.sb + int64_t(tn) * kTile * kblocks, uint32_t(rows_b * kblocks));
+      c.sc_step_a = c.sc_step_b = 16u;
+    }
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -860,7 +874,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   c.js_b = uint32_t(8 * kbytes);
   c.step_a = uint32_t(kRow) * uint32_t(TA ? lda : 1);
   c.step_b = uint32_t(kRow) * uint32_t(TB ? ldb : 1);
-  c.sc_off = uint32_t(64 * wave + lane) * uint32_t(kblocks);
+  c.sc_off = uint32_t(64 * wave + lane) * uint32_t(g.gemm_scales ? 16 : kblocks);
   const int rr = lane & 31, h = lane >> 5;
   // K-contiguous: rows 32 i + rr of a wave's half share swz(rr): 32 i only changes higher row bits;
   // chunk h (stage half 0) at h ^ swz, chunk h + 2 at that ^ 2
@@ -1011,9 +1025,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
 
 template <int FA, int FB, bool BF>
 static mx_status_t gemm_dispatch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb, int64_t M,
-                                 int64_t N, int64_t K, float alpha, void* c, int64_t ldc, hipStream_t st) {
+                                 int64_t N, int64_t K, float alpha, void* c, int64_t ldc, bool gemm_scales,
+                                 hipStream_t st) {
   const int esize = BF ? 2 : 4;
   GemmArgs g{};
+  g.gemm_scales = gemm_scales;
   g.a = a;
   g.sa = sa;
   g.b = b;
@@ -1102,16 +1118,16 @@ static mx_status_t requant_dispatch(GemmArgs g, hipStream_t st) {
 template <bool BF>
 static mx_status_t gemm_formats(int fa, int fb, const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                                 const uint8_t* sb, int64_t M, int64_t N, int64_t K, float alpha, void* c, int64_t ldc,
-                                hipStream_t st) {
-  if (fa == E4M3 && fb == E4M3) return gemm_dispatch<E4M3, E4M3, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
-  if (fa == E4M3 && fb == E5M2) return gemm_dispatch<E4M3, E5M2, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
-  if (fa == E5M2 && fb == E4M3) return gemm_dispatch<E5M2, E4M3, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
-  if (fa == E5M2 && fb == E5M2) return gemm_dispatch<E5M2, E5M2, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
-  if (fa == E2M1 && fb == E2M1) return gemm_dispatch<E2M1, E2M1, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
-  if (fa == E2M3 && fb == E2M3) return gemm_dispatch<E2M3, E2M3, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
-  if (fa == E2M3 && fb == E3M2) return gemm_dispatch<E2M3, E3M2, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
-  if (fa == E3M2 && fb == E2M3) return gemm_dispatch<E3M2, E2M3, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
-  if (fa == E3M2 && fb == E3M2) return gemm_dispatch<E3M2, E3M2, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, st);
+                                bool gs, hipStream_t st) {
+  if (fa == E4M3 && fb == E4M3) return gemm_dispatch<E4M3, E4M3, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, gs, st);
+  if (fa == E4M3 && fb == E5M2) return gemm_dispatch<E4M3, E5M2, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, gs, st);
+  if (fa == E5M2 && fb == E4M3) return gemm_dispatch<E5M2, E4M3, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, gs, st);
+  if (fa == E5M2 && fb == E5M2) return gemm_dispatch<E5M2, E5M2, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, gs, st);
+  if (fa == E2M1 && fb == E2M1) return gemm_dispatch<E2M1, E2M1, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, gs, st);
+  if (fa == E2M3 && fb == E2M3) return gemm_dispatch<E2M3, E2M3, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, gs, st);
+  if (fa == E2M3 && fb == E3M2) return gemm_dispatch<E2M3, E3M2, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, gs, st);
+  if (fa == E3M2 && fb == E2M3) return gemm_dispatch<E3M2, E2M3, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, gs, st);
+  if (fa == E3M2 && fb == E3M2) return gemm_dispatch<E3M2, E3M2, BF>(a, sa, b, sb, M, N, K, alpha, c, ldc, gs, st);
   return MX_ERR_UNSUPPORTED;
 }
 
@@ -1119,9 +1135,20 @@ static mx_status_t gemm_formats(int fa, int fb, const uint8_t* a, const uint8_t*
 
 using namespace mxk;
 
+// The GEMM scale layout groups 16 K-blocks (K % 512 == 0) and its stage offsets
+// are 32-bit (rows * K / 32 below 2^31 for both operands).
+static mx_status_t check_scale_layout(mx_scale_layout_t layout, int64_t M, int64_t N, int64_t K) {
+  if (layout != MX_SCALES_ROW_MAJOR && layout != MX_SCALES_GEMM) return MX_ERR_UNSUPPORTED;
+  if (layout == MX_SCALES_GEMM &&
+      (K % 512 != 0 || M * (K / 32) >= (int64_t(1) << 31) || N * (K / 32) >= (int64_t(1) << 31)))
+    return MX_ERR_SHAPE;
+  return MX_OK;
+}
+
 extern "C" mx_status_t mx_gemm(const uint8_t* a, const uint8_t* sa, mx_elem_t fmt_a, const uint8_t* b,
-                               const uint8_t* sb, mx_elem_t fmt_b, int64_t M, int64_t N, int64_t K, float alpha,
-                               void* c, mx_dtype_t c_dtype, int64_t ldc, hipStream_t stream) {
+                               const uint8_t* sb, mx_elem_t fmt_b, mx_scale_layout_t scale_layout, int64_t M,
+                               int64_t N, int64_t K, float alpha, void* c, mx_dtype_t c_dtype, int64_t ldc,
+                               hipStream_t stream) {
   const bool f8a = fmt_a == MX_E4M3 || fmt_a == MX_E5M2, f8b = fmt_b == MX_E4M3 || fmt_b == MX_E5M2;
   const bool f6a = fmt_a == MX_E2M3 || fmt_a == MX_E3M2, f6b = fmt_b == MX_E2M3 || fmt_b == MX_E3M2;
   if (!((f8a && f8b) || (f6a && f6b) || (fmt_a == MX_E2M1 && fmt_b == MX_E2M1))) return MX_ERR_UNSUPPORTED;
@@ -1131,12 +1158,14 @@ extern "C" mx_status_t mx_gemm(const uint8_t* a, const uint8_t* sa, mx_elem_t fm
   if (f6a && K % 64 != 0) return MX_ERR_SHAPE;
   if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return MX_ERR_SHAPE;
   if (ldc < N) return MX_ERR_SHAPE;
+  if (mx_status_t st = check_scale_layout(scale_layout, M, N, K); st != MX_OK) return st;
   if (M == 0 || N == 0) return MX_OK;
   if (!c || (K > 0 && (!a || !sa || !b || !sb))) return MX_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(c) & (c_dtype == MX_BF16 ? 1u : 3u)) != 0) return MX_ERR_ALIGN;
   if (K > 0 && (misaligned(a) || misaligned(b))) return MX_ERR_ALIGN;
-  return c_dtype == MX_BF16 ? gemm_formats<true>(fmt_a, fmt_b, a, sa, b, sb, M, N, K, alpha, c, ldc, stream)
-                            : gemm_formats<false>(fmt_a, fmt_b, a, sa, b, sb, M, N, K, alpha, c, ldc, stream);
+  const bool gs = scale_layout == MX_SCALES_GEMM;
+  return c_dtype == MX_BF16 ? gemm_formats<true>(fmt_a, fmt_b, a, sa, b, sb, M, N, K, alpha, c, ldc, gs, stream)
+                            : gemm_formats<false>(fmt_a, fmt_b, a, sa, b, sb, M, N, K, alpha, c, ldc, gs, stream);
 }
 
 extern "C" mx_status_t mm_fp8(const uint8_t* a, const uint8_t* b, mx_elem_t fmt, int64_t batch, int64_t M, int64_t N,
@@ -1175,8 +1204,9 @@ extern "C" mx_status_t mm_fp8(const uint8_t* a, const uint8_t* b, mx_elem_t fmt,
 }
 
 extern "C" mx_status_t mx_gemm_requant(const uint8_t* a, const uint8_t* sa, mx_elem_t fmt_a, const uint8_t* b,
-                                       const uint8_t* sb, mx_elem_t fmt_b, int64_t M, int64_t N, int64_t K,
-                                       float alpha, mx_elem_t fmt_c, mx_scale_rule_t rule_c, uint8_t* qc,
+                                       const uint8_t* sb, mx_elem_t fmt_b, mx_scale_layout_t scale_layout, int64_t M,
+                                       int64_t N, int64_t K, float alpha, mx_elem_t fmt_c, mx_scale_rule_t rule_c,
+                                       uint8_t* qc,
                                        uint8_t* sc, float* amax_out, hipStream_t stream) {
   const bool f8a = fmt_a == MX_E4M3 || fmt_a == MX_E5M2, f8b = fmt_b == MX_E4M3 || fmt_b == MX_E5M2;
   if (!((f8a && f8b) || (fmt_a == MX_E2M1 && fmt_b == MX_E2M1))) return MX_ERR_UNSUPPORTED;
@@ -1184,6 +1214,7 @@ extern "C" mx_status_t mx_gemm_requant(const uint8_t* a, const uint8_t* sa, mx_e
   if (rule_c != MX_SCALE_FLOOR && rule_c != MX_SCALE_CEIL) return MX_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || N % 32 != 0) return MX_ERR_SHAPE;
   if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return MX_ERR_SHAPE;
+  if (mx_status_t st = check_scale_layout(scale_layout, M, N, K); st != MX_OK) return st;
   if (M == 0 || N == 0) return MX_OK;
   if (!qc || !sc || (K > 0 && (!a || !sa || !b || !sb))) return MX_ERR_NULL;
   if (misaligned(qc) || (K > 0 && (misaligned(a) || misaligned(b)))) return MX_ERR_ALIGN;
@@ -1203,6 +1234,7 @@ extern "C" mx_status_t mx_gemm_requant(const uint8_t* a, const uint8_t* sa, mx_e
   g.amax = reinterpret_cast<uint32_t*>(amax_out);
   g.fc = int(fmt_c);
   g.rc = int(rule_c);
+  g.gemm_scales = scale_layout == MX_SCALES_GEMM;
   if (fmt_a == MX_E4M3 && fmt_b == MX_E4M3) return requant_dispatch<E4M3, E4M3>(g, stream);
   if (fmt_a == MX_E4M3 && fmt_b == MX_E5M2) return requant_dispatch<E4M3, E5M2>(g, stream);
   if (fmt_a == MX_E5M2 && fmt_b == MX_E4M3) return requant_dispatch<E5M2, E4M3>(g, stream);

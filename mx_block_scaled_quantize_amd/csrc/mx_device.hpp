@@ -130,6 +130,17 @@ __device__ __forceinline__ float pow2_neg(int e) {
   return e <= 126 ? __uint_as_float(uint32_t(127 - e) << 23) : __uint_as_float(0x00400000u);
 }
 
+// Byte offset of the E8M0 scale of K-block kb of line `line` (an operand row) in
+// a scale array of `lines` lines and `kblocks` K-blocks per line:
+//   row-major      [lines][kblocks]
+//   GEMM layout    [kblocks / 16][lines][16]: the 16 scales a GEMM stage of 16
+//                  K-blocks needs are contiguous per line, and the lines of a
+//                  stage are contiguous (kblocks % 16 == 0)
+__host__ __device__ __forceinline__ int64_t scale_offset(int64_t line, int64_t kb, int64_t lines, int64_t kblocks,
+                                                         bool gemm_layout) {
+  return gemm_layout ? (((kb >> 4) * lines + line) << 4) + (kb & 15) : line * kblocks + kb;
+}
+
 // ---------------------------------------------------------------------------
 // Input widening: 8 consecutive elements starting at element index `i`
 // (16-byte aligned for 2-byte types, 32-byte aligned for FP32).

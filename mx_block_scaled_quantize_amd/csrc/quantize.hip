@@ -175,7 +175,8 @@ constexpr int kRowUnroll = 4;
 template <int IN, int F, int R, bool HAD, bool AMAX>
 __global__ __launch_bounds__(kRowThreads) void rowwise_kernel(const void* __restrict__ x, int64_t nchunks,
                                                                uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
-                                                               uint32_t* __restrict__ amax_out, uint32_t had_mask) {
+                                                               uint32_t* __restrict__ amax_out, uint32_t had_mask,
+                                                               int64_t lines, int64_t gemm_kblocks) {
   constexpr int kW = ChunkWords<IN>::kN;
   const int lane_q = threadIdx.x & 3;
   uint32_t tmax = 0;
@@ -199,7 +200,12 @@ __global__ __launch_bounds__(kRowThreads) void rowwise_kernel(const void* __rest
     uint32_t w[Words<F, 8>::kN];
     const uint32_t sc = row_chunk_mx<IN, F, R, HAD>(raw[u], v, m, had_mask, lane_q, w);
     store_row8<F>(q, chunk[u] * 8, w);
-    if (lane_q == 0) scales[chunk[u] >> 2] = uint8_t(sc);
+    if (lane_q == 0) {
+      // block index chunk / 4 = line * kblocks + kb; gemm_kblocks != 0 selects the GEMM scale layout
+      const int64_t blk = chunk[u] >> 2;
+      scales[gemm_kblocks ? scale_offset(blk / gemm_kblocks, blk % gemm_kblocks, lines, gemm_kblocks, true) : blk] =
+          uint8_t(sc);
+    }
   }
   if constexpr (AMAX) {
     __shared__ uint32_t red[kRowThreads / 64];
@@ -419,6 +425,7 @@ struct StripArgs {
   uint32_t* amax_out;   // MX modes: max-accumulator (bit pattern of a non-negative float), may be null
   RingArgs ring;        // PT modes
   uint32_t had_mask;
+  bool gemm_scales;     // MX scales in the GEMM layout (16-block groups outermost) instead of row-major
   int strips_c;         // strips along the column axis
   int bands;            // 128-row bands (4 strips each)
   int supertiles;       // bands * strips_c
@@ -596,7 +603,9 @@ __global__ __launch_bounds__(64 * kStripWaves) void strip_kernel(StripArgs a) {
             uint32_t w[Words<F, 8>::kN];
             if constexpr (MODE == MX_DUAL) {
               const uint32_t sc = row_chunk_mx<IN, F, R, false>(raw[i], v, m, 0u, lane_q, w);
-              if (lane_q == 0) a.s_row[e0 >> 5] = uint8_t(sc);
+              if (lane_q == 0)
+                a.s_row[scale_offset(r0 + 4 * i + lrow, (c0 + lcol) >> 5, a.rows, a.cols >> 5, a.gemm_scales)] =
+                    uint8_t(sc);
             } else {
               pt_encode_f32<F, 8>(v, mult, pt_slow ? 0x7FFFFFFFu : m, w);
             }
@@ -671,7 +680,7 @@ __global__ __launch_bounds__(64 * kStripWaves) void strip_kernel(StripArgs a) {
           const int c = threadIdx.x;
           const int64_t col = c0 + c;
           if (col < a.cols) {
-            uint8_t* sp = a.s_col + col * scale_pitch + (rb >> 5);
+            uint8_t* sp = a.s_col + scale_offset(col, rb >> 5, a.cols, scale_pitch, a.gemm_scales);
             const int nst = a.rows - rb >= 128 ? 4 : int((a.rows - rb) >> 5);
             if (nst == 4 && (reinterpret_cast<uintptr_t>(sp) & 3u) == 0) {
               *reinterpret_cast<uint32_t*>(sp) = uint32_t(sc_lds[0][c]) | (uint32_t(sc_lds[1][c]) << 8) |
@@ -905,7 +914,7 @@ __global__ __launch_bounds__(256) void dual_bf16_kernel(StripArgs a, int tiles_c
     const int64_t other0 = col_side ? tr : tc, other = col_side ? a.rows : a.cols;
     if (line < lines) {
       const uint32_t v = col_side ? scol_lds[j] : srow_lds[j];
-      uint8_t* dst = (col_side ? a.s_col : a.s_row) + line * (other >> 5) + (other0 >> 5);
+      uint8_t* dst = (col_side ? a.s_col : a.s_row) + scale_offset(line, other0 >> 5, lines, other >> 5, a.gemm_scales);
       const int64_t nb = (other - other0) >> 5;
       if (nb >= 4 && (reinterpret_cast<uintptr_t>(dst) & 3u) == 0) {
         *reinterpret_cast<uint32_t*>(dst) = v;
@@ -1081,7 +1090,7 @@ __global__ __launch_bounds__(64 * ColTile<F>::kWaves) void col_bf16_kernel(Strip
   if (threadIdx.x < kDualTile) {
     const int j = threadIdx.x;
     if (tc + j < a.cols) {
-      uint8_t* dst = a.s_col + (tc + j) * (a.rows >> 5) + (tr >> 5);
+      uint8_t* dst = a.s_col + scale_offset(tc + j, tr >> 5, a.cols, a.rows >> 5, a.gemm_scales);
       const int64_t nb = (a.rows - tr) >> 5;
       if (nb >= kW && (reinterpret_cast<uintptr_t>(dst) & (kW - 1)) == 0) {
         if constexpr (kW == 8) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(scol_lds + j * kW);
@@ -1202,16 +1211,20 @@ static mx_status_t launch(K kernel, dim3 grid, dim3 block, hipStream_t s, Args..
 
 template <int IN, int F, int R>
 static mx_status_t rowwise_dispatch(const void* x, int64_t n, uint8_t* q, uint8_t* s, uint32_t* amax, bool had,
-                                    uint32_t mask, hipStream_t st) {
+                                    uint32_t mask, int64_t lines, int64_t gemm_kblocks, hipStream_t st) {
   const int64_t nchunks = n / 8;
   const int64_t per = int64_t(kRowThreads) * kRowUnroll;
   const dim3 grid{unsigned((nchunks + per - 1) / per)}, block{unsigned(kRowThreads)};
   if (had) {
-    return amax ? launch(rowwise_kernel<IN, F, R, true, true>, grid, block, st, x, nchunks, q, s, amax, mask)
-                : launch(rowwise_kernel<IN, F, R, true, false>, grid, block, st, x, nchunks, q, s, amax, mask);
+    return amax ? launch(rowwise_kernel<IN, F, R, true, true>, grid, block, st, x, nchunks, q, s, amax, mask, lines,
+                                     gemm_kblocks)
+                : launch(rowwise_kernel<IN, F, R, true, false>, grid, block, st, x, nchunks, q, s, amax, mask, lines,
+                                     gemm_kblocks);
   }
-  return amax ? launch(rowwise_kernel<IN, F, R, false, true>, grid, block, st, x, nchunks, q, s, amax, mask)
-              : launch(rowwise_kernel<IN, F, R, false, false>, grid, block, st, x, nchunks, q, s, amax, mask);
+  return amax ? launch(rowwise_kernel<IN, F, R, false, true>, grid, block, st, x, nchunks, q, s, amax, mask, lines,
+                                     gemm_kblocks)
+              : launch(rowwise_kernel<IN, F, R, false, false>, grid, block, st, x, nchunks, q, s, amax, mask, lines,
+                                     gemm_kblocks);
 }
 
 // Workgroups of `kernel` resident at once on the current device (cached per
@@ -1294,8 +1307,8 @@ static mx_status_t expand(int in, int fmt, int rule, Args&&... args) {
 
 template <int IN, int F, int R> struct RowOp {
   static mx_status_t run(const void* x, int64_t n, uint8_t* q, uint8_t* s, uint32_t* amax, bool had, uint32_t mask,
-                         hipStream_t st) {
-    return rowwise_dispatch<IN, F, R>(x, n, q, s, amax, had, mask, st);
+                         int64_t lines, int64_t gemm_kblocks, hipStream_t st) {
+    return rowwise_dispatch<IN, F, R>(x, n, q, s, amax, had, mask, lines, gemm_kblocks, st);
   }
 };
 template <int IN, int F, int R> struct ColOp {
@@ -1356,12 +1369,18 @@ using namespace mxk;
 
 extern "C" mx_status_t mx_quantize(const void* x, mx_dtype_t in, int64_t rows, int64_t cols, int block,
                                    mx_elem_t fmt, mx_scale_rule_t rule, mx_orient_t orient, int hadamard,
-                                   uint32_t hadamard_sign_mask, uint8_t* q, uint8_t* scales, float* amax_out,
-                                   hipStream_t stream) {
-  if (fmt == MX_E2M3 || fmt == MX_E3M2)
+                                   uint32_t hadamard_sign_mask, uint8_t* q, uint8_t* scales,
+                                   mx_scale_layout_t scale_layout, float* amax_out, hipStream_t stream) {
+  if (scale_layout != MX_SCALES_ROW_MAJOR && scale_layout != MX_SCALES_GEMM) return MX_ERR_UNSUPPORTED;
+  const bool gemm_scales = scale_layout == MX_SCALES_GEMM;
+  if (fmt == MX_E2M3 || fmt == MX_E3M2) {
+    if (gemm_scales) return MX_ERR_UNSUPPORTED;
     return fp6_quantize(x, in, rows, cols, block, fmt, rule, orient, hadamard, q, scales, amax_out, stream);
+  }
   if (mx_status_t st = check_common_quant(in, rows, cols, block, fmt, rule); st != MX_OK) return st;
   if (orient != MX_ROWWISE && orient != MX_COLWISE_T) return MX_ERR_UNSUPPORTED;
+  // the GEMM layout groups 16 K-blocks: the blocked axis is a multiple of 512
+  if (gemm_scales && (orient == MX_ROWWISE ? cols : rows) % 512 != 0) return MX_ERR_SHAPE;
   const int64_t n = rows * cols;
   if (n > 0 && (!x || !q || !scales)) return MX_ERR_NULL;
   if (orient == MX_ROWWISE && cols % 32 != 0) return MX_ERR_SHAPE;
@@ -1371,22 +1390,30 @@ extern "C" mx_status_t mx_quantize(const void* x, mx_dtype_t in, int64_t rows, i
   uint32_t* amax = reinterpret_cast<uint32_t*>(amax_out);
   if (n == 0) return MX_OK;
   if (orient == MX_ROWWISE)
-    return expand<RowOp>(in, fmt, rule, x, n, q, scales, amax, hadamard != 0, hadamard_sign_mask, stream);
+    return expand<RowOp>(in, fmt, rule, x, n, q, scales, amax, hadamard != 0, hadamard_sign_mask, rows,
+                         gemm_scales ? cols / 32 : int64_t(0), stream);
   StripArgs a{};
   a.x = x; a.rows = rows; a.cols = cols; a.q_col = q; a.s_col = scales; a.amax_out = amax;
   a.had_mask = hadamard_sign_mask;
+  a.gemm_scales = gemm_scales;
   return expand<ColOp>(in, fmt, rule, a, hadamard != 0, amax != nullptr, stream);
 }
 
 extern "C" mx_status_t mx_quantize_dual(const void* x, mx_dtype_t in, int64_t rows, int64_t cols, int block,
                                         mx_elem_t fmt, mx_scale_rule_t rule, uint8_t* q_row, uint8_t* s_row,
-                                        uint8_t* q_colT, uint8_t* s_colT, float* amax_out, hipStream_t stream) {
-  if (fmt == MX_E2M3 || fmt == MX_E3M2)
+                                        uint8_t* q_colT, uint8_t* s_colT, mx_scale_layout_t scale_layout,
+                                        float* amax_out, hipStream_t stream) {
+  if (scale_layout != MX_SCALES_ROW_MAJOR && scale_layout != MX_SCALES_GEMM) return MX_ERR_UNSUPPORTED;
+  const bool gemm_scales = scale_layout == MX_SCALES_GEMM;
+  if (fmt == MX_E2M3 || fmt == MX_E3M2) {
+    if (gemm_scales) return MX_ERR_UNSUPPORTED;
     return fp6_quantize_dual(x, in, rows, cols, block, fmt, rule, q_row, s_row, q_colT, s_colT, amax_out, stream);
+  }
   if (mx_status_t st = check_common_quant(in, rows, cols, block, fmt, rule); st != MX_OK) return st;
   const int64_t n = rows * cols;
   if (n > 0 && (!x || !q_row || !s_row || !q_colT || !s_colT)) return MX_ERR_NULL;
   if (rows % 32 != 0 || cols % 32 != 0) return MX_ERR_SHAPE;
+  if (gemm_scales && (rows % 512 != 0 || cols % 512 != 0)) return MX_ERR_SHAPE;
   if (n > 0 && (misaligned(x) || misaligned(q_row) || misaligned(q_colT))) return MX_ERR_ALIGN;
   // amax_out is a max-accumulator the caller initialises; nothing to do when empty
   uint32_t* amax = reinterpret_cast<uint32_t*>(amax_out);
@@ -1394,6 +1421,7 @@ extern "C" mx_status_t mx_quantize_dual(const void* x, mx_dtype_t in, int64_t ro
   StripArgs a{};
   a.x = x; a.rows = rows; a.cols = cols; a.q_row = q_row; a.s_row = s_row; a.q_col = q_colT; a.s_col = s_colT;
   a.amax_out = amax;
+  a.gemm_scales = gemm_scales;
   return expand<DualOp>(in, fmt, rule, a, amax != nullptr, stream);
 }
 

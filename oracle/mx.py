@@ -139,6 +139,31 @@ def unpack_codes(packed, fmt) -> np.ndarray:
     return np.asarray(packed).astype(np.uint8)
 
 
+def scales_to_gemm_layout(scales) -> np.ndarray:
+    """E8M0 scales of an operand, [lines][kblocks] row-major, rearranged into the
+    GEMM layout [kblocks / 16][lines][16]: byte (line, kb) moves to
+    ((kb // 16) * lines + line) * 16 + kb % 16.  A pure permutation: K-blocks in
+    groups of 16 (one GEMM stage), each group's lines contiguous ("format-aware
+    fusion" FP4 article: the quantizer writes the scale layout its consumer reads;
+    the layout itself is this library's reading, defined in its header)."""
+    s = np.asarray(scales, dtype=np.uint8)
+    lines, kblocks = s.shape
+    assert kblocks % 16 == 0, "the GEMM layout needs kblocks % 16 == 0"
+    out = np.empty((kblocks // 16, lines, 16), dtype=np.uint8)
+    for kb in range(kblocks):
+        out[kb // 16, :, kb % 16] = s[:, kb]
+    return out
+
+
+def scales_from_gemm_layout(gemm_scales, lines, kblocks) -> np.ndarray:
+    """Inverse of scales_to_gemm_layout: back to [lines][kblocks]."""
+    g = np.asarray(gemm_scales, dtype=np.uint8).reshape(kblocks // 16, lines, 16)
+    out = np.empty((lines, kblocks), dtype=np.uint8)
+    for kb in range(kblocks):
+        out[:, kb] = g[kb // 16, :, kb % 16]
+    return out
+
+
 def quantize_rowwise(x, fmt, rule, hadamard_mask=None):
     """Row-wise MX quantization of a 2-D FP32 array [R][C], blocks of 32 along C.
 

@@ -61,12 +61,13 @@ def q(*a):
 
 
 def test_mx_quantize_argument_errors():
-    # (x, in, rows, cols, block, fmt, rule, orient, had, mask, q, s, amax, stream)
-    base = [FAKE, 1, 64, 64, 32, 0, 1, 0, 0, 0, FAKE, FAKE, None, None]
+    # (x, in, rows, cols, block, fmt, rule, orient, had, mask, q, s, layout, amax, stream)
+    base = [FAKE, 1, 64, 64, 32, 0, 1, 0, 0, 0, FAKE, FAKE, 0, None, None]
 
     def call(**kw):
         args = list(base)
-        names = ["x", "in_", "rows", "cols", "block", "fmt", "rule", "orient", "had", "mask", "q", "s", "amax", "st"]
+        names = ["x", "in_", "rows", "cols", "block", "fmt", "rule", "orient", "had", "mask", "q", "s", "layout", "amax",
+                 "st"]
         for k, v in kw.items():
             args[names.index(k)] = v
         return lib.mx_quantize(*args)
@@ -85,16 +86,22 @@ def test_mx_quantize_argument_errors():
     assert call(x=FAKE + 8) == ALIGN
     assert call(q=FAKE + 4) == ALIGN
     assert call(rows=0, x=None, q=None, s=None) == OK   # empty, nothing to do
+    assert call(layout=2) == UNSUP                      # no such scale layout
+    assert call(layout=1) == SHAPE                      # the GEMM layout groups 16 blocks: cols % 512
+    assert call(layout=1, orient=1, rows=256, cols=512) == SHAPE   # column-wise: rows % 512
+    assert call(layout=1, cols=512, fmt=3) == UNSUP     # not offered for FP6
 
 
 def test_mx_quantize_dual_argument_errors():
     f = lib.mx_quantize_dual
-    assert f(FAKE, 1, 64, 48, 32, 0, 1, FAKE, FAKE, FAKE, FAKE, None, None) == SHAPE
-    assert f(FAKE, 1, 48, 64, 32, 0, 1, FAKE, FAKE, FAKE, FAKE, None, None) == SHAPE
-    assert f(FAKE, 1, 64, 64, 32, 0, 1, FAKE, FAKE, None, FAKE, None, None) == NULL
-    assert f(FAKE, 1, 64, 64, 32, 0, 1, FAKE, FAKE, FAKE + 1, FAKE, None, None) == ALIGN
-    assert f(FAKE, 1, 64, 64, 64, 0, 1, FAKE, FAKE, FAKE, FAKE, None, None) == UNSUP
-    assert f(None, 1, 0, 64, 32, 0, 1, None, None, None, None, None, None) == OK
+    assert f(FAKE, 1, 64, 48, 32, 0, 1, FAKE, FAKE, FAKE, FAKE, 0, None, None) == SHAPE
+    assert f(FAKE, 1, 48, 64, 32, 0, 1, FAKE, FAKE, FAKE, FAKE, 0, None, None) == SHAPE
+    assert f(FAKE, 1, 64, 64, 32, 0, 1, FAKE, FAKE, None, FAKE, 0, None, None) == NULL
+    assert f(FAKE, 1, 64, 64, 32, 0, 1, FAKE, FAKE, FAKE + 1, FAKE, 0, None, None) == ALIGN
+    assert f(FAKE, 1, 64, 64, 64, 0, 1, FAKE, FAKE, FAKE, FAKE, 0, None, None) == UNSUP
+    assert f(None, 1, 0, 64, 32, 0, 1, None, None, None, None, 0, None, None) == OK
+    assert f(FAKE, 1, 512, 256, 32, 0, 1, FAKE, FAKE, FAKE, FAKE, 1, None, None) == SHAPE   # GEMM layout: both % 512
+    assert f(FAKE, 1, 512, 512, 32, 3, 1, FAKE, FAKE, FAKE, FAKE, 1, None, None) == UNSUP   # not for FP6
 
 
 def test_fp8_quantize_delayed_argument_errors():
@@ -158,28 +165,32 @@ def test_ring_layout_is_the_pages():
 
 def test_mx_dequantize_argument_errors():
     f = lib.mx_dequantize
-    assert f(FAKE, FAKE, 64, 48, 32, 0, 0, FAKE, 0, None) == SHAPE
-    assert f(FAKE, FAKE, 48, 64, 32, 0, 1, FAKE, 0, None) == SHAPE
-    assert f(FAKE, FAKE, 64, 64, 32, 0, 0, FAKE, 2, None) == UNSUP     # F16 output not offered
-    assert f(FAKE, FAKE, 64, 64, 32, 0, 0, None, 0, None) == NULL
-    assert f(FAKE, FAKE, 64, 64, 32, 0, 0, FAKE + 8, 0, None) == ALIGN
-    assert f(None, None, 0, 0, 32, 0, 0, None, 0, None) == OK
+    assert f(FAKE, FAKE, 64, 48, 32, 0, 0, 0, FAKE, 0, None) == SHAPE
+    assert f(FAKE, FAKE, 48, 64, 32, 0, 1, 0, FAKE, 0, None) == SHAPE
+    assert f(FAKE, FAKE, 64, 64, 32, 0, 0, 0, FAKE, 2, None) == UNSUP     # F16 output not offered
+    assert f(FAKE, FAKE, 64, 64, 32, 0, 0, 0, None, 0, None) == NULL
+    assert f(FAKE, FAKE, 64, 64, 32, 0, 0, 0, FAKE + 8, 0, None) == ALIGN
+    assert f(None, None, 0, 0, 32, 0, 0, 0, None, 0, None) == OK
+    assert f(FAKE, FAKE, 64, 64, 32, 0, 0, 1, FAKE, 0, None) == SHAPE    # GEMM layout needs cols % 512
+    assert f(FAKE, FAKE, 64, 512, 32, 0, 0, 3, FAKE, 0, None) == UNSUP
 
 
 def test_mx_gemm_argument_errors():
     f = lib.mx_gemm
-    # (a, sa, fa, b, sb, fb, M, N, K, alpha, c, c_dtype, ldc, stream)
-    assert f(FAKE, FAKE, 0, FAKE, FAKE, 2, 64, 64, 64, 1.0, FAKE, 1, 64, None) == UNSUP   # FP8 x FP4
-    assert f(FAKE, FAKE, 3, FAKE, FAKE, 0, 64, 64, 64, 1.0, FAKE, 1, 64, None) == UNSUP   # FP6 x FP8
-    assert f(FAKE, FAKE, 3, FAKE, FAKE, 4, 64, 64, 96, 1.0, FAKE, 1, 64, None) == SHAPE   # FP6: K % 64
-    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 48, 1.0, FAKE, 1, 64, None) == SHAPE   # K % 32
-    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, FAKE, 1, 60, None) == SHAPE   # ldc < N
-    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, FAKE, 2, 64, None) == UNSUP   # F16 out
-    assert f(None, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, FAKE, 1, 64, None) == NULL
-    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, FAKE + 1, 1, 64, None) == ALIGN   # odd BF16 address
-    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, FAKE + 2, 0, 64, None) == ALIGN   # FP32 needs 4 bytes
-    assert f(FAKE + 8, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, FAKE, 1, 64, None) == ALIGN
-    assert f(None, None, 0, None, None, 0, 0, 64, 64, 1.0, None, 1, 64, None) == OK
+    # (a, sa, fa, b, sb, fb, layout, M, N, K, alpha, c, c_dtype, ldc, stream)
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 2, 0, 64, 64, 64, 1.0, FAKE, 1, 64, None) == UNSUP   # FP8 x FP4
+    assert f(FAKE, FAKE, 3, FAKE, FAKE, 0, 0, 64, 64, 64, 1.0, FAKE, 1, 64, None) == UNSUP   # FP6 x FP8
+    assert f(FAKE, FAKE, 3, FAKE, FAKE, 4, 0, 64, 64, 96, 1.0, FAKE, 1, 64, None) == SHAPE   # FP6: K % 64
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 0, 64, 64, 48, 1.0, FAKE, 1, 64, None) == SHAPE   # K % 32
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 0, 64, 64, 64, 1.0, FAKE, 1, 60, None) == SHAPE   # ldc < N
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 0, 64, 64, 64, 1.0, FAKE, 2, 64, None) == UNSUP   # F16 out
+    assert f(None, FAKE, 0, FAKE, FAKE, 0, 0, 64, 64, 64, 1.0, FAKE, 1, 64, None) == NULL
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 0, 64, 64, 64, 1.0, FAKE + 1, 1, 64, None) == ALIGN   # odd BF16 address
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 0, 64, 64, 64, 1.0, FAKE + 2, 0, 64, None) == ALIGN   # FP32 needs 4 bytes
+    assert f(FAKE + 8, FAKE, 0, FAKE, FAKE, 0, 0, 64, 64, 64, 1.0, FAKE, 1, 64, None) == ALIGN
+    assert f(None, None, 0, None, None, 0, 0, 0, 64, 64, 1.0, None, 1, 64, None) == OK
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 1, 64, 64, 256, 1.0, FAKE, 1, 64, None) == SHAPE   # GEMM layout: K % 512
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 2, 64, 64, 512, 1.0, FAKE, 1, 64, None) == UNSUP   # no such layout
 
 
 def test_mm_fp8_argument_errors():
@@ -203,19 +214,20 @@ def test_mm_fp8_argument_errors():
 
 def test_mx_gemm_requant_argument_errors():
     f = lib.mx_gemm_requant
-    # (a, sa, fa, b, sb, fb, M, N, K, alpha, fc, rc, qc, sc, amax, stream)
-    assert f(FAKE, FAKE, 0, FAKE, FAKE, 2, 64, 64, 64, 1.0, 0, 1, FAKE, FAKE, None, None) == UNSUP   # FP8 x FP4
-    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, 3, 1, FAKE, FAKE, None, None) == UNSUP   # output format
-    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, 4, 1, FAKE, FAKE, None, None) == UNSUP   # E3M2 output
-    assert f(FAKE, FAKE, 3, FAKE, FAKE, 3, 64, 64, 64, 1.0, 0, 1, FAKE, FAKE, None, None) == UNSUP   # FP6 operands
-    assert f(FAKE, FAKE, 3, FAKE, FAKE, 4, 64, 64, 64, 1.0, 0, 1, FAKE, FAKE, None, None) == UNSUP
-    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, 0, 2, FAKE, FAKE, None, None) == UNSUP   # rule
-    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 48, 64, 1.0, 0, 1, FAKE, FAKE, None, None) == SHAPE   # N % 32
-    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 48, 1.0, 0, 1, FAKE, FAKE, None, None) == SHAPE   # K % 32
-    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, 0, 1, None, FAKE, None, None) == NULL
-    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, 0, 1, FAKE, None, None, None) == NULL
-    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 64, 64, 64, 1.0, 0, 1, FAKE + 8, FAKE, None, None) == ALIGN
-    assert f(None, None, 0, None, None, 0, 0, 64, 64, 1.0, 0, 1, None, None, None, None) == OK
+    # (a, sa, fa, b, sb, fb, layout, M, N, K, alpha, fc, rc, qc, sc, amax, stream)
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 2, 0, 64, 64, 64, 1.0, 0, 1, FAKE, FAKE, None, None) == UNSUP   # FP8 x FP4
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 0, 64, 64, 64, 1.0, 3, 1, FAKE, FAKE, None, None) == UNSUP   # output format
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 0, 64, 64, 64, 1.0, 4, 1, FAKE, FAKE, None, None) == UNSUP   # E3M2 output
+    assert f(FAKE, FAKE, 3, FAKE, FAKE, 3, 0, 64, 64, 64, 1.0, 0, 1, FAKE, FAKE, None, None) == UNSUP   # FP6 operands
+    assert f(FAKE, FAKE, 3, FAKE, FAKE, 4, 0, 64, 64, 64, 1.0, 0, 1, FAKE, FAKE, None, None) == UNSUP
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 0, 64, 64, 64, 1.0, 0, 2, FAKE, FAKE, None, None) == UNSUP   # rule
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 0, 64, 48, 64, 1.0, 0, 1, FAKE, FAKE, None, None) == SHAPE   # N % 32
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 0, 64, 64, 48, 1.0, 0, 1, FAKE, FAKE, None, None) == SHAPE   # K % 32
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 0, 64, 64, 64, 1.0, 0, 1, None, FAKE, None, None) == NULL
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 0, 64, 64, 64, 1.0, 0, 1, FAKE, None, None, None) == NULL
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 0, 64, 64, 64, 1.0, 0, 1, FAKE + 8, FAKE, None, None) == ALIGN
+    assert f(None, None, 0, None, None, 0, 0, 0, 64, 64, 1.0, 0, 1, None, None, None, None) == OK
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 0, 1, 64, 64, 256, 1.0, 0, 1, FAKE, FAKE, None, None) == SHAPE
 
 
 def test_mx_quantize_sr_argument_errors():

@@ -195,7 +195,7 @@ def test_gemm_ldc_and_k_zero():
     assert (o[:, 40:] == 7.0).all()                       # columns past N untouched
     z = torch.empty((0,), dtype=torch.uint8, device="cuda")
     c = torch.full((8, 8), 3.0, dtype=torch.float32, device="cuda")
-    st = mxa.lib.mx_gemm(z.data_ptr(), z.data_ptr(), 0, z.data_ptr(), z.data_ptr(), 0, 8, 8, 0, 1.0,
+    st = mxa.lib.mx_gemm(z.data_ptr(), z.data_ptr(), 0, z.data_ptr(), z.data_ptr(), 0, 0, 8, 8, 0, 1.0,
                          c.data_ptr(), 0, 8, torch.cuda.current_stream().cuda_stream)
     assert st == 0 and (host(c) == 0).all()               # empty sum
 

@@ -219,3 +219,32 @@ def test_tensor_amax_ignores_nan():
     x = np.array([[1.0, -7.0, np.nan, 3.0]], np.float32)
     assert mx.tensor_amax(x) == 7.0
     assert mx.tensor_amax(np.zeros((2, 2), np.float32)) == 0.0
+
+
+def test_gemm_scale_layout_literal_positions():
+    """The GEMM scale layout by hand: 3 lines x 32 K-blocks, value 100 * line + kb.
+    Flat byte order: stage 0 (kb 0..15) of line 0, line 1, line 2, then stage 1."""
+    lines, kblocks = 3, 32
+    s = (100 * np.arange(lines)[:, None] + np.arange(kblocks)[None, :]).astype(np.uint8)
+    g = mx.scales_to_gemm_layout(s).reshape(-1)
+    assert g.size == lines * kblocks
+    assert list(g[:4]) == [0, 1, 2, 3]              # line 0, kb 0..3
+    assert g[15] == 15 and g[16] == 100 and g[31] == 115   # line 0 kb 15, line 1 kb 0 / 15
+    assert g[32] == 200 and g[47] == 215            # line 2, kb 0 / 15
+    assert g[48] == 16 and g[64] == 116 and g[95] == 231   # stage 1: line 0 kb 16, line 1 kb 16, line 2 kb 31
+    # byte (line, kb) at ((kb // 16) * lines + line) * 16 + kb % 16, for every entry
+    for line in range(lines):
+        for kb in range(kblocks):
+            assert g[((kb // 16) * lines + line) * 16 + kb % 16] == s[line, kb]
+    assert np.array_equal(mx.scales_from_gemm_layout(g, lines, kblocks), s)
+
+
+def test_planted_line_major_gemm_layout_is_caught(monkeypatch):
+    """A plausible wrong layout (each line's stages contiguous, i.e. row-major
+    regrouped) is a permutation too and round-trips; the literal pin must reject it."""
+    def wrong(scales):
+        s = np.asarray(scales, dtype=np.uint8)
+        return s.reshape(s.shape[0], -1, 16).copy()
+    monkeypatch.setattr(mx, "scales_to_gemm_layout", wrong)
+    with pytest.raises(AssertionError):
+        test_gemm_scale_layout_literal_positions()
