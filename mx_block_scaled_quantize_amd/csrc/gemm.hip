@@ -403,7 +403,6 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_pair0[2 * kPairOp];   // sta
 __shared__ __attribute__((aligned(1024))) uint8_t g_pair1[2 * kPairOp];   // stages 4n + 2, 4n + 3
 __shared__ __attribute__((aligned(1024))) uint32_t g_scale0[2][kTile][4];   // [A/B][row][word]
 __shared__ __attribute__((aligned(1024))) uint32_t g_scale1[2][kTile][4];
-__shared__ __attribute__((aligned(1024))) uint32_t g_sink[4][64];   // landing area of the L2 prefetches (never read)
 
 // The object holding stage buffer I (0..3): stage pair I / 2; stage I is its half I % 2.
 template <int I>
@@ -456,23 +455,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // Cache policy of the operand loads: SC0 (measured ~7% faster than the default here)
 constexpr int kPolicySc0 = 1;
 
-// LDS-DMA: lane i's BYTES bytes at rsrc + voff + soff land at lds_dst + BYTES * i
+// LDS-DMA: lane i's 16 bytes at rsrc + voff + soff land at lds_dst + 16 i
 // (lds_dst wave-uniform).  soff is uniform and lives in an SGPR.
-template <int BYTES>
 __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, void* lds_dst) {
-  static_assert(BYTES == 4 || BYTES == 16, "dword or dwordx4");
-  if constexpr (BYTES == 16)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, soff, 0,
-                                             kPolicySc0);
-  else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_dst, 4, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, soff, 0,
+                                           kPolicySc0);
 }
 
 // Workgroups are dealt to the 8 XCDs round-robin; give every XCD a contiguous
 // run of the tile order, and walk tiles in groups of 8 tile-rows so that the
 // tiles running together on one XCD share their A and B panels in its L2.
-__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn, int& a_slice,
-                                         int& b_slice) {
+__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int ntiles = tiles_m * tiles_n;
   int idx = bid;
   if ((ntiles & 7) == 0) idx = (bid & 7) * (ntiles >> 3) + (bid >> 3);
@@ -483,10 +476,6 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int&
   const int in = idx - group * kGroupM * tiles_n;
   tm = first + in % gm;
   tn = in / gm;
-  // the tiles of one XCD round (32 consecutive positions) are 8 tile-rows x 4 tile-columns:
-  // the 4 sharing an A panel split its rows by tn % 4, the 8 sharing a B panel by tile-row
-  a_slice = tn & 3;
-  b_slice = in % gm;
 }
 
 
@@ -506,9 +495,6 @@ struct Ctx {
   int tp_a, tp_b;                  // M/N-contiguous: lane's swizzled chunk byte offset (row-tile 0)
   int sc_row_a, sc_row_b;          // lane's scale row (row-tile 0)
   int h8;                          // 8 * (lane / 32): the second K-block of an MFMA step is one byte up
-  __amdgpu_buffer_rsrc_t pf;       // this wave's L2-prefetch lines (A: wave 0, B: wave 1, none: 2, 3)
-  uint32_t pf_off;                 // lane's prefetch line offset
-  uint32_t pf_step;                // bytes between stages of the prefetched operand
 };
 
 // Stage pair (t, t + 1) (t even) into stage buffers SA_, SB_ (= SA_ + 1): for each
@@ -526,16 +512,16 @@ __device__ __forceinline__ void issue_pair(const Ctx& c, int t, int wave, bool l
     const int e = j / 4, jj = j % 4;   // M/N-contiguous: stage t + e, instruction jj of that stage
     const bool live = e == 0 ? live0 : live1;
     if constexpr (TA)
-      dma<16>(live ? c.a : c.z, c.off_a[jj], uint32_t(t + e) * c.step_a,
+      dma(live ? c.a : c.z, c.off_a[jj], uint32_t(t + e) * c.step_a,
               dst + e * kOpBytes + (wave * 4 + jj) * 1024);
     else
-      dma<16>(live0 ? c.a : c.z, c.off_a[j & 1], uint32_t(t) * kRow + uint32_t(j) * c.js_a,
+      dma(live0 ? c.a : c.z, c.off_a[j & 1], uint32_t(t) * kRow + uint32_t(j) * c.js_a,
               dst + (wave * kPairLoads + j) * 1024);
     if constexpr (TB)
-      dma<16>(live ? c.b : c.z, c.off_b[jj], uint32_t(t + e) * c.step_b,
+      dma(live ? c.b : c.z, c.off_b[jj], uint32_t(t + e) * c.step_b,
               dst + kPairOp + e * kOpBytes + (wave * 4 + jj) * 1024);
     else
-      dma<16>(live0 ? c.b : c.z, c.off_b[j & 1], uint32_t(t) * kRow + uint32_t(j) * c.js_b,
+      dma(live0 ? c.b : c.z, c.off_b[j & 1], uint32_t(t) * kRow + uint32_t(j) * c.js_b,
               dst + kPairOp + (wave * kPairLoads + j) * 1024);
   }
 }
@@ -544,19 +530,8 @@ __device__ __forceinline__ void issue_pair(const Ctx& c, int t, int wave, bool l
 constexpr int kScaleOps = 2;
 template <int U>
 __device__ __forceinline__ void issue_scales(const Ctx& c, int u, int wave, bool live) {
-  dma<16>(live ? c.sa : c.z, c.sc_off, uint32_t(u) * c.sc_step_a, &scales<U>()[0][64 * wave][0]);
-  dma<16>(live ? c.sb : c.z, c.sc_off, uint32_t(u) * c.sc_step_b, &scales<U>()[1][64 * wave][0]);
-}
-
-// L2 prefetch of the 128-byte line column holding stages s and s + 1 (s even) for
-// this workgroup's slice of its XCD group's panels: one dword per line into an LDS
-// sink nobody reads.  Data that other workgroups of the group fetch with their
-// DMAs some stages later then hits in L2 instead of waiting on memory.
-constexpr int kPrefetchAhead = 6;   // stages beyond the DMA's own target
-template <bool TA, bool TB>
-__device__ __forceinline__ void issue_prefetch(const Ctx& c, int s, int wave, bool live) {
-  const uint32_t step = (TA || TB) ? c.pf_step : uint32_t(kRow);
-  dma<4>(live ? c.pf : c.z, c.pf_off, uint32_t(s) * step, &g_sink[wave][0]);
+  dma(live ? c.sa : c.z, c.sc_off, uint32_t(u) * c.sc_step_a, &scales<U>()[0][64 * wave][0]);
+  dma(live ? c.sb : c.z, c.sc_off, uint32_t(u) * c.sc_step_b, &scales<U>()[1][64 * wave][0]);
 }
 
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -687,12 +662,11 @@ constexpr int later_ops() {
   constexpr int kSO = PT ? 0 : kScaleOps;   // per-tensor mode issues no scale loads
   // both stages of a pair arrive with every one of its instructions, so the first
   // stage of a pair is complete only once the whole pair is; every pair is followed
-  // by its scale stage (if any) and one prefetch instruction
+  // by its scale stage (if any)
   if constexpr (P % 2 == 1)   // group t + 1 opens the pair issued after stage t - 2
-    return (pair_has_scales<FP4>(P - 2) ? kSO : 0) + 1;
+    return pair_has_scales<FP4>(P - 2) ? kSO : 0;
   else                         // group t + 1 closes the pair issued after stage t - 3
-    return (pair_has_scales<FP4>(P - 3) ? kSO : 0) + 1 + 2 * kCodeGroup +
-           (pair_has_scales<FP4>(P - 1) ? kSO : 0) + 1;
+    return (pair_has_scales<FP4>(P - 3) ? kSO : 0) + 2 * kCodeGroup + (pair_has_scales<FP4>(P - 1) ? kSO : 0);
 }
 
 // LDS reads of one operand step: MX FP8 keeps its measured hint; per-tensor counts
@@ -736,13 +710,12 @@ __device__ __forceinline__ void stage_steps(const Ctx& c, int t, int T, int nsup
           const int un = (t + 1) / G::kPerScale + 1;
           issue_scales<((P + 1) / G::kPerScale + 1) & 1>(c, un, wave, un < nsuper);
         }
-        issue_prefetch<TA, TB>(c, t + 3 + kPrefetchAhead, wave, t + 3 + kPrefetchAhead < T);
       }
       // after the last stage this reads stale (in-bounds) LDS that no MFMA consumes; an
       // unconditional read keeps the operand registers free of merge copies
       read_step<kFp4, SIn, Un, 0, PT, TA, TB>(c, t + 1, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
       mfma_all<FA, FB, G::kSub - 1, PT>(acc, r.a[cur], r.b[cur], r.sa[cur], r.sb[cur], t, c.h8);
-      interleave<(kIssue ? 2 * kCodeGroup + 1 : 0) + (kScales ? kScaleOps : 0), kDsReads<kFp4, PT, TA, TB>()>();
+      interleave<(kIssue ? 2 * kCodeGroup : 0) + (kScales ? kScaleOps : 0), kDsReads<kFp4, PT, TA, TB>()>();
     }
   }
 }
@@ -816,8 +789,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  int tm, tn, a_slice, b_slice;
-  map_tile(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn, a_slice, b_slice);
+  int tm, tn;
+  map_tile(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int K = int(g.K);
   const int kbytes = kFp4 ? K / 2 : K, kblocks = K / 32;
   const int T = kbytes / kRow, nsuper = kblocks / kKbPerScale;
@@ -890,14 +863,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   c.sc_row_a = wm * 128 + rr;
   c.sc_row_b = wn * 128 + rr;
   c.h8 = 8 * h;
-  c.pf = wave == 0 ? c.a : wave == 1 ? c.b : c.z;
-  // wave 0 covers a quarter of the A lines of a stage pair, wave 1 an eighth of the B lines
-  const uint32_t pf_a = TA ? uint32_t(32 * a_slice + (lane >> 1)) * uint32_t(lda) + 128u * uint32_t(lane & 1)
-                           : uint32_t(64 * a_slice + lane) * uint32_t(kbytes);
-  const uint32_t pf_b = TB ? uint32_t(16 * b_slice + ((lane & 31) >> 1)) * uint32_t(ldb) + 128u * uint32_t(lane & 1)
-                           : uint32_t(32 * b_slice + (lane & 31)) * uint32_t(kbytes);
-  c.pf_off = wave == 0 ? pf_a : pf_b;
-  c.pf_step = wave == 0 ? c.step_a : c.step_b;
 
   v16f acc[4][4];
 #pragma unroll
@@ -911,18 +876,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   // prologue: code stages 0..3, scale stages 0 and 1 (T >= 2 and even, nsuper >= 1); stages
   // and scale stages past the end of K load zeros from the empty resource, and so do the
   // dead stages of the last unrolled body, so their MFMAs add nothing
-  // same op pattern as the loop (pair, its scale stage if any, one prefetch) so that
-  // the first boundaries' wait counts hold; the prologue's prefetches are empty
+  // same op pattern as the loop (pair, then its scale stage if any) so that the
+  // first boundaries' wait counts hold
   if constexpr (!PT) issue_scales<0>(c, 0, wave, true);
   issue_pair<0, 1, TA, TB>(c, 0, wave, true, true);   // T >= 2
-  issue_prefetch<TA, TB>(c, 0, wave, false);
   issue_pair<2, 3, TA, TB>(c, 2, wave, 2 < T, 3 < T);
   if constexpr (!PT) issue_scales<1>(c, 1, wave, 1 < nsuper);
-  issue_prefetch<TA, TB>(c, 0, wave, false);
   // scale stage 0 and code stage 0 landed; the pair order interleaves stages 0 and 1
   // instruction by instruction, so wait for both: what may stay in flight is stages
-  // 2 and 3, scale stage 1 and the two prefetches
-  wait_vm_lgkm0<2 * kCodeGroup + (PT ? 0 : kScaleOps) + 2>();
+  // 2 and 3 and scale stage 1
+  wait_vm_lgkm0<2 * kCodeGroup + (PT ? 0 : kScaleOps)>();
   barrier();
   read_step<kFp4, 0, 0, 0, PT, TA, TB>(c, 0, lane, r.a[0], r.b[0], r.sa[0], r.sb[0]);
 
