@@ -342,12 +342,17 @@ __attribute__((amdgpu_waves_per_eu((kIsFp6<FA> && kIsFp6<FB>) ? 2 : 1))) void ge
 // gemm256_kernel: the large-shape path (K a multiple of 512, or of 128 per-tensor; any M, N, a partial last
 // tile row / column reading zeros past the matrix and storing only inside it).
 //
-// One workgroup of 4 waves owns a 256 x 256 output tile; each wave owns a
-// 128 x 128 quarter held as 4 x 4 MFMA accumulators (256 FP32 per lane, in
-// AGPRs).  K advances in stages of 64 code bytes per row (two K-blocks of FP8,
-// four of FP4, i.e. one or two 32 x 32 x 64 MFMA steps).  Stages go straight
-// from memory into LDS with gfx950's LDS-DMA loads (no register staging),
-// four deep: a stage's loads are issued three stages before it is consumed.
+// One workgroup of 8 waves (two per SIMD) owns a 256 x 256 output tile; each
+// wave owns a 128 x 64 eighth held as 4 x 2 MFMA accumulators (128 FP32 per
+// lane), which leaves each wave half of the SIMD's registers.  K advances in
+// stages of 64 code bytes per row (two K-blocks of FP8, four of FP4, i.e. one or
+// two 32 x 32 x 64 MFMA steps).  Stages go straight from memory into LDS with
+// gfx950's LDS-DMA loads (no register staging), four deep: a stage's loads are
+// issued three stages before it is consumed.  The LDS-DMA rate of a CU grows
+// with the number of waves issuing (measured on L2-resident data: about 84 GB/s
+// with 4 waves, 128 GB/s with 8), and the second wave of a SIMD keeps the matrix
+// unit busy while the first waits, which is why the tile is split 8 ways rather
+// than 4 (bit-identical results, 4-6% faster on every path).
 //
 // Every buffer the loop reads is its own __shared__ object, written only by
 // LDS-DMA, and the loop is unrolled so that each access names its object
@@ -386,18 +391,20 @@ namespace t256 {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTile = 256, kThreads = 256;
+constexpr int kTile = 256, kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 constexpr int kRow = 64;                      // code bytes per tile row per stage
 constexpr int kStages = 4;
 constexpr int kOpBytes = kTile * kRow;        // one operand of one stage: 16 KiB
 constexpr int kPairOp = 2 * kOpBytes;         // one operand of a stage pair: 32 KiB
 constexpr int kPairRow = 2 * kRow;            // K-contiguous row of a stage pair: one 128-byte line
-constexpr int kPairLoads = kPairOp / 1024 / 4;   // 1 KiB DMA instructions per wave per operand per pair
+constexpr int kPairLoads = kPairOp / 1024 / kWaves;   // 1 KiB DMA instructions per wave per operand per pair
 constexpr int kCodeGroup = kPairLoads;        // vector-memory instructions per wave per stage (both operands)
 constexpr int kKbPerScale = 16;               // K-blocks per scale stage
 constexpr int kMxK = 512;                     // K granule with MX scales: whole scale stages (16 K-blocks)
 constexpr int kPtK = 128;                     // K granule of the per-tensor mode: whole stage pairs
 constexpr int kMnPitch = kTile;               // M/N-contiguous stage: bytes per K-row
+constexpr int kEpBytes = 16384;               // a wave's epilogue staging area inside the stage buffers
 
 __shared__ __attribute__((aligned(1024))) uint8_t g_pair0[2 * kPairOp];   // stages 4n, 4n + 1: [A | B]
 __shared__ __attribute__((aligned(1024))) uint8_t g_pair1[2 * kPairOp];   // stages 4n + 2, 4n + 3
@@ -482,14 +489,16 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int&
 struct Ctx {
   __amdgpu_buffer_rsrc_t a, b;     // the tile's code rows (K-contiguous) or columns (M/N-contiguous) of A / B
   __amdgpu_buffer_rsrc_t sa, sb;   // the tile's 256 scale rows of A / B
+  __amdgpu_buffer_rsrc_t ss;       // this wave's scale operand (A for waves 0..3, B for 4..7)
   __amdgpu_buffer_rsrc_t z;        // empty range: loads return 0 and touch no memory (any base will do)
-  uint32_t off_a[4];               // lane's byte offset in the tile: K-contiguous, for DMA instructions of
-                                   // parity j % 2 ([0], [1]); M/N-contiguous, for instruction jj of a stage
-  uint32_t off_b[4];               // same for B
+  uint32_t off_a[2];               // lane's byte offset in the tile: K-contiguous, for DMA instructions of
+                                   // parity j % 2; M/N-contiguous, for instruction jj of a stage
+  uint32_t off_b[2];               // same for B
   uint32_t js_a, js_b;             // K-contiguous: bytes between the rows of DMA instructions j and j + 1
   uint32_t step_a, step_b;         // bytes between consecutive stages (M/N-contiguous operands)
   uint32_t sc_off;                 // lane's byte offset of its scale row (row 64 wave + lane)
   uint32_t sc_step_a, sc_step_b;   // bytes between consecutive scale stages of a row
+  uint32_t sc_step;                // the same for this wave's scale operand
   int rd_a, rd_b;                  // lane's read base inside a stage object (row-tile 0)
   int c0, c1;                      // lane's swizzled chunk offsets: chunk h and chunk h + 2
   int tp_a, tp_b;                  // M/N-contiguous: lane's swizzled chunk byte offset (row-tile 0)
@@ -498,9 +507,9 @@ struct Ctx {
 };
 
 // Stage pair (t, t + 1) (t even) into stage buffers SA_, SB_ (= SA_ + 1): for each
-// operand 8 instructions per wave, each 1 KiB.  K-contiguous: 8 rows x one 128-byte
+// operand 4 instructions per wave, each 1 KiB.  K-contiguous: 8 rows x one 128-byte
 // line holding both stages.  M/N-contiguous: 4 K-rows x 256 bytes, instructions
-// 0..3 for stage t, 4..7 for stage t + 1.  A dead stage (past the end of K) issues
+// 0, 1 for stage t, 2, 3 for stage t + 1.  A dead stage (past the end of K) issues
 // the same loads on the empty resource (zeros, no memory traffic), which keeps the
 // vmcnt bookkeeping uniform and the loop free of branches.
 template <int SA_, int SB_, bool TA, bool TB>
@@ -509,29 +518,28 @@ __device__ __forceinline__ void issue_pair(const Ctx& c, int t, int wave, bool l
   uint8_t* dst = stage<SA_>();
 #pragma unroll
   for (int j = 0; j < kPairLoads; ++j) {
-    const int e = j / 4, jj = j % 4;   // M/N-contiguous: stage t + e, instruction jj of that stage
+    const int e = j / 2, jj = j % 2;   // M/N-contiguous: stage t + e, instruction jj of that stage
     const bool live = e == 0 ? live0 : live1;
     if constexpr (TA)
-      dma(live ? c.a : c.z, c.off_a[jj], uint32_t(t + e) * c.step_a,
-              dst + e * kOpBytes + (wave * 4 + jj) * 1024);
+      dma(live ? c.a : c.z, c.off_a[jj], uint32_t(t + e) * c.step_a, dst + e * kOpBytes + (wave * 2 + jj) * 1024);
     else
-      dma(live0 ? c.a : c.z, c.off_a[j & 1], uint32_t(t) * kRow + uint32_t(j) * c.js_a,
-              dst + (wave * kPairLoads + j) * 1024);
+      dma(live0 ? c.a : c.z, c.off_a[jj], uint32_t(t) * kRow + uint32_t(j) * c.js_a,
+          dst + (wave * kPairLoads + j) * 1024);
     if constexpr (TB)
       dma(live ? c.b : c.z, c.off_b[jj], uint32_t(t + e) * c.step_b,
-              dst + kPairOp + e * kOpBytes + (wave * 4 + jj) * 1024);
+          dst + kPairOp + e * kOpBytes + (wave * 2 + jj) * 1024);
     else
-      dma(live0 ? c.b : c.z, c.off_b[j & 1], uint32_t(t) * kRow + uint32_t(j) * c.js_b,
-              dst + kPairOp + (wave * kPairLoads + j) * 1024);
+      dma(live0 ? c.b : c.z, c.off_b[jj], uint32_t(t) * kRow + uint32_t(j) * c.js_b,
+          dst + kPairOp + (wave * kPairLoads + j) * 1024);
   }
 }
 
-// Scale stage u (K-blocks 16 u .. 16 u + 15) of rows 64 wave .. 64 wave + 63: two instructions per wave.
-constexpr int kScaleOps = 2;
+// Scale stage u (K-blocks 16 u .. 16 u + 15): one instruction per wave, waves 0..3
+// fetching rows 64 (wave % 4) .. + 63 of A, waves 4..7 the same rows of B.
+constexpr int kScaleOps = 1;
 template <int U>
 __device__ __forceinline__ void issue_scales(const Ctx& c, int u, int wave, bool live) {
-  dma(live ? c.sa : c.z, c.sc_off, uint32_t(u) * c.sc_step_a, &scales<U>()[0][64 * wave][0]);
-  dma(live ? c.sb : c.z, c.sc_off, uint32_t(u) * c.sc_step_b, &scales<U>()[1][64 * wave][0]);
+  dma(live ? c.ss : c.z, c.sc_off, uint32_t(u) * c.sc_step, &scales<U>()[wave >> 2][64 * (wave & 3)][0]);
 }
 
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -565,8 +573,8 @@ __device__ __forceinline__ v8i km_operand(const Ctx& c, const uint8_t* p) {
 
 // Operands of MFMA step kk of stage t (stage buffer SI, scale buffer U).
 template <bool FP4, int SI, int U, int KK, bool PT, bool TA, bool TB>
-__device__ __forceinline__ void read_step(const Ctx& c, int t, int lane, v8i (&a)[4], v8i (&b)[4], int (&sa)[4],
-                                          int (&sb)[4]) {
+__device__ __forceinline__ void read_step(const Ctx& c, int t, int lane, v8i (&a)[4], v8i (&b)[2], int (&sa)[4],
+                                          int (&sb)[2]) {
   using G = Geo<FP4>;
   constexpr int kHalf = SI % 2;   // stage SI is this half of its pair
   const uint8_t* base = stage<SI>();
@@ -574,18 +582,20 @@ __device__ __forceinline__ void read_step(const Ctx& c, int t, int lane, v8i (&a
   for (int i = 0; i < 4; ++i) {
     if constexpr (TA) a[i] = mn_operand(base + kHalf * kOpBytes + c.rd_a + (c.tp_a ^ (32 * i)));
     else a[i] = km_operand<FP4, KK, kHalf>(c, base + c.rd_a + i * 32 * kPairRow);
-    if constexpr (TB) b[i] = mn_operand(base + kHalf * kOpBytes + c.rd_b + (c.tp_b ^ (32 * i)));
-    else b[i] = km_operand<FP4, KK, kHalf>(c, base + c.rd_b + i * 32 * kPairRow);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if constexpr (TB) b[j] = mn_operand(base + kHalf * kOpBytes + c.rd_b + (c.tp_b ^ (32 * j)));
+    else b[j] = km_operand<FP4, KK, kHalf>(c, base + c.rd_b + j * 32 * kPairRow);
   }
   if constexpr (!PT) {
     // the word holding the lane's K-block (t * kKb) % 16 + 2 kk + h; the byte is
     // picked by the consumer (scale_byte), after the read has surely landed
     const int word = ((t * G::kKb) % kKbPerScale + 2 * KK) >> 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sa[i] = scales<U>()[0][c.sc_row_a + 32 * i][word];
-      sb[i] = scales<U>()[1][c.sc_row_b + 32 * i][word];
-    }
+    for (int i = 0; i < 4; ++i) sa[i] = scales<U>()[0][c.sc_row_a + 32 * i][word];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sb[j] = scales<U>()[1][c.sc_row_b + 32 * j][word];
   }
 }
 
@@ -596,19 +606,19 @@ __device__ __forceinline__ int scale_byte(uint32_t word, int t, int h8) {
 }
 
 template <int FA, int FB, int KK, bool PT>
-__device__ __forceinline__ void mfma_all(v16f (&acc)[4][4], const v8i (&a)[4], const v8i (&b)[4], const int (&swa)[4],
-                                         const int (&swb)[4], int t, int h8) {
+__device__ __forceinline__ void mfma_all(v16f (&acc)[4][2], const v8i (&a)[4], const v8i (&b)[2], const int (&swa)[4],
+                                         const int (&swb)[2], int t, int h8) {
   constexpr bool kFp4 = FA == E2M1;
-  int sa[4], sb[4];
+  int sa[4], sb[2];
+  // per-tensor: every block scale is 2^0
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sa[i] = PT ? 127 : scale_byte<kFp4, KK>(swa[i], t, h8);   // per-tensor: every block scale is 2^0
-    sb[i] = PT ? 127 : scale_byte<kFp4, KK>(swb[i], t, h8);
-  }
+  for (int i = 0; i < 4; ++i) sa[i] = PT ? 127 : scale_byte<kFp4, KK>(swa[i], t, h8);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sb[j] = PT ? 127 : scale_byte<kFp4, KK>(swb[j], t, h8);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], MfmaFmt<FB>::kCode,
                                                                    MfmaFmt<FA>::kCode, 0, sb[j], 0, sa[i]);
 }
@@ -616,14 +626,14 @@ __device__ __forceinline__ void mfma_all(v16f (&acc)[4][4], const v8i (&a)[4], c
 // Scheduling masks of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
 
-// Interleave one MFMA step (16 MFMAs) with the memory instructions issued in
+// Interleave one MFMA step (8 MFMAs) with the memory instructions issued in
 // the same region -- VM LDS-DMA loads and DS operand reads for the next step --
 // so the LDS reads run in the shadow of the matrix unit instead of after it.
 template <int VM, int DS, int K>
 __device__ __forceinline__ void interleave_slot() {
   __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-  if constexpr (K < 8 && VM > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (VM + 7) / 8, 0);
-  constexpr int kDs = K < 14 ? DS * (K + 1) / 14 - DS * K / 14 : 0;   // all DS reads within the first 14 MFMAs
+  if constexpr (K < 4 && VM > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (VM + 3) / 4, 0);
+  constexpr int kDs = K < 7 ? DS * (K + 1) / 7 - DS * K / 7 : 0;   // all DS reads within the first 7 MFMAs
   if constexpr (kDs > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kDs, 0);
 }
 
@@ -634,13 +644,13 @@ __device__ __forceinline__ void interleave_slots(std::integer_sequence<int, K...
 
 template <int VM, int DS>
 __device__ __forceinline__ void interleave() {
-  static_assert(VM <= 25 && DS <= 32, "one step's worth");
-  interleave_slots<VM, DS>(std::make_integer_sequence<int, 16>{});
+  static_assert(VM <= 12 && DS <= 24, "one step's worth");
+  interleave_slots<VM, DS>(std::make_integer_sequence<int, 8>{});
 }
 
 struct Regs {
-  v8i a[2][4], b[2][4];
-  int sa[2][4], sb[2][4];
+  v8i a[2][4], b[2][2];
+  int sa[2][4], sb[2][2];
 };
 
 // Stage t = t0 + P (P static inside the unrolled body).  The operands of its
@@ -669,16 +679,17 @@ constexpr int later_ops() {
     return (pair_has_scales<FP4>(P - 3) ? kSO : 0) + 2 * kCodeGroup + (pair_has_scales<FP4>(P - 1) ? kSO : 0);
 }
 
-// LDS reads of one operand step: MX FP8 keeps its measured hint; per-tensor counts
-// 8 ds_read_b128 per K-contiguous operand and 16 transpose reads per M/N-contiguous one
+// LDS reads of one operand step: A's 4 row tiles and B's 2 (FP8 two ds_read_b128
+// per tile K-contiguous, four transpose reads M/N-contiguous; FP4 one
+// ds_read_b128), plus one scale word per tile in MX mode
 template <bool FP4, bool PT, bool TA, bool TB>
 constexpr int kDsReads() {
-  return PT ? (TA ? 16 : 8) + (TB ? 16 : 8) : FP4 ? 12 : 20;
+  return PT ? (TA ? 16 : 8) + (TB ? 8 : 4) : (FP4 ? 6 : 12) + 6;
 }
 
 template <int FA, int FB, int P, bool PT, bool TA, bool TB>
 __device__ __forceinline__ void stage_steps(const Ctx& c, int t, int T, int nsuper, int lane, int wave, Regs& r,
-                                            v16f (&acc)[4][4]) {
+                                            v16f (&acc)[4][2]) {
   constexpr bool kFp4 = FA == E2M1;
   using G = Geo<kFp4>;
   constexpr int SI = P % kStages;                          // this stage's buffer
@@ -722,29 +733,29 @@ __device__ __forceinline__ void stage_steps(const Ctx& c, int t, int T, int nsup
 
 template <int FA, int FB, bool PT, bool TA, bool TB, int... P>
 __device__ __forceinline__ void unrolled_body(const Ctx& c, int t0, int T, int nsuper, int lane, int wave, Regs& r,
-                                              v16f (&acc)[4][4], std::integer_sequence<int, P...>) {
+                                              v16f (&acc)[4][2], std::integer_sequence<int, P...>) {
   (stage_steps<FA, FB, P, PT, TA, TB>(c, t0 + P, T, nsuper, lane, wave, r, acc), ...);
 }
 
-// MX re-quantization of a wave's 128 x 128 quarter of C (row-wise blocks of 32
+// MX re-quantization of a wave's 128 x 64 eighth of C (row-wise blocks of 32
 // columns), one 32-row tile at a time: the wave stages the tile's FP32 values in
-// its LDS region ([32][132] floats; lane (rr, h) holds row rr, columns
-// 32 j + 8 q + 4 h + [0, 4)), then each lane encodes two whole blocks (four
-// consecutive lanes cover the four blocks of a row, so the code stores of a row
+// its LDS region ([32][68] floats; lane (rr, h) holds row rr, columns
+// 32 j + 8 q + 4 h + [0, 4)), then each lane encodes one whole block (two
+// consecutive lanes cover the two blocks of a row, so the code stores of a row
 // are contiguous).
-constexpr int kRqPitch = 132;   // floats per staged row (16-byte aligned, rows 4 banks apart)
+constexpr int kRqPitch = 68;   // floats per staged row (16-byte aligned, rows 4 banks apart)
 template <int FC, int RC>
-__device__ __forceinline__ void requant_quarter(const v16f (&acc)[4][4], float alpha, int lane, uint8_t* ep,
-                                                const GemmArgs& g, int64_t row0, int64_t col0, uint32_t& tmax) {
+__device__ __forceinline__ void requant_eighth(const v16f (&acc)[4][2], float alpha, int lane, uint8_t* ep,
+                                               const GemmArgs& g, int64_t row0, int64_t col0, uint32_t& tmax) {
   constexpr int kBits = Fmt_<FC>::kBits;
   const int rr = lane & 31, h = lane >> 5;
   const int64_t nb = g.N / 32, qpitch = g.N * kBits / 8;
   float* t = reinterpret_cast<float*>(ep);
   // the register tile is picked statically (accumulators cannot be indexed at run
   // time); the encoding below is shared by the four tiles
-  auto stage_tile = [&](const v16f (&ai)[4]) {
+  auto stage_tile = [&](const v16f (&ai)[2]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<float4*>(t + rr * kRqPitch + 32 * j + 8 * q + 4 * h) =
@@ -758,9 +769,8 @@ __device__ __forceinline__ void requant_quarter(const v16f (&acc)[4][4], float a
     else if (i == 2) stage_tile(acc[2]);
     else stage_tile(acc[3]);
     wave_lds_fence();
-#pragma unroll 1
-    for (int k = 0; k < 2; ++k) {
-      const int b = lane + 64 * k, row = b >> 2, blk = b & 3;
+    {
+      const int row = lane >> 1, blk = lane & 1;
       float v[32];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
@@ -788,7 +798,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   using G = Geo<kFp4>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;   // wave's 128 rows x 64 columns of the tile
   int tm, tn;
   map_tile(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int K = int(g.K);
@@ -832,13 +842,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // K-contiguous: instruction j of a wave covers rows 64 wave + 8 j + [0, 8), one 128-byte
+  for (int j = 0; j < 2; ++j) {
+    // K-contiguous: instruction j of a wave covers rows 32 wave + 8 j + [0, 8), one 128-byte
     // line each; swz of those rows depends on j only through j % 2 (the 8 j term moves it by 4 j)
-    const int row = 64 * wave + 8 * (j & 1) + (lane >> 3);
-    const uint32_t km = uint32_t(64 * wave + (lane >> 3)) * uint32_t(kbytes) + 16u * uint32_t((lane & 7) ^ swz(row));
-    // M/N-contiguous: instruction jj of a stage covers K-rows 16 wave + 4 jj + [0, 4), 256 bytes each
-    const int kr = 16 * wave + 4 * j + (lane >> 4);
+    const int row = 32 * wave + 8 * j + (lane >> 3);
+    const uint32_t km = uint32_t(32 * wave + (lane >> 3)) * uint32_t(kbytes) + 16u * uint32_t((lane & 7) ^ swz(row));
+    // M/N-contiguous: instruction j of a stage covers K-rows 8 wave + 4 j + [0, 4), 256 bytes each
+    const int kr = 8 * wave + 4 * j + (lane >> 4);
     const uint32_t mn_chunk = 16u * uint32_t((lane & 15) ^ (2 * (kr & 7)));
     c.off_a[j] = TA ? uint32_t(kr) * uint32_t(lda) + mn_chunk : km;
     c.off_b[j] = TB ? uint32_t(kr) * uint32_t(ldb) + mn_chunk : km;
@@ -847,7 +857,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   c.js_b = uint32_t(8 * kbytes);
   c.step_a = uint32_t(kRow) * uint32_t(TA ? lda : 1);
   c.step_b = uint32_t(kRow) * uint32_t(TB ? ldb : 1);
-  c.sc_off = uint32_t(64 * wave + lane) * uint32_t(g.gemm_scales ? 16 : kblocks);
+  c.sc_off = uint32_t(64 * (wave & 3) + lane) * uint32_t(g.gemm_scales ? 16 : kblocks);
+  if constexpr (!PT) {
+    c.ss = wave < 4 ? c.sa : c.sb;
+    c.sc_step = wave < 4 ? c.sc_step_a : c.sc_step_b;
+  }
   const int rr = lane & 31, h = lane >> 5;
   // K-contiguous: rows 32 i + rr of a wave's half share swz(rr): 32 i only changes higher row bits;
   // chunk h (stage half 0) at h ^ swz, chunk h + 2 at that ^ 2
@@ -855,20 +869,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   // 16 h + j / 2 (+ 8, 32, 40), byte 8 (j % 2) of the group's 16-column chunk
   const int tr_base = (16 * h + ((lane & 15) >> 1)) * kMnPitch + 8 * (lane & 1);
   c.rd_a = TA ? tr_base : (wm * 128 + rr) * kPairRow;
-  c.rd_b = kPairOp + (TB ? tr_base : (wn * 128 + rr) * kPairRow);
+  c.rd_b = kPairOp + (TB ? tr_base : (wn * 64 + rr) * kPairRow);
   c.tp_a = 16 * ((8 * wm) ^ (lane & 14) ^ ((lane >> 4) & 1));
-  c.tp_b = 16 * ((8 * wn) ^ (lane & 14) ^ ((lane >> 4) & 1));
+  c.tp_b = 16 * ((4 * wn) ^ (lane & 14) ^ ((lane >> 4) & 1));
   c.c0 = 16 * (h ^ swz(rr));
   c.c1 = c.c0 ^ 32;
   c.sc_row_a = wm * 128 + rr;
-  c.sc_row_b = wn * 128 + rr;
+  c.sc_row_b = wn * 64 + rr;
   c.h8 = 8 * h;
 
-  v16f acc[4][4];
+  v16f acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   Regs r;
@@ -902,18 +916,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   const float alpha = PT ? *g.alpha_ptr : g.alpha;
   const int64_t ldc = g.ldc;
   const int64_t row0 = int64_t(tm) * kTile + wm * 128;
-  const int64_t col0 = int64_t(tn) * kTile + wn * 128;
+  const int64_t col0 = int64_t(tn) * kTile + wn * 64;
   if constexpr (RQ) {
     barrier();   // every wave is done with the stage buffers
-    uint8_t* ep = (wave < 2 ? stage<0>() : stage<2>()) + (wave & 1) * kPairOp;
+    uint8_t* ep = (wave < 4 ? stage<0>() : stage<2>()) + (wave & 3) * kEpBytes;
     uint32_t tmax = 0;
     const int sel = g.fc * 2 + g.rc;
-    if (sel == E4M3 * 2 + FLOOR) requant_quarter<E4M3, FLOOR>(acc, alpha, lane, ep, g, row0, col0, tmax);
-    else if (sel == E4M3 * 2 + CEIL) requant_quarter<E4M3, CEIL>(acc, alpha, lane, ep, g, row0, col0, tmax);
-    else if (sel == E5M2 * 2 + FLOOR) requant_quarter<E5M2, FLOOR>(acc, alpha, lane, ep, g, row0, col0, tmax);
-    else if (sel == E5M2 * 2 + CEIL) requant_quarter<E5M2, CEIL>(acc, alpha, lane, ep, g, row0, col0, tmax);
-    else if (sel == E2M1 * 2 + FLOOR) requant_quarter<E2M1, FLOOR>(acc, alpha, lane, ep, g, row0, col0, tmax);
-    else requant_quarter<E2M1, CEIL>(acc, alpha, lane, ep, g, row0, col0, tmax);
+    if (sel == E4M3 * 2 + FLOOR) requant_eighth<E4M3, FLOOR>(acc, alpha, lane, ep, g, row0, col0, tmax);
+    else if (sel == E4M3 * 2 + CEIL) requant_eighth<E4M3, CEIL>(acc, alpha, lane, ep, g, row0, col0, tmax);
+    else if (sel == E5M2 * 2 + FLOOR) requant_eighth<E5M2, FLOOR>(acc, alpha, lane, ep, g, row0, col0, tmax);
+    else if (sel == E5M2 * 2 + CEIL) requant_eighth<E5M2, CEIL>(acc, alpha, lane, ep, g, row0, col0, tmax);
+    else if (sel == E2M1 * 2 + FLOOR) requant_eighth<E2M1, FLOOR>(acc, alpha, lane, ep, g, row0, col0, tmax);
+    else requant_eighth<E2M1, CEIL>(acc, alpha, lane, ep, g, row0, col0, tmax);
     if (g.amax) {
       const uint32_t m = wave_max(tmax);
       if (lane == 0 && m) atomic_max_u32(g.amax, m);
@@ -923,9 +937,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   if constexpr (BF16OUT) {
     uint16_t* C = static_cast<uint16_t*>(g.c) + int64_t(blockIdx.y) * g.batch_c;
     // per-tensor bias of the lane's 64 columns, added to alpha * acc with one rounding
-    float bias[4][4][4];
+    float bias[2][4][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint2 bw = make_uint2(0, 0);
@@ -937,15 +951,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
         bias[j][q][3] = __uint_as_float(bw.y & 0xFFFF0000u);
       }
     const bool has_bias = PT && g.bias;
-    // BF16: each wave stages its 128 x 128 quarter in a 32 KiB stage buffer (row
-    // pitch 256 B, 16-byte unit u of row r at u ^ (r % 16)), then writes whole
-    // 256-byte row segments: 16 lanes per row, 16 bytes per lane.
+    // BF16: each wave stages its 128 x 64 eighth in 16 KiB of the stage buffers (row
+    // pitch 128 B, 16-byte unit u of row r at u ^ (r % 8)), then writes whole
+    // 128-byte row segments: 8 lanes per row, 16 bytes per lane.
     barrier();   // every wave is done with the stage buffers
-    uint8_t* ep = (wave < 2 ? stage<0>() : stage<2>()) + (wave & 1) * kPairOp;
+    uint8_t* ep = (wave < 4 ? stage<0>() : stage<2>()) + (wave & 3) * kEpBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = 32 * i + rr, u = 4 * j + q;
@@ -955,15 +969,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
             o[e] = has_bias ? __builtin_fmaf(alpha, acc[i][j][4 * q + e], bias[j][q][e]) : alpha * acc[i][j][4 * q + e];
           const bf16x2 lo = __builtin_convertvector(f2{o[0], o[1]}, bf16x2);
           const bf16x2 hi = __builtin_convertvector(f2{o[2], o[3]}, bf16x2);
-          *reinterpret_cast<uint2*>(ep + row * 256 + 16 * (u ^ (row & 15)) + 8 * h) =
+          *reinterpret_cast<uint2*>(ep + row * 128 + 16 * (u ^ (row & 7)) + 8 * h) =
               make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
         }
     barrier();
-    const int u = lane & 15;
+    const int u = lane & 7;
 #pragma unroll 8
-    for (int it = 0; it < 32; ++it) {
-      const int row = 4 * it + (lane >> 4);
-      const uint4 v = *reinterpret_cast<const uint4*>(ep + row * 256 + 16 * (u ^ (row & 15)));
+    for (int it = 0; it < 16; ++it) {
+      const int row = 8 * it + (lane >> 3);
+      const uint4 v = *reinterpret_cast<const uint4*>(ep + row * 128 + 16 * (u ^ (row & 7)));
       if (row0 + row < g.M && col0 + 8 * u < g.N)   // N % 8 == 0: a piece is wholly in or out
         *reinterpret_cast<uint4*>(C + (row0 + row) * ldc + col0 + 8 * u) = v;
     }
@@ -972,7 +986,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t off = (row0 + 32 * i + rr) * ldc + col0 + 32 * j + 8 * q + 4 * h;

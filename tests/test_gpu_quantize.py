@@ -338,6 +338,78 @@ def test_delayed_scratch_shared_by_two_rings():
             assert_ring_state(rings[stream], tickets, orings[stream], f"{stream} step {t}")
 
 
+@pytest.mark.parametrize("tmode", ["scratch", "none"])
+def test_delayed_two_rings_on_two_streams(tmode):
+    """The activation ring on one stream and the gradient ring on another, launched
+    without any ordering between the streams, so the two streams' kernels may run
+    at the same time (each ring with its own ticket scratch, or none).  The ring is
+    copied on its own stream after each step; every copy, and every step's codes,
+    equal that ring's host fold."""
+    side = {s: torch.cuda.Stream() for s in ("act", "grad")}   # default priority
+    fmts = {"act": "e4m3", "grad": "e5m2"}
+    steps = 8
+    xb = {s: [workloads.delayed_step(s, t, rows=1024, cols=2048) for t in range(steps)] for s in fmts}
+    xs = {s: [upload_bf16_bits(b) for b in xb[s]] for s in fmts}
+    rings = {s: mxa.new_ring(16) for s in fmts}
+    tickets = {s: new_tickets(tmode) for s in fmts}
+    torch.cuda.synchronize()
+    out = {s: [] for s in fmts}
+    for t in range(steps):
+        for s, fmt in fmts.items():
+            with torch.cuda.stream(side[s]):
+                _, qT = mxa.fp8_quantize_delayed(xs[s][t], rings[s], t, fmt, "transposed",
+                                                 workloads.DELAYED_FP8_MAX[s], tickets=tickets[s])
+                out[s].append((qT, rings[s].clone()))
+    torch.cuda.synchronize()
+    for s, fmt in fmts.items():
+        oring = odl.Ring(16)
+        for t in range(steps):
+            _, wqT, _ = odl.quantize_delayed(workloads.bf16_to_f32(xb[s][t]), fmt, oring, t,
+                                             workloads.DELAYED_FP8_MAX[s], 1.0)
+            qT, ring_t = out[s][t]
+            assert_bytes_equal(host(qT), wqT, f"{s} step {t} qT")
+            assert_ring_state(ring_t, None, oring, f"{s} step {t}")
+        if tickets[s] is not None:
+            assert int(torch.count_nonzero(tickets[s])) == 0, f"{s}: ticket scratch not left zero"
+
+
+@pytest.mark.parametrize("tmode", ["scratch", "none"])
+def test_delayed_one_ring_across_streams(tmode):
+    """One ring whose steps alternate between two streams, each launch waiting on
+    an event recorded after the previous one: the event order is the ring's order,
+    and each step's codes and ring copy equal the host fold."""
+    side = [torch.cuda.Stream(), torch.cuda.Stream()]   # default priority
+    steps = 12
+    xb = [workloads.delayed_step("act", t, rows=768, cols=1536) for t in range(steps)]
+    xs = [upload_bf16_bits(b) for b in xb]
+    ring = mxa.new_ring(8)
+    tickets = new_tickets(tmode)
+    torch.cuda.synchronize()
+    done = None
+    out = []
+    for t in range(steps):
+        s = side[t % 2]
+        with torch.cuda.stream(s):
+            if done is not None:
+                s.wait_event(done)
+            q, qT, a = mxa.fp8_quantize_delayed(xs[t], ring, t % 8, "e4m3", "dual", amax=True, tickets=tickets)
+            out.append((q, qT, a, ring.clone()))
+            done = torch.cuda.Event()
+            done.record(s)
+    torch.cuda.synchronize()
+    oring = odl.Ring(8)
+    for t in range(steps):
+        wq, wqT, wa = odl.quantize_delayed(workloads.bf16_to_f32(xb[t]), "e4m3", oring, t % 8,
+                                           workloads.DELAYED_FP8_MAX["act"], 1.0)
+        q, qT, a, ring_t = out[t]
+        assert_bytes_equal(host(q), wq, f"step {t} q")
+        assert_bytes_equal(host(qT), wqT, f"step {t} qT")
+        assert host(a)[0] == wa
+        assert_ring_state(ring_t, None, oring, f"step {t}")
+    if tickets is not None:
+        assert int(torch.count_nonzero(tickets)) == 0, "ticket scratch not left zero"
+
+
 def test_delayed_resume_from_saved_ring():
     """The ring is the only state: copying it out at step 16 and resuming from the
     copy gives the same bytes as the uninterrupted run."""
