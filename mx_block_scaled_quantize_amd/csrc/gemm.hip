@@ -571,8 +571,11 @@ __device__ __forceinline__ v8i km_operand(const Ctx& c, const uint8_t* p) {
   }
 }
 
-// Operands of MFMA step kk of stage t (stage buffer SI, scale buffer U).
-template <bool FP4, int SI, int U, int KK, bool PT, bool TA, bool TB>
+// Operands of MFMA step kk of stage t (stage buffer SI, scale buffer U).  With
+// FRESH false the step's scale words are those of the step before (one word
+// holds 4 K-blocks: two FP8 stages, or both MFMA steps of an FP4 stage) and are
+// left to the caller to carry over.
+template <bool FP4, int SI, int U, int KK, bool PT, bool TA, bool TB, bool FRESH = true>
 __device__ __forceinline__ void read_step(const Ctx& c, int t, int lane, v8i (&a)[4], v8i (&b)[2], int (&sa)[4],
                                           int (&sb)[2]) {
   using G = Geo<FP4>;
@@ -588,7 +591,7 @@ __device__ __forceinline__ void read_step(const Ctx& c, int t, int lane, v8i (&a
     if constexpr (TB) b[j] = mn_operand(base + kHalf * kOpBytes + c.rd_b + (c.tp_b ^ (32 * j)));
     else b[j] = km_operand<FP4, KK, kHalf>(c, base + c.rd_b + j * 32 * kPairRow);
   }
-  if constexpr (!PT) {
+  if constexpr (!PT && FRESH) {
     // the word holding the lane's K-block (t * kKb) % 16 + 2 kk + h; the byte is
     // picked by the consumer (scale_byte), after the read has surely landed
     const int word = ((t * G::kKb) % kKbPerScale + 2 * KK) >> 2;
@@ -681,13 +684,23 @@ constexpr int later_ops() {
 
 // LDS reads of one operand step: A's 4 row tiles and B's 2 (FP8 two ds_read_b128
 // per tile K-contiguous, four transpose reads M/N-contiguous; FP4 one
-// ds_read_b128), plus one scale word per tile in MX mode
-template <bool FP4, bool PT, bool TA, bool TB>
+// ds_read_b128), plus one scale word per tile in MX mode when the words change
+template <bool FP4, bool PT, bool TA, bool TB, bool FRESH = true>
 constexpr int kDsReads() {
-  return PT ? (TA ? 16 : 8) + (TB ? 8 : 4) : (FP4 ? 6 : 12) + 6;
+  return PT ? (TA ? 16 : 8) + (TB ? 8 : 4) : (FP4 ? 6 : 12) + (FRESH ? 6 : 0);
 }
 
-template <int FA, int FB, int P, bool PT, bool TA, bool TB>
+// Scale words of the next step are those of the current one
+__device__ __forceinline__ void carry_scales(Regs& r, int from, int to) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.sa[to][i] = r.sa[from][i];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) r.sb[to][j] = r.sb[from][j];
+}
+
+// CARRY: FP8 stages reuse the scale words of the stage before when they hold the
+// same K-blocks (off where the re-quantizing epilogue leaves no registers for it)
+template <int FA, int FB, int P, bool PT, bool TA, bool TB, bool CARRY>
 __device__ __forceinline__ void stage_steps(const Ctx& c, int t, int T, int nsuper, int lane, int wave, Regs& r,
                                             v16f (&acc)[4][2]) {
   constexpr bool kFp4 = FA == E2M1;
@@ -701,9 +714,11 @@ __device__ __forceinline__ void stage_steps(const Ctx& c, int t, int T, int nsup
     const int cur = (P * G::kSub + kk) & 1, nxt = cur ^ 1;
     if (kk + 1 < G::kSub) {
       // next MFMA step is in this stage, already visible
-      read_step<kFp4, SI, U, 1, PT, TA, TB>(c, t, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
+      // (FP4) the stage's second step: same scale words as its first
+      read_step<kFp4, SI, U, 1, PT, TA, TB, false>(c, t, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
+      if constexpr (!PT) carry_scales(r, cur, nxt);
       mfma_all<FA, FB, 0, PT>(acc, r.a[cur], r.b[cur], r.sa[cur], r.sb[cur], t, c.h8);
-      interleave<0, 12>();
+      interleave<0, kDsReads<kFp4, PT, TA, TB, false>()>();
     } else {
       // Only a boundary into a new stage pair (odd P) synchronizes: stage t + 1 of an
       // even P arrived with stage t, in the same pair, and is visible since the
@@ -724,17 +739,20 @@ __device__ __forceinline__ void stage_steps(const Ctx& c, int t, int T, int nsup
       }
       // after the last stage this reads stale (in-bounds) LDS that no MFMA consumes; an
       // unconditional read keeps the operand registers free of merge copies
-      read_step<kFp4, SIn, Un, 0, PT, TA, TB>(c, t + 1, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
+      // FP8 stage t + 1 takes a new scale word only when it is even (P odd)
+      constexpr bool kFresh = kFp4 || P % 2 == 1 || !CARRY;
+      read_step<kFp4, SIn, Un, 0, PT, TA, TB, kFresh>(c, t + 1, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
+      if constexpr (!PT && !kFresh) carry_scales(r, cur, nxt);
       mfma_all<FA, FB, G::kSub - 1, PT>(acc, r.a[cur], r.b[cur], r.sa[cur], r.sb[cur], t, c.h8);
-      interleave<(kIssue ? 2 * kCodeGroup : 0) + (kScales ? kScaleOps : 0), kDsReads<kFp4, PT, TA, TB>()>();
+      interleave<(kIssue ? 2 * kCodeGroup : 0) + (kScales ? kScaleOps : 0), kDsReads<kFp4, PT, TA, TB, kFresh>()>();
     }
   }
 }
 
-template <int FA, int FB, bool PT, bool TA, bool TB, int... P>
+template <int FA, int FB, bool PT, bool TA, bool TB, bool CARRY, int... P>
 __device__ __forceinline__ void unrolled_body(const Ctx& c, int t0, int T, int nsuper, int lane, int wave, Regs& r,
                                               v16f (&acc)[4][2], std::integer_sequence<int, P...>) {
-  (stage_steps<FA, FB, P, PT, TA, TB>(c, t0 + P, T, nsuper, lane, wave, r, acc), ...);
+  (stage_steps<FA, FB, P, PT, TA, TB, CARRY>(c, t0 + P, T, nsuper, lane, wave, r, acc), ...);
 }
 
 // MX re-quantization of a wave's 128 x 64 eighth of C (row-wise blocks of 32
@@ -904,7 +922,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   read_step<kFp4, 0, 0, 0, PT, TA, TB>(c, 0, lane, r.a[0], r.b[0], r.sa[0], r.sb[0]);
 
   for (int t0 = 0; t0 < T; t0 += G::kUnroll)
-    unrolled_body<FA, FB, PT, TA, TB>(c, t0, T, nsuper, lane, wave, r, acc,
+    unrolled_body<FA, FB, PT, TA, TB, !RQ>(c, t0, T, nsuper, lane, wave, r, acc,
                                       std::make_integer_sequence<int, G::kUnroll>{});
 
   // the last groups (empty-range loads) still write LDS: drain them before the
