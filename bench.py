@@ -317,15 +317,25 @@ def time_calls(fn, n, warm, stream, torch):
     return e0.elapsed_time(e1) / n / 1e3
 
 
-def time_alternating(fns, n, rounds, stream, torch):
+def time_alternating(fns, n, rounds, stream, torch, warm=2):
     """Average launch durations of several variants measured in alternation
     (A B A B ...), so that a drift of the clock under load does not favour the
     variant measured first: {name: mean over the rounds of time_calls}."""
     acc = {k: 0.0 for k in fns}
     for r in range(rounds):
         for k, fn in fns.items():
-            acc[k] += time_calls(fn, n, 2 if r == 0 else 0, stream, torch)
+            acc[k] += time_calls(fn, n, warm if r == 0 else 0, stream, torch)
     return {k: v / rounds for k, v in acc.items()}
+
+
+# GEMM legs: the first launches of a burst run while the clock is still settling
+# (a trace shows their durations drifting by 20% over the first ten or so), so
+# each leg is warmed up with GEMM_WARM calls and timed over at least GEMM_CALLS.
+GEMM_WARM, GEMM_CALLS = 10, 20
+
+
+def gemm_calls(steps):
+    return max(steps, GEMM_CALLS)
 
 
 # Memory-bound legs rotate through enough buffer sets that one call's data is
@@ -442,7 +452,7 @@ def bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=1
         (qa, sa), (qw, sw) = ops[layout]
         return lambda: mxa.check(lib.mx_gemm(qa.data_ptr(), sa.data_ptr(), 0, qw.data_ptr(), sw.data_ptr(), 0,
                                              mxa.SCALE_LAYOUT[layout], M, N, K, 1.0, c.data_ptr(), 1, N, sp))
-    times = time_alternating({k: call(k) for k in ops}, max(2, steps // 2), 2, stream, torch)
+    times = time_alternating({k: call(k) for k in ops}, gemm_calls(steps), 2, stream, torch, warm=GEMM_WARM)
     del ops
     t = times["row"]
     tf = flops / t / 1e12
@@ -563,7 +573,8 @@ def bench_gemm_fp6(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=5
     qw, sw = mxa.mx_quantize(up_bf16(w_bits), "e2m3", "ceil", "row")
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     t = time_calls(lambda: mxa.check(lib.mx_gemm(qa.data_ptr(), sa.data_ptr(), 3, qw.data_ptr(), sw.data_ptr(), 3, 0, M, N,
-                                                 K, 1.0, c.data_ptr(), 1, N, sp)), steps, 1, stream, torch)
+                                                 K, 1.0, c.data_ptr(), 1, N, sp)), gemm_calls(steps), GEMM_WARM,
+                   stream, torch)
     f = 2.0 * M * N * K
     return {"mxfp6_e2m3_gemm_8192x14336x4096": {"us": round(t * 1e6, 2), "TFLOP/s": round(f / t / 1e12, 1),
                                                 "mfma_frac": round(f / t / 1e12 / FP6_PEAK_TFLOPS, 4)}}
@@ -582,7 +593,7 @@ def bench_gemm_requant(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, ste
     def call():
         mxa.check(lib.mx_gemm_requant(qa.data_ptr(), sa.data_ptr(), 0, qw.data_ptr(), sw.data_ptr(), 0, 0, M, N, K, 1.0,
                                       0, 1, qc.data_ptr(), sc.data_ptr(), None, sp))
-    t = time_calls(call, steps, 2, stream, torch)
+    t = time_calls(call, gemm_calls(steps), GEMM_WARM, stream, torch)
     tf = 2.0 * M * N * K / t / 1e12
     return {"mxfp8_gemm_requant_e4m3_8192x14336x4096": {"us": round(t * 1e6, 2), "TFLOP/s": round(tf, 1),
                                                         "mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4)}}
@@ -611,7 +622,7 @@ def bench_mm_fp8(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=10)
         def call():
             mxa.check(lib.mm_fp8(xq.data_ptr(), b.data_ptr(), 0, 1, M, N, K, 0, 0, 0, tb, scale.data_ptr(),
                                  bias.data_ptr(), c.data_ptr(), sp))
-        t = time_calls(call, steps, 2, stream, torch)
+        t = time_calls(call, gemm_calls(steps), GEMM_WARM, stream, torch)
         tf = flops / t / 1e12
         res[f"mm_fp8_e4m3_{name}_bias_8192x14336x4096"] = {"us": round(t * 1e6, 2), "TFLOP/s": round(tf, 1),
                                                             "mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4)}
@@ -627,7 +638,8 @@ def time_gemm_fp4_layouts(lib, sp, stream, dev, st_row, st_gemm, torch, steps):
         return lambda: lib.mx_gemm(st["gq"].data_ptr(), st["gs"].data_ptr(), 2, st["xq"].data_ptr(),
                                    st["xs"].data_ptr(), 2, layout, 4096, 4096, 8192, 1.0 / 32, dw.data_ptr(), 1, 4096,
                                    sp)
-    t = time_alternating({"row": call(st_row, 0), "gemm": call(st_gemm, 1)}, steps, 3, stream, torch)
+    t = time_alternating({"row": call(st_row, 0), "gemm": call(st_gemm, 1)}, gemm_calls(steps), 3, stream, torch,
+                         warm=GEMM_WARM)
     f = 2.0 * 4096 * 4096 * 8192
     leg = lambda x: {"us": round(x * 1e6, 2), "TFLOP/s": round(f / x / 1e12, 1),   # noqa: E731
                      "mfma_frac": round(f / x / 1e12 / FP4_PEAK_TFLOPS, 4)}
