@@ -258,6 +258,10 @@ static_assert(kTicketStride >= 2, "a group needs a max and a ticket word");
 // Grid cap of the per-tensor kernels when the caller passes no ticket scratch:
 // every workgroup then takes its ticket on one word.
 constexpr int64_t kNullTicketGrid = 512;
+// Grid cap of the transposed per-tensor kernel with ticket scratch: about four
+// resident workgroups per CU, each taking two or more tiles and one ticket
+// (measured 3.6% faster than one workgroup per tile on a BF16 8192 x 4096 input).
+constexpr int64_t kTicketGrid = 1024;
 
 struct RingTicket {
   uint32_t* gmax;
@@ -737,7 +741,8 @@ __device__ __forceinline__ uint32_t bf16_chunk_absmax(const uint4& c) {
 // blocks inline; every other block (non-finite, round-down rule, e = -127) goes
 // through an out-of-line general encoder, which keeps the register count of the
 // common path at 4 waves per SIMD.  (Waves that take the general encoder are
-// slow: it is kept for non-finite blocks and blocks with a subnormal amax.)
+// slow: it is kept for non-finite blocks and blocks with a subnormal amax.)  The
+// launch holds two workgroups per CU, each walking its share of the tiles.
 constexpr int kDualTile = 128, kDualWave = 64;
 
 // General MX encoding of 8 BF16 values of one block (element order, pairs
@@ -814,7 +819,7 @@ __device__ __forceinline__ uint2 dual_encode8(const uint32_t (&p)[4], uint32_t b
 }
 
 template <int F, int R, bool AMAX>
-__global__ __launch_bounds__(256) void dual_bf16_kernel(StripArgs a, int tiles_c) {
+__global__ __launch_bounds__(256) void dual_bf16_kernel(StripArgs a, int tiles_c, int ntiles) {
   constexpr int kB = Fmt_<F>::kBits;
   constexpr int kLine = kDualTile * kB / 8;                          // code bytes per tile row / column
   __shared__ __attribute__((aligned(16))) uint8_t qr_lds[kDualTile * kLine];   // [tile row][tile column]
@@ -825,105 +830,110 @@ __global__ __launch_bounds__(256) void dual_bf16_kernel(StripArgs a, int tiles_c
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // lane bits 0-1 and 4 give g, bits 2-3 and 5 give h
   const int g = (lane & 3) | ((lane >> 2) & 4), h = ((lane >> 2) & 3) | ((lane >> 3) & 4), lane_q = lane & 3;
-  const int t = blockIdx.x;
-  const int64_t tr = int64_t(t / tiles_c) * kDualTile, tc = int64_t(t % tiles_c) * kDualTile;
   const int wro = (wave >> 1) * kDualWave, wco = (wave & 1) * kDualWave;
   uint8_t* const srl = reinterpret_cast<uint8_t*>(srow_lds) + wro * 4 + (wave & 1) * 2;
   uint8_t* const scl = reinterpret_cast<uint8_t*>(scol_lds) + wco * 4 + (wave >> 1) * 2;
-  // rows and cols are multiples of 32: a quad (row blocks) and the lanes
-  // h = 4k .. 4k+3 (column blocks) are entirely in or out of range
-  const bool ok = tr + wro + 8 * h < a.rows && tc + wco + 8 * g < a.cols;
   uint32_t tmax = 0;
-  if (ok) {
-    // the wave's origin is uniform: a scalar base plus a 32-bit lane offset
-    // (the host keeps 64 * cols * 2 below 2^32)
-    const uint8_t* xb = static_cast<const uint8_t*>(a.x) + ((tr + wro) * a.cols + tc + wco) * 2;
-    const uint32_t cols = uint32_t(a.cols);
-    uint4 raw[8];
+  // one tile per workgroup, or several when the launch caps the grid
+  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t tr = int64_t(t / tiles_c) * kDualTile, tc = int64_t(t % tiles_c) * kDualTile;
+    // rows and cols are multiples of 32: a quad (row blocks) and the lanes
+    // h = 4k .. 4k+3 (column blocks) are entirely in or out of range
+    const bool ok = tr + wro + 8 * h < a.rows && tc + wco + 8 * g < a.cols;
+    if (ok) {
+      // the wave's origin is uniform: a scalar base plus a 32-bit lane offset
+      // (the host keeps 64 * cols * 2 below 2^32)
+      const uint8_t* xb = static_cast<const uint8_t*>(a.x) + ((tr + wro) * a.cols + tc + wco) * 2;
+      const uint32_t cols = uint32_t(a.cols);
+      uint4 raw[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32x4_t v = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4_t*>(xb + (uint32_t(8 * h + i) * cols + uint32_t(8 * g)) * 2u));
-      raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
-    // ---- row-wise half
+      for (int i = 0; i < 8; ++i) {
+        const u32x4_t v = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(xb + (uint32_t(8 * h + i) * cols + uint32_t(8 * g)) * 2u));
+        raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+      // ---- row-wise half
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t m = bf16_chunk_absmax(raw[i]);
-      if constexpr (AMAX) tmax = umax(tmax, m <= 0x7F800000u ? m : dual_amax_nan_chunk(raw[i]));
-      const uint32_t p[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-      uint32_t sc;
-      const uint2 w = dual_encode8<F, R>(p, quad_max(m), sc);
-      if (lane_q == 0) srl[(8 * h + i) * 4 + (g >> 2)] = uint8_t(sc);
-      uint8_t* const d = qr_lds + (wro + 8 * h + i) * kLine + (wco + 8 * g) * kB / 8;
-      if constexpr (kB == 8) *reinterpret_cast<u32x2_t*>(d) = u32x2_t{w.x, w.y};
-      else *reinterpret_cast<uint32_t*>(d) = w.x;
-    }
-    // ---- column-wise half: dword d holds columns 2d (low halves) and 2d+1
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      uint32_t mp = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mp = pk_umax16(mp, u4_word(raw[i], d) & 0x7FFF7FFFu);
-      mp = pk_umax16(mp, dpp_u32<kRowRor4>(mp));
-      mp = pk_umax16(mp, dpp_u32<kRowRor8>(mp));
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const uint32_t sel = k ? 0x07060302u : 0x05040100u;
-        uint32_t p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_perm(u4_word(raw[2 * i + 1], d), u4_word(raw[2 * i], d), sel);
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t m = bf16_chunk_absmax(raw[i]);
+        if constexpr (AMAX) tmax = umax(tmax, m <= 0x7F800000u ? m : dual_amax_nan_chunk(raw[i]));
+        const uint32_t p[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
         uint32_t sc;
-        const uint2 w = dual_encode8<F, R>(p, k ? (mp & 0xFFFF0000u) : (mp << 16), sc);
-        const int c = 8 * g + 2 * d + k;                     // column within the wave quarter
-        uint8_t* const dst = qc_lds + (wco + c) * kLine + (wro + 8 * h) * kB / 8;
-        if constexpr (kB == 8) *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{w.x, w.y};
-        else *reinterpret_cast<uint32_t*>(dst) = w.x;
-        if ((h & 3) == 0) scl[c * 4 + (h >> 2)] = uint8_t(sc);
+        const uint2 w = dual_encode8<F, R>(p, quad_max(m), sc);
+        if (lane_q == 0) srl[(8 * h + i) * 4 + (g >> 2)] = uint8_t(sc);
+        uint8_t* const d = qr_lds + (wro + 8 * h + i) * kLine + (wco + 8 * g) * kB / 8;
+        if constexpr (kB == 8) *reinterpret_cast<u32x2_t*>(d) = u32x2_t{w.x, w.y};
+        else *reinterpret_cast<uint32_t*>(d) = w.x;
+      }
+      // ---- column-wise half: dword d holds columns 2d (low halves) and 2d+1
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t mp = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mp = pk_umax16(mp, u4_word(raw[i], d) & 0x7FFF7FFFu);
+        mp = pk_umax16(mp, dpp_u32<kRowRor4>(mp));
+        mp = pk_umax16(mp, dpp_u32<kRowRor8>(mp));
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const uint32_t sel = k ? 0x07060302u : 0x05040100u;
+          uint32_t p[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            p[i] = __builtin_amdgcn_perm(u4_word(raw[2 * i + 1], d), u4_word(raw[2 * i], d), sel);
+          uint32_t sc;
+          const uint2 w = dual_encode8<F, R>(p, k ? (mp & 0xFFFF0000u) : (mp << 16), sc);
+          const int c = 8 * g + 2 * d + k;                     // column within the wave quarter
+          uint8_t* const dst = qc_lds + (wco + c) * kLine + (wro + 8 * h) * kB / 8;
+          if constexpr (kB == 8) *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{w.x, w.y};
+          else *reinterpret_cast<uint32_t*>(dst) = w.x;
+          if ((h & 3) == 0) scl[c * 4 + (h >> 2)] = uint8_t(sc);
+        }
       }
     }
+    __syncthreads();
+    // ---- codes: 16-byte pieces, kLine / 16 consecutive threads per line; a piece
+    // (16 FP8 or 32 FP4 codes) is entirely in or out of range
+#pragma unroll
+    for (int it = 0; it < kDualTile * kLine / 16 / 256; ++it) {
+      const int item = threadIdx.x + 256 * it;
+      const int r = item / (kLine / 16), pc = item % (kLine / 16);
+      const int64_t e = pc * 16 * 8 / kB;                              // first element of the piece
+      if (tr + r < a.rows && tc + e < a.cols) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qr_lds + r * kLine + pc * 16);
+        __builtin_nontemporal_store(v,
+                                    reinterpret_cast<u32x4_t*>(a.q_row + ((tr + r) * a.cols + tc) * kB / 8 + pc * 16));
+      }
+      if (tc + r < a.cols && tr + e < a.rows) {
+        const uint4 v = *reinterpret_cast<const uint4*>(qc_lds + r * kLine + pc * 16);
+        *reinterpret_cast<uint4*>(a.q_col + ((tc + r) * a.rows + tr) * kB / 8 + pc * 16) = v;
+      }
+    }
+    // ---- scales: thread j < 128 writes tile row j's 4 row scales, thread 128 + j
+    // tile column j's 4 column scales (fewer, byte by byte, on a ragged edge)
+    {
+      const int j = threadIdx.x & (kDualTile - 1);
+      const bool col_side = threadIdx.x >= kDualTile;
+      const int64_t line = col_side ? tc + j : tr + j;
+      const int64_t lines = col_side ? a.cols : a.rows;
+      const int64_t other0 = col_side ? tr : tc, other = col_side ? a.rows : a.cols;
+      if (line < lines) {
+        const uint32_t v = col_side ? scol_lds[j] : srow_lds[j];
+        uint8_t* dst =
+            (col_side ? a.s_col : a.s_row) + scale_offset(line, other0 >> 5, lines, other >> 5, a.gemm_scales);
+        const int64_t nb = (other - other0) >> 5;
+        if (nb >= 4 && (reinterpret_cast<uintptr_t>(dst) & 3u) == 0) {
+          *reinterpret_cast<uint32_t*>(dst) = v;
+        } else {
+          for (int b = 0; b < 4 && b < nb; ++b) dst[b] = uint8_t(v >> (8 * b));
+        }
+      }
+    }
+    if (t + int(gridDim.x) < ntiles) __syncthreads();   // the staging buffers are reused by the next tile
   }
   if constexpr (AMAX) {
     const uint32_t wm = wave_max(tmax);
     if (lane == 0) red[wave] = wm;
-  }
-  __syncthreads();
-  // ---- codes: 16-byte pieces, kLine / 16 consecutive threads per line; a piece
-  // (16 FP8 or 32 FP4 codes) is entirely in or out of range
-#pragma unroll
-  for (int it = 0; it < kDualTile * kLine / 16 / 256; ++it) {
-    const int item = threadIdx.x + 256 * it;
-    const int r = item / (kLine / 16), pc = item % (kLine / 16);
-    const int64_t e = pc * 16 * 8 / kB;                              // first element of the piece
-    if (tr + r < a.rows && tc + e < a.cols) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qr_lds + r * kLine + pc * 16);
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(a.q_row + ((tr + r) * a.cols + tc) * kB / 8 + pc * 16));
-    }
-    if (tc + r < a.cols && tr + e < a.rows) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qc_lds + r * kLine + pc * 16);
-      *reinterpret_cast<uint4*>(a.q_col + ((tc + r) * a.rows + tr) * kB / 8 + pc * 16) = v;
-    }
-  }
-  // ---- scales: thread j < 128 writes tile row j's 4 row scales, thread 128 + j
-  // tile column j's 4 column scales (fewer, byte by byte, on a ragged edge)
-  {
-    const int j = threadIdx.x & (kDualTile - 1);
-    const bool col_side = threadIdx.x >= kDualTile;
-    const int64_t line = col_side ? tc + j : tr + j;
-    const int64_t lines = col_side ? a.cols : a.rows;
-    const int64_t other0 = col_side ? tr : tc, other = col_side ? a.rows : a.cols;
-    if (line < lines) {
-      const uint32_t v = col_side ? scol_lds[j] : srow_lds[j];
-      uint8_t* dst = (col_side ? a.s_col : a.s_row) + scale_offset(line, other0 >> 5, lines, other >> 5, a.gemm_scales);
-      const int64_t nb = (other - other0) >> 5;
-      if (nb >= 4 && (reinterpret_cast<uintptr_t>(dst) & 3u) == 0) {
-        *reinterpret_cast<uint32_t*>(dst) = v;
-      } else {
-        for (int b = 0; b < 4 && b < nb; ++b) dst[b] = uint8_t(v >> (8 * b));
-      }
-    }
-  }
-  if constexpr (AMAX) {
+    __syncthreads();
     if (threadIdx.x == 0) {
       const uint32_t mm = umax(umax(red[0], red[1]), umax(red[2], red[3]));
       if (mm) atomic_max_u32(a.amax_out, mm);
@@ -1135,7 +1145,7 @@ __global__ __launch_bounds__(256) void pt_col_bf16_kernel(StripArgs a, int tiles
   const RingTicket tk = ring_ticket(a.ring, blockIdx.x, gridDim.x);
   const int wro = (wave >> 1) * kPtWave, wco = (wave & 1) * kPtWave;       // wave offset in the tile
   uint32_t tmax = 0, posted = 0;
-  // one tile per workgroup, unless the launch caps the grid (no ticket scratch)
+  // one tile per workgroup, unless the launch caps the grid
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t tr = int64_t(t / tiles_c) * kPtTile, tc = int64_t(t % tiles_c) * kPtTile;
     // rows are a multiple of 32 and cols of 8: a lane's 8 x 8 block is in or out
@@ -1255,6 +1265,21 @@ static int64_t resident_workgroups(K kernel, int threads) {
   return n;
 }
 
+// CUs of the current device (cached per device; 0 if the query fails).
+static int64_t device_cus() {
+  static int64_t cache[64] = {};
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
 template <typename K>
 static mx_status_t launch_strips(K kernel, const StripArgs& a, hipStream_t st) {
   const int threads = 64 * kStripWaves;
@@ -1335,9 +1360,14 @@ template <int IN, int F, int R> struct DualOp {
       const int64_t tiles_c = (a.cols + kDualTile - 1) / kDualTile;
       const int64_t ntiles = tiles_c * ((a.rows + kDualTile - 1) / kDualTile);
       if (ntiles > 0 && ntiles < (int64_t(1) << 31) && a.cols < (int64_t(1) << 25)) {
-        const dim3 grid{unsigned(ntiles)}, block{256u};
-        return amax ? launch(dual_bf16_kernel<F, R, true>, grid, block, st, a, int(tiles_c))
-                    : launch(dual_bf16_kernel<F, R, false>, grid, block, st, a, int(tiles_c));
+        // two workgroups per CU, each walking several tiles: on a BF16 8192 x 4096 input
+        // (2048 tiles) 512 workgroups measured 3.8% faster than one per tile, while
+        // 256, 384 and 640 were slower (too few waves, or unequal tile counts)
+        const int64_t cus = device_cus();
+        const int64_t cap = cus > 0 ? 2 * cus : ntiles;
+        const dim3 grid{unsigned(ntiles < cap ? ntiles : cap)}, block{256u};
+        return amax ? launch(dual_bf16_kernel<F, R, true>, grid, block, st, a, int(tiles_c), int(ntiles))
+                    : launch(dual_bf16_kernel<F, R, false>, grid, block, st, a, int(tiles_c), int(ntiles));
       }
     }
     return strip_dispatch<IN, F, R, MX_DUAL>(a, false, amax, st);
@@ -1353,7 +1383,8 @@ template <int IN, int F, int R> struct PtOp {
         const int64_t tiles_c = (a.cols + kPtTile - 1) / kPtTile;
         const int64_t ntiles = tiles_c * ((a.rows + kPtTile - 1) / kPtTile);
         if (IN == IN_BF16 && ntiles > 0 && ntiles < (int64_t(1) << 31) && a.cols < (int64_t(1) << 25)) {
-          const int64_t g = a.ring.tickets || ntiles <= kNullTicketGrid ? ntiles : kNullTicketGrid;
+          const int64_t cap = a.ring.tickets ? kTicketGrid : kNullTicketGrid;
+          const int64_t g = ntiles <= cap ? ntiles : cap;
           return launch(pt_col_bf16_kernel<F>, dim3{unsigned(g)}, dim3{256u}, st, a, int(tiles_c), int(ntiles));
         }
         return strip_dispatch<IN, F, R, PT_COL>(a, false, false, st);
