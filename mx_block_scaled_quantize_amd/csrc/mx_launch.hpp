@@ -1,13 +1,31 @@
 // Host-side argument checks shared by the libmx entry points.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "../../include/mx.h"
 
 namespace mxk {
 
 inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// CUs of the current device (cached per device; 0 if the query fails).
+inline int64_t device_cus() {
+  static int64_t cache[64] = {};
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
 
 inline mx_status_t check_common_quant(mx_dtype_t in, int64_t rows, int64_t cols, int block, mx_elem_t fmt,
                                       mx_scale_rule_t rule) {

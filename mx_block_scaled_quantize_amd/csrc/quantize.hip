@@ -1265,21 +1265,6 @@ static int64_t resident_workgroups(K kernel, int threads) {
   return n;
 }
 
-// CUs of the current device (cached per device; 0 if the query fails).
-static int64_t device_cus() {
-  static int64_t cache[64] = {};
-  static std::mutex mu;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  std::lock_guard<std::mutex> lock(mu);
-  if (cache[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
-    cache[dev] = cus;
-  }
-  return cache[dev];
-}
-
 template <typename K>
 static mx_status_t launch_strips(K kernel, const StripArgs& a, hipStream_t st) {
   const int threads = 64 * kStripWaves;
