@@ -170,7 +170,11 @@ __device__ __forceinline__ uint32_t row_chunk_mx(const uint4 (&c)[ChunkWords<IN>
 // Row-wise MX quantization (flat): row-wise blocks are contiguous in memory
 // ---------------------------------------------------------------------------
 constexpr int kRowThreads = 256;
-constexpr int kRowUnroll = 4;
+// chunks per thread, loaded before any is encoded: two for the MX row-wise
+// kernel (BF16 8192 x 4096 to E4M3: 18.8 us against 19.7 with four), four for
+// the per-tensor row-wise cast (23.8 us against 24.4 with two)
+constexpr int kRowUnroll = 2;
+constexpr int kPtRowUnroll = 4;
 
 template <int IN, int F, int R, bool HAD, bool AMAX>
 __global__ __launch_bounds__(kRowThreads) void rowwise_kernel(const void* __restrict__ x, int64_t nchunks,
@@ -374,21 +378,21 @@ __global__ __launch_bounds__(kPtRowThreads) void pt_row_kernel(const void* __res
   const float mult = ring_multiplier(r, slow);
   uint32_t tmax = 0;
   const RingTicket tk = ring_ticket(r, blockIdx.x, gridDim.x);
-  // one block of kPtRowThreads * kRowUnroll chunks per iteration; the grid covers
+  // one block of kPtRowThreads * kPtRowUnroll chunks per iteration; the grid covers
   // the input in one pass unless the launch caps it (no ticket scratch)
-  for (int64_t b = int64_t(blockIdx.x) * kPtRowThreads * kRowUnroll; b < nchunks;
-       b += int64_t(gridDim.x) * kPtRowThreads * kRowUnroll) {
-    uint4 raw[kRowUnroll][kW];
+  for (int64_t b = int64_t(blockIdx.x) * kPtRowThreads * kPtRowUnroll; b < nchunks;
+       b += int64_t(gridDim.x) * kPtRowThreads * kPtRowUnroll) {
+    uint4 raw[kPtRowUnroll][kW];
 #pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u) {
+    for (int u = 0; u < kPtRowUnroll; ++u) {
       const int64_t c = b + u * kPtRowThreads + threadIdx.x;
 #pragma unroll
       for (int k = 0; k < kW; ++k) raw[u][k] = make_uint4(0, 0, 0, 0);
       if (c < nchunks) load_chunk_nt<IN>(x, c * 8, raw[u]);
     }
-    uint32_t w[kRowUnroll][Words<F, 8>::kN];
+    uint32_t w[kPtRowUnroll][Words<F, 8>::kN];
 #pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u) {
+    for (int u = 0; u < kPtRowUnroll; ++u) {
       float v[8];
       widen_chunk<IN>(raw[u], v);
       const uint32_t m = chunk_absmax<IN>(raw[u], v);
@@ -396,7 +400,7 @@ __global__ __launch_bounds__(kPtRowThreads) void pt_row_kernel(const void* __res
       pt_encode_f32<F, 8>(v, mult, slow ? 0x7FFFFFFFu : m, w[u]);
     }
 #pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u) {
+    for (int u = 0; u < kPtRowUnroll; ++u) {
       const int64_t c = b + u * kPtRowThreads + threadIdx.x;
       if (c < nchunks) store_row8<F>(q, c * 8, w[u]);
     }
@@ -1294,7 +1298,7 @@ static mx_status_t strip_dispatch(StripArgs& a, bool had, bool amax, hipStream_t
 template <int IN, int F>
 static mx_status_t pt_row_dispatch(const void* x, int64_t n, uint8_t* q, const RingArgs& r, hipStream_t st) {
   const int64_t nchunks = n / 8;
-  const int64_t per = int64_t(kPtRowThreads) * kRowUnroll;
+  const int64_t per = int64_t(kPtRowThreads) * kPtRowUnroll;
   int64_t g = (nchunks + per - 1) / per;
   if (!r.tickets && g > kNullTicketGrid / 2) g = kNullTicketGrid / 2;   // 1024-thread workgroups
   if (g == 0) g = 1;   // an empty input still folds

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void rowwise_kernel(const void* __restric
 typedef __bf16 v32bf_t __attribute__((ext_vector_type(32)));
 typedef unsigned int v16u_t __attribute__((ext_vector_type(16)));
 typedef unsigned int v6u_t __attribute__((ext_vector_type(6)));
-constexpr int kUnrollB = 2;
+constexpr int kUnrollB = 1;   // blocks per thread (BF16 8192 x 4096: 18.4 us against 18.65 with two)
 
 template <int F, int R, bool AMAX>
 __global__ __launch_bounds__(kThreads) void rowwise_bf16_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
