@@ -566,7 +566,7 @@ def bench_wgrad_quant(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, 
 
 def bench_gemm_fp6(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, steps=5):
     """The 8192 x 14336 x 4096 MLP GEMM shape with both operands quantized row-wise to MXFP6 E2M3
-    (round-up scale), BF16 out, on the 128 x 128-tile path."""
+    (round-up scale), BF16 out, on the 256 x 256 LDS-DMA path."""
     M, N, K = 8192, 14336, 4096
     a_bits, w_bits = workloads.mlp_operands()
     qa, sa = mxa.mx_quantize(up_bf16(a_bits), "e2m3", "ceil", "row")
@@ -686,9 +686,9 @@ GEMM_PROFILES = {
         "gemm256_kernel_mm_fp8_nn_8192x14336x4096.md",
         "per-tensor FP8 E4M3 mm_fp8, x 8192x4096 @ wT (wT 4096x14336 N-contiguous, LDS transpose reads), BF16 bias",
         2.0 * 8192 * 14336 * 4096, FP8_PEAK_TFLOPS),
-    "gemm_kernel<3, 3, true, false, false, false, false>": (
-        "gemm_kernel_mxfp6_e2m3_8192x14336x4096.md",
-        "MXFP6 E2M3 GEMM 8192x4096 . (14336x4096)^T, both operands bit-stream packed, BF16 out (128x128 path)",
+    "gemm256_kernel<3, 3, true, false, false, false, false>": (
+        "gemm256_kernel_mxfp6_e2m3_8192x14336x4096.md",
+        "MXFP6 E2M3 GEMM 8192x4096 . (14336x4096)^T, both operands bit-stream packed, BF16 out",
         2.0 * 8192 * 14336 * 4096, FP6_PEAK_TFLOPS),
 }
 

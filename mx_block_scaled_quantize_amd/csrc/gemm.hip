@@ -24,7 +24,8 @@
 // the matrix are filled with code 0 and scale 2^0, which contribute nothing.
 // The next K-step's codes and scales are loaded into registers right after a
 // step is staged, so the loads run under that step's MFMAs.  This kernel serves
-// every shape the 256 x 256 kernel below does not take, and all FP6 operands.
+// every shape the 256 x 256 kernel below does not take (for FP6 x FP6: K not a
+// multiple of 512).
 
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
@@ -346,7 +347,10 @@ __attribute__((amdgpu_waves_per_eu((kIsFp6<FA> && kIsFp6<FB>) ? 2 : 1))) void ge
 // wave owns a 128 x 64 eighth held as 4 x 2 MFMA accumulators (128 FP32 per
 // lane), which leaves each wave half of the SIMD's registers.  K advances in
 // stages of 64 code bytes per row (two K-blocks of FP8, four of FP4, i.e. one or
-// two 32 x 32 x 64 MFMA steps).  Stages go straight from memory into LDS with
+// two 32 x 32 x 64 MFMA steps).  An FP6 stage is one MFMA step (two 24-byte
+// K-blocks) in a 64-byte slot: a stage pair is 96 bytes of the row, which the DMA
+// lanes place in 6 of the row's 8 LDS chunks (the lanes of the other two load
+// nothing and write zeros).  Stages go straight from memory into LDS with
 // gfx950's LDS-DMA loads (no register staging), four deep: a stage's loads are
 // issued three stages before it is consumed.  The LDS-DMA rate of a CU grows
 // with the number of waves issuing (measured on L2-resident data: about 84 GB/s
@@ -504,11 +508,14 @@ struct Ctx {
   int tp_a, tp_b;                  // M/N-contiguous: lane's swizzled chunk byte offset (row-tile 0)
   int sc_row_a, sc_row_b;          // lane's scale row (row-tile 0)
   int h8;                          // 8 * (lane / 32): the second K-block of an MFMA step is one byte up
+  uint32_t kstep;                  // K-contiguous: global bytes per stage (64; FP6 48)
+  int f6[3];                       // FP6: lane's three 8-byte pieces in a stage-pair row (stage half 0)
 };
 
 // Stage pair (t, t + 1) (t even) into stage buffers SA_, SB_ (= SA_ + 1): for each
 // operand 4 instructions per wave, each 1 KiB.  K-contiguous: 8 rows x one 128-byte
-// line holding both stages.  M/N-contiguous: 4 K-rows x 256 bytes, instructions
+// line holding both stages (FP6: the pair's 96 bytes of each row, whose stage
+// halves take 48 of their 64 bytes).  M/N-contiguous: 4 K-rows x 256 bytes, instructions
 // 0, 1 for stage t, 2, 3 for stage t + 1.  A dead stage (past the end of K) issues
 // the same loads on the empty resource (zeros, no memory traffic), which keeps the
 // vmcnt bookkeeping uniform and the loop free of branches.
@@ -523,13 +530,13 @@ __device__ __forceinline__ void issue_pair(const Ctx& c, int t, int wave, bool l
     if constexpr (TA)
       dma(live ? c.a : c.z, c.off_a[jj], uint32_t(t + e) * c.step_a, dst + e * kOpBytes + (wave * 2 + jj) * 1024);
     else
-      dma(live0 ? c.a : c.z, c.off_a[jj], uint32_t(t) * kRow + uint32_t(j) * c.js_a,
+      dma(live0 ? c.a : c.z, c.off_a[jj], uint32_t(t) * c.kstep + uint32_t(j) * c.js_a,
           dst + (wave * kPairLoads + j) * 1024);
     if constexpr (TB)
       dma(live ? c.b : c.z, c.off_b[jj], uint32_t(t + e) * c.step_b,
           dst + kPairOp + e * kOpBytes + (wave * 2 + jj) * 1024);
     else
-      dma(live0 ? c.b : c.z, c.off_b[jj], uint32_t(t) * kRow + uint32_t(j) * c.js_b,
+      dma(live0 ? c.b : c.z, c.off_b[jj], uint32_t(t) * c.kstep + uint32_t(j) * c.js_b,
           dst + kPairOp + (wave * kPairLoads + j) * 1024);
   }
 }
@@ -556,11 +563,20 @@ __device__ __forceinline__ v8i mn_operand(const uint8_t* p) {
   return v8i{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
 }
 
+// Operand kinds of the K-contiguous stages: FP8, FP4, FP6
+constexpr int kOkFp8 = 0, kOkFp4 = 1, kOkFp6 = 2;
+template <int F> constexpr int kOperandKind = F == E2M1 ? kOkFp4 : kIsFp6<F> ? kOkFp6 : kOkFp8;
+
 // Operand from a K-contiguous stage-pair row p (the lane's row start); HALF is the
 // stage's half of the row (chunks 4 HALF .. 4 HALF + 3, before the permutation).
-template <bool FP4, int KK, int HALF>
+template <int OK, int KK, int HALF>
 __device__ __forceinline__ v8i km_operand(const Ctx& c, const uint8_t* p) {
-  if constexpr (FP4) {   // the 32 codes of K-block 2 kk + h: chunk 2 kk + h
+  if constexpr (OK == kOkFp6) {   // the 24 bytes of K-block h: three 8-byte pieces of chunks 0..2
+    const uint2 x0 = *reinterpret_cast<const uint2*>(p + (c.f6[0] ^ (64 * HALF)));
+    const uint2 x1 = *reinterpret_cast<const uint2*>(p + (c.f6[1] ^ (64 * HALF)));
+    const uint2 x2 = *reinterpret_cast<const uint2*>(p + (c.f6[2] ^ (64 * HALF)));
+    return v8i{int(x0.x), int(x0.y), int(x1.x), int(x1.y), int(x2.x), int(x2.y), 0, 0};
+  } else if constexpr (OK == kOkFp4) {   // the 32 codes of K-block 2 kk + h: chunk 2 kk + h
     const int ch = (KK == 0 ? c.c0 : c.c1) ^ (64 * HALF);
     const uint4 x = *reinterpret_cast<const uint4*>(p + ch);
     return v8i{int(x.x), int(x.y), int(x.z), int(x.w), 0, 0, 0, 0};
@@ -575,21 +591,21 @@ __device__ __forceinline__ v8i km_operand(const Ctx& c, const uint8_t* p) {
 // FRESH false the step's scale words are those of the step before (one word
 // holds 4 K-blocks: two FP8 stages, or both MFMA steps of an FP4 stage) and are
 // left to the caller to carry over.
-template <bool FP4, int SI, int U, int KK, bool PT, bool TA, bool TB, bool FRESH = true>
+template <int OK, int SI, int U, int KK, bool PT, bool TA, bool TB, bool FRESH = true>
 __device__ __forceinline__ void read_step(const Ctx& c, int t, int lane, v8i (&a)[4], v8i (&b)[2], int (&sa)[4],
                                           int (&sb)[2]) {
-  using G = Geo<FP4>;
+  using G = Geo<OK == kOkFp4>;
   constexpr int kHalf = SI % 2;   // stage SI is this half of its pair
   const uint8_t* base = stage<SI>();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (TA) a[i] = mn_operand(base + kHalf * kOpBytes + c.rd_a + (c.tp_a ^ (32 * i)));
-    else a[i] = km_operand<FP4, KK, kHalf>(c, base + c.rd_a + i * 32 * kPairRow);
+    else a[i] = km_operand<OK, KK, kHalf>(c, base + c.rd_a + i * 32 * kPairRow);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if constexpr (TB) b[j] = mn_operand(base + kHalf * kOpBytes + c.rd_b + (c.tp_b ^ (32 * j)));
-    else b[j] = km_operand<FP4, KK, kHalf>(c, base + c.rd_b + j * 32 * kPairRow);
+    else b[j] = km_operand<OK, KK, kHalf>(c, base + c.rd_b + j * 32 * kPairRow);
   }
   if constexpr (!PT && FRESH) {
     // the word holding the lane's K-block (t * kKb) % 16 + 2 kk + h; the byte is
@@ -685,9 +701,10 @@ constexpr int later_ops() {
 // LDS reads of one operand step: A's 4 row tiles and B's 2 (FP8 two ds_read_b128
 // per tile K-contiguous, four transpose reads M/N-contiguous; FP4 one
 // ds_read_b128), plus one scale word per tile in MX mode when the words change
-template <bool FP4, bool PT, bool TA, bool TB, bool FRESH = true>
+template <int OK, bool PT, bool TA, bool TB, bool FRESH = true>
 constexpr int kDsReads() {
-  return PT ? (TA ? 16 : 8) + (TB ? 8 : 4) : (FP4 ? 6 : 12) + (FRESH ? 6 : 0);
+  // FP6: three ds_read_b64 per tile
+  return PT ? (TA ? 16 : 8) + (TB ? 8 : 4) : (OK == kOkFp4 ? 6 : OK == kOkFp6 ? 18 : 12) + (FRESH ? 6 : 0);
 }
 
 // Scale words of the next step are those of the current one
@@ -704,6 +721,7 @@ template <int FA, int FB, int P, bool PT, bool TA, bool TB, bool CARRY>
 __device__ __forceinline__ void stage_steps(const Ctx& c, int t, int T, int nsuper, int lane, int wave, Regs& r,
                                             v16f (&acc)[4][2]) {
   constexpr bool kFp4 = FA == E2M1;
+  constexpr int kOk = kOperandKind<FA>;
   using G = Geo<kFp4>;
   constexpr int SI = P % kStages;                          // this stage's buffer
   constexpr int U = (P / G::kPerScale) & 1;                // this stage's scale buffer
@@ -715,10 +733,10 @@ __device__ __forceinline__ void stage_steps(const Ctx& c, int t, int T, int nsup
     if (kk + 1 < G::kSub) {
       // next MFMA step is in this stage, already visible
       // (FP4) the stage's second step: same scale words as its first
-      read_step<kFp4, SI, U, 1, PT, TA, TB, false>(c, t, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
+      read_step<kOk, SI, U, 1, PT, TA, TB, false>(c, t, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
       if constexpr (!PT) carry_scales(r, cur, nxt);
       mfma_all<FA, FB, 0, PT>(acc, r.a[cur], r.b[cur], r.sa[cur], r.sb[cur], t, c.h8);
-      interleave<0, kDsReads<kFp4, PT, TA, TB, false>()>();
+      interleave<0, kDsReads<kOk, PT, TA, TB, false>()>();
     } else {
       // Only a boundary into a new stage pair (odd P) synchronizes: stage t + 1 of an
       // even P arrived with stage t, in the same pair, and is visible since the
@@ -741,10 +759,10 @@ __device__ __forceinline__ void stage_steps(const Ctx& c, int t, int T, int nsup
       // unconditional read keeps the operand registers free of merge copies
       // FP8 stage t + 1 takes a new scale word only when it is even (P odd)
       constexpr bool kFresh = kFp4 || P % 2 == 1 || !CARRY;
-      read_step<kFp4, SIn, Un, 0, PT, TA, TB, kFresh>(c, t + 1, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
+      read_step<kOk, SIn, Un, 0, PT, TA, TB, kFresh>(c, t + 1, lane, r.a[nxt], r.b[nxt], r.sa[nxt], r.sb[nxt]);
       if constexpr (!PT && !kFresh) carry_scales(r, cur, nxt);
       mfma_all<FA, FB, G::kSub - 1, PT>(acc, r.a[cur], r.b[cur], r.sa[cur], r.sb[cur], t, c.h8);
-      interleave<(kIssue ? 2 * kCodeGroup : 0) + (kScales ? kScaleOps : 0), kDsReads<kFp4, PT, TA, TB, kFresh>()>();
+      interleave<(kIssue ? 2 * kCodeGroup : 0) + (kScales ? kScaleOps : 0), kDsReads<kOk, PT, TA, TB, kFresh>()>();
     }
   }
 }
@@ -812,7 +830,9 @@ __device__ __forceinline__ void requant_eighth(const v16f (&acc)[4][2], float al
 template <int FA, int FB, bool BF16OUT, bool PT, bool TA, bool TB, bool RQ = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) {
   constexpr bool kFp4 = FA == E2M1;
+  constexpr bool kFp6 = kIsFp6<FA>;
   static_assert(!(TA || TB) || (PT && !kFp4 && BF16OUT), "M/N-contiguous operands: per-tensor FP8, BF16 out");
+  static_assert(kIsFp6<FA> == kIsFp6<FB> && !(kFp6 && (PT || RQ)), "FP6 operands: both, MX scales, plain output");
   using G = Geo<kFp4>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -820,8 +840,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   int tm, tn;
   map_tile(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int K = int(g.K);
-  const int kbytes = kFp4 ? K / 2 : K, kblocks = K / 32;
-  const int T = kbytes / kRow, nsuper = kblocks / kKbPerScale;
+  // code bytes per row; stages of 64 code bytes (FP8 64, FP4 128 K-values), FP6 of 64
+  // K-values (48 bytes, in a 64-byte stage slot)
+  const int kbytes = kFp4 ? K / 2 : kFp6 ? K / 4 * 3 : K, kblocks = K / 32;
+  const int T = kFp4 ? K / 128 : K / 64, nsuper = kblocks / kKbPerScale;
   // row pitch of the stored operands: K bytes when K-contiguous
   const int lda = TA ? int(g.lda) : kbytes, ldb = TB ? int(g.ldb) : kbytes;
   const uint8_t* A = g.a + int64_t(blockIdx.y) * g.batch_a;
@@ -864,7 +886,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
     // K-contiguous: instruction j of a wave covers rows 32 wave + 8 j + [0, 8), one 128-byte
     // line each; swz of those rows depends on j only through j % 2 (the 8 j term moves it by 4 j)
     const int row = 32 * wave + 8 * j + (lane >> 3);
-    const uint32_t km = uint32_t(32 * wave + (lane >> 3)) * uint32_t(kbytes) + 16u * uint32_t((lane & 7) ^ swz(row));
+    uint32_t km = uint32_t(32 * wave + (lane >> 3)) * uint32_t(kbytes) + 16u * uint32_t((lane & 7) ^ swz(row));
+    if constexpr (kFp6) {
+      // the lane's LDS chunk holds stage half e, chunk cc of the slot; global chunk 3 e + cc
+      // of the pair's 96 bytes, and nothing for the unused chunk 3 (an offset past any
+      // buffer's end: the load writes zeros and touches no memory)
+      const int sc = (lane & 7) ^ swz(row), e = sc >> 2, cc = sc & 3;
+      km = cc == 3 ? 0xF0000000u : uint32_t(32 * wave + (lane >> 3)) * uint32_t(kbytes) + 16u * uint32_t(3 * e + cc);
+    }
     // M/N-contiguous: instruction j of a stage covers K-rows 8 wave + 4 j + [0, 4), 256 bytes each
     const int kr = 8 * wave + 4 * j + (lane >> 4);
     const uint32_t mn_chunk = 16u * uint32_t((lane & 15) ^ (2 * (kr & 7)));
@@ -895,6 +924,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   c.sc_row_a = wm * 128 + rr;
   c.sc_row_b = wn * 64 + rr;
   c.h8 = 8 * h;
+  c.kstep = kFp6 ? 48u : uint32_t(kRow);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {   // FP6: bytes 24 h + 8 k of the stage slot, in chunk (24 h + 8 k) / 16
+    const int o = 24 * h + 8 * k;
+    c.f6[k] = 16 * ((o >> 4) ^ swz(rr)) + (o & 15);
+  }
 
   v16f acc[4][2];
 #pragma unroll
@@ -919,7 +954,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   // 2 and 3 and scale stage 1
   wait_vm_lgkm0<2 * kCodeGroup + (PT ? 0 : kScaleOps)>();
   barrier();
-  read_step<kFp4, 0, 0, 0, PT, TA, TB>(c, 0, lane, r.a[0], r.b[0], r.sa[0], r.sb[0]);
+  read_step<kOperandKind<FA>, 0, 0, 0, PT, TA, TB>(c, 0, lane, r.a[0], r.b[0], r.sa[0], r.sb[0]);
 
   for (int t0 = 0; t0 < T; t0 += G::kUnroll)
     unrolled_body<FA, FB, PT, TA, TB, !RQ>(c, t0, T, nsuper, lane, wave, r, acc,
@@ -1037,8 +1072,7 @@ static mx_status_t gemm_dispatch(const uint8_t* a, const uint8_t* sa, const uint
   g.ldb = code_bytes<FB>(K);
   g.ldc = ldc;
   g.alpha = alpha;
-  // FP6 operands run on the 128 x 128 path only (the 256 path stages 64-byte K-slices)
-  if constexpr (!kIsFp6<FA> && !kIsFp6<FB>) {
+  {
     const int64_t tm256 = (M + t256::kTile - 1) / t256::kTile, tn256 = (N + t256::kTile - 1) / t256::kTile;
     const bool big = N % (BF ? 8 : 4) == 0 && K % t256::kMxK == 0 && K > 0 && K <= (int64_t(1) << 22) &&
                      tm256 * tn256 < (int64_t(1) << 31) && !misaligned(a) && !misaligned(b) && !misaligned(sa) &&

@@ -106,9 +106,10 @@ def test_fp6_full_size():
 
 def test_fp6_gemm_full_size():
     """The bench's MXFP6 GEMM: A 8192 x 4096 and W 14336 x 4096 quantized row-wise to
-    E2M3 (round-up rule), BF16 out.  Operands compared in full; the product on
-    one whole row from every 128-row tile and one whole column from every
-    128-column tile of the launch, segment by segment."""
+    E2M3 (round-up rule), BF16 out, on the 256 x 256 path.  Operands compared in
+    full; the product on one whole row from every 128-row band and one whole
+    column from every 128-column band (so every 256 x 256 output tile of the
+    launch twice), segment by segment."""
     a_bits, w_bits = workloads.mlp_operands()
     qa, sa = mxa.mx_quantize(upload_bf16_bits(a_bits), "e2m3", "ceil", "row")
     qw, sw = mxa.mx_quantize(upload_bf16_bits(w_bits), "e2m3", "ceil", "row")

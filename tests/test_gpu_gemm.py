@@ -73,9 +73,10 @@ def test_gemm_small_parity(fa, fb, shape):
 @pytest.mark.parametrize("shape", [(128, 128, 128), (200, 136, 192), (64, 300, 512), (1, 7, 64), (256, 384, 1024),
                                    (96, 160, 320), (130, 258, 704)])   # whole K-steps of 256, then a partial one
 def test_gemm_fp6_parity(fa, fb, shape):
-    """MXFP6 operands (bit-stream packed as mx_quantize writes them) on the
-    128 x 128 path, whose FP6 K-steps are 256 long: K of 64, 128, 192, 320 and
-    704 end on a partial step, zero-filled past K."""
+    """MXFP6 operands (bit-stream packed as mx_quantize writes them).  K of 512
+    and 1024 run on the 256 x 256 LDS-DMA path; the others on the 128 x 128
+    path, whose FP6 K-steps are 256 long: K of 64, 128, 192, 320 and 704 end on
+    a partial step, zero-filled past K."""
     M, N, K = shape
     qa, sa, qb, sb = quantized_operands(M, N, K, fa, fb, seed=M + N + K + 1)
     args = (upload_u8(qa), upload_u8(sa), upload_u8(qb), upload_u8(sb), fa, fb, 0.75)
@@ -121,7 +122,7 @@ TILED_SHAPES = [(256, 256, 1024), (512, 768, 2048), (2048, 256, 1024), (256, 102
 
 
 @pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2"),
-                                   ("e2m1", "e2m1")])
+                                   ("e2m1", "e2m1"), ("e2m3", "e2m3"), ("e3m2", "e2m3"), ("e2m3", "e3m2")])
 @pytest.mark.parametrize("shape", TILED_SHAPES)
 def test_gemm_tiled_path_parity(fa, fb, shape):
     M, N, K = shape
@@ -133,14 +134,14 @@ def test_gemm_tiled_path_parity(fa, fb, shape):
     assert og.rel_frobenius(bf16_to_f64(c16), bf16_to_f64(og.f64_to_bf16_bits(ref))) <= BF16_TOL
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "e2m3"])
 def test_gemm_tiled_path_exact_on_integer_valued_operands(fmt):
     """Integer-valued operands on the tiled path: exact whatever the summation
     order, so any misplaced code, scale byte or lane shows as an exact mismatch."""
     g = np.random.default_rng(19)
     M, N, K = 512, 256, 2048
     vals = np.array([0, 1, 2, 3, 4, -1, -2, -3, -4], np.float32) if fmt == "e2m1" else \
-        np.arange(-16, 17).astype(np.float32)
+        np.arange(-7, 8).astype(np.float32) if fmt == "e2m3" else np.arange(-16, 17).astype(np.float32)
     A = g.choice(vals, size=(M, K)).astype(np.float32) * np.exp2((np.arange(K) // 32) % 5 - 2)[None, :]
     B = g.choice(vals, size=(N, K)).astype(np.float32)
     qa, sa = omx.quantize_rowwise(A.astype(np.float32), fmt, "ceil")
