@@ -474,13 +474,14 @@ __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, 
 }
 
 // Workgroups are dealt to the 8 XCDs round-robin; give every XCD a contiguous
-// run of the tile order, and walk tiles in groups of 8 tile-rows so that the
-// tiles running together on one XCD share their A and B panels in its L2.
+// run of the tile order, and walk tiles in groups of 4 tile-rows so that the
+// tiles running together on one XCD (4 x 8 of them) share their A and B panels
+// in its L2 (groups of 4 measured 1% faster than 8, groups of 16 3% slower).
 __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int ntiles = tiles_m * tiles_n;
   int idx = bid;
   if ((ntiles & 7) == 0) idx = (bid & 7) * (ntiles >> 3) + (bid >> 3);
-  constexpr int kGroupM = 8;
+  constexpr int kGroupM = 4;
   const int group = idx / (kGroupM * tiles_n);
   const int first = group * kGroupM;
   const int gm = min(tiles_m - first, kGroupM);
