@@ -510,7 +510,7 @@ struct Ctx {
   int sc_row_a, sc_row_b;          // lane's scale row (row-tile 0)
   int h8;                          // 8 * (lane / 32): the second K-block of an MFMA step is one byte up
   uint32_t kstep;                  // K-contiguous: global bytes per stage (64; FP6 48)
-  int f6[3];                       // FP6: lane's three 8-byte pieces in a stage-pair row (stage half 0)
+  int f6[2];                       // FP6: lane's 16-byte and 8-byte pieces in a stage-pair row (stage half 0)
 };
 
 // Stage pair (t, t + 1) (t even) into stage buffers SA_, SB_ (= SA_ + 1): for each
@@ -572,11 +572,13 @@ template <int F> constexpr int kOperandKind = F == E2M1 ? kOkFp4 : kIsFp6<F> ? k
 // stage's half of the row (chunks 4 HALF .. 4 HALF + 3, before the permutation).
 template <int OK, int KK, int HALF>
 __device__ __forceinline__ v8i km_operand(const Ctx& c, const uint8_t* p) {
-  if constexpr (OK == kOkFp6) {   // the 24 bytes of K-block h: three 8-byte pieces of chunks 0..2
-    const uint2 x0 = *reinterpret_cast<const uint2*>(p + (c.f6[0] ^ (64 * HALF)));
-    const uint2 x1 = *reinterpret_cast<const uint2*>(p + (c.f6[1] ^ (64 * HALF)));
-    const uint2 x2 = *reinterpret_cast<const uint2*>(p + (c.f6[2] ^ (64 * HALF)));
-    return v8i{int(x0.x), int(x0.y), int(x1.x), int(x1.y), int(x2.x), int(x2.y), 0, 0};
+  if constexpr (OK == kOkFp6) {
+    // the 24 bytes of K-block h: h = 0, chunk 0 then the low half of chunk 1; h = 1, the
+    // high half of chunk 1 then chunk 2 -- one 16-byte and one 8-byte read, put in order
+    const uint4 q = *reinterpret_cast<const uint4*>(p + (c.f6[0] ^ (64 * HALF)));
+    const uint2 d = *reinterpret_cast<const uint2*>(p + (c.f6[1] ^ (64 * HALF)));
+    return c.h8 ? v8i{int(d.x), int(d.y), int(q.x), int(q.y), int(q.z), int(q.w), 0, 0}
+                : v8i{int(q.x), int(q.y), int(q.z), int(q.w), int(d.x), int(d.y), 0, 0};
   } else if constexpr (OK == kOkFp4) {   // the 32 codes of K-block 2 kk + h: chunk 2 kk + h
     const int ch = (KK == 0 ? c.c0 : c.c1) ^ (64 * HALF);
     const uint4 x = *reinterpret_cast<const uint4*>(p + ch);
@@ -704,8 +706,8 @@ constexpr int later_ops() {
 // ds_read_b128), plus one scale word per tile in MX mode when the words change
 template <int OK, bool PT, bool TA, bool TB, bool FRESH = true>
 constexpr int kDsReads() {
-  // FP6: three ds_read_b64 per tile
-  return PT ? (TA ? 16 : 8) + (TB ? 8 : 4) : (OK == kOkFp4 ? 6 : OK == kOkFp6 ? 18 : 12) + (FRESH ? 6 : 0);
+  // FP6: a ds_read_b128 and a ds_read_b64 per tile
+  return PT ? (TA ? 16 : 8) + (TB ? 8 : 4) : (OK == kOkFp4 ? 6 : 12) + (FRESH ? 6 : 0);
 }
 
 // Scale words of the next step are those of the current one
@@ -926,11 +928,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const GemmArgs g) 
   c.sc_row_b = wn * 64 + rr;
   c.h8 = 8 * h;
   c.kstep = kFp6 ? 48u : uint32_t(kRow);
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {   // FP6: bytes 24 h + 8 k of the stage slot, in chunk (24 h + 8 k) / 16
-    const int o = 24 * h + 8 * k;
-    c.f6[k] = 16 * ((o >> 4) ^ swz(rr)) + (o & 15);
-  }
+  // FP6: chunk 2 h of the stage slot, and bytes 16 + 8 h (the half of chunk 1 that belongs to block h)
+  c.f6[0] = 16 * ((2 * h) ^ swz(rr));
+  c.f6[1] = 16 * (1 ^ swz(rr)) + 8 * h;
 
   v16f acc[4][2];
 #pragma unroll
