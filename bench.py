@@ -13,7 +13,9 @@ written) x steps / wall time of the timed region.  ``roofline.achieved`` = the
 same bytes / the kernel's own average duration (one HIP event pair around the K
 back-to-back launches on the stream the kernel runs on).  A second pass brackets
 every launch with its own events for the median and the 10th / 90th
-percentiles; the graphics clock comes from the committed rocprofv3 summary; a plain
+percentiles; the graphics clock is polled through the management library while
+the kernel runs back to back (and, for long kernels, derived from the committed
+rocprofv3 summary's cycle counter); a plain
 device copy of the same size gives the attainable copy roof.  The MXFP8 GEMM
 (8192 x 4096 x 14336) and the other workloads are reported under ``gemm`` and
 ``extra``; the CPU oracle under ``cpu_baseline``.
@@ -36,6 +38,7 @@ import re
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -123,6 +126,64 @@ def launch_distribution(fn, n, stream, torch):
     us = sorted(s.elapsed_time(e) * 1e3 for s, e in evs)
     return {"median_us": round(pct(us, 50), 2), "p10_us": round(pct(us, 10), 2), "p90_us": round(pct(us, 90), 2),
             "min_us": round(us[0], 2), "max_us": round(us[-1], 2), "launches": n}
+
+
+def clock_under_load(fn, dev, torch, seconds=2.0, settle=1.0, burst=50):
+    """Graphics clock while fn's kernel runs back to back: the management library's
+    current GFX clock and GFX activity (amdsmi), polled from a thread every 10 ms
+    after `settle` seconds of a `seconds`-long run of bursts of launches on the
+    device (found by its PCI address).  The library refreshes these figures only
+    about once or twice a second, hence the long run and the settling time.  A
+    missing library or device gives an "error" entry instead of figures."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception as e:   # no library, or no access to the device's management interface
+        return {"MHz_median": None, "error": type(e).__name__}
+    try:
+        p = torch.cuda.get_device_properties(dev)
+        bdf = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+        h = amdsmi.amdsmi_get_processor_handle_from_bdf(bdf)
+        clk, act, stop = [], [], threading.Event()
+
+        def poll():
+            t_start = time.perf_counter() + settle
+            while not stop.is_set():
+                if time.perf_counter() >= t_start:
+                    try:
+                        clk.append(int(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"]))
+                        a = amdsmi.amdsmi_get_gpu_metrics_info(h).get("average_gfx_activity")
+                        if isinstance(a, (int, float)):
+                            act.append(a)
+                    except Exception:
+                        pass
+                time.sleep(0.01)
+
+        th = threading.Thread(target=poll, daemon=True)
+        torch.cuda.synchronize()
+        th.start()
+        t_end = time.perf_counter() + seconds
+        while time.perf_counter() < t_end:
+            for _ in range(burst):
+                fn()
+            torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        if not clk:
+            return {"MHz_median": None, "error": "no samples", "bdf": bdf}
+        clk.sort()
+        act.sort()
+        return {"MHz_median": pct(clk, 50), "MHz_min": clk[0], "MHz_max": clk[-1], "samples": len(clk),
+                "gfx_activity_pct_median": pct(act, 50) if act else None, "bdf": bdf,
+                "source": f"amdsmi GFX clock, polled over the last {seconds - settle:.1f} s of {seconds:.1f} s "
+                          "of back-to-back launches"}
+    except Exception as e:
+        return {"MHz_median": None, "error": type(e).__name__}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
 
 
 def copy_roof(torch, dev, stream, nbytes=64 << 20, sets=8, n=50):
@@ -266,6 +327,7 @@ def main():
     value = algo_bytes * args.steps / wall / 1e9
     achieved = algo_bytes / avg_kern_s / 1e9
     traffic = measured_traffic()
+    clock = clock_under_load(dual, dev, torch)
     del sets
     roof = copy_roof(torch, dev, stream)
 
@@ -283,7 +345,7 @@ def main():
                      "traffic": None if traffic is None else round(traffic)},
         "kernel_us": round(avg_kern_s * 1e6, 2),
         "launch_us": dist,
-        "gpu_clock": profile_clock(TRAFFIC_FILE, QUANT_SOURCES),
+        "gpu_clock": {"under_load": clock, "profile": profile_clock(TRAFFIC_FILE, QUANT_SOURCES)},
         "copy_roof": roof,
         "frac_of_copy_roof": round(achieved / roof["GB/s"], 4),
     }
@@ -453,6 +515,7 @@ def bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=1
         return lambda: mxa.check(lib.mx_gemm(qa.data_ptr(), sa.data_ptr(), 0, qw.data_ptr(), sw.data_ptr(), 0,
                                              mxa.SCALE_LAYOUT[layout], M, N, K, 1.0, c.data_ptr(), 1, N, sp))
     times = time_alternating({k: call(k) for k in ops}, gemm_calls(steps), 2, stream, torch, warm=GEMM_WARM)
+    clock = clock_under_load(call("row"), dev, torch, burst=4)
     del ops
     t = times["row"]
     tf = flops / t / 1e12
@@ -464,7 +527,8 @@ def bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=1
             "gemm_scales": {"ms_per_call": round(times["gemm"] * 1e3, 4),
                             "TFLOP/s": round(flops / times["gemm"] / 1e12, 1),
                             "frac": round(flops / times["gemm"] / 1e12 / FP8_PEAK_TFLOPS, 4)},
-            "profile": {"file": os.path.relpath(prof, ROOT), "current": profile_is_current(prof, GEMM_SOURCES)}}
+            "profile": {"file": os.path.relpath(prof, ROOT), "current": profile_is_current(prof, GEMM_SOURCES)},
+            "gpu_clock": {"under_load": clock, "profile": profile_clock(prof, GEMM_SOURCES)}}
 
 
 def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
