@@ -391,9 +391,10 @@ def time_alternating(fns, n, rounds, stream, torch, warm=2):
 
 
 # GEMM legs: the first launches of a burst run while the clock is still settling
-# (a trace shows their durations drifting by 20% over the first ten or so), so
-# each leg is warmed up with GEMM_WARM calls and timed over at least GEMM_CALLS.
-GEMM_WARM, GEMM_CALLS = 10, 20
+# (their durations drift by up to 20% over the first 30 to 40 calls of an 8192 x
+# 14336 x 4096 GEMM, about 15 ms), so each leg is warmed up with GEMM_WARM calls
+# and timed over at least GEMM_CALLS.
+GEMM_WARM, GEMM_CALLS = 40, 20
 
 
 def gemm_calls(steps):
