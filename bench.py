@@ -518,6 +518,7 @@ def bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=1
     times = time_alternating({k: call(k) for k in ops}, gemm_calls(steps), 2, stream, torch, warm=GEMM_WARM)
     clock = clock_under_load(call("row"), dev, torch, burst=4)
     del ops
+    vendor = vendor_fp8_reference(lib, sp, stream, dev, up_bf16, workloads, torch, c, steps)
     t = times["row"]
     tf = flops / t / 1e12
     prof = os.path.join(ROOT, "profiles", "gemm256_kernel_mxfp8_8192x14336x4096.md")
@@ -529,7 +530,45 @@ def bench_gemm(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch, steps=1
                             "TFLOP/s": round(flops / times["gemm"] / 1e12, 1),
                             "frac": round(flops / times["gemm"] / 1e12 / FP8_PEAK_TFLOPS, 4)},
             "profile": {"file": os.path.relpath(prof, ROOT), "current": profile_is_current(prof, GEMM_SOURCES)},
-            "gpu_clock": {"under_load": clock, "profile": profile_clock(prof, GEMM_SOURCES)}}
+            "gpu_clock": {"under_load": clock, "profile": profile_clock(prof, GEMM_SOURCES)},
+            "vendor_reference": vendor}
+
+
+def vendor_fp8_reference(lib, sp, stream, dev, up_bf16, workloads, torch, c, steps):
+    """Context only, not this library's figure: the vendor BLAS's per-tensor FP8 GEMM
+    (torch._scaled_mm, served by hipBLASLt) on the same shape and box, timed in
+    alternation with this library's per-tensor mm_fp8 on the same FP8 operands."""
+    M, N, K = 8192, 14336, 4096
+    a_bits, w_bits = workloads.mlp_operands()
+    try:
+        x, w = up_bf16(a_bits), up_bf16(w_bits)
+        sx = (x.float().abs().max() / 448).reshape(())
+        sw = (w.float().abs().max() / 448).reshape(())
+        x8 = (x.float() / sx).to(torch.float8_e4m3fn)
+        w8 = (w.float() / sw).to(torch.float8_e4m3fn)
+        del x, w
+        scale = (sx * sw).reshape(1).contiguous()
+
+        def ours():
+            st = lib.mm_fp8(x8.data_ptr(), w8.data_ptr(), 0, 1, M, N, K, 0, 0, 0, 1, scale.data_ptr(), None,
+                            c.data_ptr(), sp)
+            if st != 0:
+                raise RuntimeError(lib.mx_status_str(st).decode())
+
+        def vendor():
+            torch._scaled_mm(x8, w8.t(), scale_a=sx.float(), scale_b=sw.float(), out_dtype=torch.bfloat16)
+
+        times = time_alternating({"ours": ours, "vendor": vendor}, gemm_calls(steps), 2, stream, torch,
+                                 warm=GEMM_WARM)
+    except Exception as e:   # an FP8 GEMM the installed torch cannot run here
+        return {"error": f"{type(e).__name__}: {str(e)[:120]}"}
+    flops = 2.0 * M * N * K
+    return {"what": "per-tensor FP8 E4M3 GEMM 8192x4096 x (14336x4096)^T, BF16 out: torch._scaled_mm (hipBLASLt) "
+                    "against this library's mm_fp8, in alternation; context only",
+            "vendor_ms_per_call": round(times["vendor"] * 1e3, 4),
+            "vendor_frac": round(flops / times["vendor"] / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "mm_fp8_ms_per_call": round(times["ours"] * 1e3, 4),
+            "mm_fp8_frac": round(flops / times["ours"] / 1e12 / FP8_PEAK_TFLOPS, 4)}
 
 
 def bench_extra(lib, sp, stream, dev, up_bf16, mxa, workloads, np, torch):
