@@ -299,14 +299,25 @@ def main():
                          a=torch.zeros(1, dtype=torch.float32, device=dev)))
     idx = [0]
 
+    # the call's arguments per buffer set, built once: the per-launch host work (a
+    # ctypes call and HIP's launch) must stay below the kernel's ~28 us, or the
+    # event timing measures the host loop rather than the kernel
+    dual_fn = lib.mx_quantize_dual
+    dual_args = [(s["x"].data_ptr(), 1, R, C, 32, 0, 1, s["qr"].data_ptr(), s["sr"].data_ptr(), s["qc"].data_ptr(),
+                  s["sc"].data_ptr(), 0, s["a"].data_ptr(), sp) for s in sets]
+
     def dual():
-        s = sets[idx[0] % nsets]
-        idx[0] += 1
-        st = lib.mx_quantize_dual(s["x"].data_ptr(), 1, R, C, 32, 0, 1, s["qr"].data_ptr(), s["sr"].data_ptr(),
-                                  s["qc"].data_ptr(), s["sc"].data_ptr(), 0, s["a"].data_ptr(), sp)
+        i = idx[0]
+        idx[0] = i + 1
+        st = dual_fn(*dual_args[i % nsets])
         if st != 0:
             raise RuntimeError(lib.mx_status_str(st).decode())
 
+    # the graphics clock under this load: two seconds of the same launches, before
+    # the warm-up, so that the timed region starts on a GPU out of its idle state
+    # (a fresh box otherwise spends the first milliseconds ramping up, longer than
+    # a short timed region)
+    clock = clock_under_load(dual, dev, torch)
     for i in range(args.warmup):
         dual()
     torch.cuda.synchronize()
@@ -327,7 +338,6 @@ def main():
     value = algo_bytes * args.steps / wall / 1e9
     achieved = algo_bytes / avg_kern_s / 1e9
     traffic = measured_traffic()
-    clock = clock_under_load(dual, dev, torch)
     del sets
     roof = copy_roof(torch, dev, stream)
 
