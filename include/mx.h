@@ -178,9 +178,12 @@ mx_status_t mx_quantize_dual(const void* x, mx_dtype_t in, int64_t rows, int64_t
  *   on one line serialize.  With NULL every workgroup takes its ticket on the
  *   ring's own amax and ticket words, and the launch caps the grid at a few
  *   hundred persistent workgroups to bound that queue; the codes and the ring
- *   are the same either way, only the time differs.  4-byte aligned (128-byte
- *   alignment keeps each group on one line).  One scratch buffer may serve many
- *   rings, but not two calls in flight at once.
+ *   are the same either way, only the time differs.  Small inputs (a grid of
+ *   at most 16 workgroups) use the ring's words even when scratch is given, and
+ *   a grid of one workgroup takes no ticket at all; the scratch is then left
+ *   untouched.  4-byte aligned (128-byte alignment keeps each group on one
+ *   line).  One scratch buffer may serve many rings, but not two calls in flight
+ *   at once.
  *
  * Each call: y = fl32(x * m) with the m the ring holds at launch, q = RNE +
  * saturating cast of y to `fmt` (Inf saturates, NaN gives NaN), written as

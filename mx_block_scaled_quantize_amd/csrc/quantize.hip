@@ -250,8 +250,10 @@ struct RingArgs {
 //      (again dependent RMWs);
 //   4. the last top ticket reads the overall max, folds it into the history,
 //      publishes s and m = 1/s and clears the top words.
-// Without scratch, steps 1-2 use the ring's own amax and ticket words and the
-// first arrival at step 2 that completes the count goes straight to step 4.
+// Without scratch, and for grids of at most kSingleLevelGrid workgroups, steps
+// 1-2 use the ring's own amax and ticket words and the arrival at step 2 that
+// completes the count goes straight to step 4.  A grid of one workgroup takes no
+// ticket: it folds its own max (step 4) with no atomic at all.
 // Atomics on one cache line serialize (about 12 ns each on MI355X, more under
 // load) while different lines proceed in parallel, so every group sits on a
 // 128-byte line of its own; the single-word mode is kept to few workgroups by
@@ -266,26 +268,39 @@ constexpr int64_t kNullTicketGrid = 512;
 // resident workgroups per CU, each taking two or more tiles and one ticket
 // (measured 3.6% faster than one workgroup per tile on a BF16 8192 x 4096 input).
 constexpr int64_t kTicketGrid = 1024;
+// Grids up to this size take a single-level ticket on the ring's words even with
+// scratch: two dependent round trips fewer for the last arrival, and at most
+// 2 x 16 atomics queued on the line (well under a microsecond).  This is the
+// launch-bound regime of small tensors, where the round trips are the call's cost.
+constexpr unsigned kSingleLevelGrid = 16;
 
 struct RingTicket {
   uint32_t* gmax;
   uint32_t* gctr;
   unsigned members;    // workgroups in this group
   bool two_level;
+  bool solo;           // the grid's only workgroup: no ticket, it folds its own max
 };
 
 __device__ __forceinline__ RingTicket ring_ticket(const RingArgs& r, unsigned wg, unsigned num_wg) {
-  if (r.tickets == nullptr) {
+  if (num_wg == 1) return RingTicket{nullptr, nullptr, 1u, false, true};
+  if (r.tickets == nullptr || num_wg <= kSingleLevelGrid) {
     uint32_t* top = reinterpret_cast<uint32_t*>(r.ring + r.hist_len + 2);
-    return RingTicket{top, top + 1, num_wg, false};
+    return RingTicket{top, top + 1, num_wg, false, false};
   }
   const unsigned g = wg % kTicketGroups;
   return RingTicket{r.tickets + g * kTicketStride, r.tickets + g * kTicketStride + 1,
-                    num_wg / kTicketGroups + (g < num_wg % kTicketGroups ? 1u : 0u), true};
+                    num_wg / kTicketGroups + (g < num_wg % kTicketGroups ? 1u : 0u), true, false};
 }
 
-// step 1: returns the value the ticket increment will depend on
+// step 1: returns the value the ticket increment will depend on (for the only
+// workgroup of the grid: its own max, the value the fold takes)
 __device__ __forceinline__ uint32_t ring_post_max(const RingTicket& t, uint32_t wg_max) {
+  if (t.solo) return wg_max;
+  // a few workgroups on one word: post directly (the read below saves atomics
+  // only where many workgroups share the word, and costs a round trip)
+  if (!t.two_level && t.members <= kSingleLevelGrid)
+    return __hip_atomic_fetch_max(t.gmax, wg_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t seen = __hip_atomic_load(t.gmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (wg_max <= seen) return seen;
   return __hip_atomic_fetch_max(t.gmax, wg_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -305,14 +320,57 @@ __device__ __forceinline__ uint32_t ticket_inc(uint32_t posted, float mult) {
   return (posted == 0xFFFFFFFFu ? 2u : 1u) + zero_after(__float_as_uint(mult));
 }
 
-// steps 2-4 (mult: the multiplier this workgroup read from the ring)
+// Max of the history without slot hist_idx (and 0).  The loads go out sixteen
+// at a time, independent of each other (a plain loop waits for each load before
+// the next).  Issuing them before the ticket, to overlap its round trips, measured
+// slower on small grids: the atomics queue behind them.
+__device__ __forceinline__ float hist_rest_max(const RingArgs& r) {
+  const float* hist = r.ring;
+  float h = 0.0f;
+  int i = 0;
+  for (; i + 16 <= r.hist_len; i += 16) {
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = hist[i + k];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (i + k != r.hist_idx) h = fmaxf(h, v[k]);
+  }
+  for (; i < r.hist_len; ++i)
+    if (i != r.hist_idx) h = fmaxf(h, hist[i]);
+  return h;
+}
+
+// step 4: this call's amax (FP32 bits) enters the history at hist_idx; s and
+// m = 1/s follow from the history's max h (max is exact, so its order does not
+// matter) when h is finite and non-zero.
+__device__ __forceinline__ void ring_fold(const RingArgs& r, uint32_t amax_bits, float hist_rest) {
+  const float amax = __uint_as_float(amax_bits);
+  r.ring[r.hist_idx] = amax;
+  const float h = fmaxf(hist_rest, amax);
+  if (h > 0.0f && h < __uint_as_float(0x7F800000u)) {
+    const float s = (h / r.fp8_max) / r.margin;   // correctly rounded FP32 divisions
+    r.ring[r.hist_len] = s;
+    r.ring[r.hist_len + 1] = 1.0f / s;
+  }
+  if (r.amax_out) *r.amax_out = amax;
+}
+
+// steps 2-4 (mult: the multiplier this workgroup read from the ring).  The only
+// workgroup of a grid goes straight to step 4 with its own max: every lane that
+// read the multiplier used it before the workgroup's last barrier, so the fold
+// cannot overtake those reads, and the ring's amax and ticket words stay zero.
 __device__ __forceinline__ void ring_finish(const RingArgs& r, const RingTicket& t, uint32_t posted, float mult,
                                             unsigned num_wg) {
+  uint32_t* amax_slot = reinterpret_cast<uint32_t*>(r.ring + r.hist_len + 2);
+  uint32_t* ticket = reinterpret_cast<uint32_t*>(r.ring + r.hist_len + 3);
+  if (t.solo) {
+    ring_fold(r, posted, hist_rest_max(r));
+    return;
+  }
   const uint32_t tg = __hip_atomic_fetch_add(t.gctr, ticket_inc(posted, mult), __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
   if (tg != t.members - 1) return;
-  uint32_t* amax_slot = reinterpret_cast<uint32_t*>(r.ring + r.hist_len + 2);
-  uint32_t* ticket = reinterpret_cast<uint32_t*>(r.ring + r.hist_len + 3);
   if (t.two_level) {
     const uint32_t gm = __hip_atomic_fetch_or(t.gmax, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(t.gmax, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -324,17 +382,7 @@ __device__ __forceinline__ void ring_finish(const RingArgs& r, const RingTicket&
     if (tt != ngroups - 1) return;
   }
   const uint32_t ab = __hip_atomic_fetch_or(amax_slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const float amax = __uint_as_float(ab);
-  float* hist = r.ring;
-  hist[r.hist_idx] = amax;
-  float h = 0.0f;
-  for (int i = 0; i < r.hist_len; ++i) h = fmaxf(h, hist[i]);
-  if (h > 0.0f && h < __uint_as_float(0x7F800000u)) {
-    const float s = (h / r.fp8_max) / r.margin;   // correctly rounded FP32 divisions
-    r.ring[r.hist_len] = s;
-    r.ring[r.hist_len + 1] = 1.0f / s;
-  }
-  if (r.amax_out) *r.amax_out = amax;
+  ring_fold(r, ab, hist_rest_max(r));
   __hip_atomic_store(amax_slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -321,6 +321,34 @@ def test_delayed_many_workgroups(layout, dtype, tmode):
         assert_ring_state(ring, tickets, oring, f"step {t}")
 
 
+@pytest.mark.parametrize("tmode", ["scratch", "none"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("layout", ["row", "transposed", "dual"])
+@pytest.mark.parametrize("cols", [128, 256, 2048, 2176, 4096, 4352])
+def test_delayed_small_grids(cols, layout, dtype, tmode):
+    """128-row inputs whose grids straddle the ticket modes: one workgroup (no
+    ticket, it folds its own max), 2 to 16 (a single-level ticket on the ring's
+    words, also with scratch) and 17 or more (the two-level ticket with scratch).
+    Transposed BF16 and dual launch one workgroup per 128 x 128 tile (1, 2, 16,
+    17, 32, 34 here), row-wise one per 32768 elements (1, 1, 8, 9, 16, 17).  Six
+    steps: codes, amax and ring exact, scratch left zero."""
+    ring = mxa.new_ring(4)
+    tickets = new_tickets(tmode)
+    oring = odl.Ring(4)
+    for t in range(6):
+        xb = workloads.delayed_step("act", t, rows=128, cols=cols)
+        x = make_input(workloads.bf16_to_f32(xb), dtype)
+        xs = f32_of_input(x)
+        q, qT, a = mxa.fp8_quantize_delayed(x, ring, t % 4, "e4m3", layout, 448.0, 1.0, amax=True, tickets=tickets)
+        wq, wqT, wa = odl.quantize_delayed(xs, "e4m3", oring, t % 4, 448.0, 1.0)
+        if q is not None:
+            assert_bytes_equal(host(q), wq, f"step {t} q")
+        if qT is not None:
+            assert_bytes_equal(host(qT), wqT, f"step {t} qT")
+        assert host(a)[0] == wa
+        assert_ring_state(ring, tickets, oring, f"step {t}")
+
+
 def test_delayed_scratch_shared_by_two_rings():
     """One ticket scratch serves calls on different rings in stream order; each
     ring follows its own host fold."""
