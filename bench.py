@@ -901,7 +901,9 @@ def summarize(args):
     calls = int(stats[0]["Calls"])
     lines = [f"# {args.kernel} -- {title}", "", f"command: {args.command}", "",
              f"kernel_avg_ns: {avg_ns:.0f}", f"kernel_min_ns: {float(stats[0]['MinNs']):.0f}",
-             f"kernel_max_ns: {float(stats[0]['MaxNs']):.0f}", f"kernel_calls: {calls}",
+             f"kernel_max_ns: {float(stats[0]['MaxNs']):.0f}", f"kernel_calls: {calls}" +
+             ("  (the timed steps, the warm-up and the clock probe: two seconds of the same launches)"
+              if args.workload == "dual" else ""),
              f"algorithmic_bytes_per_launch: {algo}", f"achieved_GBps_at_avg: {algo / avg_ns:.1f}",
              f"fraction_of_hbm_peak: {algo / avg_ns / HBM_PEAK_GBS:.4f}"]
     if args.fetch and args.write and args.copy_fetch and args.copy_write:
