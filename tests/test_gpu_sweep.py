@@ -1,8 +1,9 @@
 """Seeded random sweeps over shapes, formats, rules, input types and scale layouts,
 each case compared with the oracle exactly as the targeted tests do: quantized
-bytes and scales bit for bit, dequantized values bit for bit, GEMM results within
-the FP32 bounds of test_gpu_gemm (1e-3 relative Frobenius and the per-element
-accumulation bound).  The cases are drawn from one fixed seed, so a failure names a
+bytes and scales bit for bit, dequantized values bit for bit, delayed-scaling
+codes, amax and the whole ring bit for bit, GEMM results within the bounds of
+test_gpu_gemm and test_gpu_mm_fp8 (1e-3 relative Frobenius and the per-element
+accumulation bound), re-quantized GEMM outputs bit for bit.  The cases are drawn from one fixed seed, so a failure names a
 reproducible case; every failing case is listed, not just the first."""
 
 import numpy as np
@@ -10,7 +11,10 @@ import pytest
 import torch
 
 import workloads
+from oracle import delayed as odl
+from oracle import formats as ofmt
 from oracle import mx as omx
+from tests import test_gpu_mm_fp8 as tmm
 from tests.gpu_util import (assert_float_equal, f32_of_input, host, import_library, upload_bf16_bits,
                             upload_f16_from_f32, upload_f32, upload_u8)
 from tests.test_gpu_gemm import check_fp32
@@ -160,6 +164,126 @@ def test_gemm_random_cases():
             c = host(mxa.mx_gemm(upload_u8(qa), upload_u8(ga), upload_u8(qb), upload_u8(gb), fa, fb, alpha,
                                  out_dtype=torch.float32, scale_layout=layout))
             check_fp32(c, qa, sa, fa, qb, sb, fb, alpha=alpha)
+        except Exception as e:   # noqa: BLE001
+            failures.append(f"{case}: {type(e).__name__}: {str(e)[:160]}")
+    _report(failures, n)
+
+
+def test_delayed_random_cases():
+    """Per-tensor delayed scaling: 60 random cases of three successive steps (rows a
+    multiple of 32 up to 1536, columns of 8 up to 1536, every layout, FP32 / BF16 /
+    FP16 input, both formats, history length 1 to 40 with random slots, random
+    fp8_max and margin, with and without ticket scratch): codes, amax and the whole
+    ring after every step, the scratch left zero."""
+    rng = np.random.default_rng(20261206)
+    failures = []
+    n = 60
+    for i in range(n):
+        layout = ["row", "transposed", "dual"][rng.integers(3)]
+        dtype = ["f32", "bf16", "f16"][rng.integers(3)]
+        fmt = ["e4m3", "e5m2"][rng.integers(2)]
+        R, C = 32 * int(rng.integers(1, 49)), 8 * int(rng.integers(1, 193))
+        hist_len = int(rng.integers(1, 41))
+        fp8_max = float(rng.choice([448.0, 57344.0, 240.0, 1.0]))
+        margin = float(rng.choice([1.0, 2.0, 0.75]))
+        scratch = bool(rng.integers(2))
+        seed = int(rng.integers(1 << 30))
+        case = (f"{layout} {fmt} {dtype} {R}x{C} hist_len={hist_len} fp8_max={fp8_max} margin={margin} "
+                f"scratch={scratch} seed={seed}")
+        try:
+            ring = mxa.new_ring(hist_len)
+            tickets = mxa.new_tickets() if scratch else None
+            oring = odl.Ring(hist_len)
+            g = np.random.default_rng(seed)
+            for t in range(3):
+                idx = int(g.integers(hist_len))
+                x32 = (g.standard_normal((R, C)) * np.exp2(g.uniform(-12, 12))).astype(np.float32)
+                if dtype == "f32":
+                    x = upload_f32(x32)
+                elif dtype == "bf16":
+                    x = upload_bf16_bits(workloads.to_bf16_bits(x32.astype(np.float64)))
+                else:
+                    x = upload_f16_from_f32(x32)
+                xs = f32_of_input(x)
+                q, qT, a = mxa.fp8_quantize_delayed(x, ring, idx, fmt, layout, fp8_max, margin, amax=True,
+                                                    tickets=tickets)
+                wq, wqT, wa = odl.quantize_delayed(xs, fmt, oring, idx, fp8_max, margin)
+                ok = host(a)[0] == wa
+                if q is not None:
+                    ok = ok and np.array_equal(host(q), wq)
+                if qT is not None:
+                    ok = ok and np.array_equal(host(qT), wqT)
+                gr, wr = host(ring), oring.as_array()
+                ok = ok and np.array_equal(gr.view(np.uint32), np.asarray(wr, dtype=np.float32).view(np.uint32))
+                if tickets is not None:
+                    ok = ok and int(torch.count_nonzero(tickets)) == 0
+                if not ok:
+                    failures.append(f"{case} step {t}")
+                    break
+        except Exception as e:   # noqa: BLE001
+            failures.append(f"{case}: {type(e).__name__}: {str(e)[:160]}")
+    _report(failures, n)
+
+
+def test_mm_fp8_random_cases():
+    """Per-tensor FP8 GEMM: 80 random cases (M, N up to 600, K up to 2100, both formats,
+    every transpose combination, random scale, with and without bias, sometimes a
+    batch of 2 or 3 on either side)."""
+    rng = np.random.default_rng(20261207)
+    failures = []
+    n = 80
+    for i in range(n):
+        fmt = ["e4m3", "e5m2"][rng.integers(2)]
+        ta, tb = bool(rng.integers(2)), bool(rng.integers(2))
+        M, N = int(rng.integers(1, 600)), int(rng.integers(1, 600))
+        K = 16 * int(rng.integers(1, 132)) if rng.random() < 0.5 else 128 * int(rng.integers(1, 17))
+        scale = float(np.exp2(rng.integers(-12, 3)) * rng.choice([1.0, 1.25, 0.75]))
+        batch = [None, None, (2, None), (None, 3), (3, 3)][rng.integers(5)] if K <= 1024 else (None, None)
+        use_bias = bool(rng.integers(2))
+        seed = int(rng.integers(1 << 20))
+        case = f"{fmt} ta={ta} tb={tb} M={M} N={N} K={K} scale={scale} batch={batch} bias={use_bias} seed={seed}"
+        try:
+            ba, bb = batch if batch else (None, None)
+            a = tmm.codes(tmm.stored((M, K), ta, ba), seed, fmt)
+            b = tmm.codes(tmm.stored((K, N), tb, bb), seed + 1, fmt)
+            bias = (ofmt.f32_to_bf16_bits(workloads.random_tensor((N,), seed % 97, "normal") * 4)
+                    if use_bias else None)
+            tmm.check(tmm.run(a, b, fmt, scale, ta, tb, bias), a, b, fmt, scale, ta, tb, bias, case)
+        except Exception as e:   # noqa: BLE001
+            failures.append(f"{case}: {type(e).__name__}: {str(e)[:200]}")
+    _report(failures, n)
+
+
+def test_requant_random_cases():
+    """GEMM with MX re-quantization in the epilogue: 60 random cases (FP8 and FP4
+    operand pairs, M up to 600, N a multiple of 32 up to 608, K on both GEMM kernels,
+    every output format and rule, random alpha): codes, scales and amax bit for bit
+    against the oracle's row-wise quantizer applied to mx_gemm's FP32 output."""
+    rng = np.random.default_rng(20261208)
+    failures = []
+    n = 60
+    pairs = [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e2m1", "e2m1")]
+    for i in range(n):
+        fa, fb = pairs[rng.integers(len(pairs))]
+        fc = ["e4m3", "e5m2", "e2m1"][rng.integers(3)]
+        rc = ["floor", "ceil"][rng.integers(2)]
+        M, N = int(rng.integers(1, 600)), 32 * int(rng.integers(1, 20))
+        K = 512 * int(rng.integers(1, 4)) if rng.random() < 0.5 else 32 * int(rng.integers(1, 50))
+        alpha = float(rng.choice([1.0, 0.75, 1.0 / 32, 5.0]))
+        seed = int(rng.integers(1 << 30))
+        case = f"{fa}x{fb}->{fc} {rc} M={M} N={N} K={K} alpha={alpha} seed={seed}"
+        try:
+            A = workloads.random_tensor((M, K), seed, "normal")
+            B = workloads.random_tensor((N, K), seed + 1, "rows")
+            qa, sa = omx.quantize_rowwise(A, fa, "ceil")
+            qb, sb = omx.quantize_rowwise(B, fb, "ceil")
+            args = (upload_u8(qa), upload_u8(sa), upload_u8(qb), upload_u8(sb), fa, fb, alpha)
+            c32 = host(mxa.mx_gemm(*args, out_dtype=torch.float32))
+            q, s_, a = mxa.mx_gemm_requant(*args, fmt_c=fc, rule_c=rc, amax=True)
+            wq, ws = omx.quantize_rowwise(c32, fc, rc)
+            if not (np.array_equal(host(q), wq) and np.array_equal(host(s_), ws)
+                    and host(a)[0] == omx.tensor_amax(c32)):
+                failures.append(case)
         except Exception as e:   # noqa: BLE001
             failures.append(f"{case}: {type(e).__name__}: {str(e)[:160]}")
     _report(failures, n)
