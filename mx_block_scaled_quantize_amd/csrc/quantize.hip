@@ -890,24 +890,46 @@ __global__ __launch_bounds__(256) void dual_bf16_kernel(StripArgs a, int tiles_c
   uint8_t* const srl = reinterpret_cast<uint8_t*>(srow_lds) + wro * 4 + (wave & 1) * 2;
   uint8_t* const scl = reinterpret_cast<uint8_t*>(scol_lds) + wco * 4 + (wave >> 1) * 2;
   uint32_t tmax = 0;
+  const uint32_t cols = uint32_t(a.cols);
+  // whether the lane's 8 x 8 patch of tile t is in the matrix (rows and cols are
+  // multiples of 32: a quad (row blocks) and the lanes h = 4k .. 4k+3 (column
+  // blocks) are entirely in or out of range)
+  auto patch_ok = [&](int t) {
+    const int64_t tr = int64_t(t / tiles_c) * kDualTile, tc = int64_t(t % tiles_c) * kDualTile;
+    return t < ntiles && tr + wro + 8 * h < a.rows && tc + wco + 8 * g < a.cols;
+  };
+  auto load_patch = [&](int t, uint4 (&dst)[8]) {
+    const int64_t tr = int64_t(t / tiles_c) * kDualTile, tc = int64_t(t % tiles_c) * kDualTile;
+    // the wave's origin is uniform: a scalar base plus a 32-bit lane offset
+    // (the host keeps 64 * cols * 2 below 2^32)
+    const uint8_t* xb = static_cast<const uint8_t*>(a.x) + ((tr + wro) * a.cols + tc + wco) * 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4_t v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(xb + (uint32_t(8 * h + i) * cols + uint32_t(8 * g)) * 2u));
+      dst[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  };
+  // FP8: the next tile's input is loaded while this one converts and stores (32 more
+  // VGPRs, within the two waves per SIMD of the launch).  On a BF16 8192 x 4096
+  // input that measured 3% faster for FP8 and 4% slower for FP4, whose stores are
+  // half as large.
+  constexpr bool kPrefetch = kB == 8;
+  uint4 raw[8];
+  if constexpr (kPrefetch) {
+    if (patch_ok(blockIdx.x)) load_patch(blockIdx.x, raw);
+  }
   // one tile per workgroup, or several when the launch caps the grid
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t tr = int64_t(t / tiles_c) * kDualTile, tc = int64_t(t % tiles_c) * kDualTile;
-    // rows and cols are multiples of 32: a quad (row blocks) and the lanes
-    // h = 4k .. 4k+3 (column blocks) are entirely in or out of range
-    const bool ok = tr + wro + 8 * h < a.rows && tc + wco + 8 * g < a.cols;
+    const bool ok = patch_ok(t);
+    uint4 nxt[8];
+    if constexpr (kPrefetch) {
+      if (patch_ok(t + int(gridDim.x))) load_patch(t + int(gridDim.x), nxt);
+    } else if (ok) {
+      load_patch(t, raw);
+    }
     if (ok) {
-      // the wave's origin is uniform: a scalar base plus a 32-bit lane offset
-      // (the host keeps 64 * cols * 2 below 2^32)
-      const uint8_t* xb = static_cast<const uint8_t*>(a.x) + ((tr + wro) * a.cols + tc + wco) * 2;
-      const uint32_t cols = uint32_t(a.cols);
-      uint4 raw[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const u32x4_t v = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(xb + (uint32_t(8 * h + i) * cols + uint32_t(8 * g)) * 2u));
-        raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
-      }
       // ---- row-wise half
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -985,6 +1007,10 @@ __global__ __launch_bounds__(256) void dual_bf16_kernel(StripArgs a, int tiles_c
       }
     }
     if (t + int(gridDim.x) < ntiles) __syncthreads();   // the staging buffers are reused by the next tile
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) raw[i] = nxt[i];
+    }
   }
   if constexpr (AMAX) {
     const uint32_t wm = wave_max(tmax);
@@ -1201,7 +1227,9 @@ __global__ __launch_bounds__(256) void pt_col_bf16_kernel(StripArgs a, int tiles
   const RingTicket tk = ring_ticket(a.ring, blockIdx.x, gridDim.x);
   const int wro = (wave >> 1) * kPtWave, wco = (wave & 1) * kPtWave;       // wave offset in the tile
   uint32_t tmax = 0, posted = 0;
-  // one tile per workgroup, unless the launch caps the grid
+  // one tile per workgroup, unless the launch caps the grid (loading the next
+  // tile's input while this one converts and stores, as the FP8 dual does,
+  // measured 5% slower on a BF16 8192 x 4096 input)
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t tr = int64_t(t / tiles_c) * kPtTile, tc = int64_t(t % tiles_c) * kPtTile;
     // rows are a multiple of 32 and cols of 8: a lane's 8 x 8 block is in or out
