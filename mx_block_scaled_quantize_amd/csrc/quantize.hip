@@ -1283,16 +1283,22 @@ __global__ __launch_bounds__(256) void pt_col_bf16_kernel(StripArgs a, int tiles
     // post the workgroup's max now; the dependent ticket is taken after the stores
     if (last && threadIdx.x == 0) posted = ring_post_max(tk, umax(umax(red[0], red[1]), umax(red[2], red[3])));
     // transposed codes: 8 consecutive threads per 128-byte line (column c, 128 rows)
-#pragma unroll
-    for (int it = 0; it < kPtTile * kPtTile / 16 / 256; ++it) {
-      const int item = threadIdx.x + 256 * it;
+    auto store_piece = [&](int item) {
       const int c = item >> 3, pc = item & 7;
       if (tc + c < a.cols && tr + 16 * pc < a.rows) {
         const uint4 v = *reinterpret_cast<const uint4*>(qc_lds + c * kPtTile + 16 * pc);
         *reinterpret_cast<uint4*>(a.q_col + (tc + c) * a.rows + tr + 16 * pc) = v;
       }
+    };
+    if (!last) {
+#pragma unroll
+      for (int it = 0; it < kPtTile * kPtTile / 16 / 256; ++it) store_piece(threadIdx.x + 256 * it);
+      __syncthreads();   // the staging buffer is reused by the next tile
+    } else if (wave != 0) {
+      // the last tile's pieces go out from waves 1-3, so that wave 0 takes the ticket
+      // at once: a wave's atomics return only after its own earlier stores complete
+      for (int item = threadIdx.x - 64; item < kPtTile * kPtTile / 16; item += 192) store_piece(item);
     }
-    if (!last) __syncthreads();   // the staging buffer is reused by the next tile
   }
   if (threadIdx.x == 0) ring_finish(a.ring, tk, posted, mult, gridDim.x);
 }
