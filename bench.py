@@ -207,8 +207,10 @@ def copy_roof(torch, dev, stream, nbytes=64 << 20, sets=8, n=50):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 500 warm-up launches after the clock probe, 1000 timed (about 45 ms): with 5 and
+    # 200 the first launches after the probe, still slower, raised the average by 5%
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--mode", choices=["full", "dual", "delayed", "delayed_grad", "col", "sr", "fp6dual", "gemm",
