@@ -416,11 +416,16 @@ def gemm_calls(steps):
 # Memory-bound legs rotate through enough buffer sets that one call's data is
 # long gone from the 256 MiB last-level cache when it comes round again.
 CACHE_DEFEAT_BYTES = 768 << 20
+# ... and are warmed up with at least HBM_WARM launches and timed over at least
+# HBM_CALLS (a multiple of 32: whole 32-step delayed-scaling sequences): the
+# first launches after a pause run slower (5% on the dual after 5 warm-up launches).
+HBM_WARM, HBM_CALLS = 300, 320
 
 
 def time_rotating(make_set, call, per_call_bytes, n, warm, stream, torch, dist=False):
-    """time_calls over ceil(768 MiB / per_call_bytes) (2..16) buffer sets used in turn;
-    with dist, also the per-launch distribution."""
+    """time_calls over ceil(768 MiB / per_call_bytes) (2..16) buffer sets used in turn,
+    with at least HBM_WARM warm-up and HBM_CALLS timed launches; with dist, also the
+    per-launch distribution of n launches."""
     k = max(2, min(16, -(-CACHE_DEFEAT_BYTES // per_call_bytes)))
     sets = [make_set(i) for i in range(k)]
     idx = [0]
@@ -428,7 +433,7 @@ def time_rotating(make_set, call, per_call_bytes, n, warm, stream, torch, dist=F
     def fn():
         call(sets[idx[0] % k], idx[0])
         idx[0] += 1
-    t = time_calls(fn, n, warm, stream, torch)
+    t = time_calls(fn, max(n, HBM_CALLS), max(warm, HBM_WARM), stream, torch)
     d = launch_distribution(fn, n, stream, torch) if dist else None
     del sets
     return (t, k, d) if dist else (t, k)
