@@ -35,7 +35,9 @@
 //                       quad of lanes (DPP max) and a column block is 4 lanes
 //                       of a DPP row (row_ror max).  Both code copies are
 //                       staged in LDS and leave as 16-byte pieces of whole
-//                       128-byte lines; the scales leave as dwords.
+//                       128-byte lines; the scales leave as dwords.  Two
+//                       workgroups per CU walk the tiles; for FP8 each loads
+//                       its next tile's input while the current one converts.
 //   col_bf16_kernel     MX column-wise (optionally after the 32-point Hadamard
 //                       transform, butterflies across the quad), same staging
 //                       of the transposed codes; 256-row tiles for FP4 so that
