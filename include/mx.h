@@ -164,7 +164,8 @@ mx_status_t mx_quantize_dual(const void* x, mx_dtype_t in, int64_t rows, int64_t
  *
  * ring: caller-owned FP32 device buffer of MX_RING_WORDS(hist_len) = hist_len + 4
  *   words, the page's [hist n | scale | legacy | amax | done]:
- *     hist[0 .. hist_len-1]  the amax history;
+ *     hist[0 .. hist_len-1]  the amax history (amaxes: non-negative, never NaN;
+ *             a NaN placed there by the caller is passed over by the max);
  *     s       the dequantization scale (x ~ q * s);
  *     m       ("legacy") the multiplier the cast uses, m = 1 / s;
  *     amax    scratch that must read 0 before the first call;

@@ -456,6 +456,41 @@ def test_delayed_resume_from_saved_ring():
     assert torch.equal(saved, ring)
 
 
+@pytest.mark.parametrize("hist_len", [17, 4096])
+@pytest.mark.parametrize("cols", [128, 256, 4352])
+@pytest.mark.parametrize("tmode", ["scratch", "none"])
+def test_delayed_fold_of_a_preset_history(hist_len, cols, tmode):
+    """A ring resumed with arbitrary history entries -- +Inf, subnormals, zeros,
+    large and small normal values -- at the longest history and at one that is
+    not a multiple of the fold's 16-entry batches, on grids of one workgroup
+    (no ticket), two and 34 workgroups: the fold takes the max over the history
+    exactly as the host fold does, for slots at both ends and inside."""
+    g = np.random.default_rng(hist_len + cols)
+    hist = (g.standard_normal(hist_len) ** 2 * np.exp2(g.integers(-30, 30, size=hist_len))).astype(np.float32)
+    hist[g.integers(hist_len, size=4)] = 0.0
+    hist[g.integers(hist_len, size=2)] = np.float32(1e-40)     # subnormal
+    init = np.concatenate([hist, np.array([0.5, 2.0, 0.0, 0.0], dtype=np.float32)])
+    ring = torch.from_numpy(init.copy()).to("cuda")
+    tickets = new_tickets(tmode)
+    oring = odl.Ring.from_array(init)
+    slots = [0, hist_len - 1, hist_len // 2, 5]
+    for t, idx in enumerate(slots):
+        if t == 2:   # an Inf entry elsewhere holds s and m where they are
+            ring[(idx + 3) % hist_len] = float("inf")
+            oring.hist[(idx + 3) % hist_len] = np.inf
+        if t == 3:   # and once it is overwritten the max of the rest takes over again
+            ring[(slots[2] + 3) % hist_len] = 0.0
+            oring.hist[(slots[2] + 3) % hist_len] = 0.0
+        xb = workloads.delayed_step("act", 40 + t, rows=128, cols=cols)
+        x = upload_bf16_bits(xb)
+        _, qT, a = mxa.fp8_quantize_delayed(x, ring, idx, "e4m3", "transposed", 448.0, 1.0, amax=True,
+                                            tickets=tickets)
+        _, wqT, wa = odl.quantize_delayed(workloads.bf16_to_f32(xb), "e4m3", oring, idx, 448.0, 1.0)
+        assert_bytes_equal(host(qT), wqT, f"step {t} qT")
+        assert host(a)[0] == wa
+        assert_ring_state(ring, tickets, oring, f"step {t}")
+
+
 @pytest.mark.parametrize("dtype,layout,shape", [("f32", "dual", (64, 64)), ("bf16", "transposed", (64, 64)),
                                                 ("bf16", "transposed", (160, 200))])
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
