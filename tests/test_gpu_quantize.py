@@ -537,6 +537,26 @@ def test_activation_dual_full_size():
     assert (wsr == 0).sum() >= 16 and (wsc == 0).sum() >= 16
 
 
+@pytest.mark.parametrize("fmt,rule,shape", [("e5m2", "floor", (8192, 4096)), ("e2m1", "ceil", (8192, 4096)),
+                                             ("e4m3", "ceil", (4128, 4128)), ("e4m3", "floor", (2080, 8224))])
+def test_dual_multi_tile_workgroups(fmt, rule, shape):
+    """Inputs with more 128 x 128 tiles than the launch's two workgroups per CU, so
+    each workgroup walks several tiles (FP8: loading the next tile's input while it
+    converts the current one), with ragged last tile rows and columns in the
+    smaller shapes: every code, scale and the amax against the oracle."""
+    R, C = shape
+    x32 = workloads.random_tensor(shape, R + C, "wide")
+    x = upload_bf16_bits(workloads.to_bf16_bits(x32.astype(np.float64)))
+    xs = f32_of_input(x)
+    qr, sr, qc, sc, a = mxa.mx_quantize_dual(x, fmt, rule, amax=True)
+    wqr, wsr, wqc, wsc = omx.quantize_dual(xs, fmt, rule)
+    assert_bytes_equal(host(sr), wsr, "row scales")
+    assert_bytes_equal(host(qr), wqr, "row codes")
+    assert_bytes_equal(host(sc), wsc, "col scales")
+    assert_bytes_equal(host(qc), wqc, "col codes")
+    assert host(a)[0] == omx.tensor_amax(xs)
+
+
 @pytest.mark.parametrize("stream", ["act", "grad"])
 def test_delayed_full_size_32_steps(stream):
     """BF16 8192 x 4096 delayed scaling, 32 steps on one ring of 16 in the bench's
