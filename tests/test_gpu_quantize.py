@@ -349,6 +349,27 @@ def test_delayed_small_grids(cols, layout, dtype, tmode):
         assert_ring_state(ring, tickets, oring, f"step {t}")
 
 
+@pytest.mark.parametrize("tmode", ["scratch", "none"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_delayed_multi_tile_ragged(fmt, tmode):
+    """BF16 4128 x 4136 transposed: 33 x 33 tiles, more than the capped grid, so
+    some workgroups take two tiles (all waves store the first, waves 1-3 the
+    last), with a partial last tile row and column.  Three steps: every code,
+    the amax and the whole ring."""
+    ring = mxa.new_ring(16)
+    tickets = new_tickets(tmode)
+    oring = odl.Ring(16)
+    for t in range(3):
+        xb = workloads.delayed_step("act" if fmt == "e4m3" else "grad", 50 + t, rows=4128, cols=4136)
+        x = upload_bf16_bits(xb)
+        fp8_max = 448.0 if fmt == "e4m3" else 57344.0
+        _, qT, a = mxa.fp8_quantize_delayed(x, ring, t, fmt, "transposed", fp8_max, 1.0, amax=True, tickets=tickets)
+        _, wqT, wa = odl.quantize_delayed(workloads.bf16_to_f32(xb), fmt, oring, t, fp8_max, 1.0)
+        assert_bytes_equal(host(qT), wqT, f"step {t} qT")
+        assert host(a)[0] == wa
+        assert_ring_state(ring, tickets, oring, f"step {t}")
+
+
 def test_delayed_scratch_shared_by_two_rings():
     """One ticket scratch serves calls on different rings in stream order; each
     ring follows its own host fold."""
