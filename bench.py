@@ -213,7 +213,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--mode", choices=["full", "dual", "delayed", "delayed_grad", "col", "sr", "fp6dual", "gemm",
+    ap.add_argument("--mode", choices=["full", "dual", "delayed", "delayed_grad", "delayed_small", "col", "sr",
+                                       "fp6dual", "gemm",
                                        "copy"], default="full")
     ap.add_argument("--workload", default="dual", help="which workload --summarize describes")
     ap.add_argument("--summarize", metavar="OUT_MD")
@@ -261,6 +262,10 @@ def main():
         t = time_calls(lambda: dst.copy_(src), args.steps, args.warmup, stream, torch)
         print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "us": round(t * 1e6, 2),
                           "GB/s": round(2 * n / t / 1e9, 1)}), flush=True)
+        return
+    if args.mode == "delayed_small":   # the per-call cost of a launch-bound delayed-scaling call only
+        res = bench_delayed(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, streams=(), with_null=False)
+        print(json.dumps({"mode": args.mode, **res}), flush=True)
         return
     if args.mode in ("delayed", "delayed_grad"):
         res = bench_delayed(lib, sp, stream, dev, up_bf16, mxa, workloads, torch, args.steps,
