@@ -891,6 +891,9 @@ WORKLOADS = {
                 R8 * C4 * 2 + R8 * C4 + 80, QUANT_SOURCES),
     "delayed_grad": ("per-tensor delayed-scaling FP8 E5M2 cast (gradient stream), BF16 8192x4096 -> transposed "
                      "codes, ring of 16", R8 * C4 * 2 + R8 * C4 + 80, QUANT_SOURCES),
+    "delayed_small": ("per-tensor delayed-scaling FP8 E4M3 cast of a launch-bound BF16 128x256 tensor -> transposed "
+                      "codes, ring of 16 (two workgroups, single-level ticket)", 128 * 256 * 2 + 128 * 256 + 80,
+                      QUANT_SOURCES),
     "col": ("fixed-sign Hadamard + column-wise MXFP4 E2M1 quantization of one BF16 8192x4096 weight-gradient "
             "operand (8192 tokens), round-up scale", R8 * C4 * 2 + R8 * C4 // 2 + R8 * C4 // 32, QUANT_SOURCES),
     "sr": ("stochastic-rounding MXFP4 row-wise, BF16 8192x4096 + one uint32 word per element",
