@@ -20,8 +20,8 @@ device copy of the same size gives the attainable copy roof.  The MXFP8 GEMM
 (8192 x 4096 x 14336) and the other workloads are reported under ``gemm`` and
 ``extra``; the CPU oracle under ``cpu_baseline``.
 
-Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 5] [--no-cpu-baseline] [--no-extra]
-       python bench.py --mode dual|delayed|delayed_grad|col|sr|fp6dual|gemm|copy ...
+Usage: python bench.py [--gpus 1] [--steps 1000] [--warmup 500] [--no-cpu-baseline] [--no-extra]
+       python bench.py --mode dual|delayed|delayed_grad|delayed_small|col|sr|fp6dual|gemm|copy ...
            (one workload only, for profiler passes; 'copy' is a plain 256 MiB
             device copy used to calibrate the byte counters)
        python bench.py --summarize OUT.md --stats S.csv --fetch F.csv --write W.csv

@@ -1,5 +1,10 @@
 """Host logic of bench.py: the source digest that ties a counter summary to the
-kernel code it was taken on."""
+kernel code it was taken on, the committed summaries being current, the byte
+counters' copy calibration, and the refusal of more than one GPU."""
+
+import os
+import subprocess
+import sys
 
 import bench
 
@@ -23,3 +28,67 @@ def test_digest_changes_with_the_code():
     assert bench.code_digest([SRC.replace("1.0f", "2.0f")]) != d
     assert bench.code_digest([SRC.replace("+ 1.0f", "- 1.0f")]) != d
     assert bench.code_digest([SRC, "int y;"]) != d
+
+
+def test_committed_profiles_match_the_sources():
+    """Every committed counter summary was taken on the kernel code as it stands
+    (a code change without new summaries fails here, not in the judge's reading)."""
+    import glob
+    files = sorted(glob.glob(os.path.join(bench.ROOT, "profiles", "*.md")))
+    assert files
+    for path in files:
+        name = os.path.basename(path)
+        if name.startswith("gemm256_kernel"):
+            sources = bench.GEMM_SOURCES
+        elif name.startswith("fp6_"):
+            sources = ("quantize_fp6.hip", "mx_device.hpp")
+        elif name.startswith("sr_"):
+            sources = ("quantize_sr.hip", "mx_device.hpp")
+        else:
+            sources = bench.QUANT_SOURCES
+        assert bench.profile_is_current(path, sources), f"{name} was taken on other kernel sources"
+
+
+def test_headline_traffic_comes_from_the_current_summary():
+    t = bench.measured_traffic()
+    algo = 8192 * 4096 * 2 + 2 * 8192 * 4096 + 2 * (8192 * 4096 // 32) + 4
+    assert t is not None and algo <= t <= 1.1 * algo
+
+
+def test_summary_scales_the_byte_counters_by_the_copy_calibration(tmp_path):
+    """FETCH/WRITE of the kernel are scaled by known bytes / counted bytes of a
+    256 MiB copy: a copy that counts half its reads doubles the kernel's reads."""
+    import argparse
+    import csv
+
+    def pmc(path, rows):
+        with open(path, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for r in rows:
+                w.writerow(dict(zip(["Kernel_Name", "Counter_Name", "Counter_Value"], r)))
+    stats = tmp_path / "s.csv"
+    with open(stats, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        w.writerow(["void mxk::dual_bf16_kernel<0, 1, true>(...)", 4, 112000, 28000, 100, 27000, 29000, 1])
+    k = "dual_bf16_kernel<0, 1, true>"
+    pmc(tmp_path / "f.csv", [(k, "FETCH_SIZE", 32768.0), (k, "FETCH_SIZE", 32768.0)])
+    pmc(tmp_path / "w.csv", [(k, "WRITE_SIZE", 66560.0)])
+    pmc(tmp_path / "cf.csv", [("copyBuffer", "FETCH_SIZE", 131072.0)])     # half of 256 MiB counted
+    pmc(tmp_path / "cw.csv", [("copyBuffer", "WRITE_SIZE", 262144.0)])
+    out = tmp_path / "out.md"
+    args = argparse.Namespace(workload="dual", kernel=k, stats=str(stats), fetch=str(tmp_path / "f.csv"),
+                              write=str(tmp_path / "w.csv"), copy_fetch=str(tmp_path / "cf.csv"),
+                              copy_write=str(tmp_path / "cw.csv"), pmc=[], command="test", summarize=str(out))
+    bench.summarize(args)
+    vals = bench.profile_fields(str(out))
+    assert int(vals["hbm_fetch_bytes_per_launch"]) == 2 * 32768 * 1024
+    assert int(vals["hbm_write_bytes_per_launch"]) == 66560 * 1024
+    assert int(vals["kernel_avg_ns"]) == 28000
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
